@@ -1,0 +1,181 @@
+"""CPU oracle for the Maglev attention + recurrent K/V injection path.
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product library never does.
+
+The arithmetic lives in `maglev_oracle.c` (plain C, double precision, OpenMP),
+compiled by `build()` with gcc. This module only marshals arrays: every input
+is converted to float64 holding exactly the stored value (bf16 or fp32), and
+every result comes back as float64 numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "maglev_oracle.c")
+_LIB = os.path.join(_HERE, "libmaglev_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, IEEE semantics kept: no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(ctypes.c_double)
+        I64 = ctypes.c_int64
+        I32 = ctypes.c_int
+        D = ctypes.c_double
+        PI64 = ctypes.POINTER(ctypes.c_int64)
+        L.oracle_round_bf16.argtypes = [D]
+        L.oracle_round_bf16.restype = D
+        L.oracle_mem_project.argtypes = [I64, I64, I32, I32, I32, I32, P, P, P, P, P]
+        L.oracle_mem_project.restype = None
+        L.oracle_swa_inject_fwd.argtypes = [I64, I64, I32, I32, I64, I64, D, D,
+                                            P, P, P, P, P, P, P, P]
+        L.oracle_swa_inject_fwd.restype = None
+        L.oracle_swa_inject_bwd.argtypes = [I64, I64, I32, I32, I32, I64, I64, D, D,
+                                            P, P, P, P, P, P, P, P,
+                                            P, P, P, P, P, P, P]
+        L.oracle_swa_inject_bwd.restype = None
+        L.oracle_consistency_loss.argtypes = [I64, I32, D, P, P, P, P]
+        L.oracle_consistency_loss.restype = D
+        L.oracle_decode_step.argtypes = [I64, I32, I32, I64, D, D, I32,
+                                         P, P, P, P, P, P, P, P, PI64, P]
+        L.oracle_decode_step.restype = None
+        L.oracle_swa_inject_fwd_rows.argtypes = [I64, I64, I32, I32, I64, I64, D, D,
+                                                 P, P, P, P, P, P, I64, PI64, P, P]
+        L.oracle_swa_inject_fwd_rows.restype = None
+        _lib = L
+    return _lib
+
+
+def f64(x) -> np.ndarray:
+    """Exact float64 copy of a torch tensor (any float dtype) or array-like."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags.c_contiguous
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def round_bf16(x: float) -> float:
+    return float(_load().oracle_round_bf16(float(x)))
+
+
+def mem_project(m, W_Km, W_Vm, H: int, Dh: int, shift: int = 1):
+    """kmem, vmem [B,T,H,Dh] from m [B,T,d] (shift=1: row t reads m[t-1], row 0 is zero)."""
+    m, WK, WV = f64(m), f64(W_Km), f64(W_Vm)
+    B, T, d = m.shape
+    kmem = np.empty((B, T, H, Dh))
+    vmem = np.empty((B, T, H, Dh))
+    _load().oracle_mem_project(B, T, H, Dh, d, int(shift), _p(m), _p(WK), _p(WV), _p(kmem), _p(vmem))
+    return kmem, vmem
+
+
+def swa_inject_fwd(q, k, v, kmem, vmem, gate_logit, W: int, pos0: int = 0,
+                   rope_base: float = 10000.0, scale: float = 0.0):
+    """O [B,T,H,Dh] and lse [B,H,T]."""
+    q, k, v, km, vm, g = (f64(a) for a in (q, k, v, kmem, vmem, gate_logit))
+    B, T, H, Dh = q.shape
+    o = np.empty((B, T, H, Dh))
+    lse = np.empty((B, H, T))
+    _load().oracle_swa_inject_fwd(B, T, H, Dh, int(W), int(pos0), float(rope_base), float(scale),
+                                  _p(q), _p(k), _p(v), _p(km), _p(vm), _p(g), _p(o), _p(lse))
+    return o, lse
+
+
+def swa_inject_fwd_rows(q, k, v, kmem, vmem, gate_logit, W: int, rows, pos0: int = 0,
+                        rope_base: float = 10000.0, scale: float = 0.0):
+    """O and lse of selected queries; rows is an [n,3] array of (b, h, i)."""
+    q, k, v, km, vm, g = (f64(a) for a in (q, k, v, kmem, vmem, gate_logit))
+    B, T, H, Dh = q.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    n = rows.shape[0]
+    o = np.empty((n, Dh))
+    lse = np.empty((n,))
+    _load().oracle_swa_inject_fwd_rows(B, T, H, Dh, int(W), int(pos0), float(rope_base),
+                                       float(scale), _p(q), _p(k), _p(v), _p(km), _p(vm), _p(g),
+                                       n, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                       _p(o), _p(lse))
+    return o, lse
+
+
+def swa_inject_bwd(q, k, v, m_prime, W_Km, W_Vm, gate_logit, dO, W: int, pos0: int = 0,
+                   rope_base: float = 10000.0, scale: float = 0.0):
+    """Gradients of the whole layer path (shift, projection, mix, attention).
+
+    Returns dict with dq, dk, dv [B,T,H,Dh], dm_prime [B,T,d], dW_Km, dW_Vm [H*Dh,d], dgate [H].
+    """
+    q, k, v, mp, WK, WV, g, dO = (f64(a) for a in (q, k, v, m_prime, W_Km, W_Vm, gate_logit, dO))
+    B, T, H, Dh = q.shape
+    d = mp.shape[-1]
+    out = {
+        "dq": np.empty_like(q), "dk": np.empty_like(q), "dv": np.empty_like(q),
+        "dm_prime": np.empty((B, T, d)), "dW_Km": np.empty((H * Dh, d)),
+        "dW_Vm": np.empty((H * Dh, d)), "dgate": np.empty((H,)),
+    }
+    _load().oracle_swa_inject_bwd(B, T, H, Dh, d, int(W), int(pos0), float(rope_base), float(scale),
+                                  _p(q), _p(k), _p(v), _p(mp), _p(WK), _p(WV), _p(g), _p(dO),
+                                  _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dm_prime"]),
+                                  _p(out["dW_Km"]), _p(out["dW_Vm"]), _p(out["dgate"]))
+    return out
+
+
+def consistency_loss(m, m_prime, lam: float):
+    """(loss, dm, dm_prime) for L = lam/(N sqrt d) * sum (m - m')^2 over N rows of width d."""
+    m, mp = f64(m), f64(m_prime)
+    d = m.shape[-1]
+    N = m.size // d
+    dm = np.empty_like(m)
+    dmp = np.empty_like(m)
+    loss = _load().oracle_consistency_loss(N, d, float(lam), _p(m), _p(mp), _p(dm), _p(dmp))
+    return float(loss), dm, dmp
+
+
+def decode_step(q, k, v, kmem, vmem, gate_logit, kcache: np.ndarray, vcache: np.ndarray, pos,
+                rope_base: float = 10000.0, scale: float = 0.0, ring_bf16: bool = True):
+    """One decode step; kcache/vcache (float64 [Bs,H,W,Dh]) are updated in place. Returns o."""
+    q, k, v, km, vm, g = (f64(a) for a in (q, k, v, kmem, vmem, gate_logit))
+    assert kcache.dtype == np.float64 and kcache.flags.c_contiguous
+    assert vcache.dtype == np.float64 and vcache.flags.c_contiguous
+    Bs, H, W, Dh = kcache.shape
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(Bs))
+    o = np.empty((Bs, H, Dh))
+    _load().oracle_decode_step(Bs, H, Dh, W, float(rope_base), float(scale), int(bool(ring_bf16)),
+                               _p(q), _p(k), _p(v), _p(km), _p(vm), _p(g), _p(kcache), _p(vcache),
+                               pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(o))
+    return o
+
+
+def omp_threads() -> int:
+    """Threads the oracle's OpenMP regions use (OMP_NUM_THREADS or all cores)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.strip().isdigit():
+        return int(env)
+    return os.cpu_count() or 1
