@@ -1,0 +1,214 @@
+/*
+ * maglev.h -- C ABI of the MI355X (gfx950) library for the Maglev decoder-P
+ * attention path: causal sliding-window attention with recurrent K/V
+ * injection, its backward, the memory-consistency loss and the recurrent
+ * decode step on a W-slot ring cache.
+ *
+ * Sources (web summaries of the preprint "Maglev: Sliding Recurrent Memory"):
+ *   [R-bg]   paper.rainbus.top, "Maglev：滑动窗口循环记忆", section 前置知识
+ *            (sliding-window attention over the W most recent tokens; KV cache;
+ *            feature-consistency loss; RoPE on both the local and the injected
+ *            key before mixing).
+ *   [R-mot]  same page, section 研究动机 (interface p(x_{t+1}, m_t | x_{t-W+1:t},
+ *            M_{t-1}); memory window of W entries; cache cost equal to SWA).
+ *   [R-core] same page, section 核心方法 (decoder P is sliding-window only, W=512;
+ *            the shifted memory goes through a shared projection into K/V
+ *            features mixed into the existing cache entries; no extra slots).
+ *   [R-step] same page, section 方法步骤详情 (P(x_{1:T}, m'_{0:T-1}) with m'_0 = 0;
+ *            recurrent K/V features from W^rec m'_{t-1}; gated mix; attention
+ *            over the W most recent mixed entries; loss
+ *            1/|I| sum_t [CE + lambda ||m_t - m'_t||^2 / sqrt(d)]; recurrent
+ *            inference m_t = P(x_{t-W+1:t}, M_{t-1})).
+ *   [G-train] gist.science, "Technische Samenvatting: Maglev - Sliding Recurrent
+ *            Memory", section Trainingsmechanisme: Lifted Parallel Training
+ *            (two parallel passes replace the sequential unroll).
+ *   [G-inf]  same page, section Inferentiemechanisme (K/V injection through
+ *            learned projections and gates; bounded decode cost).
+ *
+ * Mixing form implemented (the pages leave it open; one summary prints a
+ * gated variant with a local gate and a normalised memory key):
+ *   kmem_j = W_Km m'_{j-1},  vmem_j = W_Vm m'_{j-1}   (m'_{-1} := 0)
+ *   k~_j   = R_j k_j + s_h R_j kmem_j,   v~_j = v_j + s_h vmem_j,
+ *   s_h    = sigmoid(gate_logit[h]), one float32 logit per head,
+ *   O_i    = sum_{j = max(0, i-W+1)}^{i} softmax_j(scale <R_i q_i, k~_j>) v~_j.
+ * R_p rotates channel pair (c, c + Dh/2) by angle p * base^(-2c/Dh) (p = pos0 + t).
+ *
+ * Common conventions
+ *   - Layouts are row-major: activations [B,T,H,Dh] (the [B,T,d_model] tensor
+ *     viewed per head), memories [B,T,d], projection weights [H*Dh, d]
+ *     (the weight of a linear layer d -> H*Dh), lse [B,H,T], ring caches
+ *     [Bs,H,W,Dh].
+ *   - Every pointer is a DEVICE pointer unless stated, owned by the caller; the
+ *     library never frees caller memory and keeps no pointer after a call.
+ *   - All work is enqueued on `stream`; calls are asynchronous and do not
+ *     synchronise. Device faults surface at the caller's next synchronisation.
+ *   - Element dtype: MAGLEV_F32 (float) or MAGLEV_BF16 (bfloat16) for the
+ *     activation tensors named "dtype" below; gate logits, lse, loss and every
+ *     parameter gradient are float32. Arithmetic accumulates in float32.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error the call returns a status other than MAGLEV_OK and writes nothing.
+ *   - The library keeps one internal device table per (device, Dh, rope_base):
+ *     float32 cos/sin of the RoPE angles, computed on the host in double
+ *     precision. It is created or grown on first use (a synchronous upload);
+ *     call maglev_prepare() before capturing a HIP graph.
+ */
+#ifndef MAGLEV_H
+#define MAGLEV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAGLEV_ABI_VERSION 1
+
+typedef enum {
+    MAGLEV_OK = 0,
+    MAGLEV_ERR_INVALID_VALUE = 1, /* bad shape, NULL pointer, bad enum */
+    MAGLEV_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. Dh not in {64,128}) */
+    MAGLEV_ERR_MISALIGNED = 3,    /* a pointer is not 16-byte aligned */
+    MAGLEV_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than the query says */
+    MAGLEV_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} maglev_status_t;
+
+typedef enum { MAGLEV_F32 = 0, MAGLEV_BF16 = 1 } maglev_dtype_t;
+
+/* Geometry of one attention layer call.
+ *   B, T      batch and sequence length (T >= 1)
+ *   H, Dh     heads and head width; Dh in {64, 128}
+ *   d         width of the memory m (d_model); multiple of 16
+ *   W         window: query i sees keys max(0, i-W+1) .. i (W >= 1)
+ *   pos0      absolute position of t = 0 (RoPE angle uses pos0 + t), >= 0
+ *   rope_base RoPE base (10000 for nanochat); <= 0 disables the rotation
+ *   scale     softmax scale; <= 0 selects 1/sqrt(Dh)
+ *   dtype     maglev_dtype_t of the activation tensors */
+typedef struct {
+    int64_t B, T;
+    int32_t H, Dh, d, W;
+    int64_t pos0;
+    float rope_base;
+    float scale;
+    int32_t dtype;
+} maglev_geom_t;
+
+/* Memory projection with the one-step shift ([R-step]: P consumes m'_{0:T-1}
+ * with m'_0 = 0; [R-core]: the shifted memory passes through a shared
+ * projection into K/V features).
+ *   shift = 1: input row (b,t) is m[b,t-1], row (b,0) is zero;
+ *   shift = 0: input row (b,t) is m[b,t] (decode injects m_{t-1} directly).
+ *   m [B,T,d] dtype; W_Km, W_Vm [H*Dh, d] dtype;
+ *   kmem, vmem [B,T,H,Dh] dtype, written: kmem = input W_Km^T, vmem = input W_Vm^T.
+ * Uses g->B, T, H, Dh, d, dtype. */
+maglev_status_t maglev_mem_project(const maglev_geom_t *g, int shift, const void *m,
+                                   const void *W_Km, const void *W_Vm, void *kmem, void *vmem,
+                                   hipStream_t stream);
+
+/* Forward of the injected sliding-window attention ([R-bg], [R-core], [R-step]):
+ * rotate q, form k~ and v~ as above, attend over the W most recent mixed
+ * entries (fully masked key tiles are skipped).
+ *   q, k, v, kmem, vmem [B,T,H,Dh] dtype (kmem/vmem from maglev_mem_project);
+ *   gate_logit [H] float32;
+ *   o [B,T,H,Dh] dtype, written;
+ *   lse [B,H,T] float32, written (log-sum-exp of the scaled scores; may be NULL
+ *   when no backward follows). */
+maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *k,
+                                      const void *v, const void *kmem, const void *vmem,
+                                      const float *gate_logit, void *o, float *lse,
+                                      hipStream_t stream);
+
+/* Bytes of device workspace maglev_swa_inject_bwd needs for this geometry
+ * (0 on invalid geometry). */
+size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g);
+
+/* Backward of the layer path: attention, mixing, shift and projection (the
+ * chain rule through the forward above; [R-step], [G-train]).
+ * Inputs: the forward's q, k, v, kmem, vmem, gate_logit, o, lse; the upstream
+ * gradient dO [B,T,H,Dh] dtype; m_prime [B,T,d] dtype (UNshifted, as given to
+ * maglev_mem_project with shift = 1); W_Km, W_Vm [H*Dh, d] dtype.
+ * Outputs:
+ *   dq, dk, dv [B,T,H,Dh] dtype (overwritten);
+ *   dm_prime [B,T,d] float32: gradient w.r.t. m'; row T-1 gets no injection
+ *     gradient (it is never consumed);
+ *   dW_Km, dW_Vm [H*Dh, d] float32; dgate [H] float32 (w.r.t. the logits).
+ * accumulate: bit 0 -> dm_prime +=, bit 1 -> dW_Km/dW_Vm +=, bit 2 -> dgate +=;
+ *   a clear bit overwrites.
+ * workspace: device buffer of at least maglev_swa_inject_bwd_workspace(g)
+ *   bytes, owned by the caller; contents are scratch on return.
+ * The result is deterministic: no floating-point atomics are used. */
+maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *k,
+                                      const void *v, const void *kmem, const void *vmem,
+                                      const float *gate_logit, const void *o, const float *lse,
+                                      const void *dO, const void *m_prime, const void *W_Km,
+                                      const void *W_Vm, void *dq, void *dk, void *dv,
+                                      float *dm_prime, float *dW_Km, float *dW_Vm, float *dgate,
+                                      unsigned accumulate, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace maglev_consistency_loss needs (0 on invalid sizes). */
+size_t maglev_consistency_loss_workspace(int64_t N, int32_t d);
+
+/* Memory-consistency loss ([R-core], [R-step]):
+ *   loss = lambda / (N sqrt(d)) * sum_{n,e} (m - m')^2     (float32 scalar)
+ *   dm = 2 lambda (m - m') / (N sqrt(d)),  dm_prime = -dm   (float32 [N,d])
+ *   m, m_prime [N, d] dtype; loss: device float32 scalar (written, or += when
+ *   accumulate bit 2 is set); dm / dm_prime may be NULL; accumulate bit 0 ->
+ *   dm +=, bit 1 -> dm_prime +=. d must be a multiple of 8.
+ * The reduction is two-stage and deterministic. */
+maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int32_t dtype,
+                                        const void *m, const void *m_prime, float *loss,
+                                        float *dm, float *dm_prime, unsigned accumulate,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Bytes of device workspace maglev_decode_step needs (0 on invalid sizes). */
+size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W);
+
+/* One recurrent decode step of one layer ([R-step] recurrent inference,
+ * [R-mot] W-entry window, [G-inf] memory carried in the ordinary K/V cache).
+ * Stream b is at absolute position p = pos[b] (read on the device, not
+ * advanced). The new entry
+ *   k~ = R_p k + s_h R_p kmem,  v~ = v + s_h vmem   (kmem/vmem: maglev_mem_project
+ *   of m_{t-1} with shift = 0, T = 1)
+ * is written to ring slot p mod W; then R_p q attends over the valid slots
+ * (slot s holds position p - ((p - s) mod W), valid iff that is >= 0).
+ *   q, k, v, kmem, vmem [Bs,H,Dh] dtype; gate_logit [H] float32;
+ *   kcache, vcache [Bs,H,W,Dh] dtype, read and updated in place;
+ *   pos [Bs] int64 device; o [Bs,H,Dh] dtype, written.
+ * workspace: device buffer of at least maglev_decode_workspace() bytes, owned
+ *   by the caller (per-split partial softmax state; scratch on return).
+ * The ring holds dtype values: the new entry is rounded once (ties to even).
+ * The RoPE angle of the new position is evaluated on the device in double
+ * precision, so no table bounds the position. Positions must be >= 0. */
+maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
+                                   float rope_base, float scale, int32_t dtype, const void *q,
+                                   const void *k, const void *v, const void *kmem,
+                                   const void *vmem, const float *gate_logit, void *kcache,
+                                   void *vcache, const int64_t *pos, void *o, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/* pos[b] += 1 for b < Bs on the device (moves every stream to its next ring
+ * slot; kept separate so one decode step can be captured and replayed). */
+maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream);
+
+/* Ensure the RoPE table for (Dh, rope_base) covers positions [0, max_pos) on
+ * the current device. Synchronous; call before HIP-graph capture. */
+maglev_status_t maglev_prepare(int32_t Dh, float rope_base, int64_t max_pos);
+
+/* Human-readable name of a status code (static storage). */
+const char *maglev_status_string(maglev_status_t status);
+
+/* Text of the last HIP error seen by this thread (static per thread). */
+const char *maglev_last_error(void);
+
+/* MAGLEV_ABI_VERSION of the built library. */
+int maglev_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAGLEV_H */

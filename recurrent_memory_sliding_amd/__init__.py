@@ -1,0 +1,272 @@
+"""Python binding of libmaglev.so, the MI355X (gfx950) library for the Maglev
+decoder-P attention path with recurrent K/V injection.
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks their dtype/shape/contiguity, and calls the C entry
+point of the same name on the current torch stream. All arithmetic runs in
+the library's HIP kernels; there is no other code path. If the library has
+not been built, every call raises MaglevError.
+
+Build:  python -m recurrent_memory_sliding_amd.build
+C ABI:  include/maglev.h
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MaglevError", "MAGLEV_F32", "MAGLEV_BF16", "lib", "library_path",
+    "maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
+    "maglev_swa_inject_bwd_workspace", "maglev_consistency_loss",
+    "maglev_consistency_loss_workspace", "maglev_decode_step", "maglev_decode_workspace",
+    "maglev_decode_advance", "maglev_prepare", "maglev_abi_version",
+]
+
+MAGLEV_F32 = 0
+MAGLEV_BF16 = 1
+_DT = {torch.float32: MAGLEV_F32, torch.bfloat16: MAGLEV_BF16}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmaglev.so")
+_lib = None
+
+
+class MaglevError(RuntimeError):
+    pass
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64),
+        ("H", ctypes.c_int32), ("Dh", ctypes.c_int32), ("d", ctypes.c_int32), ("W", ctypes.c_int32),
+        ("pos0", ctypes.c_int64), ("rope_base", ctypes.c_float), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises MaglevError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MaglevError("libmaglev.so is not built; run: python -m recurrent_memory_sliding_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, sz, i32, i64, f32, u32 = (ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                      ctypes.c_int64, ctypes.c_float, ctypes.c_uint)
+        G = ctypes.POINTER(Geom)
+        sig = {
+            "maglev_mem_project": ([G, ctypes.c_int, vp, vp, vp, vp, vp, vp], i32),
+            "maglev_swa_inject_fwd": ([G, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+            "maglev_swa_inject_bwd_workspace": ([G], sz),
+            "maglev_swa_inject_bwd": ([G] + [vp] * 19 + [u32, vp, sz, vp], i32),
+            "maglev_consistency_loss_workspace": ([i64, i32], sz),
+            "maglev_consistency_loss": ([i64, i32, f32, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp], i32),
+            "maglev_decode_workspace": ([i32, i32, i32, i32], sz),
+            "maglev_decode_step": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 10 + [vp, sz, vp], i32),
+            "maglev_decode_advance": ([i32, vp, vp], i32),
+            "maglev_prepare": ([i32, f32, i64], i32),
+            "maglev_status_string": ([i32], ctypes.c_char_p),
+            "maglev_last_error": ([], ctypes.c_char_p),
+            "maglev_abi_version": ([], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise MaglevError("%s failed: %s (%s)" % (what, L.maglev_status_string(status).decode(),
+                                                  L.maglev_last_error().decode()))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise MaglevError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise MaglevError("tensors must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise MaglevError("dtype must be float32 or bfloat16, got %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _same(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t is not None and t.dtype != ref.dtype:
+            raise MaglevError("mixed activation dtypes")
+
+
+def make_geom(B, T, H, Dh, d, W, pos0=0, rope_base=10000.0, scale=0.0, dtype=MAGLEV_BF16) -> Geom:
+    return Geom(B, T, H, Dh, d, W, pos0, rope_base, scale, dtype)
+
+
+def maglev_abi_version() -> int:
+    return lib().maglev_abi_version()
+
+
+def maglev_prepare(Dh: int, rope_base: float, max_pos: int):
+    """Make the RoPE table cover positions [0, max_pos) (call before graph capture)."""
+    _check(lib().maglev_prepare(Dh, rope_base, max_pos), "maglev_prepare")
+
+
+def maglev_mem_project(m, W_Km, W_Vm, H: int, Dh: int, shift: int = 1, kmem=None, vmem=None,
+                       stream=None):
+    """kmem, vmem [B,T,H,Dh] = (m shifted by `shift` rows) projected by W_Km, W_Vm."""
+    _dev(m, W_Km, W_Vm, kmem, vmem)
+    _same(m, W_Km, W_Vm, kmem, vmem)
+    B, T, d = m.shape
+    if tuple(W_Km.shape) != (H * Dh, d) or tuple(W_Vm.shape) != (H * Dh, d):
+        raise MaglevError("W_Km / W_Vm must be [H*Dh, d]")
+    kmem = torch.empty((B, T, H, Dh), dtype=m.dtype, device=m.device) if kmem is None else kmem
+    vmem = torch.empty((B, T, H, Dh), dtype=m.dtype, device=m.device) if vmem is None else vmem
+    g = make_geom(B, T, H, Dh, d, 1, dtype=_dtype_code(m))
+    _check(lib().maglev_mem_project(ctypes.byref(g), shift, _ptr(m), _ptr(W_Km), _ptr(W_Vm),
+                                    _ptr(kmem), _ptr(vmem), _stream(stream)), "maglev_mem_project")
+    return kmem, vmem
+
+
+def maglev_swa_inject_fwd(q, k, v, kmem, vmem, gate_logit, W: int, pos0: int = 0,
+                          rope_base: float = 10000.0, scale: float = 0.0, d: int = 0, o=None,
+                          lse=None, need_lse: bool = True, stream=None):
+    """O [B,T,H,Dh] and lse [B,H,T] (float32; None when need_lse is False)."""
+    _dev(q, k, v, kmem, vmem, gate_logit, o, lse)
+    _same(q, k, v, kmem, vmem, o)
+    B, T, H, Dh = q.shape
+    if gate_logit.dtype != torch.float32 or gate_logit.numel() != H:
+        raise MaglevError("gate_logit must be float32 [H]")
+    o = torch.empty_like(q) if o is None else o
+    if need_lse and lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    g = make_geom(B, T, H, Dh, d or H * Dh, W, pos0, rope_base, scale, _dtype_code(q))
+    _check(lib().maglev_swa_inject_fwd(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(kmem),
+                                       _ptr(vmem), _ptr(gate_logit), _ptr(o),
+                                       _ptr(lse) if need_lse else None, _stream(stream)),
+           "maglev_swa_inject_fwd")
+    return o, lse
+
+
+def maglev_swa_inject_bwd_workspace(B, T, H, Dh, d, W, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, d, W, dtype=dtype)
+    return int(lib().maglev_swa_inject_bwd_workspace(ctypes.byref(g)))
+
+
+def maglev_swa_inject_bwd(q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km, W_Vm,
+                          W: int, pos0: int = 0, rope_base: float = 10000.0, scale: float = 0.0,
+                          accumulate: int = 0, out: Optional[dict] = None, workspace=None,
+                          stream=None) -> dict:
+    """Gradients dq, dk, dv (activation dtype), dm_prime, dW_Km, dW_Vm, dgate (float32)."""
+    _dev(q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km, W_Vm, workspace)
+    _same(q, k, v, kmem, vmem, o, dO, m_prime, W_Km, W_Vm)
+    B, T, H, Dh = q.shape
+    d = m_prime.shape[-1]
+    dev = q.device
+    if out is None:
+        out = {}
+    f32 = torch.float32
+    out.setdefault("dq", torch.empty_like(q))
+    out.setdefault("dk", torch.empty_like(q))
+    out.setdefault("dv", torch.empty_like(q))
+    out.setdefault("dm_prime", torch.empty((B, T, d), dtype=f32, device=dev))
+    out.setdefault("dW_Km", torch.empty((H * Dh, d), dtype=f32, device=dev))
+    out.setdefault("dW_Vm", torch.empty((H * Dh, d), dtype=f32, device=dev))
+    out.setdefault("dgate", torch.empty((H,), dtype=f32, device=dev))
+    _dev(*out.values())
+    g = make_geom(B, T, H, Dh, d, W, pos0, rope_base, scale, _dtype_code(q))
+    need = int(lib().maglev_swa_inject_bwd_workspace(ctypes.byref(g)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().maglev_swa_inject_bwd(
+        ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
+        _ptr(o), _ptr(lse), _ptr(dO), _ptr(m_prime), _ptr(W_Km), _ptr(W_Vm), _ptr(out["dq"]),
+        _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dm_prime"]), _ptr(out["dW_Km"]),
+        _ptr(out["dW_Vm"]), _ptr(out["dgate"]), accumulate, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "maglev_swa_inject_bwd")
+    return out
+
+
+def maglev_consistency_loss_workspace(N: int, d: int) -> int:
+    return int(lib().maglev_consistency_loss_workspace(N, d))
+
+
+def maglev_consistency_loss(m, m_prime, lam: float, loss=None, dm=None, dm_prime=None,
+                            want_grads: bool = True, accumulate: int = 0, workspace=None,
+                            stream=None):
+    """(loss [1] float32, dm, dm_prime [..., d] float32)."""
+    _dev(m, m_prime, loss, dm, dm_prime, workspace)
+    _same(m, m_prime)
+    d = m.shape[-1]
+    N = m.numel() // d
+    dev = m.device
+    loss = torch.empty((1,), dtype=torch.float32, device=dev) if loss is None else loss
+    if want_grads:
+        dm = torch.empty(m.shape, dtype=torch.float32, device=dev) if dm is None else dm
+        dm_prime = torch.empty(m.shape, dtype=torch.float32, device=dev) if dm_prime is None else dm_prime
+    need = int(lib().maglev_consistency_loss_workspace(N, d))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().maglev_consistency_loss(N, d, lam, _dtype_code(m), _ptr(m), _ptr(m_prime),
+                                         _ptr(loss), _ptr(dm), _ptr(dm_prime), accumulate,
+                                         _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream)), "maglev_consistency_loss")
+    return loss, dm, dm_prime
+
+
+def maglev_decode_workspace(Bs: int, H: int, Dh: int, W: int) -> int:
+    return int(lib().maglev_decode_workspace(Bs, H, Dh, W))
+
+
+def maglev_decode_step(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o=None,
+                       rope_base: float = 10000.0, scale: float = 0.0, workspace=None,
+                       stream=None):
+    """One decode step; kcache/vcache [Bs,H,W,Dh] are updated in place. Returns o [Bs,H,Dh]."""
+    _dev(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o, workspace)
+    _same(q, k, v, kmem, vmem, kcache, vcache, o)
+    Bs, H, W, Dh = kcache.shape
+    if pos.dtype != torch.int64 or pos.numel() != Bs:
+        raise MaglevError("pos must be int64 [Bs]")
+    o = torch.empty_like(q) if o is None else o
+    if workspace is None:
+        need = int(lib().maglev_decode_workspace(Bs, H, Dh, W))
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().maglev_decode_step(Bs, H, Dh, W, rope_base, scale, _dtype_code(q), _ptr(q),
+                                    _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
+                                    _ptr(kcache), _ptr(vcache), _ptr(pos), _ptr(o),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "maglev_decode_step")
+    return o
+
+
+def maglev_decode_advance(pos, stream=None):
+    _dev(pos)
+    _check(lib().maglev_decode_advance(pos.numel(), _ptr(pos), _stream(stream)), "maglev_decode_advance")
+
+
+def default_scale(Dh: int) -> float:
+    return 1.0 / math.sqrt(Dh)

@@ -1,0 +1,131 @@
+// common.hpp -- device-side vocabulary shared by the gfx950 kernels of the
+// Maglev attention path: vector types, bf16 conversion, MFMA wrappers, the
+// LDS transpose read, and small helpers.
+//
+// MFMA lane layouts (checked on gfx950 by an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16: operand lane l holds row/column (l % 32) and the
+//     8 consecutive K entries 8*(l/32) .. +7; result lane l holds column l % 32,
+//     rows 8*(e/4) + 4*(l/32) + (e % 4) for e = 0..15.
+//   ds_read_tr16_b64: inside each group of 16 lanes, lane i receives element
+//     (i % 4) of the 4-element rows addressed by lanes i/4 + 4k, k = 0..3. With
+//     lane j addressing row k0 + j/4 at column n0 + 4*(j%4), lane i receives the
+//     4 consecutive rows k0..k0+3 of column n0 + i.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace maglev {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define MAGLEV_DEV __device__ __forceinline__
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// float -> bf16, round to nearest even (the gfx950 conversion instruction).
+MAGLEV_DEV bf16 f2bf(float x) { return (bf16)x; }
+MAGLEV_DEV float bf2f(bf16 x) { return (float)x; }
+
+// Storage-type agnostic load/store of one element.
+template <typename T> MAGLEV_DEV float to_f(T x);
+template <> MAGLEV_DEV float to_f<float>(float x) { return x; }
+template <> MAGLEV_DEV float to_f<bf16>(bf16 x) { return (float)x; }
+template <typename T> MAGLEV_DEV T from_f(float x);
+template <> MAGLEV_DEV float from_f<float>(float x) { return x; }
+template <> MAGLEV_DEV bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// 8 consecutive elements of type T as floats (16-byte or 32-byte loads).
+MAGLEV_DEV void load8(const bf16 *p, float *out)
+{
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+}
+MAGLEV_DEV void load8(const float *p, float *out)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+}
+MAGLEV_DEV void store8(bf16 *p, const float *in)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+    *reinterpret_cast<bf16x8 *>(p) = v;
+}
+MAGLEV_DEV void store8(float *p, const float *in)
+{
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = in[i]; b[i] = in[4 + i]; }
+    *reinterpret_cast<f32x4 *>(p) = a;
+    *reinterpret_cast<f32x4 *>(p + 4) = b;
+}
+
+MAGLEV_DEV bf16x8 pack8(const float *in)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+    return v;
+}
+
+MAGLEV_DEV f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+MAGLEV_DEV f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transpose read of four 16-bit values (see the layout note above).
+MAGLEV_DEV i16x4 lds_read_tr16(const bf16 *p)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+}
+
+// Two transpose reads joined into one 8-entry MFMA operand.
+MAGLEV_DEV bf16x8 join_tr(i16x4 lo, i16x4 hi)
+{
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    i16x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+MAGLEV_DEV float gate_sigmoid(float g) { return 1.0f / (1.0f + __expf(-g)); }
+
+// Wave-wide exchange with the lane 32 positions away.
+MAGLEV_DEV float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+MAGLEV_DEV float wave_sum(float x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Map a linear workgroup id so that consecutive logical tiles share an XCD
+// (workgroups are dispatched round-robin over the 8 XCDs, each with its own L2).
+MAGLEV_DEV int xcd_remap(int wg, int nwg)
+{
+    if ((nwg & 7) != 0) return wg;
+    return (wg & 7) * (nwg >> 3) + (wg >> 3);
+}
+
+}  // namespace maglev

@@ -1,0 +1,70 @@
+// internal.hpp -- host-side declarations shared by the C-ABI layer and the
+// kernel translation units. Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "maglev.h"
+
+namespace maglev {
+
+// Validated geometry handed to launchers (mirrors maglev_geom_t).
+struct Geom {
+    int64_t B, T;
+    int H, Dh, d, W;
+    int64_t pos0;
+    float rope_base;
+    float scale;   // resolved: > 0
+    int dtype;     // maglev_dtype_t
+    int64_t N() const { return B * T; }
+    int HD() const { return H * Dh; }
+};
+
+// RoPE table: float2 (cos, sin) [max_pos][Dh/2] for (device, Dh, base), or
+// nullptr when base <= 0. Grows on demand (synchronous upload).
+maglev_status_t rope_table(int Dh, float base, int64_t max_pos, const float2 **table);
+
+// ---- memory projection: out rows (b,t) = in(b, t - shift) * W^T ----------
+hipError_t launch_project(const Geom &g, int shift, const void *m, const void *W_Km,
+                          const void *W_Vm, void *kmem, void *vmem, hipStream_t s);
+
+// ---- attention forward -----------------------------------------------------
+hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *k, const void *v,
+                           const void *kmem, const void *vmem, const float *gate,
+                           const float2 *rope, void *o, float *lse, hipStream_t s);
+
+// ---- backward --------------------------------------------------------------
+struct BwdWorkspace {
+    float *D;            // [B,H,T]  rowsum(dO * O)
+    float *ds_part;      // [B,H,n_key_tiles] partial d loss / d s_h
+    void *W_scaled;      // [2*H*Dh, d] dtype: s_h * [W_Km; W_Vm] (rows scaled)
+    float *dW_part;      // [ksplit, 2*H*Dh, d] split-K partials (may be unused)
+    int ksplit;
+    int n_key_tiles;
+};
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base);
+
+hipError_t launch_bwd(const Geom &g, const void *q, const void *k, const void *v,
+                      const void *kmem, const void *vmem, const float *gate, const void *o,
+                      const float *lse, const void *dO, const void *m_prime, const void *W_Km,
+                      const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime,
+                      float *dW_Km, float *dW_Vm, float *dgate, unsigned accumulate,
+                      const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+
+// ---- consistency loss -------------------------------------------------------
+size_t loss_workspace_bytes(int64_t N, int d);
+hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
+                       const void *mp, float *loss, float *dm, float *dmp, unsigned accumulate,
+                       void *ws, hipStream_t s);
+
+// ---- decode -----------------------------------------------------------------
+size_t decode_workspace_bytes(int Bs, int H, int Dh, int W);
+hipError_t launch_decode(int Bs, int H, int Dh, int W, float rope_base, float scale, int dtype,
+                         const void *q, const void *k, const void *v, const void *kmem,
+                         const void *vmem, const float *gate, void *kcache, void *vcache,
+                         const int64_t *pos, void *o, void *ws, hipStream_t s);
+hipError_t launch_advance(int Bs, int64_t *pos, hipStream_t s);
+
+}  // namespace maglev

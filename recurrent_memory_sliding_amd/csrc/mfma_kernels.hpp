@@ -1,0 +1,39 @@
+// mfma_kernels.hpp -- launchers of the bf16 MFMA kernels (gfx950,
+// v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+#pragma once
+
+#include "internal.hpp"
+
+namespace maglev {
+namespace mfma {
+
+// kmem/vmem = input * [W_Km; W_Vm]^T with the shift folded into the row loads.
+void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
+                         void *km, void *vm, hipStream_t s);
+
+// Banded flash-style forward with RoPE and gate mixing fused into the K/V tile load.
+void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
+                          const void *km, const void *vm, const float *gate, const float2 *rope,
+                          void *o, float *lse, hipStream_t s);
+
+// Attention backward: rowsum(dO*O), key-stationary dK/dV pass (with the gate
+// partials), query-stationary dQ pass.
+void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
+                          const void *km, const void *vm, const float *gate, const void *o,
+                          const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                          const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+
+// Number of gate partials per (b, h) the dK/dV pass writes.
+int64_t ds_part_per_bh(const Geom &g);
+
+// Projection backward: dm' (shifted back) and dW_Km/dW_Vm (split-K, fixed-order reduction).
+void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const void *m_prime,
+                          const void *wk, const void *wv, const float *gate, float *dm_prime,
+                          float *dWk, float *dWv, unsigned acc, const BwdWorkspace &ws,
+                          hipStream_t s);
+
+// Split-K factor the dW GEMM uses for this geometry (workspace sizing).
+int dw_ksplit(const Geom &g);
+
+}  // namespace mfma
+}  // namespace maglev

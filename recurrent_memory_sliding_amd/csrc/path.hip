@@ -1,0 +1,307 @@
+// path.hip -- launchers of the training-pass kernels: memory projection,
+// attention forward and the backward sequence. bf16 runs on the MFMA kernels
+// (mfma_*.hip); float32 runs on the vector-ALU kernels of simt_kernels.hpp.
+//
+// Method: Maglev summary on paper.rainbus.top ("Maglev：滑动窗口循环记忆"),
+// section 方法步骤详情 (P consumes the shifted targets m'_{0:T-1}, m'_0 = 0;
+// projection W^rec m'_{t-1} into K/V features; gated mix; sliding-window
+// attention over the W most recent mixed entries) and gist.science
+// ("Technische Samenvatting: Maglev - Sliding Recurrent Memory"), section
+// Trainingsmechanisme (the second parallel pass through P). The backward is
+// the chain rule through those steps.
+#include "common.hpp"
+#include "internal.hpp"
+#include "mfma_kernels.hpp"
+#include "simt_kernels.hpp"
+
+namespace maglev {
+
+namespace {
+
+template <typename T>
+struct ProjA {  // row (b,t) of the projection input: m[b, t - shift] or 0
+    const T *m;
+    int64_t T_;
+    int d, shift;
+    __device__ float operator()(int64_t row, int64_t e) const
+    {
+        const int64_t t = row % T_;
+        return t >= shift ? to_f<T>(m[(row - shift) * d + e]) : 0.0f;
+    }
+};
+template <typename T>
+struct ProjB {  // column n of the stacked weight [W_Km; W_Vm]^T
+    const T *wk, *wv;
+    int HD, d;
+    __device__ float operator()(int64_t e, int64_t n) const
+    {
+        return n < HD ? to_f<T>(wk[n * d + e]) : to_f<T>(wv[(n - HD) * d + e]);
+    }
+};
+template <typename T>
+struct ProjStore {
+    T *km, *vm;
+    int HD;
+    __device__ void operator()(int64_t row, int64_t n, float x) const
+    {
+        if (n < HD) km[row * HD + n] = from_f<T>(x);
+        else vm[row * HD + (n - HD)] = from_f<T>(x);
+    }
+};
+
+// d loss / d input row (b,t) = sum_r s_h(r) (dk[b,t,r] W_Km[r,:] + dv[b,t,r] W_Vm[r,:]);
+// it lands on dm'[b, t-1] (t >= 1).
+template <typename T>
+struct DmA {
+    const T *dk, *dv;
+    int HD;
+    __device__ float operator()(int64_t row, int64_t r) const
+    {
+        return r < HD ? to_f<T>(dk[row * HD + r]) : to_f<T>(dv[row * HD + r - HD]);
+    }
+};
+template <typename T>
+struct DmB {
+    const T *wk, *wv;
+    const float *gate;
+    int HD, Dh, d;
+    __device__ float operator()(int64_t r, int64_t e) const
+    {
+        const int rr = (int)(r < HD ? r : r - HD);
+        const float s = gate_sigmoid(gate[rr / Dh]);
+        return s * (r < HD ? to_f<T>(wk[r * d + e]) : to_f<T>(wv[rr * (int64_t)d + e]));
+    }
+};
+struct DmStore {
+    float *dm;
+    int64_t T_;
+    int d;
+    bool acc;
+    __device__ void operator()(int64_t row, int64_t e, float x) const
+    {
+        if (row % T_ == 0) return;   // d/d input row (b,0) has no source memory
+        float *p = dm + (row - 1) * d + e;
+        *p = acc ? *p + x : x;
+    }
+};
+
+// dW[r, e] = s_h(r) sum_{b,t} dkv[b,t,r] input[b,t,e].
+template <typename T>
+struct DwA {
+    const T *dk, *dv;
+    int HD;
+    __device__ float operator()(int64_t r, int64_t row) const
+    {
+        return r < HD ? to_f<T>(dk[row * HD + r]) : to_f<T>(dv[row * HD + r - HD]);
+    }
+};
+struct DwStore {
+    float *wk, *wv;
+    const float *gate;
+    int HD, Dh, d;
+    bool acc;
+    __device__ void operator()(int64_t r, int64_t e, float x) const
+    {
+        const int rr = (int)(r < HD ? r : r - HD);
+        x *= gate_sigmoid(gate[rr / Dh]);
+        float *p = (r < HD ? wk : wv) + (int64_t)rr * d + e;
+        *p = acc ? *p + x : x;
+    }
+};
+
+__global__ void fill_zero(float *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+__global__ void zero_last_rows(float *dm, int64_t B, int64_t T, int d)
+{
+    const int64_t b = blockIdx.x;
+    for (int e = threadIdx.x; e < d; e += blockDim.x) dm[(b * T + T - 1) * d + e] = 0.0f;
+}
+
+// dgate[h] = s(1-s) * sum of the per-row or per-tile partials of head h, in a
+// fixed order (deterministic).
+__global__ __launch_bounds__(256) void dgate_reduce(const float *part, int64_t B, int H,
+                                                    int64_t per_bh, const float *gate,
+                                                    float *dgate, unsigned acc)
+{
+    __shared__ float red[4];
+    const int h = blockIdx.x;
+    float t = 0.0f;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = threadIdx.x; i < per_bh; i += 256) t += part[(b * H + h) * per_bh + i];
+    t = wave_sum(t);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float s = gate_sigmoid(gate[h]);
+        const float g = s * (1.0f - s) * (red[0] + red[1] + red[2] + red[3]);
+        dgate[h] = (acc & 4u) ? dgate[h] + g : g;
+    }
+}
+
+simt::RowArgs row_args(const Geom &g, const float *gate, const float2 *rope)
+{
+    simt::RowArgs a;
+    a.B = g.B; a.T = g.T; a.H = g.H; a.W = g.W; a.pos0 = g.pos0; a.scale = g.scale;
+    a.rope = rope; a.gate = gate;
+    return a;
+}
+
+template <typename T>
+void project_simt(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
+                  void *km, void *vm, hipStream_t s)
+{
+    const int64_t M = g.N(), N = 2 * g.HD(), K = g.d;
+    ProjA<T> la{static_cast<const T *>(m), g.T, g.d, shift};
+    ProjB<T> lb{static_cast<const T *>(wk), static_cast<const T *>(wv), g.HD(), g.d};
+    ProjStore<T> st{static_cast<T *>(km), static_cast<T *>(vm), g.HD()};
+    hipLaunchKernelGGL((simt::gemm_tiled<ProjA<T>, ProjB<T>, ProjStore<T>>),
+                       dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, K, la, lb, st);
+}
+
+template <typename T, int DH>
+void fwd_simt(const Geom &g, const void *q, const void *k, const void *v, const void *km,
+              const void *vm, const float *gate, const float2 *rope, void *o, float *lse,
+              hipStream_t s)
+{
+    hipLaunchKernelGGL((simt::attn_fwd_rows<T, DH>), dim3(g.T, g.H, g.B), dim3(DH), 0, s,
+                       row_args(g, gate, rope), static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(v),
+                       static_cast<const T *>(km), static_cast<const T *>(vm),
+                       static_cast<T *>(o), lse);
+}
+
+template <typename T, int DH>
+void attn_bwd_simt(const Geom &g, const void *q, const void *k, const void *v, const void *km,
+                   const void *vm, const float *gate, const void *o, const float *lse,
+                   const void *dO, void *dq, void *dk, void *dv, const BwdWorkspace &ws,
+                   const float2 *rope, hipStream_t s)
+{
+    const simt::RowArgs a = row_args(g, gate, rope);
+    const dim3 grid(g.T, g.H, g.B);
+    hipLaunchKernelGGL((simt::bwd_rowdot<T, DH>), grid, dim3(DH), 0, s, a,
+                       static_cast<const T *>(o), static_cast<const T *>(dO), ws.D);
+    hipLaunchKernelGGL((simt::bwd_dq_rows<T, DH>), grid, dim3(DH), 0, s, a,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<const T *>(km),
+                       static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
+                       static_cast<T *>(dq));
+    hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH>), grid, dim3(DH), 0, s, a,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<const T *>(km),
+                       static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
+                       static_cast<T *>(dk), static_cast<T *>(dv), ws.ds_part);
+}
+
+template <typename T>
+void proj_bwd_simt(const Geom &g, const void *dk, const void *dv, const void *m_prime,
+                   const void *wk, const void *wv, const float *gate, float *dm_prime,
+                   float *dWk, float *dWv, unsigned acc, hipStream_t s)
+{
+    const int HD = g.HD();
+    {
+        const int64_t M = g.N(), N = g.d, K = 2 * HD;
+        DmA<T> la{static_cast<const T *>(dk), static_cast<const T *>(dv), HD};
+        DmB<T> lb{static_cast<const T *>(wk), static_cast<const T *>(wv), gate, HD, g.Dh, g.d};
+        DmStore st{dm_prime, g.T, g.d, (acc & 1u) != 0};
+        hipLaunchKernelGGL((simt::gemm_tiled<DmA<T>, DmB<T>, DmStore>),
+                           dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, K, la, lb, st);
+    }
+    {
+        const int64_t M = 2 * HD, N = g.d, K = g.N();
+        DwA<T> la{static_cast<const T *>(dk), static_cast<const T *>(dv), HD};
+        ProjA<T> lb{static_cast<const T *>(m_prime), g.T, g.d, 1};
+        DwStore st{dWk, dWv, gate, HD, g.Dh, g.d, (acc & 2u) != 0};
+        hipLaunchKernelGGL((simt::gemm_tiled<DwA<T>, ProjA<T>, DwStore>),
+                           dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, M, N, K, la, lb, st);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_project(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
+                          void *km, void *vm, hipStream_t s)
+{
+    if (g.dtype == MAGLEV_BF16)
+        mfma::launch_project_bf16(g, shift, m, wk, wv, km, vm, s);
+    else
+        project_simt<float>(g, shift, m, wk, wv, km, vm, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *k, const void *v,
+                           const void *km, const void *vm, const float *gate, const float2 *rope,
+                           void *o, float *lse, hipStream_t s)
+{
+    if (g.dtype == MAGLEV_BF16) {
+        mfma::launch_attn_fwd_bf16(g, q, k, v, km, vm, gate, rope, o, lse, s);
+    } else {
+        if (g.Dh == 128) fwd_simt<float, 128>(g, q, k, v, km, vm, gate, rope, o, lse, s);
+        else fwd_simt<float, 64>(g, q, k, v, km, vm, gate, rope, o, lse, s);
+    }
+    return hipGetLastError();
+}
+
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base)
+{
+    auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+    const size_t esz = g.dtype == MAGLEV_BF16 ? 2 : 4;
+    const int64_t BHT = g.B * (int64_t)g.H * g.T;
+    L->n_key_tiles = (int)((g.T + 127) / 128);
+    L->ksplit = g.dtype == MAGLEV_BF16 ? mfma::dw_ksplit(g) : 0;
+    size_t off = 0;
+    const size_t oD = off; off = align(off + (size_t)BHT * sizeof(float));
+    const size_t oS = off; off = align(off + (size_t)BHT * sizeof(float));
+    const size_t oW = off; off = align(off + (size_t)2 * g.HD() * g.d * esz);
+    const size_t oP = off; off = align(off + (size_t)L->ksplit * 2 * g.HD() * g.d * sizeof(float));
+    L->D = base ? reinterpret_cast<float *>(base + oD) : nullptr;
+    L->ds_part = base ? reinterpret_cast<float *>(base + oS) : nullptr;
+    L->W_scaled = base ? static_cast<void *>(base + oW) : nullptr;
+    L->dW_part = base ? reinterpret_cast<float *>(base + oP) : nullptr;
+    return off;
+}
+
+hipError_t launch_bwd(const Geom &g, const void *q, const void *k, const void *v, const void *km,
+                      const void *vm, const float *gate, const void *o, const float *lse,
+                      const void *dO, const void *m_prime, const void *wk, const void *wv,
+                      void *dq, void *dk, void *dv, float *dm_prime, float *dWk, float *dWv,
+                      float *dgate, unsigned acc, const BwdWorkspace &ws, const float2 *rope,
+                      hipStream_t s)
+{
+    const int HD = g.HD();
+    if (g.N() == 0) {
+        // No tokens: the parameter gradients are zero (left alone when accumulating).
+        const int64_t nw = (int64_t)HD * g.d;
+        if (!(acc & 2u)) {
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWk, nw);
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWv, nw);
+        }
+        if (!(acc & 4u)) hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, s, dgate, (int64_t)g.H);
+        return hipGetLastError();
+    }
+    int64_t per_bh;
+    if (g.dtype == MAGLEV_BF16) {
+        mfma::launch_attn_bwd_bf16(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+        per_bh = mfma::ds_part_per_bh(g);
+    } else {
+        if (g.Dh == 128)
+            attn_bwd_simt<float, 128>(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+        else
+            attn_bwd_simt<float, 64>(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+        per_bh = g.T;
+    }
+    hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,
+                       gate, dgate, acc);
+    if (!(acc & 1u))
+        hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
+    if (g.dtype == MAGLEV_BF16)
+        mfma::launch_proj_bwd_bf16(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, ws, s);
+    else
+        proj_bwd_simt<float>(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, s);
+    return hipGetLastError();
+}
+
+}  // namespace maglev

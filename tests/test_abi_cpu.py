@@ -1,0 +1,156 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/maglev.h declares, sizes its workspaces, and rejects
+invalid arguments with the documented status before anything is enqueued.
+No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import recurrent_memory_sliding_amd as rms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maglev.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WORKSPACE, HIP = range(6)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rms.library_path()):
+        pytest.skip("libmaglev.so not built")
+    return rms.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(maglev_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
+              "maglev_decode_step", "maglev_consistency_loss"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.maglev_abi_version() == 1
+    assert L.maglev_status_string(OK) == b"MAGLEV_OK"
+    assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
+    assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: every case below fails validation
+FAKE_ODD = ctypes.c_void_p(0x10008)  # 8-byte aligned only
+
+
+def geom(**kw):
+    base = dict(B=2, T=64, H=2, Dh=128, d=256, W=16, pos0=0, rope_base=1e4, scale=0.0, dtype=1)
+    base.update(kw)
+    return rms.Geom(**base)
+
+
+def project(L, g, shift=1, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return L.maglev_mem_project(ctypes.byref(g) if g is not None else None, shift, *p, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Dh=96), UNSUPPORTED), (dict(Dh=32), UNSUPPORTED), (dict(H=0), INVALID),
+    (dict(d=100), INVALID), (dict(d=0), INVALID), (dict(W=0), INVALID), (dict(B=-1), INVALID),
+    (dict(T=-5), INVALID), (dict(pos0=-1), INVALID), (dict(dtype=7), INVALID),
+    (dict(scale=float("nan")), INVALID),
+])
+def test_projection_rejects_bad_geometry(L, kw, status):
+    assert project(L, geom(**kw)) == status
+
+
+def test_projection_rejects_null_geometry_shift_and_pointers(L):
+    assert project(L, None) == INVALID
+    assert project(L, geom(), shift=2) == INVALID
+    assert project(L, geom(), ptrs=[FAKE, None, FAKE, FAKE, FAKE]) == INVALID
+    assert project(L, geom(), ptrs=[FAKE, FAKE, FAKE, FAKE_ODD, FAKE]) == MISALIGNED
+    assert b"aligned" in L.maglev_last_error()
+
+
+def test_empty_batch_is_a_no_op(L):
+    # B = 0 returns OK without touching any pointer or the device.
+    assert project(L, geom(B=0)) == OK
+    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(T=0)), *([FAKE] * 7), None, None) == OK
+
+
+def test_forward_validation(L):
+    g = geom()
+    args = [FAKE] * 5 + [FAKE, FAKE, FAKE, None]
+    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(Dh=80)), *args) == UNSUPPORTED
+    bad = list(args); bad[5] = None  # gate
+    assert L.maglev_swa_inject_fwd(ctypes.byref(g), *bad, None) == INVALID
+    bad = list(args); bad[7] = FAKE_ODD  # lse misaligned
+    assert L.maglev_swa_inject_fwd(ctypes.byref(g), *bad, None) == MISALIGNED
+
+
+def test_backward_workspace_query_and_validation(L):
+    g = geom(B=8, T=2048, H=10, Dh=128, d=1280, W=512)
+    need = L.maglev_swa_inject_bwd_workspace(ctypes.byref(g))
+    # row-dot + gate partials (B*H*T floats each) + scaled weights + split-K partials
+    assert need >= 2 * 8 * 10 * 2048 * 4 + 2 * 1280 * 1280 * 2
+    assert L.maglev_swa_inject_bwd_workspace(ctypes.byref(geom(Dh=96))) == 0
+    ptrs = [FAKE] * 19
+    assert L.maglev_swa_inject_bwd(ctypes.byref(g), *ptrs, 0, None, 0, None) == WORKSPACE
+    assert L.maglev_swa_inject_bwd(ctypes.byref(g), *ptrs, 0, FAKE, need - 1, None) == WORKSPACE
+    assert L.maglev_swa_inject_bwd(ctypes.byref(g), *ptrs, 8, FAKE, need, None) == INVALID
+    bad = list(ptrs); bad[12] = None  # dq
+    assert L.maglev_swa_inject_bwd(ctypes.byref(g), *bad, 0, FAKE, need, None) == INVALID
+
+
+def test_loss_validation(L):
+    need = L.maglev_consistency_loss_workspace(16384, 1280)
+    assert need > 0
+    assert L.maglev_consistency_loss_workspace(10, 12) == 0
+    base = [FAKE, FAKE, FAKE, None, None, 0, FAKE, need, None]
+    assert L.maglev_consistency_loss(-1, 64, 1.0, 1, *base) == INVALID
+    assert L.maglev_consistency_loss(4, 12, 1.0, 1, *base) == INVALID
+    assert L.maglev_consistency_loss(4, 64, 1.0, 5, *base) == INVALID
+    assert L.maglev_consistency_loss(4, 64, float("nan"), 1, *base) == INVALID
+    nows = list(base); nows[6] = None
+    assert L.maglev_consistency_loss(4, 64, 1.0, 1, *nows) == WORKSPACE
+    noloss = list(base); noloss[2] = None
+    assert L.maglev_consistency_loss(4, 64, 1.0, 1, *noloss) == INVALID
+
+
+def test_decode_validation(L):
+    need = L.maglev_decode_workspace(64, 10, 128, 512)
+    assert need == 64 * 10 * 8 * (128 + 4) * 4
+    ptrs = [FAKE] * 10
+    args = lambda **kw: [kw.get("Bs", 64), 10, kw.get("Dh", 128), kw.get("W", 512), 1e4, 0.0,
+                         kw.get("dtype", 1)]
+    assert L.maglev_decode_step(*args(Dh=48), *ptrs, FAKE, need, None) == UNSUPPORTED
+    assert L.maglev_decode_step(*args(W=0), *ptrs, FAKE, need, None) == INVALID
+    assert L.maglev_decode_step(*args(), *ptrs, None, 0, None) == WORKSPACE
+    bad = list(ptrs); bad[8] = None  # pos
+    assert L.maglev_decode_step(*args(), *bad, FAKE, need, None) == INVALID
+    assert L.maglev_decode_step(*args(Bs=0), *ptrs, FAKE, need, None) == OK
+    assert L.maglev_decode_advance(5, None, None) == INVALID
+    assert L.maglev_decode_advance(0, FAKE, None) == OK
+
+
+def test_prepare_validation(L):
+    assert L.maglev_prepare(100, 1e4, 10) == UNSUPPORTED
+    assert L.maglev_prepare(128, 1e4, -1) == INVALID
+    # rope_base <= 0 disables the rotation: nothing to allocate
+    assert L.maglev_prepare(128, 0.0, 1000) == OK
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    x = torch.zeros(2, 4, 64)
+    with pytest.raises(rms.MaglevError):
+        rms.maglev_mem_project(x, torch.zeros(64, 64), torch.zeros(64, 64), 1, 64)
