@@ -63,6 +63,8 @@ def _load():
         L.oracle_swa_inject_fwd_rows.argtypes = [I64, I64, I32, I32, I64, I64, D, D,
                                                  P, P, P, P, P, P, I64, PI64, P, P]
         L.oracle_swa_inject_fwd_rows.restype = None
+        L.oracle_mixed_entries.argtypes = [I64, I64, I32, I32, I64, D, P, P, P, P, P, P, P]
+        L.oracle_mixed_entries.restype = None
         _lib = L
     return _lib
 
@@ -96,6 +98,19 @@ def mem_project(m, W_Km, W_Vm, H: int, Dh: int, shift: int = 1):
     vmem = np.empty((B, T, H, Dh))
     _load().oracle_mem_project(B, T, H, Dh, d, int(shift), _p(m), _p(WK), _p(WV), _p(kmem), _p(vmem))
     return kmem, vmem
+
+
+def mixed_entries(k, v, kmem, vmem, gate_logit, pos0: int = 0, rope_base: float = 10000.0):
+    """kmix = R k + s R kmem, vmix = v + s vmem, both [B,T,H,Dh] (s = sigmoid(gate))."""
+    k, v, km, vm, g = (f64(a) for a in (k, v, kmem, vmem, gate_logit))
+    B, T, H, Dh = k.shape
+    if Dh > 512:
+        raise ValueError("Dh above 512")
+    kx = np.empty((B, T, H, Dh))
+    vx = np.empty((B, T, H, Dh))
+    _load().oracle_mixed_entries(B, T, H, Dh, int(pos0), float(rope_base), _p(k), _p(v), _p(km),
+                                 _p(vm), _p(g), _p(kx), _p(vx))
+    return kx, vx
 
 
 def swa_inject_fwd(q, k, v, kmem, vmem, gate_logit, W: int, pos0: int = 0,

@@ -169,6 +169,37 @@ static void head_view_fill(head_view *hv, int64_t b, int h, int64_t T, int H, in
     }
 }
 
+/* Mixed cache entries of every position ([R-bg]: both the local key and the
+ * injected memory key are rotated before they are mixed; [R-step]: the gated
+ * mix with the local K/V features):
+ *     kmix_t = R_t k_t + s_h R_t kmem_t,   vmix_t = v_t + s_h vmem_t,
+ * with R_t the rotation of absolute position pos0 + t. */
+ORACLE_API void oracle_mixed_entries(int64_t B, int64_t T, int H, int Dh, int64_t pos0,
+                                     double base, const double *k, const double *v,
+                                     const double *kmem, const double *vmem,
+                                     const double *gate_logit, double *kmix, double *vmix)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < T; ++t) {
+            double rk[512], rm[512];
+            const double p = (double)(pos0 + t);
+            for (int h = 0; h < H; ++h) {
+                const int64_t off = ((b * T + t) * H + h) * Dh;
+                const double s = gate_sigmoid(gate_logit[h]);
+                memcpy(rk, k + off, (size_t)Dh * sizeof(double));
+                rope_rotate(rk, Dh, p, base, 0);
+                memcpy(rm, kmem + off, (size_t)Dh * sizeof(double));
+                rope_rotate(rm, Dh, p, base, 0);
+                for (int c = 0; c < Dh; ++c) {
+                    kmix[off + c] = rk[c] + s * rm[c];
+                    vmix[off + c] = v[off + c] + s * vmem[off + c];
+                }
+            }
+        }
+    }
+}
+
 static double default_scale(double scale, int Dh) { return scale > 0.0 ? scale : 1.0 / sqrt((double)Dh); }
 
 /* Softmax weights of query i over its window J(i) = {max(0, i-W+1) .. i}

@@ -233,6 +233,53 @@ def test_memory_key_rotated_at_local_key_position():
     assert np.abs(o - o_bad).max() > 1e-3
 
 
+# ----------------------------------------------------------------------------
+# mixed cache entries
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("pos0,base", [(0, 10000.0), (1000, 10000.0), (5, 0.0)])
+def test_mixed_entries_match_complex_rotation(pos0, base):
+    """k~ = R k + s R kmem and v~ = v + s vmem against numpy's complex rotation."""
+    sh = small_shape(T=23, W=5)
+    inp = wl.layer_inputs(sh, seed=12)
+    km, vm = oracle.mem_project(inp["m_prime"], inp["W_Km"], inp["W_Vm"], sh.H, sh.Dh, shift=1)
+    kx, vx = oracle.mixed_entries(inp["k"], inp["v"], km, vm, inp["gate_logit"], pos0, base)
+    pos = np.arange(sh.T) + pos0
+    s = expit(oracle.f64(inp["gate_logit"]))[None, None, :, None]
+    k, v = oracle.f64(inp["k"]), oracle.f64(inp["v"])
+    np.testing.assert_allclose(kx, rope_complex(k, pos, base) + s * rope_complex(km, pos, base),
+                               rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(vx, v + s * vm, rtol=1e-14, atol=1e-15)
+
+
+def test_mixed_entries_gate_limits():
+    """s = 0 leaves the rotated local entry; s = 1 with k = v = 0 leaves the
+    rotated memory entry."""
+    sh = small_shape(T=17, W=5)
+    inp = wl.layer_inputs(sh, seed=13)
+    km, vm = oracle.mem_project(inp["m_prime"], inp["W_Km"], inp["W_Vm"], sh.H, sh.Dh, shift=1)
+    pos = np.arange(sh.T)
+    kx, vx = oracle.mixed_entries(inp["k"], inp["v"], km, vm, np.full(sh.H, -np.inf))
+    np.testing.assert_allclose(kx, rope_complex(oracle.f64(inp["k"]), pos, 1e4), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(vx, oracle.f64(inp["v"]))
+    z = np.zeros((sh.B, sh.T, sh.H, sh.Dh))
+    kx, vx = oracle.mixed_entries(z, z, km, vm, np.full(sh.H, 40.0))
+    np.testing.assert_allclose(kx, rope_complex(km, pos, 1e4), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(vx, vm)
+
+
+def test_forward_is_attention_over_mixed_entries():
+    """The forward equals band-masked SDPA of (R q, k~, v~) with k~, v~ taken
+    from the mixed-entries function: the two oracle functions agree."""
+    sh = small_shape(T=31, W=6)
+    inp = wl.layer_inputs(sh, seed=14)
+    (o, lse), km, vm = run_oracle_fwd(inp, sh.W, pos0=7)
+    kx, vx = oracle.mixed_entries(inp["k"], inp["v"], km, vm, inp["gate_logit"], 7)
+    qh = rope_complex(oracle.f64(inp["q"]), np.arange(sh.T) + 7, 1e4)
+    o_ref, lse_ref = sdpa_reference(qh, kx, vx, sh.W)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-10, atol=1e-11)
+
+
 def test_fwd_rows_equal_full_forward():
     sh = small_shape(T=45, W=9)
     inp = wl.layer_inputs(sh, seed=10)
