@@ -97,6 +97,8 @@ def train_setup(sh, seed=2):
     buf = {
         "km": torch.empty((B, T, H, Dh), dtype=bf, device=dev),
         "vm": torch.empty((B, T, H, Dh), dtype=bf, device=dev),
+        "kx": torch.empty((B, T, H, Dh), dtype=bf, device=dev),
+        "vx": torch.empty((B, T, H, Dh), dtype=bf, device=dev),
         "o": torch.empty((B, T, H, Dh), dtype=bf, device=dev),
         "lse": torch.empty((B, H, T), dtype=f32, device=dev),
         "loss": torch.empty((1,), dtype=f32, device=dev),
@@ -129,18 +131,20 @@ def train_step(sh, g, buf, timer=None):
             timer.add(name, s)
 
     run("maglev_mem_project", lambda: rms.maglev_mem_project(
-        g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh, shift=1, kmem=buf["km"], vmem=buf["vm"]))
+        g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh, shift=1, kmem=buf["km"], vmem=buf["vm"],
+        k=g["k"], v=g["v"], gate_logit=g["gate_logit"], kmix=buf["kx"], vmix=buf["vx"],
+        pos0=sh.pos0, rope_base=sh.rope_base))
     run("maglev_swa_inject_fwd", lambda: rms.maglev_swa_inject_fwd(
-        g["q"], g["k"], g["v"], buf["km"], buf["vm"], g["gate_logit"], sh.W, d=sh.d, o=buf["o"],
-        lse=buf["lse"]))
-    # loss writes dm' (= -dm); the backward then adds the injection gradient (accumulate bit 0)
+        g["q"], buf["kx"], buf["vx"], sh.W, pos0=sh.pos0, rope_base=sh.rope_base, d=sh.d,
+        o=buf["o"], lse=buf["lse"]))
+    # the backward writes dm'; the loss then adds its own term (accumulate bit 1)
+    run("maglev_swa_inject_bwd", lambda: rms.maglev_swa_inject_bwd(
+        g["q"], buf["kx"], buf["vx"], buf["km"], buf["vm"], g["gate_logit"], buf["o"], buf["lse"],
+        g["dO"], g["m_prime"], g["W_Km"], g["W_Vm"], sh.W, pos0=sh.pos0, rope_base=sh.rope_base,
+        accumulate=0, out=buf["grads"], workspace=buf["ws_bwd"]))
     run("maglev_consistency_loss", lambda: rms.maglev_consistency_loss(
         g["m"], g["m_prime"], sh.lam, loss=buf["loss"], dm=buf["dm"],
-        dm_prime=buf["grads"]["dm_prime"], workspace=buf["ws_loss"]))
-    run("maglev_swa_inject_bwd", lambda: rms.maglev_swa_inject_bwd(
-        g["q"], g["k"], g["v"], buf["km"], buf["vm"], g["gate_logit"], buf["o"], buf["lse"],
-        g["dO"], g["m_prime"], g["W_Km"], g["W_Vm"], sh.W, accumulate=1, out=buf["grads"],
-        workspace=buf["ws_bwd"]))
+        dm_prime=buf["grads"]["dm_prime"], accumulate=2, workspace=buf["ws_loss"]))
 
 
 def bench_train(sh, steps, warmup):

@@ -31,6 +31,8 @@
  *   k~_j   = R_j k_j + s_h R_j kmem_j,   v~_j = v_j + s_h vmem_j,
  *   s_h    = sigmoid(gate_logit[h]), one float32 logit per head,
  *   O_i    = sum_{j = max(0, i-W+1)}^{i} softmax_j(scale <R_i q_i, k~_j>) v~_j.
+ * The mixed entries k~, v~ are formed once per token by maglev_mem_project
+ * and read by the attention forward and backward.
  * R_p rotates channel pair (c, c + Dh/2) by angle p * base^(-2c/Dh) (p = pos0 + t).
  *
  * Common conventions
@@ -47,6 +49,10 @@
  *     parameter gradient are float32. Arithmetic accumulates in float32.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error the call returns a status other than MAGLEV_OK and writes nothing.
+ *   - A call with no rows (B*T == 0, Bs == 0, N == 0) returns MAGLEV_OK after
+ *     the geometry check without reading its data pointers (empty tensors may
+ *     be NULL); only the parameter gradients of the backward are still
+ *     written (zeroed unless accumulating).
  *   - The library keeps one internal device table per (device, Dh, rope_base):
  *     float32 cos/sin of the RoPE angles, computed on the host in double
  *     precision. It is created or grown on first use (a synchronous upload);
@@ -64,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MAGLEV_ABI_VERSION 1
+#define MAGLEV_ABI_VERSION 2
 
 typedef enum {
     MAGLEV_OK = 0,
@@ -95,30 +101,37 @@ typedef struct {
     int32_t dtype;
 } maglev_geom_t;
 
-/* Memory projection with the one-step shift ([R-step]: P consumes m'_{0:T-1}
- * with m'_0 = 0; [R-core]: the shifted memory passes through a shared
- * projection into K/V features).
+/* Memory projection with the one-step shift, and the gated mix of the
+ * projected memory into each token's own K/V entry ([R-step]: P consumes
+ * m'_{0:T-1} with m'_0 = 0; [R-core]: the shifted memory passes through a
+ * shared projection into K/V features mixed into the existing entries;
+ * [R-bg]: the injected key is rotated at the local key's position before
+ * mixing).
  *   shift = 1: input row (b,t) is m[b,t-1], row (b,0) is zero;
  *   shift = 0: input row (b,t) is m[b,t] (decode injects m_{t-1} directly).
  *   m [B,T,d] dtype; W_Km, W_Vm [H*Dh, d] dtype;
  *   kmem, vmem [B,T,H,Dh] dtype, written: kmem = input W_Km^T, vmem = input W_Vm^T.
- * Uses g->B, T, H, Dh, d, dtype. */
+ * Mixing (all five of k, v, gate_logit, kmix, vmix non-NULL, or all NULL):
+ *   k, v [B,T,H,Dh] dtype (the token's local key/value, before RoPE);
+ *   gate_logit [H] float32;
+ *   kmix, vmix [B,T,H,Dh] dtype, written:
+ *     kmix = R_{pos0+t} k + s_h R_{pos0+t} kmem,  vmix = v + s_h vmem.
+ * Uses g->B, T, H, Dh, d, pos0, rope_base, dtype. */
 maglev_status_t maglev_mem_project(const maglev_geom_t *g, int shift, const void *m,
-                                   const void *W_Km, const void *W_Vm, void *kmem, void *vmem,
-                                   hipStream_t stream);
+                                   const void *W_Km, const void *W_Vm, const void *k,
+                                   const void *v, const float *gate_logit, void *kmem,
+                                   void *vmem, void *kmix, void *vmix, hipStream_t stream);
 
 /* Forward of the injected sliding-window attention ([R-bg], [R-core], [R-step]):
- * rotate q, form k~ and v~ as above, attend over the W most recent mixed
- * entries (fully masked key tiles are skipped).
- *   q, k, v, kmem, vmem [B,T,H,Dh] dtype (kmem/vmem from maglev_mem_project);
- *   gate_logit [H] float32;
+ * rotate q and attend over the W most recent mixed entries (fully masked key
+ * tiles are skipped).
+ *   q [B,T,H,Dh] dtype (before RoPE);
+ *   kmix, vmix [B,T,H,Dh] dtype: the mixed entries written by maglev_mem_project;
  *   o [B,T,H,Dh] dtype, written;
  *   lse [B,H,T] float32, written (log-sum-exp of the scaled scores; may be NULL
  *   when no backward follows). */
-maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *k,
-                                      const void *v, const void *kmem, const void *vmem,
-                                      const float *gate_logit, void *o, float *lse,
-                                      hipStream_t stream);
+maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *kmix,
+                                      const void *vmix, void *o, float *lse, hipStream_t stream);
 
 /* Bytes of device workspace maglev_swa_inject_bwd needs for this geometry
  * (0 on invalid geometry). */
@@ -126,11 +139,12 @@ size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g);
 
 /* Backward of the layer path: attention, mixing, shift and projection (the
  * chain rule through the forward above; [R-step], [G-train]).
- * Inputs: the forward's q, k, v, kmem, vmem, gate_logit, o, lse; the upstream
- * gradient dO [B,T,H,Dh] dtype; m_prime [B,T,d] dtype (UNshifted, as given to
- * maglev_mem_project with shift = 1); W_Km, W_Vm [H*Dh, d] dtype.
+ * Inputs: q; the mixed entries kmix, vmix and the memory terms kmem, vmem
+ * written by maglev_mem_project; gate_logit; the forward's o and lse; the
+ * upstream gradient dO [B,T,H,Dh] dtype; m_prime [B,T,d] dtype (UNshifted, as
+ * given to maglev_mem_project with shift = 1); W_Km, W_Vm [H*Dh, d] dtype.
  * Outputs:
- *   dq, dk, dv [B,T,H,Dh] dtype (overwritten);
+ *   dq, dk, dv [B,T,H,Dh] dtype (overwritten): gradients w.r.t. q, k, v;
  *   dm_prime [B,T,d] float32: gradient w.r.t. m'; row T-1 gets no injection
  *     gradient (it is never consumed);
  *   dW_Km, dW_Vm [H*Dh, d] float32; dgate [H] float32 (w.r.t. the logits).
@@ -139,8 +153,8 @@ size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g);
  * workspace: device buffer of at least maglev_swa_inject_bwd_workspace(g)
  *   bytes, owned by the caller; contents are scratch on return.
  * The result is deterministic: no floating-point atomics are used. */
-maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *k,
-                                      const void *v, const void *kmem, const void *vmem,
+maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *kmix,
+                                      const void *vmix, const void *kmem, const void *vmem,
                                       const float *gate_logit, const void *o, const float *lse,
                                       const void *dO, const void *m_prime, const void *W_Km,
                                       const void *W_Vm, void *dq, void *dk, void *dv,

@@ -62,8 +62,8 @@ def lib() -> ctypes.CDLL:
                                       ctypes.c_int64, ctypes.c_float, ctypes.c_uint)
         G = ctypes.POINTER(Geom)
         sig = {
-            "maglev_mem_project": ([G, ctypes.c_int, vp, vp, vp, vp, vp, vp], i32),
-            "maglev_swa_inject_fwd": ([G, vp, vp, vp, vp, vp, vp, vp, vp, vp], i32),
+            "maglev_mem_project": ([G, ctypes.c_int] + [vp] * 10 + [vp], i32),
+            "maglev_swa_inject_fwd": ([G, vp, vp, vp, vp, vp, vp], i32),
             "maglev_swa_inject_bwd_workspace": ([G], sz),
             "maglev_swa_inject_bwd": ([G] + [vp] * 19 + [u32, vp, sz, vp], i32),
             "maglev_consistency_loss_workspace": ([i64, i32], sz),
@@ -136,36 +136,58 @@ def maglev_prepare(Dh: int, rope_base: float, max_pos: int):
 
 
 def maglev_mem_project(m, W_Km, W_Vm, H: int, Dh: int, shift: int = 1, kmem=None, vmem=None,
-                       stream=None):
-    """kmem, vmem [B,T,H,Dh] = (m shifted by `shift` rows) projected by W_Km, W_Vm."""
-    _dev(m, W_Km, W_Vm, kmem, vmem)
-    _same(m, W_Km, W_Vm, kmem, vmem)
+                       k=None, v=None, gate_logit=None, kmix=None, vmix=None, pos0: int = 0,
+                       rope_base: float = 10000.0, stream=None):
+    """kmem, vmem [B,T,H,Dh] = (m shifted by `shift` rows) projected by W_Km, W_Vm.
+
+    With k, v [B,T,H,Dh] and gate_logit [H] (float32) it also writes the mixed
+    entries kmix = R(k + s kmem), vmix = v + s vmem (s = sigmoid(gate_logit),
+    R the rotation at position pos0 + t) and returns (kmem, vmem, kmix, vmix).
+    """
+    mixing = k is not None or v is not None or gate_logit is not None
+    if mixing and (k is None or v is None or gate_logit is None):
+        raise MaglevError("k, v and gate_logit come together")
+    _dev(m, W_Km, W_Vm, kmem, vmem, k, v, gate_logit, kmix, vmix)
+    _same(m, W_Km, W_Vm, kmem, vmem, k, v, kmix, vmix)
     B, T, d = m.shape
     if tuple(W_Km.shape) != (H * Dh, d) or tuple(W_Vm.shape) != (H * Dh, d):
         raise MaglevError("W_Km / W_Vm must be [H*Dh, d]")
-    kmem = torch.empty((B, T, H, Dh), dtype=m.dtype, device=m.device) if kmem is None else kmem
-    vmem = torch.empty((B, T, H, Dh), dtype=m.dtype, device=m.device) if vmem is None else vmem
-    g = make_geom(B, T, H, Dh, d, 1, dtype=_dtype_code(m))
+    shp = (B, T, H, Dh)
+    kmem = torch.empty(shp, dtype=m.dtype, device=m.device) if kmem is None else kmem
+    vmem = torch.empty(shp, dtype=m.dtype, device=m.device) if vmem is None else vmem
+    if mixing:
+        if tuple(k.shape) != shp or tuple(v.shape) != shp:
+            raise MaglevError("k / v must be [B,T,H,Dh]")
+        if gate_logit.dtype != torch.float32 or gate_logit.numel() != H:
+            raise MaglevError("gate_logit must be float32 [H]")
+        kmix = torch.empty(shp, dtype=m.dtype, device=m.device) if kmix is None else kmix
+        vmix = torch.empty(shp, dtype=m.dtype, device=m.device) if vmix is None else vmix
+    else:
+        kmix = vmix = None
+    g = make_geom(B, T, H, Dh, d, 1, pos0, rope_base, 0.0, _dtype_code(m))
     _check(lib().maglev_mem_project(ctypes.byref(g), shift, _ptr(m), _ptr(W_Km), _ptr(W_Vm),
-                                    _ptr(kmem), _ptr(vmem), _stream(stream)), "maglev_mem_project")
+                                    _ptr(k), _ptr(v), _ptr(gate_logit), _ptr(kmem), _ptr(vmem),
+                                    _ptr(kmix), _ptr(vmix), _stream(stream)),
+           "maglev_mem_project")
+    if mixing:
+        return kmem, vmem, kmix, vmix
     return kmem, vmem
 
 
-def maglev_swa_inject_fwd(q, k, v, kmem, vmem, gate_logit, W: int, pos0: int = 0,
-                          rope_base: float = 10000.0, scale: float = 0.0, d: int = 0, o=None,
-                          lse=None, need_lse: bool = True, stream=None):
+def maglev_swa_inject_fwd(q, kmix, vmix, W: int, pos0: int = 0, rope_base: float = 10000.0,
+                          scale: float = 0.0, d: int = 0, o=None, lse=None,
+                          need_lse: bool = True, stream=None):
     """O [B,T,H,Dh] and lse [B,H,T] (float32; None when need_lse is False)."""
-    _dev(q, k, v, kmem, vmem, gate_logit, o, lse)
-    _same(q, k, v, kmem, vmem, o)
+    _dev(q, kmix, vmix, o, lse)
+    _same(q, kmix, vmix, o)
     B, T, H, Dh = q.shape
-    if gate_logit.dtype != torch.float32 or gate_logit.numel() != H:
-        raise MaglevError("gate_logit must be float32 [H]")
+    if tuple(kmix.shape) != tuple(q.shape) or tuple(vmix.shape) != tuple(q.shape):
+        raise MaglevError("kmix / vmix must match q")
     o = torch.empty_like(q) if o is None else o
     if need_lse and lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     g = make_geom(B, T, H, Dh, d or H * Dh, W, pos0, rope_base, scale, _dtype_code(q))
-    _check(lib().maglev_swa_inject_fwd(ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(kmem),
-                                       _ptr(vmem), _ptr(gate_logit), _ptr(o),
+    _check(lib().maglev_swa_inject_fwd(ctypes.byref(g), _ptr(q), _ptr(kmix), _ptr(vmix), _ptr(o),
                                        _ptr(lse) if need_lse else None, _stream(stream)),
            "maglev_swa_inject_fwd")
     return o, lse
@@ -176,13 +198,15 @@ def maglev_swa_inject_bwd_workspace(B, T, H, Dh, d, W, dtype=MAGLEV_BF16) -> int
     return int(lib().maglev_swa_inject_bwd_workspace(ctypes.byref(g)))
 
 
-def maglev_swa_inject_bwd(q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km, W_Vm,
-                          W: int, pos0: int = 0, rope_base: float = 10000.0, scale: float = 0.0,
-                          accumulate: int = 0, out: Optional[dict] = None, workspace=None,
-                          stream=None) -> dict:
-    """Gradients dq, dk, dv (activation dtype), dm_prime, dW_Km, dW_Vm, dgate (float32)."""
-    _dev(q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km, W_Vm, workspace)
-    _same(q, k, v, kmem, vmem, o, dO, m_prime, W_Km, W_Vm)
+def maglev_swa_inject_bwd(q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km,
+                          W_Vm, W: int, pos0: int = 0, rope_base: float = 10000.0,
+                          scale: float = 0.0, accumulate: int = 0, out: Optional[dict] = None,
+                          workspace=None, stream=None) -> dict:
+    """Gradients dq, dk, dv (activation dtype), dm_prime, dW_Km, dW_Vm, dgate (float32).
+
+    dk, dv are the gradients of the token's own k, v (before mixing)."""
+    _dev(q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km, W_Vm, workspace)
+    _same(q, kmix, vmix, kmem, vmem, o, dO, m_prime, W_Km, W_Vm)
     B, T, H, Dh = q.shape
     d = m_prime.shape[-1]
     dev = q.device
@@ -202,7 +226,7 @@ def maglev_swa_inject_bwd(q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, 
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _check(lib().maglev_swa_inject_bwd(
-        ctypes.byref(g), _ptr(q), _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
+        ctypes.byref(g), _ptr(q), _ptr(kmix), _ptr(vmix), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
         _ptr(o), _ptr(lse), _ptr(dO), _ptr(m_prime), _ptr(W_Km), _ptr(W_Vm), _ptr(out["dq"]),
         _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dm_prime"]), _ptr(out["dW_Km"]),
         _ptr(out["dW_Vm"]), _ptr(out["dgate"]), accumulate, _ptr(workspace),

@@ -30,9 +30,14 @@ maglev_status_t rope_table(int Dh, float base, int64_t max_pos, const float2 **t
 hipError_t launch_project(const Geom &g, int shift, const void *m, const void *W_Km,
                           const void *W_Vm, void *kmem, void *vmem, hipStream_t s);
 
+// ---- gated mix of the memory terms into the local K/V entries -----------------
+//   kmix = R (k + s_h kmem), vmix = v + s_h vmem   (R linear: R k + s R kmem)
+hipError_t launch_mix(const Geom &g, const void *k, const void *v, const void *kmem,
+                      const void *vmem, const float *gate, const float2 *rope, void *kmix,
+                      void *vmix, hipStream_t s);
+
 // ---- attention forward -----------------------------------------------------
-hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *k, const void *v,
-                           const void *kmem, const void *vmem, const float *gate,
+hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kmix, const void *vmix,
                            const float2 *rope, void *o, float *lse, hipStream_t s);
 
 // ---- backward --------------------------------------------------------------
@@ -46,7 +51,7 @@ struct BwdWorkspace {
 };
 size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base);
 
-hipError_t launch_bwd(const Geom &g, const void *q, const void *k, const void *v,
+hipError_t launch_bwd(const Geom &g, const void *q, const void *kmix, const void *vmix,
                       const void *kmem, const void *vmem, const float *gate, const void *o,
                       const float *lse, const void *dO, const void *m_prime, const void *W_Km,
                       const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime,

@@ -193,36 +193,48 @@ maglev_status_t maglev_prepare(int32_t Dh, float rope_base, int64_t max_pos)
 }
 
 maglev_status_t maglev_mem_project(const maglev_geom_t *g, int shift, const void *m,
-                                   const void *W_Km, const void *W_Vm, void *kmem, void *vmem,
-                                   hipStream_t stream)
+                                   const void *W_Km, const void *W_Vm, const void *k,
+                                   const void *v, const float *gate_logit, void *kmem,
+                                   void *vmem, void *kmix, void *vmix, hipStream_t stream)
 {
     Geom G;
     maglev_status_t st = check_geom(g, &G);
     if (st != MAGLEV_OK) return st;
     if (shift != 0 && shift != 1) return fail(MAGLEV_ERR_INVALID_VALUE, "shift must be 0 or 1");
-    if (G.N() == 0) return MAGLEV_OK;   // nothing to read or write
+    if (G.N() == 0) return MAGLEV_OK;   // nothing to read or write (empty tensors may be null)
+    const int nmix = (k != nullptr) + (v != nullptr) + (gate_logit != nullptr) +
+                     (kmix != nullptr) + (vmix != nullptr);
+    if (nmix != 0 && nmix != 5)
+        return fail(MAGLEV_ERR_INVALID_VALUE, "k, v, gate_logit, kmix, vmix: give all or none");
     st = check_ptrs({m, W_Km, W_Vm, kmem, vmem});
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_project(G, shift, m, W_Km, W_Vm, kmem, vmem, stream));
+    const float2 *rope = nullptr;
+    if (nmix) {
+        st = check_ptrs({k, v, kmix, vmix});
+        if (st != MAGLEV_OK) return st;
+        st = table_for(G, stream, &rope);
+        if (st != MAGLEV_OK) return st;
+    }
+    hipError_t e = launch_project(G, shift, m, W_Km, W_Vm, kmem, vmem, stream);
+    if (e == hipSuccess && nmix)
+        e = launch_mix(G, k, v, kmem, vmem, gate_logit, rope, kmix, vmix, stream);
+    return hip_status(e);
 }
 
-maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *k,
-                                      const void *v, const void *kmem, const void *vmem,
-                                      const float *gate_logit, void *o, float *lse,
-                                      hipStream_t stream)
+maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *kmix,
+                                      const void *vmix, void *o, float *lse, hipStream_t stream)
 {
     Geom G;
     maglev_status_t st = check_geom(g, &G);
     if (st != MAGLEV_OK) return st;
     if (G.N() == 0) return MAGLEV_OK;   // nothing to read or write
-    st = check_ptrs({q, k, v, kmem, vmem, o});
+    st = check_ptrs({q, kmix, vmix, o});
     if (st != MAGLEV_OK) return st;
-    if (!gate_logit) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit is NULL");
     if (lse && !aligned16(lse)) return fail(MAGLEV_ERR_MISALIGNED, "lse is not 16-byte aligned");
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_attn_fwd(G, q, k, v, kmem, vmem, gate_logit, rope, o, lse, stream));
+    return hip_status(launch_attn_fwd(G, q, kmix, vmix, rope, o, lse, stream));
 }
 
 size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g)
@@ -233,8 +245,8 @@ size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g)
     return bwd_workspace_bytes(G, &layout, nullptr);
 }
 
-maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *k,
-                                      const void *v, const void *kmem, const void *vmem,
+maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *kmix,
+                                      const void *vmix, const void *kmem, const void *vmem,
                                       const float *gate_logit, const void *o, const float *lse,
                                       const void *dO, const void *m_prime, const void *W_Km,
                                       const void *W_Vm, void *dq, void *dk, void *dv,
@@ -248,7 +260,7 @@ maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, con
     if (G.N() == 0)   // no tokens: only the parameter gradients are written (as zeros)
         st = check_ptrs({W_Km, W_Vm, dW_Km, dW_Vm});
     else
-        st = check_ptrs({q, k, v, kmem, vmem, o, lse, dO, m_prime, W_Km, W_Vm, dq, dk, dv,
+        st = check_ptrs({q, kmix, vmix, kmem, vmem, o, lse, dO, m_prime, W_Km, W_Vm, dq, dk, dv,
                          dm_prime, dW_Km, dW_Vm});
     if (st != MAGLEV_OK) return st;
     if (!gate_logit || !dgate) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit or dgate is NULL");
@@ -262,7 +274,7 @@ maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, con
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_bwd(G, q, k, v, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km,
+    return hip_status(launch_bwd(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km,
                                  W_Vm, dq, dk, dv, dm_prime, dW_Km, dW_Vm, dgate, accumulate,
                                  layout, rope, stream));
 }

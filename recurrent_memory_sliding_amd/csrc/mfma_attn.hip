@@ -16,9 +16,10 @@
 // column: the softmax state is per lane, the probabilities stay in registers
 // and feed the next product directly (their key order is permuted to match
 // the accumulator layout, and the K/V operand is read in the same order
-// through ds_read_b64_tr_b16). K/V tiles are mixed and rotated while being
-// staged into LDS; key tiles wholly outside a wave's band are skipped, and
-// only tiles that straddle a band edge are masked.
+// through ds_read_b64_tr_b16). The mixed entries k~, v~ arrive precomputed
+// (the projection call writes them), so a K/V tile is a plain copy into LDS;
+// key tiles wholly outside a wave's band are skipped, and only tiles that
+// straddle a band edge are masked.
 #include "common.hpp"
 #include "mfma_kernels.hpp"
 
@@ -26,8 +27,7 @@ namespace maglev {
 namespace mfma {
 
 struct AttnArgs {
-    const bf16 *q, *k, *v, *km, *vm;
-    const float *gate;
+    const bf16 *q, *kx, *vx, *km, *vm;   // kx/vx: mixed entries k~, v~
     const float2 *rope;   // [pos][Dh/2] (cos, sin) or nullptr
     int64_t B, T;
     int H, W;
@@ -59,48 +59,25 @@ MAGLEV_DEV void rotate8(float *lo, float *hi, const float2 *cs, float sign)
     }
 }
 
-// Stage keys [j0, j0+64) of (b, h) into LDS, mixed and rotated:
-//   Ks[kk][c] = k~_{j0+kk}[c], Vs[kk][c] = v~_{j0+kk}[c]; rows outside [0, T) are zero.
+// Stage keys [j0, j0+64) of (b, h) into LDS: Ks[kk][c] = k~_{j0+kk}[c],
+// Vs[kk][c] = v~_{j0+kk}[c]; rows outside [0, T) are zero.
 template <int DH, int KSTR, int VSTR>
-MAGLEV_DEV void stage_kv_tile(const AttnArgs &a, int64_t b, int h, int64_t j0, float sg, bf16 *Ks,
-                              bf16 *Vs, int tid)
+MAGLEV_DEV void stage_kv_tile(const AttnArgs &a, int64_t b, int h, int64_t j0, bf16 *Ks, bf16 *Vs,
+                              int tid)
 {
-    constexpr int CP = DH / 16;   // chunk pairs (c, c + DH/2) per row
+    constexpr int CH = DH / 8;   // 16-byte chunks per row
 #pragma unroll
-    for (int u = tid; u < 64 * CP; u += 256) {
-        const int kk = u / CP, cc = u % CP;
+    for (int u = tid; u < 64 * CH; u += 256) {
+        const int kk = u / CH, cc = u % CH;
         const int64_t j = j0 + kk;
-        float klo[8], khi[8], vlo[8], vhi[8];
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
         if (j >= 0 && j < a.T) {
             const int64_t base = act_row(a, b, j, h) * DH + 8 * cc;
-            float t0[8], t1[8];
-            load8(a.k + base, klo);
-            load8(a.k + base + DH / 2, khi);
-            load8(a.km + base, t0);
-            load8(a.km + base + DH / 2, t1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                klo[e] += sg * t0[e];
-                khi[e] += sg * t1[e];
-            }
-            if (a.rope) rotate8(klo, khi, a.rope + (a.pos0 + j) * (DH / 2) + 8 * cc, 1.0f);
-            load8(a.v + base, vlo);
-            load8(a.v + base + DH / 2, vhi);
-            load8(a.vm + base, t0);
-            load8(a.vm + base + DH / 2, t1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vlo[e] += sg * t0[e];
-                vhi[e] += sg * t1[e];
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) klo[e] = khi[e] = vlo[e] = vhi[e] = 0.0f;
+            kv = *reinterpret_cast<const u32x4 *>(a.kx + base);
+            vv = *reinterpret_cast<const u32x4 *>(a.vx + base);
         }
-        store8(Ks + kk * KSTR + 8 * cc, klo);
-        store8(Ks + kk * KSTR + DH / 2 + 8 * cc, khi);
-        store8(Vs + kk * VSTR + 8 * cc, vlo);
-        store8(Vs + kk * VSTR + DH / 2 + 8 * cc, vhi);
+        *reinterpret_cast<u32x4 *>(Ks + kk * KSTR + 8 * cc) = kv;
+        *reinterpret_cast<u32x4 *>(Vs + kk * VSTR + 8 * cc) = vv;
     }
 }
 
@@ -176,7 +153,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const int h = (int)(bh % a.H);
     const int64_t b = bh / a.H;
     const int64_t i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
-    const float sg = gate_sigmoid(a.gate[h]);
 
     bf16x8 qf[NF];
     if (qi < a.T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
@@ -197,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
 
     for (int64_t j0 = (klo / 64) * 64; j0 < khi; j0 += 64) {
         __syncthreads();
-        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, sg, Ks, Vs, tid);
+        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, Ks, Vs, tid);
         __syncthreads();
         if (!active || j0 > whi || j0 + 63 < wlo) continue;
 
@@ -326,41 +302,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     const int h = (int)(bh % a.H);
     const int64_t b = bh / a.H;
     const int64_t j0 = kt * 128, kw0 = j0 + 32 * w, kj = kw0 + l32;
-    const float sg = gate_sigmoid(a.gate[h]);
     const float qscale = a.scale * kLog2e;
 
-    // This lane's key: k~ (rotated mix) and v~ as B operands.
+    // This lane's key: k~ and v~ as B operands (fragment s: channels 16 s + 8 g .. +7).
     bf16x8 kf[NF], vf[NF];
     if (kj < a.T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
-        constexpr int HS = DH / 32;
 #pragma unroll
-        for (int s = 0; s < HS; ++s) {
-            const int c0 = 16 * s + 8 * g;
-            float lo[8], hi[8], t0[8], t1[8];
-            load8(a.k + base + c0, lo);
-            load8(a.k + base + c0 + DH / 2, hi);
-            load8(a.km + base + c0, t0);
-            load8(a.km + base + c0 + DH / 2, t1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lo[e] += sg * t0[e];
-                hi[e] += sg * t1[e];
-            }
-            if (a.rope) rotate8(lo, hi, a.rope + (a.pos0 + kj) * (DH / 2) + c0, 1.0f);
-            kf[s] = pack8(lo);
-            kf[s + HS] = pack8(hi);
-            load8(a.v + base + c0, lo);
-            load8(a.v + base + c0 + DH / 2, hi);
-            load8(a.vm + base + c0, t0);
-            load8(a.vm + base + c0 + DH / 2, t1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lo[e] += sg * t0[e];
-                hi[e] += sg * t1[e];
-            }
-            vf[s] = pack8(lo);
-            vf[s + HS] = pack8(hi);
+        for (int s = 0; s < NF; ++s) {
+            kf[s] = *reinterpret_cast<const bf16x8 *>(a.kx + base + 16 * s + 8 * g);
+            vf[s] = *reinterpret_cast<const bf16x8 *>(a.vx + base + 16 * s + 8 * g);
         }
     } else {
         zero_frags(kf, NF);
@@ -504,7 +455,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
     const int h = (int)(bh % a.H);
     const int64_t b = bh / a.H;
     const int64_t i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
-    const float sg = gate_sigmoid(a.gate[h]);
 
     bf16x8 qf[NF], df[NF];
     float lse2 = 0.0f, Dq = 0.0f;
@@ -532,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
 
     for (int64_t j0 = (klo / 64) * 64; j0 < khi; j0 += 64) {
         __syncthreads();
-        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, sg, Ks, Vs, tid);
+        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, Ks, Vs, tid);
         __syncthreads();
         if (!active || j0 > whi || j0 + 63 < wlo) continue;
 
@@ -602,26 +552,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
 // ============================================================================
 // Launchers
 // ============================================================================
-static AttnArgs make_args(const Geom &g, const void *q, const void *k, const void *v,
-                          const void *km, const void *vm, const float *gate, const float2 *rope)
+static AttnArgs make_args(const Geom &g, const void *q, const void *kx, const void *vx,
+                          const void *km, const void *vm, const float2 *rope)
 {
     AttnArgs a;
     a.q = static_cast<const bf16 *>(q);
-    a.k = static_cast<const bf16 *>(k);
-    a.v = static_cast<const bf16 *>(v);
+    a.kx = static_cast<const bf16 *>(kx);
+    a.vx = static_cast<const bf16 *>(vx);
     a.km = static_cast<const bf16 *>(km);
     a.vm = static_cast<const bf16 *>(vm);
-    a.gate = gate;
     a.rope = rope;
     a.B = g.B; a.T = g.T; a.H = g.H; a.W = g.W; a.pos0 = g.pos0; a.scale = g.scale;
     return a;
 }
 
-void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
-                          const void *km, const void *vm, const float *gate, const float2 *rope,
-                          void *o, float *lse, hipStream_t s)
+void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
+                          const float2 *rope, void *o, float *lse, hipStream_t s)
 {
-    const AttnArgs a = make_args(g, q, k, v, km, vm, gate, rope);
+    const AttnArgs a = make_args(g, q, kx, vx, nullptr, nullptr, rope);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     if (g.Dh == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(nwg), dim3(256), 0, s, a, static_cast<bf16 *>(o), lse);
@@ -631,12 +579,13 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *k, const voi
 
 int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
 
-void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
+void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const void *km, const void *vm, const float *gate, const void *o,
                           const float *lse, const void *dO, void *dq, void *dk, void *dv,
                           const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
 {
-    const AttnArgs a = make_args(g, q, k, v, km, vm, gate, rope);
+    (void)gate;
+    const AttnArgs a = make_args(g, q, kx, vx, km, vm, rope);
     const int64_t rows = g.N() * g.H;
     const int CH = g.Dh / 8;
     const unsigned pre_blocks = (unsigned)((rows * CH + 255) / 256);

@@ -20,58 +20,99 @@
 namespace maglev {
 namespace mfma {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_ = 3>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
     static constexpr int NT = WM_ * WN_ * 64;
+    static constexpr int NW = WM_ * WN_;
     static constexpr int FM = BM_ / WM_ / 32;   // 32x32 blocks per wave along M
     static constexpr int FN = BN_ / WN_ / 32;
+    static constexpr int STAGES = STAGES_;
 };
 
-// LDS footprint of one operand tile. K-major: [R][BK + 8] (row stride 80 B for
-// BK = 32: conflict-free 16-byte reads). MN-major: [BK][R + 32] (row stride
-// 320 B for R = 128: conflict-free transpose reads per half wave).
-template <bool KMAJOR, int R, int BK>
+// LDS layout of one operand tile, no padding, 16-byte chunks XOR-swizzled so
+// that every read pass is free of bank conflicts:
+//   K-major [R][64] (128-byte rows): chunk c of row r sits in slot c ^ ((r >> 1) & 7);
+//     a ds_read_b128 pass (16 lanes, 16 rows, one chunk) then covers all 64 banks.
+//   MN-major [64][R] (R >= 128): chunk c of row k sits in slot c ^ ((k & 3) << 2);
+//     a transpose-read half wave (4 rows x 4 chunks) then covers all 64 banks.
+template <bool KMAJOR, int R>
 struct OpTile {
-    static constexpr int STRIDE = KMAJOR ? BK + 8 : R + 32;
-    static constexpr int ROWS = KMAJOR ? R : BK;
-    static constexpr int ELEMS = ROWS * STRIDE;
-    static constexpr int CHUNKS = R * BK / 8;
+    static constexpr int ELEMS = R * 64;
+    static constexpr int ROW = KMAJOR ? 64 : R;           // elements per LDS row
+    static constexpr int CPR = ROW / 8;                    // chunks per row
+    static constexpr int ROWS_PER_INSTR = 64 / CPR;        // rows one wave instruction fills
+    static constexpr int INSTR = (KMAJOR ? R : 64) / ROWS_PER_INSTR;
+    MAGLEV_DEV static int slot(int row, int c)
+    {
+        return KMAJOR ? (c ^ ((row >> 1) & 7)) : (c ^ ((row & 3) << 2));
+    }
 };
+
+// Source of rows that must read as zero (the shift's first row, K tails).
+__device__ __attribute__((aligned(256))) bf16 g_zero_rows[64] = {};
 
 MAGLEV_DEV bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 
-template <bool KMAJOR, int STRIDE>
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes from global memory straight into LDS at base + lane * 16.
+MAGLEV_DEV void dma16(const bf16 *src, bf16 *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+MAGLEV_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <bool KMAJOR, int R>
 MAGLEV_DEV bf16x8 read_frag(const bf16 *lds, int rb, int ks, int lane)
 {
+    using L = OpTile<KMAJOR, R>;
     if constexpr (KMAJOR) {
-        return *reinterpret_cast<const bf16x8 *>(lds + (rb * 32 + (lane & 31)) * STRIDE + ks * 16 +
-                                                 8 * (lane >> 5));
+        const int r = rb * 32 + (lane & 31);
+        const int c = 2 * ks + (lane >> 5);
+        return *reinterpret_cast<const bf16x8 *>(lds + r * 64 + L::slot(r, c) * 8);
     } else {
         const int n0 = rb * 32 + 16 * ((lane >> 4) & 1);
         const int k0 = ks * 16 + 8 * (lane >> 5);
         const int j = lane & 15;
-        const i16x4 lo = lds_read_tr16(lds + (k0 + (j >> 2)) * STRIDE + n0 + 4 * (j & 3));
-        const i16x4 hi = lds_read_tr16(lds + (k0 + 4 + (j >> 2)) * STRIDE + n0 + 4 * (j & 3));
+        const int n = n0 + 4 * (j & 3);
+        const int c = n >> 3, e = n & 7;
+        const int ka = k0 + (j >> 2), kb = ka + 4;
+        const i16x4 lo = lds_read_tr16(lds + ka * R + L::slot(ka, c) * 8 + e);
+        const i16x4 hi = lds_read_tr16(lds + kb * R + L::slot(kb, c) * 8 + e);
         return join_tr(lo, hi);
     }
 }
 
 // C[M,N] = sum_k A(m,k) B(n,k) over k in this workgroup's split.
-// P supplies: M, N, K; A_KMAJOR/B_KMAJOR; a_ptr/b_ptr giving the address of
-// 8 consecutive elements along the contiguous dimension (nullptr = zeros);
-// store(m, n, value, split).
+// P supplies: M, N, K; A_KMAJOR/B_KMAJOR; for a K-major operand x_ptr(row, k),
+// the address of 8 elements along k, linear in k inside segments of x_kseg
+// elements (0: one segment); for an MN-major operand (stored [k][col]) x_lin(k,
+// col), the address of 8 elements along col, rows x_ld elements apart; nullptr
+// marks a chunk outside the matrix (M/N tails). Operands hold no zero rows:
+// the shifts are applied in store(m, t, n, value, split), where t = m mod T.
+// Pipeline: a ring of 3 LDS stages filled by direct global->LDS loads two
+// stages ahead of the MFMA work; one barrier per 64-wide K step.
 template <class Cfg, class P>
 __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
 {
-    using TA = OpTile<P::A_KMAJOR, Cfg::BM, Cfg::BK>;
-    using TB = OpTile<P::B_KMAJOR, Cfg::BN, Cfg::BK>;
-    constexpr int CA = TA::CHUNKS / Cfg::NT;
-    constexpr int CB = TB::CHUNKS / Cfg::NT;
-    static_assert(TA::CHUNKS % Cfg::NT == 0 && TB::CHUNKS % Cfg::NT == 0, "tile/thread mismatch");
-    __shared__ __attribute__((aligned(16))) bf16 lds[2][TA::ELEMS + TB::ELEMS];
+    using TA = OpTile<P::A_KMAJOR, Cfg::BM>;
+    using TB = OpTile<P::B_KMAJOR, Cfg::BN>;
+    constexpr int STAGE = TA::ELEMS + TB::ELEMS;
+    static_assert(TA::INSTR % Cfg::NW == 0 && TB::INSTR % Cfg::NW == 0, "tile/wave mismatch");
+    constexpr int IA = TA::INSTR / Cfg::NW, IB = TB::INSTR / Cfg::NW;   // DMA instructions per wave
+    constexpr int PER_STAGE = IA + IB;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[Cfg::STAGES * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
     const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
@@ -83,54 +124,75 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
     const int64_t ke = kb + kper < p.K ? kb + kper : p.K;
     const int nk = ke > kb ? (int)((ke - kb + Cfg::BK - 1) / Cfg::BK) : 0;
 
-    bf16x8 ra[CA], rb[CB];
-    auto gload = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int c = tid + i * Cfg::NT;
-            const bf16 *src;
-            if constexpr (P::A_KMAJOR) {
-                const int r = c / (Cfg::BK / 8), kc = c % (Cfg::BK / 8);
-                src = (k0 + 8 * kc < ke) ? p.a_ptr(m0 + r, k0 + 8 * kc) : nullptr;
-            } else {
-                const int kr = c / (Cfg::BM / 8), mc = c % (Cfg::BM / 8);
-                src = (k0 + kr < ke) ? p.a_ptr(k0 + kr, m0 + 8 * mc) : nullptr;
-            }
-            ra[i] = src ? *reinterpret_cast<const bf16x8 *>(src) : zero8();
-        }
-#pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int c = tid + i * Cfg::NT;
-            const bf16 *src;
-            if constexpr (P::B_KMAJOR) {
-                const int r = c / (Cfg::BK / 8), kc = c % (Cfg::BK / 8);
-                src = (k0 + 8 * kc < ke) ? p.b_ptr(n0 + r, k0 + 8 * kc) : nullptr;
-            } else {
-                const int kr = c / (Cfg::BN / 8), nc = c % (Cfg::BN / 8);
-                src = (k0 + kr < ke) ? p.b_ptr(k0 + kr, n0 + 8 * nc) : nullptr;
-            }
-            rb[i] = src ? *reinterpret_cast<const bf16x8 *>(src) : zero8();
-        }
+    // This lane's chunk of every DMA instruction: row inside the tile (its LDS
+    // slot is fixed by the lane), the chunk it fetches (the swizzle is an
+    // involution), and the global address at the current K step.
+    const bf16 *pa[IA];
+    const bf16 *pb[IB];
+    int ka[IA], kbk[IB];   // k offset of the chunk inside the 64-wide step
+    auto a_addr = [&](int i, int64_t k0) -> const bf16 * {
+        const int row = (wave * IA + i) * TA::ROWS_PER_INSTR + lane / TA::CPR;
+        const int c = TA::slot(row, lane % TA::CPR);
+        if constexpr (P::A_KMAJOR) return p.a_ptr(m0 + row, k0 + 8 * c);
+        else return p.a_lin(k0 + row, m0 + 8 * c);
     };
-    auto lstore = [&](int buf) {
-        bf16 *la = lds[buf];
-        bf16 *lb = lds[buf] + TA::ELEMS;
+    auto b_addr = [&](int i, int64_t k0) -> const bf16 * {
+        const int row = (wave * IB + i) * TB::ROWS_PER_INSTR + lane / TB::CPR;
+        const int c = TB::slot(row, lane % TB::CPR);
+        if constexpr (P::B_KMAJOR) return p.b_ptr(n0 + row, k0 + 8 * c);
+        else return p.b_lin(k0 + row, n0 + 8 * c);
+    };
 #pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int c = tid + i * Cfg::NT;
-            int off;
-            if constexpr (P::A_KMAJOR) off = (c / (Cfg::BK / 8)) * TA::STRIDE + 8 * (c % (Cfg::BK / 8));
-            else off = (c / (Cfg::BM / 8)) * TA::STRIDE + 8 * (c % (Cfg::BM / 8));
-            *reinterpret_cast<bf16x8 *>(la + off) = ra[i];
+    for (int i = 0; i < IA; ++i) {
+        const int row = (wave * IA + i) * TA::ROWS_PER_INSTR + lane / TA::CPR;
+        ka[i] = P::A_KMAJOR ? 8 * TA::slot(row, lane % TA::CPR) : row;
+        pa[i] = a_addr(i, kb);
+    }
+#pragma unroll
+    for (int i = 0; i < IB; ++i) {
+        const int row = (wave * IB + i) * TB::ROWS_PER_INSTR + lane / TB::CPR;
+        kbk[i] = P::B_KMAJOR ? 8 * TB::slot(row, lane % TB::CPR) : row;
+        pb[i] = b_addr(i, kb);
+    }
+    const int64_t a_step = P::A_KMAJOR ? Cfg::BK : Cfg::BK * p.a_ld;
+    const int64_t b_step = P::B_KMAJOR ? Cfg::BK : Cfg::BK * p.b_ld;
+
+    // DMA of K step `it` into stage `buf` (the pointers are at step it), then
+    // advance the pointers. Tails and segment switches take the slow branch.
+    auto issue = [&](int it, int buf) {
+        const int64_t k0 = kb + (int64_t)it * Cfg::BK;
+        bf16 *sa = lds + buf * STAGE;
+        bf16 *sb = sa + TA::ELEMS;
+        const bool tail = k0 + Cfg::BK > ke;
+        if (p.a_kseg > 0 && it > 0 && (k0 % p.a_kseg) == 0) {
+#pragma unroll
+            for (int i = 0; i < IA; ++i) pa[i] = a_addr(i, k0);
+        }
+        if (p.b_kseg > 0 && it > 0 && (k0 % p.b_kseg) == 0) {
+#pragma unroll
+            for (int i = 0; i < IB; ++i) pb[i] = b_addr(i, k0);
+        }
+        if (!tail) {
+#pragma unroll
+            for (int i = 0; i < IA; ++i) dma16(pa[i] ? pa[i] : g_zero_rows, sa + (wave * IA + i) * 512);
+#pragma unroll
+            for (int i = 0; i < IB; ++i) dma16(pb[i] ? pb[i] : g_zero_rows, sb + (wave * IB + i) * 512);
+        } else {
+#pragma unroll
+            for (int i = 0; i < IA; ++i) {
+                const bool z = !pa[i] || k0 + ka[i] >= ke;
+                dma16(z ? g_zero_rows : pa[i], sa + (wave * IA + i) * 512);
+            }
+#pragma unroll
+            for (int i = 0; i < IB; ++i) {
+                const bool z = !pb[i] || k0 + kbk[i] >= ke;
+                dma16(z ? g_zero_rows : pb[i], sb + (wave * IB + i) * 512);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int c = tid + i * Cfg::NT;
-            int off;
-            if constexpr (P::B_KMAJOR) off = (c / (Cfg::BK / 8)) * TB::STRIDE + 8 * (c % (Cfg::BK / 8));
-            else off = (c / (Cfg::BN / 8)) * TB::STRIDE + 8 * (c % (Cfg::BN / 8));
-            *reinterpret_cast<bf16x8 *>(lb + off) = rb[i];
-        }
+        for (int i = 0; i < IA; ++i) pa[i] = pa[i] ? pa[i] + a_step : nullptr;
+#pragma unroll
+        for (int i = 0; i < IB; ++i) pb[i] = pb[i] ? pb[i] + b_step : nullptr;
     };
 
     f32x16 acc[Cfg::FM][Cfg::FN];
@@ -141,135 +203,223 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    if (nk > 0) {
-        gload(kb);
-        lstore(0);
-    }
-    __syncthreads();
+    constexpr int AHEAD = Cfg::STAGES - 1;         // K steps in flight ahead of the MFMA work
+#pragma unroll
+    for (int s0 = 0; s0 < AHEAD; ++s0)
+        if (s0 < nk) issue(s0, s0);
     for (int it = 0; it < nk; ++it) {
-        const int cur = it & 1;
-        if (it + 1 < nk) gload(kb + (int64_t)(it + 1) * Cfg::BK);
-        const bf16 *la = lds[cur];
-        const bf16 *lb = lds[cur] + TA::ELEMS;
+        // stage it has landed once at most (AHEAD - 1) later stages are still in flight
+        if (AHEAD >= 2 && it + 1 < nk) wait_vmcnt<(AHEAD >= 2 ? PER_STAGE : 0)>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();                // every wave's share of stage it is in LDS,
+                                                     // and stage it-1 is no longer being read
+        if (it + AHEAD < nk) issue(it + AHEAD, (it + AHEAD) % Cfg::STAGES);
+        const bf16 *la = lds + (it % Cfg::STAGES) * STAGE;
+        const bf16 *lb = la + TA::ELEMS;
+        bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) af[0][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) bfr[0][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, 0, lane);
 #pragma unroll
         for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
-            bf16x8 af[Cfg::FM], bfr[Cfg::FN];
+            const int cur = ks & 1;
+            if (ks + 1 < Cfg::BK / 16) {
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+                    af[cur ^ 1][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, ks + 1, lane);
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    bfr[cur ^ 1][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, ks + 1, lane);
+            }
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
-                af[i] = read_frag<P::A_KMAJOR, TA::STRIDE>(la, wm * Cfg::FM + i, ks, lane);
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j)
-                bfr[j] = read_frag<P::B_KMAJOR, TB::STRIDE>(lb, wn * Cfg::FN + j, ks, lane);
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[cur][i], bfr[cur][j], acc[i][j]);
         }
-        if (it + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
     }
 
+    // Epilogue: row index m and its position t = m mod T (from m0 mod T).
     const int g = lane >> 5;
+    const int64_t t0 = p.T > 0 ? m0 % p.T : 0;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
+        for (int e = 0; e < 16; ++e) {
+            const int r = (wm * Cfg::FM + i) * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+            const int64_t m = m0 + r;
+            if (m >= p.M) continue;
+            int64_t t = t0 + r;
+            if (p.T > 0) while (t >= p.T) t -= p.T;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + (wm * Cfg::FM + i) * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (m < p.M && n < p.N) p.store(m, n, acc[i][j][e], blockIdx.z);
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
+                if (n < p.N) p.store(m, t, n, acc[i][j][e], blockIdx.z);
             }
         }
+}
+
+// Skinny product for M <= 64 rows (the decode step projects one memory row per
+// stream): each workgroup owns 16 output columns, its four waves split K, and
+// operands come straight from global memory (both K-contiguous) into
+// v_mfma_f32_16x16x32_bf16 fragments; the four partial tiles are summed in LDS.
+//   16x16x32 layout: operand lane l holds row/column l % 16 and K entries
+//   8 (l / 16) .. +7; result lane l holds column l % 16, rows 4 (l / 16) .. +3.
+template <class P>
+__global__ __launch_bounds__(256) void gemm_skinny_bf16(P p)
+{
+    static_assert(P::A_KMAJOR && P::B_KMAJOR, "skinny path needs K-contiguous operands");
+    __shared__ float red[4][4][64][4];     // [wave][row block][lane][e]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t kq = ((p.K + 127) / 128) * 32;              // K quarter, multiple of 32
+    const int64_t k_lo = w * kq, k_hi = (k_lo + kq < p.K) ? k_lo + kq : p.K;
+    const int r16 = lane & 15, kg = 8 * (lane >> 4);
+    f32x4 acc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t k0 = k_lo; k0 < k_hi; k0 += 32) {
+        const int64_t k = k0 + kg;
+        const bool kin = k < k_hi;
+        const bf16 *bp = kin ? p.b_ptr(n0 + r16, k) : nullptr;
+        const bf16x8 bf = bp ? *reinterpret_cast<const bf16x8 *>(bp) : zero8();
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const bf16 *ap = kin ? p.a_ptr(16 * rb + r16, k) : nullptr;
+            const bf16x8 af = ap ? *reinterpret_cast<const bf16x8 *>(ap) : zero8();
+            acc[rb] = mfma16(af, bf, acc[rb]);
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[w][rb][lane][e] = acc[rb][e];
+    __syncthreads();
+    // thread t sums one (row block, lane) slot over the four waves: 256 slots
+    const int rb = tid >> 6, l = tid & 63;
+    const int64_t n = n0 + (l & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x = red[0][rb][l][e] + red[1][rb][l][e] + red[2][rb][l][e] + red[3][rb][l][e];
+        const int64_t m = 16 * rb + 4 * (l >> 4) + e;
+        if (m < p.M && n < p.N) p.store(m, m % p.T, n, x, 0);
+    }
 }
 
 // ---------------------------------------------------------------------------
 // Problems
 // ---------------------------------------------------------------------------
-// kmem | vmem [N_tok, 2HD] = X [N_tok, d] * Wcat[2HD, d]^T
+// The three products. Operands are plain row-major matrices; the one-token
+// shift of the memory is applied where results are stored.
+//
+// Y [N_tok, 2HD] = m [N_tok, d] * [W_Km; W_Vm]^T. With shift 1, Y row (b,t)
+// is the memory term of token (b,t+1): kmem[b,t+1] = Y[b,t] (t <= T-2) and
+// kmem[b,0] = 0; with shift 0, kmem = Y.
 struct ProjFwd {
     static constexpr bool A_KMAJOR = true, B_KMAJOR = true;
     const bf16 *m, *wk, *wv;
     bf16 *km, *vm;
     int64_t M, N, K, T;
     int HD, shift;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0, b_ld = 0;
     MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const
     {
-        if (row >= M) return nullptr;
-        if (row % T < shift) return nullptr;
-        return m + (row - shift) * K + k;
+        return row < M ? m + row * K + k : nullptr;
     }
     MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const
     {
         if (n >= N) return nullptr;
         return n < HD ? wk + n * K + k : wv + (n - HD) * K + k;
     }
-    MAGLEV_DEV void store(int64_t row, int64_t n, float x, int) const
+    MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV void store(int64_t row, int64_t t, int64_t n, float x, int) const
     {
-        if (n < HD) km[row * HD + n] = f2bf(x);
-        else vm[row * HD + (n - HD)] = f2bf(x);
+        bf16 *out = n < HD ? km : vm;
+        const int64_t c = n < HD ? n : n - HD;
+        if (shift) {
+            if (t == 0) out[row * HD + c] = f2bf(0.0f);
+            if (t + 1 < T) out[(row + 1) * HD + c] = f2bf(x);
+        } else {
+            out[row * HD + c] = f2bf(x);
+        }
     }
 };
 
-// dX [N_tok, d] = G [N_tok, 2HD] * Ws [2HD, d]; row (b,t) lands on dm'[b,t-1].
+// dX [N_tok, d] = G [N_tok, 2HD] * Ws [2HD, d], G = [dk | dv] (k segments of
+// HD), Ws = s_h-scaled [W_Km; W_Vm] stored [k][d]. dX row (b,t) is the
+// gradient of the memory row m'[b,t-1] (t >= 1).
 struct ProjBwdDm {
     static constexpr bool A_KMAJOR = true, B_KMAJOR = false;
-    const bf16 *dk, *dv, *ws;   // ws = s_h-scaled [W_Km; W_Vm]
+    const bf16 *dk, *dv, *ws;
     float *dm;
     int64_t M, N, K, T;
     int HD;
     bool acc;
+    int64_t a_kseg, b_ld;
+    static constexpr int64_t b_kseg = 0, a_ld = 0;
     MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const
     {
         if (row >= M) return nullptr;
         return k < HD ? dk + row * HD + k : dv + row * HD + (k - HD);
     }
-    MAGLEV_DEV const bf16 *b_ptr(int64_t k, int64_t n) const
+    MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const
     {
-        if (n >= N) return nullptr;
-        return ws + k * N + n;
+        return n < N ? ws + k * N + n : nullptr;
     }
-    MAGLEV_DEV void store(int64_t row, int64_t n, float x, int) const
+    MAGLEV_DEV void store(int64_t row, int64_t t, int64_t n, float x, int) const
     {
-        if (row % T == 0) return;
+        if (t == 0) return;
         float *p = dm + (row - 1) * N + n;
         *p = acc ? *p + x : x;
     }
 };
 
-// dW [2HD, d] = G^T [2HD, N_tok] * X [N_tok, d], one split of the token range.
+// dW partial [2HD, d] = sum over tokens u of G[u+1]^T m'[u] (u = 0 .. N_tok-2),
+// one split of that range. A = G rows shifted by one token, stored [u][2HD]
+// (columns < HD from dk, the rest from dv); B = m' stored [u][d]. The pairs
+// that cross a sequence boundary (u = b T - 1) are subtracted in dw_reduce.
 struct ProjBwdDw {
     static constexpr bool A_KMAJOR = false, B_KMAJOR = false;
     const bf16 *dk, *dv, *m;
     float *part;      // [ksplit][2HD][d]
     int64_t M, N, K, T;
     int HD;
-    MAGLEV_DEV const bf16 *a_ptr(int64_t tok, int64_t r) const
+    int64_t a_ld, b_ld;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0;
+    MAGLEV_DEV const bf16 *a_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t u, int64_t r) const
     {
         if (r >= M) return nullptr;
-        return r < HD ? dk + tok * HD + r : dv + tok * HD + (r - HD);
+        return r < HD ? dk + (u + 1) * HD + r : dv + (u + 1) * HD + (r - HD);
     }
-    MAGLEV_DEV const bf16 *b_ptr(int64_t tok, int64_t e) const
+    MAGLEV_DEV const bf16 *b_lin(int64_t u, int64_t e) const
     {
-        if (e >= N) return nullptr;
-        if (tok % T == 0) return nullptr;
-        return m + (tok - 1) * N + e;
+        return e < N ? m + u * N + e : nullptr;
     }
-    MAGLEV_DEV void store(int64_t r, int64_t e, float x, int split) const
+    MAGLEV_DEV void store(int64_t r, int64_t, int64_t e, float x, int split) const
     {
         part[((int64_t)split * M + r) * N + e] = x;
     }
 };
 
-using GemmCfg = TileCfg<128, 128, 32, 2, 2>;
+// Tile configurations, chosen by timing the three products at the d20 shape
+// (N_tok = 16384, d = 1280, 10 x 128 heads): two LDS stages and 8 or 16 waves
+// per workgroup, so that each SIMD has several waves to cover LDS and barrier
+// latency (one wave per SIMD left the matrix cores idle most of the time).
+using ProjCfg = TileCfg<128, 128, 2, 4, 2>;   // wave tile 64 x 32, 2 workgroups per CU
+using DwCfg = TileCfg<256, 256, 4, 4, 2>;     // wave tile 64 x 64, split over tokens
 
-template <class P>
+template <class Cfg, class P>
 static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s)
 {
-    const int64_t ntm = (p.M + GemmCfg::BM - 1) / GemmCfg::BM;
-    const int64_t ntn = (p.N + GemmCfg::BN - 1) / GemmCfg::BN;
-    hipLaunchKernelGGL((gemm_bf16<GemmCfg, P>), dim3((unsigned)(ntm * ntn), 1, ksplit),
-                       dim3(GemmCfg::NT), 0, s, p, kper);
+    const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
+    const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
+    hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn), 1, ksplit),
+                       dim3(Cfg::NT), 0, s, p, kper);
 }
 
 void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
@@ -283,7 +433,11 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
     p.vm = static_cast<bf16 *>(vm);
     p.M = g.N(); p.N = 2 * (int64_t)g.HD(); p.K = g.d; p.T = g.T;
     p.HD = g.HD(); p.shift = shift;
-    run_gemm(p, 1, p.K, s);
+    if (p.M <= 64)
+        hipLaunchKernelGGL(gemm_skinny_bf16<ProjFwd>, dim3((unsigned)((p.N + 15) / 16)), dim3(256), 0,
+                           s, p);
+    else
+        run_gemm<ProjCfg>(p, 1, p.K, s);
 }
 
 // s_h-scaled copy of [W_Km; W_Vm] (bf16), 8 elements per thread.
@@ -304,27 +458,35 @@ __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate,
     store8(out + i * 8, x);
 }
 
-// dW = s_h * sum over splits (fixed order), optionally added to the output.
-__global__ void dw_reduce(const float *part, int ksplit, int HD, int Dh, int d, const float *gate,
-                          float *dwk, float *dwv, bool acc)
+// dW = s_h * (sum over splits, fixed order, minus the sequence-boundary pairs
+// G[bT]^T m'[bT-1], b = 1..B-1), optionally added to the output.
+__global__ void dw_reduce(const float *part, int ksplit, int HD, int Dh, int d, int64_t B,
+                          int64_t T, const bf16 *dk, const bf16 *dv, const bf16 *m,
+                          const float *gate, float *dwk, float *dwv, bool acc)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tot = 2 * (int64_t)HD * d;
     if (i >= tot) return;
     float x = 0.0f;
     for (int sp = 0; sp < ksplit; ++sp) x += part[sp * tot + i];
-    const int64_t r = i / d;
+    const int64_t r = i / d, e = i % d;
     const int rr = (int)(r < HD ? r : r - HD);
+    const bf16 *G = r < HD ? dk : dv;
+    for (int64_t b = 1; b < B; ++b)
+        x -= bf2f(G[(b * T) * HD + rr]) * bf2f(m[(b * T - 1) * d + e]);
     x *= gate_sigmoid(gate[rr / Dh]);
-    float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d + (i % d);
+    float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d + e;
     *out = acc ? *out + x : x;
 }
 
 int dw_ksplit(const Geom &g)
 {
-    const int64_t tiles = ((2 * (int64_t)g.HD() + 127) / 128) * ((g.d + 127) / 128);
-    int64_t ks = (1024 + tiles - 1) / tiles;            // aim for about 4 workgroups per CU
-    const int64_t max_by_k = (g.N() + 1023) / 1024;      // keep >= 1024 tokens per split
+    // 256 x 256 tiles of dW (one workgroup per CU at a time): split the token
+    // range so that the grid is close to one workgroup per CU, keeping >= 1024
+    // tokens per split.
+    const int64_t tiles = ((2 * (int64_t)g.HD() + 255) / 256) * ((g.d + 255) / 256);
+    int64_t ks = 256 / tiles;
+    const int64_t max_by_k = (g.N() + 1023) / 1024;
     if (ks > max_by_k) ks = max_by_k;
     if (ks > 16) ks = 16;
     if (ks < 1) ks = 1;
@@ -353,7 +515,9 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         p.M = g.N(); p.N = g.d; p.K = 2 * (int64_t)HD; p.T = g.T;
         p.HD = HD;
         p.acc = (acc & 1u) != 0;
-        run_gemm(p, 1, p.K, s);
+        p.a_kseg = HD;
+        p.b_ld = g.d;
+        run_gemm<ProjCfg>(p, 1, p.K, s);
     }
     {
         ProjBwdDw p;
@@ -361,15 +525,18 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         p.dv = static_cast<const bf16 *>(dv);
         p.m = static_cast<const bf16 *>(m_prime);
         p.part = ws.dW_part;
-        p.M = 2 * (int64_t)HD; p.N = g.d; p.K = g.N(); p.T = g.T;
+        p.M = 2 * (int64_t)HD; p.N = g.d; p.K = g.N() - 1; p.T = 0;
         p.HD = HD;
+        p.a_ld = HD;
+        p.b_ld = g.d;
         const int ks = ws.ksplit;
         int64_t kper = (p.K + ks - 1) / ks;
-        kper = (kper + GemmCfg::BK - 1) / GemmCfg::BK * GemmCfg::BK;
-        run_gemm(p, ks, kper, s);
+        kper = (kper + 63) / 64 * 64;
+        run_gemm<DwCfg>(p, ks, kper, s);
         const int64_t tot = 2 * (int64_t)HD * g.d;
         hipLaunchKernelGGL(dw_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s,
-                           ws.dW_part, ks, HD, g.Dh, g.d, gate, dWk, dWv, (acc & 2u) != 0);
+                           ws.dW_part, ks, HD, g.Dh, g.d, g.B, g.T, p.dk, p.dv, p.m, gate, dWk,
+                           dWv, (acc & 2u) != 0);
     }
 }
 

@@ -11,14 +11,14 @@ namespace mfma {
 void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
                          void *km, void *vm, hipStream_t s);
 
-// Banded flash-style forward with RoPE and gate mixing fused into the K/V tile load.
-void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
-                          const void *km, const void *vm, const float *gate, const float2 *rope,
-                          void *o, float *lse, hipStream_t s);
+// Banded flash-style forward over the mixed entries (K/V tiles staged by
+// direct global->LDS loads, double-buffered).
+void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
+                          const float2 *rope, void *o, float *lse, hipStream_t s);
 
 // Attention backward: rowsum(dO*O), key-stationary dK/dV pass (with the gate
 // partials), query-stationary dQ pass.
-void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *k, const void *v,
+void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const void *km, const void *vm, const float *gate, const void *o,
                           const float *lse, const void *dO, void *dq, void *dk, void *dv,
                           const BwdWorkspace &ws, const float2 *rope, hipStream_t s);

@@ -163,19 +163,30 @@ void project_simt(const Geom &g, int shift, const void *m, const void *wk, const
 }
 
 template <typename T, int DH>
-void fwd_simt(const Geom &g, const void *q, const void *k, const void *v, const void *km,
-              const void *vm, const float *gate, const float2 *rope, void *o, float *lse,
-              hipStream_t s)
+void fwd_simt(const Geom &g, const void *q, const void *kx, const void *vx, const float2 *rope,
+              void *o, float *lse, hipStream_t s)
 {
     hipLaunchKernelGGL((simt::attn_fwd_rows<T, DH>), dim3(g.T, g.H, g.B), dim3(DH), 0, s,
-                       row_args(g, gate, rope), static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v),
-                       static_cast<const T *>(km), static_cast<const T *>(vm),
+                       row_args(g, nullptr, rope), static_cast<const T *>(q),
+                       static_cast<const T *>(kx), static_cast<const T *>(vx),
                        static_cast<T *>(o), lse);
 }
 
 template <typename T, int DH>
-void attn_bwd_simt(const Geom &g, const void *q, const void *k, const void *v, const void *km,
+void mix_launch(const Geom &g, const void *k, const void *v, const void *km, const void *vm,
+                const float *gate, const float2 *rope, void *kx, void *vx, hipStream_t s)
+{
+    const int64_t rows = g.N() * g.H;
+    const int64_t threads = rows * (DH / 16);
+    hipLaunchKernelGGL((simt::mix_entries<T, DH>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, s, rows, g.H, g.T, g.pos0, rope, gate,
+                       static_cast<const T *>(k), static_cast<const T *>(v),
+                       static_cast<const T *>(km), static_cast<const T *>(vm),
+                       static_cast<T *>(kx), static_cast<T *>(vx));
+}
+
+template <typename T, int DH>
+void attn_bwd_simt(const Geom &g, const void *q, const void *kx, const void *vx, const void *km,
                    const void *vm, const float *gate, const void *o, const float *lse,
                    const void *dO, void *dq, void *dk, void *dv, const BwdWorkspace &ws,
                    const float2 *rope, hipStream_t s)
@@ -185,13 +196,12 @@ void attn_bwd_simt(const Geom &g, const void *q, const void *k, const void *v, c
     hipLaunchKernelGGL((simt::bwd_rowdot<T, DH>), grid, dim3(DH), 0, s, a,
                        static_cast<const T *>(o), static_cast<const T *>(dO), ws.D);
     hipLaunchKernelGGL((simt::bwd_dq_rows<T, DH>), grid, dim3(DH), 0, s, a,
-                       static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), static_cast<const T *>(km),
-                       static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
+                       static_cast<const T *>(q), static_cast<const T *>(kx),
+                       static_cast<const T *>(vx), static_cast<const T *>(dO), lse, ws.D,
                        static_cast<T *>(dq));
     hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH>), grid, dim3(DH), 0, s, a,
-                       static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), static_cast<const T *>(km),
+                       static_cast<const T *>(q), static_cast<const T *>(kx),
+                       static_cast<const T *>(vx), static_cast<const T *>(km),
                        static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
                        static_cast<T *>(dk), static_cast<T *>(dv), ws.ds_part);
 }
@@ -232,15 +242,27 @@ hipError_t launch_project(const Geom &g, int shift, const void *m, const void *w
     return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *k, const void *v,
-                           const void *km, const void *vm, const float *gate, const float2 *rope,
-                           void *o, float *lse, hipStream_t s)
+hipError_t launch_mix(const Geom &g, const void *k, const void *v, const void *km, const void *vm,
+                      const float *gate, const float2 *rope, void *kx, void *vx, hipStream_t s)
 {
     if (g.dtype == MAGLEV_BF16) {
-        mfma::launch_attn_fwd_bf16(g, q, k, v, km, vm, gate, rope, o, lse, s);
+        if (g.Dh == 128) mix_launch<bf16, 128>(g, k, v, km, vm, gate, rope, kx, vx, s);
+        else mix_launch<bf16, 64>(g, k, v, km, vm, gate, rope, kx, vx, s);
     } else {
-        if (g.Dh == 128) fwd_simt<float, 128>(g, q, k, v, km, vm, gate, rope, o, lse, s);
-        else fwd_simt<float, 64>(g, q, k, v, km, vm, gate, rope, o, lse, s);
+        if (g.Dh == 128) mix_launch<float, 128>(g, k, v, km, vm, gate, rope, kx, vx, s);
+        else mix_launch<float, 64>(g, k, v, km, vm, gate, rope, kx, vx, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kx, const void *vx,
+                           const float2 *rope, void *o, float *lse, hipStream_t s)
+{
+    if (g.dtype == MAGLEV_BF16) {
+        mfma::launch_attn_fwd_bf16(g, q, kx, vx, rope, o, lse, s);
+    } else {
+        if (g.Dh == 128) fwd_simt<float, 128>(g, q, kx, vx, rope, o, lse, s);
+        else fwd_simt<float, 64>(g, q, kx, vx, rope, o, lse, s);
     }
     return hipGetLastError();
 }
@@ -264,7 +286,7 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base)
     return off;
 }
 
-hipError_t launch_bwd(const Geom &g, const void *q, const void *k, const void *v, const void *km,
+hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *vx, const void *km,
                       const void *vm, const float *gate, const void *o, const float *lse,
                       const void *dO, const void *m_prime, const void *wk, const void *wv,
                       void *dq, void *dk, void *dv, float *dm_prime, float *dWk, float *dWv,
@@ -284,13 +306,13 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *k, const void *v
     }
     int64_t per_bh;
     if (g.dtype == MAGLEV_BF16) {
-        mfma::launch_attn_bwd_bf16(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
         per_bh = mfma::ds_part_per_bh(g);
     } else {
         if (g.Dh == 128)
-            attn_bwd_simt<float, 128>(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+            attn_bwd_simt<float, 128>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
         else
-            attn_bwd_simt<float, 64>(g, q, k, v, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+            attn_bwd_simt<float, 64>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
         per_bh = g.T;
     }
     hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,

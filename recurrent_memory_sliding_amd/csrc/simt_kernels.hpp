@@ -79,39 +79,25 @@ MAGLEV_DEV const float2 *rope_row(const RowArgs &a, int64_t t, int Dh)
     return a.rope ? a.rope + (a.pos0 + t) * (Dh / 2) : nullptr;
 }
 
-// Mixed key / value of channel c at (b, t, h):
-//   k~ = R k + s R kmem,   v~ = v + s vmem.
-template <typename T, int DH>
-MAGLEV_DEV void mixed_kv(const RowArgs &a, const T *k, const T *v, const T *km, const T *vm,
-                         int64_t row, int64_t t, int c, float s, float &kt, float &vt)
-{
-    const float2 *tab = rope_row(a, t, DH);
-    const T *kr = k + row * DH, *kmr = km + row * DH;
-    kt = rope_channel<T, DH>(kr, c, tab, false) + s * rope_channel<T, DH>(kmr, c, tab, false);
-    vt = to_f<T>(v[row * DH + c]) + s * to_f<T>(vm[row * DH + c]);
-}
-
 // ---------------------------------------------------------------------------
 // Forward: one workgroup per (i, h, b), one thread per channel.
 // ---------------------------------------------------------------------------
 template <typename T, int DH>
-__global__ __launch_bounds__(DH) void attn_fwd_rows(RowArgs a, const T *q, const T *k, const T *v,
-                                                     const T *km, const T *vm, T *o, float *lse)
+__global__ __launch_bounds__(DH) void attn_fwd_rows(RowArgs a, const T *q, const T *kx,
+                                                     const T *vx, T *o, float *lse)
 {
     __shared__ float red[2];
     const int64_t i = blockIdx.x;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int c = threadIdx.x;
-    const float s = gate_sigmoid(a.gate[h]);
     const int64_t qrow = (b * a.T + i) * a.H + h;
     const float qh = rope_channel<T, DH>(q + qrow * DH, c, rope_row(a, i, DH), false);
     const int64_t lo = i - a.W + 1 > 0 ? i - a.W + 1 : 0;
     float mx = -INFINITY, l = 0.0f, acc = 0.0f;
     for (int64_t j = lo; j <= i; ++j) {
         const int64_t krow = (b * a.T + j) * a.H + h;
-        float kt, vt;
-        mixed_kv<T, DH>(a, k, v, km, vm, krow, j, c, s, kt, vt);
+        const float kt = to_f<T>(kx[krow * DH + c]), vt = to_f<T>(vx[krow * DH + c]);
         const float sc = block_sum<DH>(qh * kt, red) * a.scale;
         const float mn = fmaxf(mx, sc);
         const float corr = __expf(mx - mn);
@@ -142,9 +128,9 @@ __global__ __launch_bounds__(DH) void bwd_rowdot(RowArgs a, const T *o, const T 
 //   P_ij = exp(scale q^_i.k~_j - lse_i), dP_ij = dO_i.v~_j, dS_ij = P_ij (dP_ij - D_i),
 //   dq^_i = scale sum_j dS_ij k~_j, dq_i = R_i^T dq^_i.
 template <typename T, int DH>
-__global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T *k, const T *v,
-                                                   const T *km, const T *vm, const T *dO,
-                                                   const float *lse, const float *D, T *dq)
+__global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T *kx, const T *vx,
+                                                   const T *dO, const float *lse, const float *D,
+                                                   T *dq)
 {
     __shared__ float red[2];
     __shared__ float dqh[DH];
@@ -152,7 +138,6 @@ __global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int c = threadIdx.x;
-    const float s = gate_sigmoid(a.gate[h]);
     const int64_t qrow = (b * a.T + i) * a.H + h;
     const float2 *tab_i = rope_row(a, i, DH);
     const float qh = rope_channel<T, DH>(q + qrow * DH, c, tab_i, false);
@@ -163,8 +148,7 @@ __global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T
     float acc = 0.0f;
     for (int64_t j = lo; j <= i; ++j) {
         const int64_t krow = (b * a.T + j) * a.H + h;
-        float kt, vt;
-        mixed_kv<T, DH>(a, k, v, km, vm, krow, j, c, s, kt, vt);
+        const float kt = to_f<T>(kx[krow * DH + c]), vt = to_f<T>(vx[krow * DH + c]);
         const float sc = block_sum<DH>(qh * kt, red) * a.scale;
         const float dp = block_sum<DH>(dOi * vt, red);
         const float p = __expf(sc - li);
@@ -175,15 +159,15 @@ __global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T
     dq[qrow * DH + c] = from_f<T>(rope_channel_f<DH>(dqh, c, tab_i, true));
 }
 
-// dk, dv: one workgroup per key row j; queries i in [j, j+W-1].
+// dk, dv: one workgroup per key row j; queries i in [j, j+W-1]; k~ = kx, v~ = vx.
 //   dk~_j = scale sum_i dS_ij q^_i, dv~_j = sum_i P_ij dO_i,
 //   dk_j = R_j^T dk~_j, dv_j = dv~_j,
 //   ds_part[b,h,j] = <kmem_j, dk_j> + <vmem_j, dv_j>  (d loss / d s_h, this key).
 template <typename T, int DH>
-__global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const T *k, const T *v,
-                                                     const T *km, const T *vm, const T *dO,
-                                                     const float *lse, const float *D, T *dk,
-                                                     T *dv, float *ds_part)
+__global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const T *kx,
+                                                     const T *vx, const T *km, const T *vm,
+                                                     const T *dO, const float *lse, const float *D,
+                                                     T *dk, T *dv, float *ds_part)
 {
     __shared__ float red[2];
     __shared__ float dkt[DH];
@@ -191,10 +175,8 @@ __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int c = threadIdx.x;
-    const float s = gate_sigmoid(a.gate[h]);
     const int64_t krow = (b * a.T + j) * a.H + h;
-    float kt, vt;
-    mixed_kv<T, DH>(a, k, v, km, vm, krow, j, c, s, kt, vt);
+    const float kt = to_f<T>(kx[krow * DH + c]), vt = to_f<T>(vx[krow * DH + c]);
     const int64_t hi = j + a.W - 1 < a.T - 1 ? j + a.W - 1 : a.T - 1;
     float acck = 0.0f, accv = 0.0f;
     for (int64_t i = j; i <= hi; ++i) {
@@ -216,6 +198,59 @@ __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const
     const float part = dkc * to_f<T>(km[krow * DH + c]) + accv * to_f<T>(vm[krow * DH + c]);
     const float tot = block_sum<DH>(part, red);
     if (c == 0) ds_part[(b * a.H + h) * a.T + j] = tot;
+}
+
+// ---------------------------------------------------------------------------
+// Gated mix, one 8-channel chunk pair (c, c + Dh/2) per thread:
+//   kmix = R_p (k + s_h kmem),  vmix = v + s_h vmem,  p = pos0 + t.
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void mix_entries(int64_t rows, int H, int64_t Tlen, int64_t pos0,
+                                                   const float2 *rope, const float *gate,
+                                                   const T *k, const T *v, const T *km,
+                                                   const T *vm, T *kx, T *vx)
+{
+    constexpr int CP = DH / 16;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / CP;            // (b*T + t)*H + h
+    if (row >= rows) return;
+    const int cc = (int)(gid % CP);
+    const int h = (int)(row % H);
+    const int64_t t = (row / H) % Tlen;
+    const float s = gate_sigmoid(gate[h]);
+    const int64_t base = row * DH + 8 * cc;
+    float lo[8], hi[8], mlo[8], mhi[8];
+    load8(k + base, lo);
+    load8(k + base + DH / 2, hi);
+    load8(km + base, mlo);
+    load8(km + base + DH / 2, mhi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo[e] += s * mlo[e];
+        hi[e] += s * mhi[e];
+    }
+    if (rope) {
+        const float2 *cs = rope + (pos0 + t) * (DH / 2) + 8 * cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = cs[e].x, sn = cs[e].y, x0 = lo[e], x1 = hi[e];
+            lo[e] = x0 * c - x1 * sn;
+            hi[e] = x0 * sn + x1 * c;
+        }
+    }
+    store8(kx + base, lo);
+    store8(kx + base + DH / 2, hi);
+    load8(v + base, lo);
+    load8(v + base + DH / 2, hi);
+    load8(vm + base, mlo);
+    load8(vm + base + DH / 2, mhi);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo[e] += s * mlo[e];
+        hi[e] += s * mhi[e];
+    }
+    store8(vx + base, lo);
+    store8(vx + base + DH / 2, hi);
 }
 
 // ---------------------------------------------------------------------------

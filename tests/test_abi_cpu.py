@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.maglev_abi_version() == 1
+    assert L.maglev_abi_version() == 2
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
     assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
     assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
@@ -58,8 +58,11 @@ def geom(**kw):
     return rms.Geom(**base)
 
 
+NO_MIX = [FAKE] * 3 + [None] * 3 + [FAKE] * 2 + [None] * 2   # m W_Km W_Vm | k v gate | kmem vmem | kmix vmix
+
+
 def project(L, g, shift=1, ptrs=None):
-    p = ptrs or [FAKE] * 5
+    p = ptrs or NO_MIX
     return L.maglev_mem_project(ctypes.byref(g) if g is not None else None, shift, *p, None)
 
 
@@ -76,24 +79,35 @@ def test_projection_rejects_bad_geometry(L, kw, status):
 def test_projection_rejects_null_geometry_shift_and_pointers(L):
     assert project(L, None) == INVALID
     assert project(L, geom(), shift=2) == INVALID
-    assert project(L, geom(), ptrs=[FAKE, None, FAKE, FAKE, FAKE]) == INVALID
-    assert project(L, geom(), ptrs=[FAKE, FAKE, FAKE, FAKE_ODD, FAKE]) == MISALIGNED
+    bad = list(NO_MIX); bad[1] = None   # W_Km
+    assert project(L, geom(), ptrs=bad) == INVALID
+    bad = list(NO_MIX); bad[6] = FAKE_ODD   # kmem
+    assert project(L, geom(), ptrs=bad) == MISALIGNED
     assert b"aligned" in L.maglev_last_error()
+
+
+@pytest.mark.parametrize("present", [(3,), (3, 4, 5), (3, 4, 5, 8), (8, 9), (5,)])
+def test_projection_mixing_arguments_come_together(L, present):
+    """k, v, gate, kmix, vmix (positions 3, 4, 5, 8, 9) are all given or all null."""
+    p = list(NO_MIX)
+    for i in present:
+        p[i] = FAKE
+    assert project(L, geom(), ptrs=p) == INVALID
 
 
 def test_empty_batch_is_a_no_op(L):
     # B = 0 returns OK without touching any pointer or the device.
     assert project(L, geom(B=0)) == OK
-    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(T=0)), *([FAKE] * 7), None, None) == OK
+    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(T=0)), *([FAKE] * 5), None) == OK
 
 
 def test_forward_validation(L):
     g = geom()
-    args = [FAKE] * 5 + [FAKE, FAKE, FAKE, None]
-    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(Dh=80)), *args) == UNSUPPORTED
-    bad = list(args); bad[5] = None  # gate
+    args = [FAKE] * 5   # q kmix vmix o lse
+    assert L.maglev_swa_inject_fwd(ctypes.byref(geom(Dh=80)), *args, None) == UNSUPPORTED
+    bad = list(args); bad[1] = None  # kmix
     assert L.maglev_swa_inject_fwd(ctypes.byref(g), *bad, None) == INVALID
-    bad = list(args); bad[7] = FAKE_ODD  # lse misaligned
+    bad = list(args); bad[4] = FAKE_ODD  # lse misaligned
     assert L.maglev_swa_inject_fwd(ctypes.byref(g), *bad, None) == MISALIGNED
 
 

@@ -17,7 +17,7 @@ import oracle
 import recurrent_memory_sliding_amd as rms
 import workloads as wl
 from recurrent_memory_sliding_amd.decode import DecodeStack
-from layer_util import check, flush, gpu, max_scale
+from layer_util import check, flush, gpu, gpu_project, max_scale
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -52,8 +52,10 @@ def oracle_query_row(inp, sh, b, h, i):
     km, vm = oracle.mem_project(sl["m_prime"], sl["W_Km"], sl["W_Vm"], 1, sh.Dh, shift=1)
     o, lse = oracle.swa_inject_fwd(sl["q"], sl["k"], sl["v"], km, vm, sl["gate_logit"], sh.W,
                                    pos0=s0, rope_base=sh.rope_base)
+    kx, vx = oracle.mixed_entries(sl["k"], sl["v"], km, vm, sl["gate_logit"], s0, sh.rope_base)
     first = 1 if s0 > 0 else 0   # slice row 0 lacks its memory row when s0 > 0
-    return o[0, -1, 0], lse[0, 0, -1], km[0, first:, 0], vm[0, first:, 0], s0 + first
+    return (o[0, -1, 0], lse[0, 0, -1], km[0, first:, 0], vm[0, first:, 0], kx[0, first:, 0],
+            vx[0, first:, 0], s0 + first)
 
 
 def oracle_key_grads(inp, sh, b, h, j):
@@ -73,20 +75,23 @@ def sample_queries(sh):
 
 def run_forward_fullsize(sh, inp):
     g = gpu(inp)
-    km, vm = rms.maglev_mem_project(g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh)
-    o, lse = rms.maglev_swa_inject_fwd(g["q"], g["k"], g["v"], km, vm, g["gate_logit"], sh.W, d=sh.d)
+    km, vm = gpu_project(g, sh)
+    o, lse = rms.maglev_swa_inject_fwd(g["q"], g["kx"], g["vx"], sh.W, d=sh.d)
     torch.cuda.synchronize()
     return g, km, vm, o, lse
 
 
-def check_forward_samples(sh, inp, km, vm, o, lse):
+def check_forward_samples(sh, inp, g, km, vm, o, lse):
     worst = 0.0
     for b, h, i in sample_queries(sh):
-        ro, rl, rkm, rvm, t0 = oracle_query_row(inp, sh, b, h, i)
+        ro, rl, rkm, rvm, rkx, rvx, t0 = oracle_query_row(inp, sh, b, h, i)
         worst = max(worst, check("o[%d,%d,%d]" % (b, i, h), o[b, i, h], ro, TOL))
         check("lse", lse[b, h, i], rl, TOL)
         check("kmem rows", km[b, t0:i + 1, h], rkm, TOL)
         check("vmem rows", vm[b, t0:i + 1, h], rvm, TOL)
+        # stored bf16 entries of magnitude above 4: judged relative to max(1, max|ref|)
+        check("kmix rows", g["kx"][b, t0:i + 1, h], rkx, TOL, max_scale(rkx))
+        check("vmix rows", g["vx"][b, t0:i + 1, h], rvx, TOL, max_scale(rvx))
     return worst
 
 
@@ -94,14 +99,14 @@ def test_d20_layer_forward_fullsize():
     sh = wl.D20_LAYER
     flush("d20 layer forward, B=8 T=2048 W=512")
     inp = wl.layer_inputs(sh, 1)
-    _, km, vm, o, lse = run_forward_fullsize(sh, inp)
-    flush("  worst o error %.3e" % check_forward_samples(sh, inp, km, vm, o, lse))
+    g, km, vm, o, lse = run_forward_fullsize(sh, inp)
+    flush("  worst o error %.3e" % check_forward_samples(sh, inp, g, km, vm, o, lse))
 
 
 def backward_fullsize(sh, seed, keys):
     inp = wl.layer_inputs(sh, seed, grads=True)
     g, km, vm, o, lse = run_forward_fullsize(sh, inp)
-    gr = rms.maglev_swa_inject_bwd(g["q"], g["k"], g["v"], km, vm, g["gate_logit"], o, lse,
+    gr = rms.maglev_swa_inject_bwd(g["q"], g["kx"], g["vx"], km, vm, g["gate_logit"], o, lse,
                                    g["dO"], g["m_prime"], g["W_Km"], g["W_Vm"], sh.W)
     torch.cuda.synchronize()
     for b, h, j in keys:

@@ -12,7 +12,7 @@ import oracle
 import recurrent_memory_sliding_amd as rms
 import workloads as wl
 from layer_util import (TOL, check, check_backward, check_forward, flush, gpu, gpu_backward,
-                        gpu_forward, oracle_backward, oracle_forward)
+                        gpu_forward, gpu_project, oracle_backward, oracle_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,8 +105,8 @@ def test_empty_batch_backward_zeroes_parameter_gradients():
     sh = shape(B=0, T=64)
     inp = wl.layer_inputs(shape(B=1, T=64), 8, grads=True)
     g = gpu({k: v[:0] if v.dim() >= 3 else v for k, v in inp.items()})
-    km, vm = rms.maglev_mem_project(g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh)
-    o, lse = rms.maglev_swa_inject_fwd(g["q"], g["k"], g["v"], km, vm, g["gate_logit"], sh.W)
+    km, vm = gpu_project(g, sh)
+    o, lse = rms.maglev_swa_inject_fwd(g["q"], g["kx"], g["vx"], sh.W)
     out = {"dW_Km": torch.full((sh.H * sh.Dh, sh.d), 5.0, device="cuda"),
            "dW_Vm": torch.full((sh.H * sh.Dh, sh.d), 5.0, device="cuda"),
            "dgate": torch.full((sh.H,), 5.0, device="cuda")}
