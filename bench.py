@@ -15,6 +15,7 @@ Prints ONE JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -67,24 +68,76 @@ def decode_bytes(sh: wl.DecodeShape) -> float:
     return float(per_layer * sh.layers)
 
 
-class Timer:
-    """HIP events around each call on the launching stream."""
+def kernel_work(sh: wl.LayerShape) -> dict:
+    """Algorithmic work of one launch of each kernel of the training step:
+    {timing name: (FLOPs, HBM bytes)}. FLOPs count in-window pairs and the
+    projection products only; bytes count each tensor the kernel must read or
+    write once (bf16 activations, fp32 lse/D/gradients)."""
+    T, W, B, H, Dh, d = sh.T, sh.W, sh.B, sh.H, sh.Dh, sh.d
+    N, HD = B * T, H * Dh
+    pairs = sum(min(i + 1, W) for i in range(T))
+    attn = 2.0 * pairs * Dh * B * H          # one contraction over the band
+    proj = 2.0 * N * d * 2 * HD              # one [N x d] x [d x 2HD] product
+    act = 2.0 * N * HD                       # one bf16 activation tensor [B,T,H,Dh]
+    rowf = 4.0 * N * H                       # one fp32 [B,H,T] vector
+    mem = 2.0 * N * d                        # one bf16 [B,T,d] tensor
+    wts = 2.0 * 2 * HD * d                   # W_Km and W_Vm, bf16
+    f32nd = 4.0 * N * d
+    return {
+        "proj_fwd": (proj, mem + wts + 2 * act),
+        "mix": (0.0, 6 * act),                                  # k v kmem vmem -> kmix vmix
+        "attn_fwd": (2 * attn, 4 * act + rowf),                 # q kmix vmix -> o, lse
+        "attn_bwd_rowdot": (0.0, 2 * act + rowf),               # o dO -> D
+        "attn_bwd_dkdv": (3 * attn, 8 * act + 2 * rowf + 4.0 * B * H * ((T + 127) // 128)),
+        "attn_bwd_dq": (attn, 5 * act + 2 * rowf),              # q dO kmix vmix -> dq
+        "proj_bwd_scale_w": (0.0, 2 * wts),
+        "proj_bwd_dm": (proj, 2 * act + wts + f32nd),           # dk dv Ws -> dm'
+        "proj_bwd_dw": (proj, 2 * act + mem),                   # partials counted separately
+        "proj_bwd_dw_reduce": (0.0, 4.0 * 2 * HD * d * 2),
+        "loss_partial": (0.0, 2 * mem + f32nd + 2 * f32nd),     # m m' -> dm, dm' +=
+    }
 
-    def __init__(self):
-        self.ev = {}
 
-    def mark(self, name):
-        s = torch.cuda.Event(enable_timing=True)
-        s.record(torch.cuda.current_stream())
-        return s
+CALL_KERNELS = {
+    "maglev_mem_project": ("proj_fwd", "mix"),
+    "maglev_swa_inject_fwd": ("attn_fwd",),
+    "maglev_swa_inject_bwd": ("attn_bwd_rowdot", "attn_bwd_dkdv", "attn_bwd_dq", "dgate_reduce",
+                              "zero_last_rows", "proj_bwd_scale_w", "proj_bwd_dm", "proj_bwd_dw",
+                              "proj_bwd_dw_reduce"),
+    "maglev_consistency_loss": ("loss_partial", "loss_final"),
+}
 
-    def add(self, name, start):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(torch.cuda.current_stream())
-        self.ev.setdefault(name, []).append((start, e))
 
-    def avg_ms(self):
-        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.ev.items()}
+def roofline_of(flops, nbytes, seconds):
+    """Roofline record of one kernel: bound by whichever of MFMA time and HBM
+    time is larger at peak, achieved rate in that unit."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        a = flops / seconds / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / PEAK_BF16_TFLOPS, 4)}
+    a = nbytes / seconds / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4)}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (profiles/pmc_traffic.json), or None when they are missing or were taken
+    on a different source of that kernel."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+        src = os.path.join(ROOT, "recurrent_memory_sliding_amd", "csrc", rec["source"])
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if sha != rec["source_sha256"]:
+        return None
+    return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
 
 
 def train_setup(sh, seed=2):
@@ -121,48 +174,51 @@ def train_setup(sh, seed=2):
     return g, buf
 
 
-def train_step(sh, g, buf, timer=None):
-    def run(name, fn):
-        if timer is None:
-            fn()
-        else:
-            s = timer.mark(name)
-            fn()
-            timer.add(name, s)
-
-    run("maglev_mem_project", lambda: rms.maglev_mem_project(
+def train_step(sh, g, buf):
+    rms.maglev_mem_project(
         g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh, shift=1, kmem=buf["km"], vmem=buf["vm"],
         k=g["k"], v=g["v"], gate_logit=g["gate_logit"], kmix=buf["kx"], vmix=buf["vx"],
-        pos0=sh.pos0, rope_base=sh.rope_base))
-    run("maglev_swa_inject_fwd", lambda: rms.maglev_swa_inject_fwd(
+        pos0=sh.pos0, rope_base=sh.rope_base)
+    rms.maglev_swa_inject_fwd(
         g["q"], buf["kx"], buf["vx"], sh.W, pos0=sh.pos0, rope_base=sh.rope_base, d=sh.d,
-        o=buf["o"], lse=buf["lse"]))
+        o=buf["o"], lse=buf["lse"])
     # the backward writes dm'; the loss then adds its own term (accumulate bit 1)
-    run("maglev_swa_inject_bwd", lambda: rms.maglev_swa_inject_bwd(
+    rms.maglev_swa_inject_bwd(
         g["q"], buf["kx"], buf["vx"], buf["km"], buf["vm"], g["gate_logit"], buf["o"], buf["lse"],
         g["dO"], g["m_prime"], g["W_Km"], g["W_Vm"], sh.W, pos0=sh.pos0, rope_base=sh.rope_base,
-        accumulate=0, out=buf["grads"], workspace=buf["ws_bwd"]))
-    run("maglev_consistency_loss", lambda: rms.maglev_consistency_loss(
+        accumulate=0, out=buf["grads"], workspace=buf["ws_bwd"])
+    rms.maglev_consistency_loss(
         g["m"], g["m_prime"], sh.lam, loss=buf["loss"], dm=buf["dm"],
-        dm_prime=buf["grads"]["dm_prime"], accumulate=2, workspace=buf["ws_loss"]))
+        dm_prime=buf["grads"]["dm_prime"], accumulate=2, workspace=buf["ws_loss"])
 
 
 def bench_train(sh, steps, warmup):
+    """Wall time per step over the timed steps. Every kernel is timed with HIP
+    events during the warmup steps after the first (the per-kernel table); the
+    timed steps then record events around the kernel with the most time only."""
     g, buf = train_setup(sh)
-    for _ in range(warmup):
+    train_step(sh, g, buf)
+    torch.cuda.synchronize()
+    rms.maglev_profile_enable(True)
+    for _ in range(max(warmup - 1, 1)):
         train_step(sh, g, buf)
     torch.cuda.synchronize()
-    timer = Timer()
+    rms.maglev_profile_enable(False)
+    survey = rms.maglev_profile_read()
+    work = kernel_work(sh)
+    dom = max((k for k in survey if k in work), key=lambda k: survey[k][1] / survey[k][0])
+    rms.maglev_profile_enable(True, only=dom)
     t0 = time.perf_counter()
     for _ in range(steps):
-        train_step(sh, g, buf, timer)
+        train_step(sh, g, buf)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    rms.maglev_profile_enable(False)
+    timed = rms.maglev_profile_read()
     ms = (t1 - t0) * 1e3 / steps
-    calls = timer.avg_ms()
     del g, buf
     torch.cuda.empty_cache()
-    return ms, calls
+    return ms, survey, dom, timed[dom]
 
 
 def bench_decode(sh, steps, warmup, seed=4):
@@ -201,13 +257,13 @@ def bench_decode(sh, steps, warmup, seed=4):
 
 def cpu_baseline(sh):
     """The oracle, as it stands, on a bounded slice of the training workload:
-    sequences 0-3 of 8, all heads, full T. The slice is half of the layer's
-    attention pairs and projection rows, so the full-step time is scaled by 2."""
+    sequences 0-5 of 8, all heads, full T. The slice holds 6/8 of the layer's
+    attention pairs and projection rows, so the full-step time is scaled by 8/6."""
     import oracle
 
     oracle.build(force=False)
     inp = wl.layer_inputs(sh, 2, grads=True)
-    nb = 4
+    nb = 6
     nh = sh.H
     Dh = sh.Dh
     sl = {n: inp[n][:nb, :, :nh].contiguous() for n in ("q", "k", "v", "dO")}
@@ -230,8 +286,8 @@ def cpu_baseline(sh):
         "unit": "tokens/s",
         "cores": oracle.omp_threads(),
         "kind": "oracle",
-        "sample": "sequences 0-3 (all heads) of the d20 layer fwd+bwd+loss (T=2048, W=512): "
-                  "%.1f s, scaled by %g to the full batch" % (dt, factor),
+        "sample": "sequences 0-%d (all heads) of the d20 layer fwd+bwd+loss (T=2048, W=512): "
+                  "%.1f s, scaled by %.4g to the full batch" % (nb - 1, dt, factor),
         "sample_seconds": round(dt, 2),
         "cpu": platform.processor() or platform.machine(),
     }
@@ -259,19 +315,27 @@ def main():
     sh = wl.D20_LAYER
     flops = layer_flops(sh)
     total_flops = sum(flops.values())
-    ms, calls = bench_train(sh, args.steps, args.warmup)
+    ms, survey, dom, (n_dom, t_dom) = bench_train(sh, args.steps, args.warmup)
     tokens = sh.B * sh.T
     value = tokens / (ms / 1e3)
     path_tflops = total_flops / (ms / 1e3) / 1e12
 
-    # roofline of the single-kernel call with the largest time
-    per_call_flops = {"maglev_mem_project": flops["project_fwd"],
-                      "maglev_swa_inject_fwd": flops["attn_fwd"]}
-    dom = max(per_call_flops, key=lambda k: calls.get(k, 0.0))
-    dom_tflops = per_call_flops[dom] / (calls[dom] / 1e3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_tflops, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    # per-kernel averages over the warmup steps; live roofline of the dominant kernel
+    work = kernel_work(sh)
+    per_kernel = {}
+    for name, (n, tot) in sorted(survey.items(), key=lambda kv: -kv[1][1]):
+        rec = {"launches": n, "avg_us": round(tot * 1e3 / n, 2)}
+        if name in work:
+            rec["roofline"] = roofline_of(work[name][0], work[name][1], tot / n / 1e3)
+        per_kernel[name] = rec
+    calls = {c: round(sum(survey[k][1] / survey[k][0] for k in ks if k in survey), 4)
+             for c, ks in CALL_KERNELS.items()}
+    roofline = roofline_of(work[dom][0], work[dom][1], t_dom / n_dom / 1e3)
+    roofline["traffic"] = measured_traffic(dom)
+    roofline["kernel"] = dom
+    roofline["avg_us"] = round(t_dom * 1e3 / n_dom, 2)
+    roofline["launches"] = n_dom
+    roofline["algorithmic_per_launch"] = (work[dom][0] if roofline["bound"] == "mfma" else work[dom][1])
 
     result = {
         "metric": "SWA+KV-inject fwd+bwd tokens/s & %bf16 MFMA peak (d20,T=2048,W=512); decode GB/s",
@@ -293,7 +357,7 @@ def main():
         "path": {"algorithmic_TFLOP_per_step": round(total_flops / 1e12, 4),
                  "TFLOP/s": round(path_tflops, 1),
                  "frac_bf16_peak": round(path_tflops / PEAK_BF16_TFLOPS, 4),
-                 "calls_ms": {k: round(v, 4) for k, v in calls.items()}},
+                 "calls_ms": calls, "kernels_warmup": per_kernel},
         "roofline": roofline,
     }
     if not args.no_decode:

@@ -221,6 +221,23 @@ const char *maglev_last_error(void);
 /* MAGLEV_ABI_VERSION of the built library. */
 int maglev_abi_version(void);
 
+/* Kernel timing (diagnostic, for measurement tools). While switched on, every
+ * kernel the library launches is bracketed by two HIP events recorded on its
+ * launch stream; launches on a stream under graph capture are not recorded.
+ *   maglev_profile_enable(1, only) clears earlier totals and starts recording
+ *   every kernel (only == NULL) or just the kernel named `only` (host string,
+ *   copied; fewer events leave fewer gaps in the stream);
+ *   maglev_profile_enable(0, NULL) stops recording (totals are kept);
+ *   maglev_profile_count() waits for the recorded events, folds them into
+ *   per-kernel totals and returns the number of kernel names;
+ *   maglev_profile_entry(i, ...) gives name i (static until the next enable),
+ *   its launch count and its summed duration in milliseconds.
+ * The events add a small gap between kernels; timing is off by default. */
+maglev_status_t maglev_profile_enable(int on, const char *only);
+int maglev_profile_count(void);
+maglev_status_t maglev_profile_entry(int index, const char **name, int64_t *launches,
+                                     double *total_ms);
+
 #ifdef __cplusplus
 }
 #endif

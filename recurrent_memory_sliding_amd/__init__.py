@@ -24,7 +24,8 @@ __all__ = [
     "maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
     "maglev_swa_inject_bwd_workspace", "maglev_consistency_loss",
     "maglev_consistency_loss_workspace", "maglev_decode_step", "maglev_decode_workspace",
-    "maglev_decode_advance", "maglev_prepare", "maglev_abi_version",
+    "maglev_decode_advance", "maglev_prepare", "maglev_abi_version", "maglev_profile_enable",
+    "maglev_profile_read",
 ]
 
 MAGLEV_F32 = 0
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
             "maglev_status_string": ([i32], ctypes.c_char_p),
             "maglev_last_error": ([], ctypes.c_char_p),
             "maglev_abi_version": ([], ctypes.c_int),
+            "maglev_profile_enable": ([ctypes.c_int, ctypes.c_char_p], i32),
+            "maglev_profile_count": ([], ctypes.c_int),
+            "maglev_profile_entry": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                      ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -128,6 +133,28 @@ def make_geom(B, T, H, Dh, d, W, pos0=0, rope_base=10000.0, scale=0.0, dtype=MAG
 
 def maglev_abi_version() -> int:
     return lib().maglev_abi_version()
+
+
+def maglev_profile_enable(on: bool = True, only: Optional[str] = None):
+    """Switch per-kernel event timing on (clearing earlier totals; every kernel,
+    or only the one named `only`) or off."""
+    _check(lib().maglev_profile_enable(1 if on else 0, only.encode() if only else None),
+           "maglev_profile_enable")
+
+
+def maglev_profile_read() -> dict:
+    """{kernel name: (launches, total milliseconds)} of the events recorded so far
+    (waits for them)."""
+    L = lib()
+    out = {}
+    for i in range(L.maglev_profile_count()):
+        name = ctypes.c_char_p()
+        n = ctypes.c_int64()
+        ms = ctypes.c_double()
+        _check(L.maglev_profile_entry(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+               "maglev_profile_entry")
+        out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out
 
 
 def maglev_prepare(Dh: int, rope_base: float, max_pos: int):

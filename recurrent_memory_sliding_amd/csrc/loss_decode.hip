@@ -10,6 +10,7 @@
 // Maglev - Sliding Recurrent Memory"), section Inferentiemechanisme.
 #include "common.hpp"
 #include "internal.hpp"
+#include "profile.hpp"
 
 namespace maglev {
 
@@ -99,6 +100,8 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
     const float c = N > 0 ? (float)((double)lambda / ((double)N * sqrt((double)d))) : 0.0f;
     const int nb = loss_blocks(n8);
     float *partial = static_cast<float *>(ws);
+    {
+    prof::Scope ts("loss_partial", s);
     if (dtype == MAGLEV_BF16)
         hipLaunchKernelGGL(loss_partial<bf16>, dim3(nb), dim3(kLossThreads), 0, s, n8,
                            static_cast<const bf16 *>(m), static_cast<const bf16 *>(mp), 2.0f * c,
@@ -107,6 +110,8 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
         hipLaunchKernelGGL(loss_partial<float>, dim3(nb), dim3(kLossThreads), 0, s, n8,
                            static_cast<const float *>(m), static_cast<const float *>(mp), 2.0f * c,
                            dm, dmp, acc, partial);
+    }
+    prof::Scope ts("loss_final", s);
     hipLaunchKernelGGL(loss_final, dim3(1), dim3(1024), 0, s, partial, nb, c, loss, acc);
     return hipGetLastError();
 }
@@ -288,11 +293,15 @@ static void launch_decode_t(int Bs, int H, int W, float rope_base, float scale, 
                             void *ws, hipStream_t s)
 {
     const int ns = decode_splits(W);
+    {
+    prof::Scope ts("decode_partial", s);
     hipLaunchKernelGGL((decode_partial<T, DH>), dim3(ns, H, Bs), dim3(kDecThreads), 0, s, H, W,
                        rope_base, scale, static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), static_cast<const T *>(km),
                        static_cast<const T *>(vm), gate, static_cast<T *>(kc),
                        static_cast<T *>(vc), pos, static_cast<float *>(ws));
+    }
+    prof::Scope ts("decode_combine", s);
     hipLaunchKernelGGL((decode_combine<T, DH>), dim3(H, Bs), dim3(DH), 0, s, H, ns,
                        static_cast<const float *>(ws), static_cast<T *>(o));
 }

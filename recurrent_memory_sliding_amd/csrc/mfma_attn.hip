@@ -22,6 +22,7 @@
 // straddle a band edge are masked.
 #include "common.hpp"
 #include "mfma_kernels.hpp"
+#include "profile.hpp"
 
 namespace maglev {
 namespace mfma {
@@ -571,6 +572,7 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const vo
 {
     const AttnArgs a = make_args(g, q, kx, vx, nullptr, nullptr, rope);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
+    prof::Scope ts("attn_fwd", s);
     if (g.Dh == 128)
         hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(nwg), dim3(256), 0, s, a, static_cast<bf16 *>(o), lse);
     else
@@ -578,6 +580,26 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const vo
 }
 
 int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
+
+template <int DH>
+static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, const float *lse,
+                              void *dq, void *dk, void *dv, const BwdWorkspace &ws, int64_t rows,
+                              unsigned pre_blocks, unsigned nwg, hipStream_t s)
+{
+    {
+        prof::Scope ts("attn_bwd_rowdot", s);
+        hipLaunchKernelGGL(bwd_rowdot_kernel<DH>, dim3(pre_blocks), dim3(256), 0, s, o, dO, ws.D,
+                           rows, a.H, a.T);
+    }
+    {
+        prof::Scope ts("attn_bwd_dkdv", s);
+        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<DH>, dim3(nwg), dim3(256), 0, s, a, dO, lse, ws.D,
+                           static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), ws.ds_part);
+    }
+    prof::Scope ts("attn_bwd_dq", s);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<DH>, dim3(nwg), dim3(256), 0, s, a, dO, lse, ws.D,
+                       static_cast<bf16 *>(dq));
+}
 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const void *km, const void *vm, const float *gate, const void *o,
@@ -592,19 +614,10 @@ void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const vo
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     const bf16 *ob = static_cast<const bf16 *>(o);
     const bf16 *dOb = static_cast<const bf16 *>(dO);
-    if (g.Dh == 128) {
-        hipLaunchKernelGGL(bwd_rowdot_kernel<128>, dim3(pre_blocks), dim3(256), 0, s, ob, dOb, ws.D, rows, g.H, g.T);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, dim3(nwg), dim3(256), 0, s, a, dOb, lse, ws.D,
-                           static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), ws.ds_part);
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, dim3(nwg), dim3(256), 0, s, a, dOb, lse, ws.D,
-                           static_cast<bf16 *>(dq));
-    } else {
-        hipLaunchKernelGGL(bwd_rowdot_kernel<64>, dim3(pre_blocks), dim3(256), 0, s, ob, dOb, ws.D, rows, g.H, g.T);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, dim3(nwg), dim3(256), 0, s, a, dOb, lse, ws.D,
-                           static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), ws.ds_part);
-        hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, dim3(nwg), dim3(256), 0, s, a, dOb, lse, ws.D,
-                           static_cast<bf16 *>(dq));
-    }
+    if (g.Dh == 128)
+        launch_attn_bwd_t<128>(a, ob, dOb, lse, dq, dk, dv, ws, rows, pre_blocks, nwg, s);
+    else
+        launch_attn_bwd_t<64>(a, ob, dOb, lse, dq, dk, dv, ws, rows, pre_blocks, nwg, s);
 }
 
 }  // namespace mfma

@@ -16,6 +16,7 @@
 // epilogue (dW).
 #include "common.hpp"
 #include "mfma_kernels.hpp"
+#include "profile.hpp"
 
 namespace maglev {
 namespace mfma {
@@ -414,10 +415,11 @@ using ProjCfg = TileCfg<128, 128, 2, 4, 2>;   // wave tile 64 x 32, 2 workgroups
 using DwCfg = TileCfg<256, 256, 4, 4, 2>;     // wave tile 64 x 64, split over tokens
 
 template <class Cfg, class P>
-static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s)
+static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const char *name)
 {
     const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
     const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
+    prof::Scope ts(name, s);
     hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn), 1, ksplit),
                        dim3(Cfg::NT), 0, s, p, kper);
 }
@@ -433,11 +435,13 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
     p.vm = static_cast<bf16 *>(vm);
     p.M = g.N(); p.N = 2 * (int64_t)g.HD(); p.K = g.d; p.T = g.T;
     p.HD = g.HD(); p.shift = shift;
-    if (p.M <= 64)
+    if (p.M <= 64) {
+        prof::Scope ts("proj_fwd_skinny", s);
         hipLaunchKernelGGL(gemm_skinny_bf16<ProjFwd>, dim3((unsigned)((p.N + 15) / 16)), dim3(256), 0,
                            s, p);
-    else
-        run_gemm<ProjCfg>(p, 1, p.K, s);
+    } else {
+        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_fwd");
+    }
 }
 
 // s_h-scaled copy of [W_Km; W_Vm] (bf16), 8 elements per thread.
@@ -502,6 +506,7 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
     bf16 *wsc = static_cast<bf16 *>(ws.W_scaled);
     {
         const int64_t chunks = 2 * (int64_t)HD * g.d / 8;
+        prof::Scope ts("proj_bwd_scale_w", s);
         hipLaunchKernelGGL(scale_weights, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
                            static_cast<const bf16 *>(wk), static_cast<const bf16 *>(wv), gate, wsc,
                            HD, g.Dh, g.d);
@@ -517,7 +522,7 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         p.acc = (acc & 1u) != 0;
         p.a_kseg = HD;
         p.b_ld = g.d;
-        run_gemm<ProjCfg>(p, 1, p.K, s);
+        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm");
     }
     {
         ProjBwdDw p;
@@ -532,8 +537,9 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         const int ks = ws.ksplit;
         int64_t kper = (p.K + ks - 1) / ks;
         kper = (kper + 63) / 64 * 64;
-        run_gemm<DwCfg>(p, ks, kper, s);
+        run_gemm<DwCfg>(p, ks, kper, s, "proj_bwd_dw");
         const int64_t tot = 2 * (int64_t)HD * g.d;
+        prof::Scope ts("proj_bwd_dw_reduce", s);
         hipLaunchKernelGGL(dw_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s,
                            ws.dW_part, ks, HD, g.Dh, g.d, g.B, g.T, p.dk, p.dv, p.m, gate, dWk,
                            dWv, (acc & 2u) != 0);

@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "internal.hpp"
 #include "mfma_kernels.hpp"
+#include "profile.hpp"
 #include "simt_kernels.hpp"
 
 namespace maglev {
@@ -178,6 +179,7 @@ void mix_launch(const Geom &g, const void *k, const void *v, const void *km, con
 {
     const int64_t rows = g.N() * g.H;
     const int64_t threads = rows * (DH / 16);
+    prof::Scope ts("mix", s);
     hipLaunchKernelGGL((simt::mix_entries<T, DH>), dim3((unsigned)((threads + 255) / 256)),
                        dim3(256), 0, s, rows, g.H, g.T, g.pos0, rope, gate,
                        static_cast<const T *>(k), static_cast<const T *>(v),
@@ -315,10 +317,15 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *
             attn_bwd_simt<float, 64>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
         per_bh = g.T;
     }
-    hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,
-                       gate, dgate, acc);
-    if (!(acc & 1u))
+    {
+        prof::Scope ts("dgate_reduce", s);
+        hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,
+                           gate, dgate, acc);
+    }
+    if (!(acc & 1u)) {
+        prof::Scope ts("zero_last_rows", s);
         hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
+    }
     if (g.dtype == MAGLEV_BF16)
         mfma::launch_proj_bwd_bf16(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, ws, s);
     else
