@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MAGLEV_ABI_VERSION 2
+#define MAGLEV_ABI_VERSION 3
 
 typedef enum {
     MAGLEV_OK = 0,
@@ -189,19 +189,25 @@ size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W);
  *   of m_{t-1} with shift = 0, T = 1)
  * is written to ring slot p mod W; then R_p q attends over the valid slots
  * (slot s holds position p - ((p - s) mod W), valid iff that is >= 0).
- *   q, k, v, kmem, vmem [Bs,H,Dh] dtype; gate_logit [H] float32;
+ *   q, k, v [Bs,H,Dh] dtype; gate_logit [H] float32;
+ *   kmem, vmem: dtype, stream b's [H,Dh] block starts at element b * mem_stride
+ *     (mem_stride >= H*Dh, a multiple of 8; 0 selects H*Dh, the packed layout).
+ *     A stride above H*Dh lets one projection of m_{t-1} by every layer's
+ *     stacked weights feed all layers of a step;
  *   kcache, vcache [Bs,H,W,Dh] dtype, read and updated in place;
  *   pos [Bs] int64 device; o [Bs,H,Dh] dtype, written.
  * workspace: device buffer of at least maglev_decode_workspace() bytes, owned
- *   by the caller (per-split partial softmax state; scratch on return).
+ *   by the caller (per-chunk partial softmax states; scratch on return; calls
+ *   that overlap in time need their own workspaces).
  * The ring holds dtype values: the new entry is rounded once (ties to even).
  * The RoPE angle of the new position is evaluated on the device in double
  * precision, so no table bounds the position. Positions must be >= 0. */
 maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
                                    float rope_base, float scale, int32_t dtype, const void *q,
                                    const void *k, const void *v, const void *kmem,
-                                   const void *vmem, const float *gate_logit, void *kcache,
-                                   void *vcache, const int64_t *pos, void *o, void *workspace,
+                                   const void *vmem, int64_t mem_stride,
+                                   const float *gate_logit, void *kcache, void *vcache,
+                                   const int64_t *pos, void *o, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
 /* pos[b] += 1 for b < Bs on the device (moves every stream to its next ring

@@ -70,7 +70,8 @@ def lib() -> ctypes.CDLL:
             "maglev_consistency_loss_workspace": ([i64, i32], sz),
             "maglev_consistency_loss": ([i64, i32, f32, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp], i32),
             "maglev_decode_workspace": ([i32, i32, i32, i32], sz),
-            "maglev_decode_step": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 10 + [vp, sz, vp], i32),
+            "maglev_decode_step": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
+                                   + [vp] * 5 + [vp, sz, vp], i32),
             "maglev_decode_advance": ([i32, vp, vp], i32),
             "maglev_prepare": ([i32, f32, i64], i32),
             "maglev_status_string": ([i32], ctypes.c_char_p),
@@ -295,21 +296,34 @@ def maglev_decode_workspace(Bs: int, H: int, Dh: int, W: int) -> int:
 
 def maglev_decode_step(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o=None,
                        rope_base: float = 10000.0, scale: float = 0.0, workspace=None,
-                       stream=None):
-    """One decode step; kcache/vcache [Bs,H,W,Dh] are updated in place. Returns o [Bs,H,Dh]."""
-    _dev(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o, workspace)
+                       mem_stride: int = 0, stream=None):
+    """One decode step; kcache/vcache [Bs,H,W,Dh] are updated in place. Returns o [Bs,H,Dh].
+
+    kmem/vmem hold stream b's [H,Dh] block at element b*mem_stride (0: packed
+    [Bs,H,Dh]; a larger stride reads one layer's slice of a stacked projection).
+    A workspace passed in must be zero-filled before its first use (calls
+    leave it so)."""
+    _dev(q, k, v, gate_logit, kcache, vcache, pos, o, workspace)
     _same(q, k, v, kmem, vmem, kcache, vcache, o)
     Bs, H, W, Dh = kcache.shape
     if pos.dtype != torch.int64 or pos.numel() != Bs:
         raise MaglevError("pos must be int64 [Bs]")
+    stride = mem_stride or H * Dh
+    for t in (kmem, vmem):   # may be strided views into a stacked projection
+        if not t.is_cuda:
+            raise MaglevError("tensors must be on the GPU")
+        span = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+        if Bs > 0 and span < (Bs - 1) * stride + H * Dh:
+            raise MaglevError("kmem/vmem too small for Bs x mem_stride")
     o = torch.empty_like(q) if o is None else o
     if workspace is None:
         need = int(lib().maglev_decode_workspace(Bs, H, Dh, W))
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=q.device)
     _check(lib().maglev_decode_step(Bs, H, Dh, W, rope_base, scale, _dtype_code(q), _ptr(q),
-                                    _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
-                                    _ptr(kcache), _ptr(vcache), _ptr(pos), _ptr(o),
-                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem), int(mem_stride),
+                                    _ptr(gate_logit), _ptr(kcache), _ptr(vcache), _ptr(pos),
+                                    _ptr(o), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "maglev_decode_step")
     return o
 

@@ -68,8 +68,8 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
 size_t decode_workspace_bytes(int Bs, int H, int Dh, int W);
 hipError_t launch_decode(int Bs, int H, int Dh, int W, float rope_base, float scale, int dtype,
                          const void *q, const void *k, const void *v, const void *kmem,
-                         const void *vmem, const float *gate, void *kcache, void *vcache,
-                         const int64_t *pos, void *o, void *ws, hipStream_t s);
+                         const void *vmem, int64_t mem_stride, const float *gate, void *kcache,
+                         void *vcache, const int64_t *pos, void *o, void *ws, hipStream_t s);
 hipError_t launch_advance(int Bs, int64_t *pos, hipStream_t s);
 
 }  // namespace maglev

@@ -119,208 +119,254 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
 // ============================================================================
 // Decode step
 // ============================================================================
-// Work split: every (stream b, head h) ring of W slots is cut into chunks of
-// kSlotsPerSplit slots; one workgroup per (chunk, h, b) computes a partial
-// softmax state (running max, sum, unnormalised output) into the workspace,
-// and a combine kernel merges the chunks. Only the chunk that owns slot
-// p mod W writes the new entry; it also uses the new entry from shared memory,
-// so no workgroup reads a ring slot another workgroup writes.
-constexpr int kSlotsPerSplit = 64;
+// One workgroup of 4 waves per (stream b, head h) covers the whole ring, so no
+// cross-workgroup merge is needed and every workgroup of a 64-stream x
+// 10-head step is resident at once (3 per CU fit). A slot row of Dh channels
+// is read by Dh/8 lanes with 16-byte loads, so each wave instruction reads
+// 64/(Dh/8) consecutive slots contiguously. The ring is cut into batches of
+// kBatchPasses wave passes; batch j goes to wave j mod 4, which keeps an
+// online softmax state per lane group. The loads of a wave's first batch do
+// not depend on the position (the slot about to be overwritten is read and
+// discarded), so they are issued before pos[b] arrives and before the
+// rotation of the new position is evaluated.
 constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kBatchPasses = 8;
 
-static int decode_splits(int W) { return (W + kSlotsPerSplit - 1) / kSlotsPerSplit; }
+size_t decode_workspace_bytes(int, int, int, int) { return 0; }
 
-size_t decode_workspace_bytes(int Bs, int H, int Dh, int W)
+// Eight ring elements held as loaded (converted to float only when used).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    u32x4 x;
+    MAGLEV_DEV void load(const bf16 *p) { x = *reinterpret_cast<const u32x4 *>(p); }
+    MAGLEV_DEV void get(float *out) const
+    {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+    }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    MAGLEV_DEV void load(const float *p)
+    {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    MAGLEV_DEV void get(float *out) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+    }
+};
+
+// Merge softmax state (m2, l2, a2) into (m, l, a); -inf max marks an empty state.
+template <int N>
+MAGLEV_DEV void merge_state(float &m, float &l, float *a, float m2, float l2, const float *a2)
 {
-    return (size_t)Bs * H * decode_splits(W) * (Dh + 4) * sizeof(float);
-}
-
-// p - ((p - s) mod W) >= 0  <=>  slot s has been written at or before position p.
-MAGLEV_DEV bool slot_valid(int64_t p, int64_t s, int W)
-{
-    int64_t back = (p - s) % W;
-    if (back < 0) back += W;
-    return p - back >= 0;
+    const float mn = fmaxf(m, m2);
+    const float f1 = m == -INFINITY ? 0.0f : exp2f(m - mn);
+    const float f2 = m2 == -INFINITY ? 0.0f : exp2f(m2 - mn);
+    m = mn;
+    l = l * f1 + l2 * f2;
+#pragma unroll
+    for (int e = 0; e < N; ++e) a[e] = a[e] * f1 + a2[e] * f2;
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(kDecThreads) void decode_partial(
-    int H, int W, float rope_base, float scale, const T *q, const T *k, const T *v, const T *km,
-    const T *vm, const float *gate, T *kcache, T *vcache, const int64_t *pos, float *ws)
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    int H, int W, float rope_base, double log2_base, float scale, const T *q, const T *k,
+    const T *v, const T *km,
+    const T *vm, int64_t mem_stride, const float *gate, T *kcache, T *vcache,
+    const int64_t *pos, T *o)
 {
-    constexpr int CH = DH / 8;                 // 8-element chunks per row
-    constexpr int ROWS = kDecThreads / CH;     // slots per pass
-    constexpr int PASSES = kSlotsPerSplit / ROWS;
+    constexpr int CH = DH / 8;                   // lanes per slot row
+    constexpr int G = 64 / CH;                   // slots per wave pass
+    constexpr int SB = G * kBatchPasses;         // slots per batch
     __shared__ float qh[DH];
     __shared__ float knew[DH], vnew[DH];
-    __shared__ float sc[kSlotsPerSplit];
-    __shared__ float opart[ROWS][DH + 4];
+    __shared__ float wst[kDecWaves][2];
+    __shared__ float wacc[kDecWaves][DH];
 
-    const int split = blockIdx.x, h = blockIdx.y;
-    const int64_t b = blockIdx.z;
-    const int nsplit = gridDim.x;
-    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;              // b * H + h
+    const int h = (int)(row % H);
+    const int64_t b = row / H;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane / CH, ch = lane % CH;
+    const T *kring = kcache + row * (int64_t)W * DH + ch * 8;
+    const T *vring = vcache + row * (int64_t)W * DH + ch * 8;
+    const int nbatch = (W + SB - 1) / SB;
+
+    // 1. First batch of this wave: every slot inside the ring, valid or not.
+    Raw8<T> kr[kBatchPasses], vr[kBatchPasses];
+    auto issue = [&](int j) {
+#pragma unroll
+        for (int ps = 0; ps < kBatchPasses; ++ps) {
+            int sl = j * SB + ps * G + g;
+            sl = sl < W ? sl : W - 1;            // tail lanes re-read a slot inside the ring
+            kr[ps].load(kring + (int64_t)sl * DH);
+            vr[ps].load(vring + (int64_t)sl * DH);
+        }
+    };
+    if (w < nbatch) issue(w);
+
+    // 2. Position, rotation of position p (double precision: no table bounds
+    //    p), rotated query, and the new entry (written by this workgroup only).
     const int64_t p = pos[b];
     const int slot_new = (int)(p % W);
-    const int s0 = split * kSlotsPerSplit;
-    const int s1 = min(W, s0 + kSlotsPerSplit);
-    const bool owns_new = slot_new >= s0 && slot_new < s1;
-    const int64_t row = b * H + h;                  // [Bs,H,*] row
-    const float sg = gate_sigmoid(gate[h]);
-
-    // Rotation of position p, evaluated in double precision (exact enough for
-    // any position; no table bound).
+    const int nvalid = p + 1 < (int64_t)W ? (int)(p + 1) : W;   // slots 0 .. nvalid-1 hold positions >= 0
     if (tid < DH / 2) {
         const int i = tid;
         float cs = 1.0f, sn = 0.0f;
         if (rope_base > 0.0f) {
-            const double theta = pow((double)rope_base, -2.0 * (double)i / (double)DH);
-            double sd, cd;
-            sincos((double)p * theta, &sd, &cd);
-            cs = (float)cd;
-            sn = (float)sd;
+            // theta_i = base^(-2i/Dh) and the angle p * theta_i in double
+            // precision, reduced to [-pi, pi] in double (two-term 2*pi), then
+            // the float sine and cosine of the reduced angle.
+            const double theta = exp2(-(2.0 * (double)i / (double)DH) * log2_base);
+            const double phi = (double)p * theta;
+            const double kq = rint(phi * 0.15915494309189535);          // 1 / (2 pi)
+            double r = fma(-kq, 6.283185307179586, phi);                  // 2 pi, leading part
+            r = fma(-kq, 2.4492935982947064e-16, r);                      // 2 pi, remainder
+            sincosf((float)r, &sn, &cs);
         }
-        const T *qr = q + row * DH;
+        const float sg = gate_sigmoid(gate[h]);        const T *qr = q + row * DH;
         const float a0 = to_f<T>(qr[i]), a1 = to_f<T>(qr[i + DH / 2]);
         const float ls = scale * kLog2e;
         qh[i] = (a0 * cs - a1 * sn) * ls;
         qh[i + DH / 2] = (a0 * sn + a1 * cs) * ls;
-        if (owns_new) {
-            const T *kr = k + row * DH, *kmr = km + row * DH;
-            const float x0 = to_f<T>(kr[i]) + sg * to_f<T>(kmr[i]);
-            const float x1 = to_f<T>(kr[i + DH / 2]) + sg * to_f<T>(kmr[i + DH / 2]);
-            const T k0 = from_f<T>(x0 * cs - x1 * sn);
-            const T k1 = from_f<T>(x0 * sn + x1 * cs);
-            const T v0 = from_f<T>(to_f<T>(v[row * DH + i]) + sg * to_f<T>(vm[row * DH + i]));
-            const T v1 = from_f<T>(to_f<T>(v[row * DH + i + DH / 2]) +
-                                   sg * to_f<T>(vm[row * DH + i + DH / 2]));
-            T *kc = kcache + (row * W + slot_new) * DH;
-            T *vc = vcache + (row * W + slot_new) * DH;
-            kc[i] = k0; kc[i + DH / 2] = k1;
-            vc[i] = v0; vc[i + DH / 2] = v1;
-            knew[i] = to_f<T>(k0); knew[i + DH / 2] = to_f<T>(k1);
-            vnew[i] = to_f<T>(v0); vnew[i + DH / 2] = to_f<T>(v1);
-        }
+        const int64_t mrow = b * mem_stride + (int64_t)h * DH;
+        const T *kk = k + row * DH, *kmr = km + mrow, *vmr = vm + mrow;
+        const float x0 = to_f<T>(kk[i]) + sg * to_f<T>(kmr[i]);
+        const float x1 = to_f<T>(kk[i + DH / 2]) + sg * to_f<T>(kmr[i + DH / 2]);
+        const T k0 = from_f<T>(x0 * cs - x1 * sn);
+        const T k1 = from_f<T>(x0 * sn + x1 * cs);
+        const T v0 = from_f<T>(to_f<T>(v[row * DH + i]) + sg * to_f<T>(vmr[i]));
+        const T v1 = from_f<T>(to_f<T>(v[row * DH + i + DH / 2]) + sg * to_f<T>(vmr[i + DH / 2]));
+        knew[i] = to_f<T>(k0); knew[i + DH / 2] = to_f<T>(k1);
+        vnew[i] = to_f<T>(v0); vnew[i + DH / 2] = to_f<T>(v1);
+        // Whatever any wave reads from this slot (old or new contents) is
+        // replaced by knew/vnew, so the write needs no ordering with the loads.
+        T *kc = kcache + (row * W + slot_new) * DH;
+        T *vc = vcache + (row * W + slot_new) * DH;
+        kc[i] = k0; kc[i + DH / 2] = k1;
+        vc[i] = v0; vc[i + DH / 2] = v1;
     }
     __syncthreads();
 
-    const int r = tid / CH, ch = tid % CH;
     float qv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) qv[e] = qh[ch * 8 + e];
 
-    // Issue every K and V load of this thread before using any of them.
-    float kv[PASSES][8], vv[PASSES][8];
-    bool ok[PASSES];
+    // 3. Batches of this wave, online softmax per lane group.
+    float m_run = -INFINITY, l_run = 0.0f, acc[8] = {};
+    for (int j = w; j < nbatch; j += kDecWaves) {
+        if (j != w) issue(j);
+        float sc[kBatchPasses];
+        float bmax = -INFINITY;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-        const int sl = s0 + ps * ROWS + r;
-        ok[ps] = sl < s1 && slot_valid(p, sl, W);
-        if (ok[ps] && sl != slot_new) {
-            load8(kcache + (row * W + sl) * DH + ch * 8, kv[ps]);
-            load8(vcache + (row * W + sl) * DH + ch * 8, vv[ps]);
-        } else {
+        for (int ps = 0; ps < kBatchPasses; ++ps) {
+            const int sl = j * SB + ps * G + g;
+            float kv[8];
+            if (sl == slot_new) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kv[ps][e] = ok[ps] ? knew[ch * 8 + e] : 0.0f;
-                vv[ps][e] = ok[ps] ? vnew[ch * 8 + e] : 0.0f;
+                for (int e = 0; e < 8; ++e) kv[e] = knew[ch * 8 + e];
+            } else {
+                kr[ps].get(kv);
             }
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qv[e] * kv[e];
+#pragma unroll
+            for (int o2 = CH / 2; o2 > 0; o2 >>= 1) d += __shfl_xor(d, o2, 64);
+            sc[ps] = sl < nvalid ? d : -INFINITY;
+            bmax = fmaxf(bmax, sc[ps]);
         }
-    }
+        if (bmax == -INFINITY) continue;         // nothing valid in this batch for this group
+        const float mn = fmaxf(m_run, bmax);
+        const float corr = m_run == -INFINITY ? 0.0f : exp2f(m_run - mn);
+        l_run *= corr;
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-        float d = 0.0f;
+        for (int e = 0; e < 8; ++e) acc[e] *= corr;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d += qv[e] * kv[ps][e];
+        for (int ps = 0; ps < kBatchPasses; ++ps) {
+            const int sl = j * SB + ps * G + g;
+            if (sl >= nvalid) continue;          // never read: an unwritten slot may hold anything
+            const float pr = exp2f(sc[ps] - mn);
+            float vv[8];
+            if (sl == slot_new) {
 #pragma unroll
-        for (int o = CH / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
-        if (ch == 0) sc[ps * ROWS + r] = ok[ps] ? d : -INFINITY;
-    }
-    __syncthreads();
-    float mx = -INFINITY;
-    for (int i = 0; i < kSlotsPerSplit; ++i) mx = fmaxf(mx, sc[i]);
-    float acc[8] = {};
-    float lsum = 0.0f;
-    if (mx != -INFINITY) {
+                for (int e = 0; e < 8; ++e) vv[e] = vnew[ch * 8 + e];
+            } else {
+                vr[ps].get(vv);
+            }
+            l_run += pr;
 #pragma unroll
-        for (int ps = 0; ps < PASSES; ++ps) {
-            const float pr = ok[ps] ? exp2f(sc[ps * ROWS + r] - mx) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += pr * vv[ps][e];
+            for (int e = 0; e < 8; ++e) acc[e] += pr * vv[e];
         }
-        for (int i = 0; i < kSlotsPerSplit; ++i) lsum += (sc[i] == -INFINITY) ? 0.0f : exp2f(sc[i] - mx);
+        m_run = mn;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) opart[r][ch * 8 + e] = acc[e];
-    __syncthreads();
-    float *out = ws + ((row * nsplit) + split) * (DH + 4);
-    if (tid < DH) {
-        float t = 0.0f;
-#pragma unroll
-        for (int rr = 0; rr < ROWS; ++rr) t += opart[rr][tid];
-        out[4 + tid] = t;
-    }
-    if (tid == 0) {
-        out[0] = mx;
-        out[1] = lsum;
-    }
-}
 
-template <typename T, int DH>
-__global__ __launch_bounds__(DH) void decode_combine(int H, int nsplit, const float *ws, T *o)
-{
-    const int h = blockIdx.x;
-    const int64_t b = blockIdx.y;
-    const int64_t row = b * H + h;
-    const float *base = ws + row * nsplit * (DH + 4);
-    float mx = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, base[s * (DH + 4)]);
-    float l = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float ms = base[s * (DH + 4)];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - mx);
-        l += f * base[s * (DH + 4) + 1];
-        acc += f * base[s * (DH + 4) + 4 + threadIdx.x];
+    // 4. Merge the lane groups of the wave (same channels, other slots), then the waves.
+#pragma unroll
+    for (int off = CH; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m_run, off, 64), l2 = __shfl_xor(l_run, off, 64);
+        float a2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[e], off, 64);
+        merge_state<8>(m_run, l_run, acc, m2, l2, a2);
     }
-    o[row * DH + threadIdx.x] = from_f<T>(acc / l);
+    if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wacc[w][ch * 8 + e] = acc[e];
+        if (ch == 0) {
+            wst[w][0] = m_run;
+            wst[w][1] = l_run;
+        }
+    }
+    __syncthreads();
+    if (tid < DH) {
+        float m = -INFINITY, l = 0.0f, a = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kDecWaves; ++ww) {
+            const float a2 = wacc[ww][tid];
+            merge_state<1>(m, l, &a, wst[ww][0], wst[ww][1], &a2);
+        }
+        o[row * DH + tid] = from_f<T>(a / l);
+    }
 }
 
 template <typename T, int DH>
 static void launch_decode_t(int Bs, int H, int W, float rope_base, float scale, const void *q,
                             const void *k, const void *v, const void *km, const void *vm,
-                            const float *gate, void *kc, void *vc, const int64_t *pos, void *o,
-                            void *ws, hipStream_t s)
+                            int64_t mem_stride, const float *gate, void *kc, void *vc,
+                            const int64_t *pos, void *o, void *, hipStream_t s)
 {
-    const int ns = decode_splits(W);
-    {
-    prof::Scope ts("decode_partial", s);
-    hipLaunchKernelGGL((decode_partial<T, DH>), dim3(ns, H, Bs), dim3(kDecThreads), 0, s, H, W,
-                       rope_base, scale, static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), static_cast<const T *>(km),
-                       static_cast<const T *>(vm), gate, static_cast<T *>(kc),
-                       static_cast<T *>(vc), pos, static_cast<float *>(ws));
-    }
-    prof::Scope ts("decode_combine", s);
-    hipLaunchKernelGGL((decode_combine<T, DH>), dim3(H, Bs), dim3(DH), 0, s, H, ns,
-                       static_cast<const float *>(ws), static_cast<T *>(o));
+    prof::Scope ts("decode_step", s);
+    hipLaunchKernelGGL((decode_kernel<T, DH>), dim3((unsigned)((int64_t)Bs * H)), dim3(kDecThreads),
+                       0, s, H, W, rope_base, rope_base > 0.0f ? log2((double)rope_base) : 0.0,
+                       scale, static_cast<const T *>(q),
+                       static_cast<const T *>(k), static_cast<const T *>(v),
+                       static_cast<const T *>(km), static_cast<const T *>(vm), mem_stride, gate,
+                       static_cast<T *>(kc), static_cast<T *>(vc), pos, static_cast<T *>(o));
 }
 
 hipError_t launch_decode(int Bs, int H, int Dh, int W, float rope_base, float scale, int dtype,
                          const void *q, const void *k, const void *v, const void *km,
-                         const void *vm, const float *gate, void *kc, void *vc,
-                         const int64_t *pos, void *o, void *ws, hipStream_t s)
+                         const void *vm, int64_t mem_stride, const float *gate, void *kc,
+                         void *vc, const int64_t *pos, void *o, void *ws, hipStream_t s)
 {
     if (dtype == MAGLEV_BF16) {
         if (Dh == 128)
-            launch_decode_t<bf16, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, gate, kc, vc, pos, o, ws, s);
+            launch_decode_t<bf16, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
         else
-            launch_decode_t<bf16, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, gate, kc, vc, pos, o, ws, s);
+            launch_decode_t<bf16, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
     } else {
         if (Dh == 128)
-            launch_decode_t<float, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, gate, kc, vc, pos, o, ws, s);
+            launch_decode_t<float, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
         else
-            launch_decode_t<float, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, gate, kc, vc, pos, o, ws, s);
+            launch_decode_t<float, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
     }
     return hipGetLastError();
 }

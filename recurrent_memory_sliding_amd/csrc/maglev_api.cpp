@@ -321,8 +321,9 @@ size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W)
 maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
                                    float rope_base, float scale, int32_t dtype, const void *q,
                                    const void *k, const void *v, const void *kmem,
-                                   const void *vmem, const float *gate_logit, void *kcache,
-                                   void *vcache, const int64_t *pos, void *o, void *workspace,
+                                   const void *vmem, int64_t mem_stride,
+                                   const float *gate_logit, void *kcache, void *vcache,
+                                   const int64_t *pos, void *o, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream)
 {
     if (Bs < 0 || H < 1 || W < 1) return fail(MAGLEV_ERR_INVALID_VALUE, "need Bs >= 0, H >= 1, W >= 1");
@@ -331,6 +332,9 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
         return fail(MAGLEV_ERR_INVALID_VALUE, "scale and rope_base must not be NaN");
     maglev_status_t st = check_dtype(dtype);
     if (st != MAGLEV_OK) return st;
+    if (mem_stride == 0) mem_stride = (int64_t)H * Dh;
+    if (mem_stride < (int64_t)H * Dh || mem_stride % 8 != 0)
+        return fail(MAGLEV_ERR_INVALID_VALUE, "mem_stride must be 0 or a multiple of 8 >= H*Dh");
     if (Bs == 0) return MAGLEV_OK;   // no streams
     st = check_ptrs({q, k, v, kmem, vmem, kcache, vcache, o});
     if (st != MAGLEV_OK) return st;
@@ -343,7 +347,8 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
         return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)Dh));
     return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kmem, vmem,
-                                    gate_logit, kcache, vcache, pos, o, workspace, stream));
+                                    mem_stride, gate_logit, kcache, vcache, pos, o, workspace,
+                                    stream));
 }
 
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream)

@@ -413,6 +413,9 @@ struct ProjBwdDw {
 // latency (one wave per SIMD left the matrix cores idle most of the time).
 using ProjCfg = TileCfg<128, 128, 2, 4, 2>;   // wave tile 64 x 32, 2 workgroups per CU
 using DwCfg = TileCfg<256, 256, 4, 4, 2>;     // wave tile 64 x 64, split over tokens
+// At most 64 rows (decode: one memory row per stream) against many output
+// columns (every layer's stacked weights): one 64-row tile, weights streamed once.
+using WideCfg = TileCfg<64, 128, 1, 4, 2>;    // wave tile 64 x 32
 
 template <class Cfg, class P>
 static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const char *name)
@@ -435,7 +438,9 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
     p.vm = static_cast<bf16 *>(vm);
     p.M = g.N(); p.N = 2 * (int64_t)g.HD(); p.K = g.d; p.T = g.T;
     p.HD = g.HD(); p.shift = shift;
-    if (p.M <= 64) {
+    if (p.M <= 64 && p.N >= 8192) {
+        run_gemm<WideCfg>(p, 1, p.K, s, "proj_fwd_wide");
+    } else if (p.M <= 64) {
         prof::Scope ts("proj_fwd_skinny", s);
         hipLaunchKernelGGL(gemm_skinny_bf16<ProjFwd>, dim3((unsigned)((p.N + 15) / 16)), dim3(256), 0,
                            s, p);

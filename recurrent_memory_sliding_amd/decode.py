@@ -4,12 +4,14 @@ The state of every stream is exactly what the method keeps at inference
 (Maglev summary on paper.rainbus.top, "Maglev：滑动窗口循环记忆", section
 方法步骤详情; gist.science summary, section Inferentiemechanisme): one W-slot
 K/V ring per layer holding mixed entries, the stream's absolute position, and
-the previous step's memory m_{t-1}. One step runs, for every layer, the memory
-projection of m_{t-1} (shift 0) and the decode step on that layer's ring; the
-memory of the next step is then taken from the last layer's output (the
-attention path stands in for the rest of the decoder block, which is outside
-this library). All work is issued through the C ABI on one stream, and a step
-can be captured once as a HIP graph and replayed.
+the previous step's memory m_{t-1}. Every layer of a step injects the same
+m_{t-1}, so one step runs a single memory projection of m_{t-1} by all layers'
+stacked weights (shift 0), then the decode step on each layer's ring, which
+reads its layer's slice of that projection; the memory of the next step is
+then taken from the last layer's output (the attention path stands in for the
+rest of the decoder block, which is outside this library). All work is issued
+through the C ABI on one stream, and a step can be captured once as a HIP
+graph and replayed.
 """
 from __future__ import annotations
 
@@ -44,26 +46,34 @@ class DecodeStack:
         dev, dt = m.device, m.dtype
         self.m = m.reshape(Bs, 1, self.d).clone()
         self.rope_base = rope_base
-        self.kmem = [torch.empty((Bs, 1, H, Dh), dtype=dt, device=dev) for _ in range(self.L)]
-        self.vmem = [torch.empty((Bs, 1, H, Dh), dtype=dt, device=dev) for _ in range(self.L)]
-        # The last layer writes its output straight into the memory buffer: every
-        # layer's projection of this step has read m before that write is issued.
+        # all layers' projection weights stacked along the output rows: one GEMM per step
+        self.Wk_all = torch.cat([w["W_Km"] for w in weights], dim=0).contiguous()
+        self.Wv_all = torch.cat([w["W_Vm"] for w in weights], dim=0).contiguous()
+        self.HD = H * Dh
+        self.kmem_all = torch.empty((Bs, 1, self.L * H, Dh), dtype=dt, device=dev)
+        self.vmem_all = torch.empty((Bs, 1, self.L * H, Dh), dtype=dt, device=dev)
+        flat_k = self.kmem_all.view(Bs, self.L * self.HD)
+        flat_v = self.vmem_all.view(Bs, self.L * self.HD)
+        self.kmem = [flat_k[:, l * self.HD:(l + 1) * self.HD] for l in range(self.L)]
+        self.vmem = [flat_v[:, l * self.HD:(l + 1) * self.HD] for l in range(self.L)]
+        # The last layer writes its output straight into the memory buffer: the
+        # step's projection has read m before that write is issued.
         self.out = [torch.empty((Bs, H, Dh), dtype=dt, device=dev) for _ in range(self.L - 1)]
         self.out.append(self.m.view(Bs, H, Dh))
         need = maglev_decode_workspace(Bs, H, Dh, W)
-        self.ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros((max(need, 1),), dtype=torch.uint8, device=dev)
         self.graphs = {}
 
     def _issue(self, q: List[torch.Tensor], k: List[torch.Tensor], v: List[torch.Tensor]):
         """Enqueue one step; q/k/v are per-layer [Bs, H, Dh] tensors."""
+        maglev_mem_project(self.m, self.Wk_all, self.Wv_all, self.L * self.H, self.Dh, shift=0,
+                           kmem=self.kmem_all, vmem=self.vmem_all)
+        stride = self.L * self.HD
         for l in range(self.L):
-            w = self.weights[l]
-            maglev_mem_project(self.m, w["W_Km"], w["W_Vm"], self.H, self.Dh, shift=0,
-                               kmem=self.kmem[l], vmem=self.vmem[l])
-            maglev_decode_step(q[l], k[l], v[l], self.kmem[l].view(self.Bs, self.H, self.Dh),
-                               self.vmem[l].view(self.Bs, self.H, self.Dh), w["gate_logit"],
-                               self.kcache[l], self.vcache[l], self.pos, o=self.out[l],
-                               rope_base=self.rope_base, workspace=self.ws)
+            maglev_decode_step(q[l], k[l], v[l], self.kmem[l], self.vmem[l],
+                               self.weights[l]["gate_logit"], self.kcache[l], self.vcache[l],
+                               self.pos, o=self.out[l], rope_base=self.rope_base,
+                               workspace=self.ws, mem_stride=stride)
         maglev_decode_advance(self.pos)
 
     def step(self, q, k, v):

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.maglev_abi_version() == 2
+    assert L.maglev_abi_version() == 3
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
     assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
     assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
@@ -142,16 +142,21 @@ def test_loss_validation(L):
 
 def test_decode_validation(L):
     need = L.maglev_decode_workspace(64, 10, 128, 512)
-    assert need == 64 * 10 * 8 * (128 + 4) * 4
-    ptrs = [FAKE] * 10
+    assert need == 0                                     # the step needs no scratch
+    head = [FAKE] * 5                                    # q k v kmem vmem
+    tail = [FAKE] * 5                                    # gate kcache vcache pos o
     args = lambda **kw: [kw.get("Bs", 64), 10, kw.get("Dh", 128), kw.get("W", 512), 1e4, 0.0,
                          kw.get("dtype", 1)]
-    assert L.maglev_decode_step(*args(Dh=48), *ptrs, FAKE, need, None) == UNSUPPORTED
-    assert L.maglev_decode_step(*args(W=0), *ptrs, FAKE, need, None) == INVALID
-    assert L.maglev_decode_step(*args(), *ptrs, None, 0, None) == WORKSPACE
-    bad = list(ptrs); bad[8] = None  # pos
-    assert L.maglev_decode_step(*args(), *bad, FAKE, need, None) == INVALID
-    assert L.maglev_decode_step(*args(Bs=0), *ptrs, FAKE, need, None) == OK
+    step = lambda a, stride=0, t=tail, ws=FAKE, n=need: L.maglev_decode_step(*a, *head, stride, *t,
+                                                                             ws, n, None)
+    assert step(args(Dh=48)) == UNSUPPORTED
+    assert step(args(W=0)) == INVALID
+    bad = list(tail); bad[3] = None  # pos
+    assert step(args(), t=bad) == INVALID
+    assert step(args(), stride=10 * 128 - 8) == INVALID   # below H*Dh
+    assert step(args(), stride=10 * 128 + 4) == INVALID   # not a multiple of 8
+    assert step(args(Bs=0)) == OK
+    assert step(args(Bs=0), stride=20 * 10 * 128) == OK
     assert L.maglev_decode_advance(5, None, None) == INVALID
     assert L.maglev_decode_advance(0, FAKE, None) == OK
 

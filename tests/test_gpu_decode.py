@@ -128,6 +128,42 @@ def test_memory_projection_of_one_row():
     check("vmem", vm, rvm, 2e-2)
 
 
+def test_wide_projection_of_few_rows():
+    """Few rows against many output columns (the per-step projection of every
+    layer's stacked weights): 5 rows x 2 x 40 heads x 128."""
+    Bs, d, H, Dh = 5, 256, 40, 128
+    gen = torch.Generator().manual_seed(61)
+    m = torch.randn(Bs, 1, d, generator=gen).bfloat16()
+    WK = (torch.randn(H * Dh, d, generator=gen) / d ** 0.5).bfloat16()
+    WV = (torch.randn(H * Dh, d, generator=gen) / d ** 0.5).bfloat16()
+    km, vm = rms.maglev_mem_project(m.cuda(), WK.cuda(), WV.cuda(), H, Dh, shift=0)
+    torch.cuda.synchronize()
+    rkm, rvm = oracle.mem_project(m, WK, WV, H, Dh, shift=0)
+    check("kmem", km, rkm, 2e-2)
+    check("vmem", vm, rvm, 2e-2)
+
+
+def test_strided_memory_equals_packed():
+    """Reading one layer's slice of a stacked projection through mem_stride
+    gives bit-identical steps to the same values packed."""
+    Bs, H, Dh, W, L, d = 3, 2, 128, 24, 3, 256
+    gen = torch.Generator().manual_seed(62)
+    rnd = lambda *s: torch.randn(*s, generator=gen).bfloat16().cuda()
+    kall, vall = rnd(Bs, L * H * Dh), rnd(Bs, L * H * Dh)
+    gate = torch.randn(H, generator=gen).cuda()
+    q, k, v = rnd(Bs, H, Dh), rnd(Bs, H, Dh), rnd(Bs, H, Dh)
+    kc0, vc0 = rnd(Bs, H, W, Dh), rnd(Bs, H, W, Dh)
+    pos = torch.tensor([W + 3, 5, 1000], dtype=torch.int64, device="cuda")
+    for l in range(L):
+        sk, sv = kall[:, l * H * Dh:(l + 1) * H * Dh], vall[:, l * H * Dh:(l + 1) * H * Dh]
+        kc1, vc1, kc2, vc2 = kc0.clone(), vc0.clone(), kc0.clone(), vc0.clone()
+        o1 = rms.maglev_decode_step(q, k, v, sk, sv, gate, kc1, vc1, pos, mem_stride=L * H * Dh)
+        o2 = rms.maglev_decode_step(q, k, v, sk.contiguous().view(Bs, H, Dh),
+                                    sv.contiguous().view(Bs, H, Dh), gate, kc2, vc2, pos)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(kc1, kc2) and torch.equal(vc1, vc2), l
+
+
 def test_snapshot_restore_is_bit_identical():
     """The whole recurrent state of a stream is (ring, position, memory):
     copying it out and back in gives a bit-identical continuation."""
