@@ -120,6 +120,33 @@ MAGLEV_DEV float wave_sum(float x)
     return x;
 }
 
+typedef __attribute__((address_space(3))) bf16 lds_bf16;
+
+// 16 bytes from global memory straight into LDS: lane L's bytes land at
+// lds_wave_base + 16 L (global_load_lds_dwordx4, LDS base in M0; counted by
+// vmcnt). Written as inline assembly so that the compiler does not track it
+// as an LDS store: it would otherwise wait for every load in flight before
+// the next LDS read, which defeats multi-stage pipelining. The callers wait
+// explicitly (wait_vmcnt) before a barrier that publishes the stage. The
+// instruction has no register results.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 is reserved; it is clobbered on purpose
+MAGLEV_DEV void dma16(const bf16 *src, bf16 *lds_wave_base)
+{
+    const unsigned m = (unsigned)(uintptr_t)(lds_bf16 *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+MAGLEV_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // Map a linear workgroup id so that consecutive logical tiles share an XCD
 // (workgroups are dispatched round-robin over the 8 XCDs, each with its own L2).
 MAGLEV_DEV int xcd_remap(int wg, int nwg)

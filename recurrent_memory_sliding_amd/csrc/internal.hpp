@@ -46,6 +46,10 @@ struct BwdWorkspace {
     float *ds_part;      // [B,H,n_key_tiles] partial d loss / d s_h
     void *W_scaled;      // [2*H*Dh, d] dtype: s_h * [W_Km; W_Vm] (rows scaled)
     float *dW_part;      // [ksplit, 2*H*Dh, d] split-K partials (may be unused)
+    void *q_rot;         // [B,T,H,Dh] dtype: rotated queries (bf16 path)
+    float *lse2;         // [B*H, Tp] lse * log2(e), zero beyond T (bf16 path)
+    float *Dp;           // [B*H, Tp] rowsum(dO * O), zero beyond T (bf16 path)
+    int64_t Tp;          // T rounded up to a multiple of 32
     int ksplit;
     int n_key_tiles;
 };

@@ -1,24 +1,30 @@
 // mfma_attn.hip -- bf16 MFMA kernels of the injected sliding-window attention:
-// forward, and the backward's row-dot, key-stationary dK/dV pass and
-// query-stationary dQ pass.
+// forward, and the backward's preprocess (row dot and rotated queries),
+// key-stationary dK/dV pass and query-stationary dQ pass.
 //
 // Method: Maglev summary on paper.rainbus.top ("Maglev：滑动窗口循环记忆"),
 // sections 前置知识 (each position attends to the W most recent tokens; RoPE
 // rotates q and k by absolute-position angles, the injected key included,
 // before mixing) and 方法步骤详情 (the gated mix of the projected shifted
 // memory into the token's own K/V entry; attention over the W most recent
-// mixed entries). Mixed entries: k~_j = R_j (k_j + s_h kmem_j),
-// v~_j = v_j + s_h vmem_j (R is linear, so R k + s R kmem = R (k + s kmem)).
+// mixed entries). The mixed entries k~_j = R_j (k_j + s_h kmem_j),
+// v~_j = v_j + s_h vmem_j arrive precomputed (the projection call writes them).
 //
 // Design (gfx950): 256-thread workgroups of four 64-wide waves, each wave
 // owning 32 rows; v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Scores are
-// computed transposed (S^T = K~ Q^T) so that each lane owns one query (or key)
-// column: the softmax state is per lane, the probabilities stay in registers
-// and feed the next product directly (their key order is permuted to match
-// the accumulator layout, and the K/V operand is read in the same order
-// through ds_read_b64_tr_b16). The mixed entries k~, v~ arrive precomputed
-// (the projection call writes them), so a K/V tile is a plain copy into LDS;
-// key tiles wholly outside a wave's band are skipped, and only tiles that
+// computed transposed (S^T = K~ Q^T) where that makes each lane own one query
+// (or key) column: the softmax state is per lane, the probabilities stay in
+// registers and feed the next product directly (their key order is permuted
+// to match the accumulator layout, and the other operand is read in the same
+// order through ds_read_b64_tr_b16).
+//
+// Streamed tiles (K~/V~ in the forward and dQ passes, Q^/dO in the dK/dV pass)
+// go from global memory straight into LDS (global_load_lds, 16 bytes a lane)
+// through a ring of pipeline stages: the next tiles' loads are in flight
+// while the current one is used. Tiles are unpadded [rows][Dh] with 16-byte chunks XOR-swizzled so
+// that both the row reads (ds_read_b128, 16 rows a pass) and the transposed
+// reads (4 rows x 64 bytes a half-wave pass) hit every LDS bank once. Key
+// tiles wholly outside a wave's band are skipped, and only tiles that
 // straddle a band edge are masked.
 #include "common.hpp"
 #include "mfma_kernels.hpp"
@@ -28,8 +34,10 @@ namespace maglev {
 namespace mfma {
 
 struct AttnArgs {
-    const bf16 *q, *kx, *vx, *km, *vm;   // kx/vx: mixed entries k~, v~
-    const float2 *rope;   // [pos][Dh/2] (cos, sin) or nullptr
+    const bf16 *q;      // queries before rotation (forward)
+    const bf16 *qr;     // rotated queries R q (backward)
+    const bf16 *kx, *vx, *km, *vm;
+    const float2 *rope; // [pos][Dh/2] (cos, sin) or nullptr
     int64_t B, T;
     int H, W;
     int64_t pos0;
@@ -41,6 +49,69 @@ MAGLEV_DEV int64_t act_row(const AttnArgs &a, int64_t b, int64_t t, int h)
     return (b * a.T + t) * a.H + h;
 }
 
+// Source of tile rows outside the sequence.
+__device__ __attribute__((aligned(256))) bf16 g_attn_zero[128] = {};
+
+// ---------------------------------------------------------------------------
+// Swizzled tiles: chunk c (8 channels) of row r sits in slot c ^ swz(r).
+//   Dh = 128 (16 chunks a row, 256 bytes = all 64 banks): swz is a bijection
+//     of r mod 16 (row reads: 16 rows of one chunk -> 16 slots) whose bits
+//     2-3 are r mod 4 (transposed reads: 4 rows of one 64-byte group -> 4 groups).
+//   Dh = 64 (8 chunks, 128 bytes: rows alternate bank halves): bijective on
+//     r/2 mod 8 for the row reads; rows r, r+2 of a group differ by 64 bytes.
+// ---------------------------------------------------------------------------
+template <int DH>
+MAGLEV_DEV int swz(int r)
+{
+    if constexpr (DH == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+template <int DH>
+MAGLEV_DEV int tile_off(int r, int c)
+{
+    return r * DH + ((c ^ swz<DH>(r)) << 3);
+}
+
+// Row operand: rows 32 rb + (lane % 32), channels 16 s + 8 (lane / 32) .. +7.
+template <int DH>
+MAGLEV_DEV bf16x8 tile_rows(const bf16 *t, int rb, int s, int lane)
+{
+    const int r = rb * 32 + (lane & 31);
+    return *reinterpret_cast<const bf16x8 *>(t + tile_off<DH>(r, 2 * s + (lane >> 5)));
+}
+
+// Transposed operand: reduction rows 16 tt + 4 g + {0..3} and 16 tt + 8 + 4 g + {0..3}
+// (g = lane / 32), column 32 db + (lane % 32): the row order of the
+// probabilities held in a score accumulator.
+template <int DH>
+MAGLEV_DEV bf16x8 tile_tr(const bf16 *t, int tt, int db, int lane)
+{
+    const int g = lane >> 5, j = lane & 15;
+    const int n = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    const int c = n >> 3, e = n & 7;
+    const int ra = 16 * tt + 4 * g + (j >> 2);
+    const i16x4 lo = lds_read_tr16(t + tile_off<DH>(ra, c) + e);
+    const i16x4 hi = lds_read_tr16(t + tile_off<DH>(ra + 8, c) + e);
+    return join_tr(lo, hi);
+}
+
+// DMA of a ROWS x DH tile by NW waves: one instruction moves 1 KB = RPI rows.
+template <int DH, int ROWS, int NW>
+struct TileDma {
+    static constexpr int CPR = DH / 8;
+    static constexpr int RPI = 64 / CPR;
+    static constexpr int INSTR = ROWS / RPI;
+    static constexpr int PER_WAVE = INSTR / NW;
+    static_assert(INSTR % NW == 0, "tile / wave mismatch");
+    // Tile row and source chunk of this lane in instruction `ins`.
+    MAGLEV_DEV static int row(int ins, int lane) { return ins * RPI + lane / CPR; }
+    MAGLEV_DEV static int chunk(int r, int lane) { return (lane % CPR) ^ swz<DH>(r); }
+};
+
+// ---------------------------------------------------------------------------
+// Register helpers
+// ---------------------------------------------------------------------------
 // Rotate the channel pairs (lo[e], hi[e]) = (c0 + e, c0 + e + Dh/2) by the
 // table entries cs[0..7] (forward if sign = +1, inverse if -1).
 MAGLEV_DEV void rotate8(float *lo, float *hi, const float2 *cs, float sign)
@@ -57,28 +128,6 @@ MAGLEV_DEV void rotate8(float *lo, float *hi, const float2 *cs, float sign)
             lo[e] = x0 * c - x1 * sn;
             hi[e] = x0 * sn + x1 * c;
         }
-    }
-}
-
-// Stage keys [j0, j0+64) of (b, h) into LDS: Ks[kk][c] = k~_{j0+kk}[c],
-// Vs[kk][c] = v~_{j0+kk}[c]; rows outside [0, T) are zero.
-template <int DH, int KSTR, int VSTR>
-MAGLEV_DEV void stage_kv_tile(const AttnArgs &a, int64_t b, int h, int64_t j0, bf16 *Ks, bf16 *Vs,
-                              int tid)
-{
-    constexpr int CH = DH / 8;   // 16-byte chunks per row
-#pragma unroll
-    for (int u = tid; u < 64 * CH; u += 256) {
-        const int kk = u / CH, cc = u % CH;
-        const int64_t j = j0 + kk;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (j >= 0 && j < a.T) {
-            const int64_t base = act_row(a, b, j, h) * DH + 8 * cc;
-            kv = *reinterpret_cast<const u32x4 *>(a.kx + base);
-            vv = *reinterpret_cast<const u32x4 *>(a.vx + base);
-        }
-        *reinterpret_cast<u32x4 *>(Ks + kk * KSTR + 8 * cc) = kv;
-        *reinterpret_cast<u32x4 *>(Vs + kk * VSTR + 8 * cc) = vv;
     }
 }
 
@@ -112,20 +161,6 @@ MAGLEV_DEV void zero_frags(bf16x8 *f, int n)
     for (int i = 0; i < n; ++i) f[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
 
-// Transpose-read operand: rows k0..k0+3 and k0+8..k0+11 (k0 = 16 t + 4 g) of
-// an LDS tile [rows][STR], columns 32 db + (lane % 32): the key/query order of
-// the probabilities held in the score accumulator.
-template <int STR>
-MAGLEV_DEV bf16x8 tr_operand(const bf16 *lds, int t, int db, int lane)
-{
-    const int g = lane >> 5, j = lane & 15;
-    const int n0 = 32 * db + 16 * ((lane >> 4) & 1);
-    const int k0 = 16 * t + 4 * g;
-    const i16x4 lo = lds_read_tr16(lds + (k0 + (j >> 2)) * STR + n0 + 4 * (j & 3));
-    const i16x4 hi = lds_read_tr16(lds + (k0 + 8 + (j >> 2)) * STR + n0 + 4 * (j & 3));
-    return join_tr(lo, hi);
-}
-
 // Accumulator elements 8 (t % 2) .. +7 of block t / 2 as one bf16 operand.
 MAGLEV_DEV bf16x8 acc_to_operand(const f32x16 &x, int half)
 {
@@ -135,28 +170,78 @@ MAGLEV_DEV bf16x8 acc_to_operand(const f32x16 &x, int half)
     return r;
 }
 
+// Keys j0 .. j0+KT-1 of (b, h) from kx and vx into one K tile and one V tile
+// (this wave's share); rows at or beyond T read zeros.
+template <int DH, int KT>
+MAGLEV_DEV void issue_kv_tile(const bf16 *kbase, const bf16 *vbase, int tok_stride, int T, int j0,
+                              bf16 *kt, bf16 *vt, int w, int lane)
+{
+    using Dma = TileDma<DH, KT, 4>;
+#pragma unroll
+    for (int i = 0; i < Dma::PER_WAVE; ++i) {
+        const int ins = w * Dma::PER_WAVE + i;
+        const int r = Dma::row(ins, lane);
+        const int c = Dma::chunk(r, lane);
+        const int j = j0 + r;
+        const bool in = j < T;
+        const int64_t off = (int64_t)j * tok_stride + c * 8;
+        dma16(in ? kbase + off : g_attn_zero, kt + ins * 512);
+        dma16(in ? vbase + off : g_attn_zero, vt + ins * 512);
+    }
+}
+
+// Pipeline bookkeeping shared by the streamed loops: tile `it` of nt lives in
+// stage it % ST; ST - 1 tiles are issued ahead. At the top of iteration it a
+// wave waits until only the (at most ST - 2) later tiles' loads of its own are
+// outstanding, then the barrier makes every wave's share visible and frees
+// the stage the next issue overwrites (read last in iteration it - 1).
+template <int ST, int PER>
+MAGLEV_DEV void pipeline_wait(int it, int nt)
+{
+    if (ST > 2 && it + ST - 2 < nt) wait_vmcnt<(ST > 2 ? (ST - 2) * PER : 0)>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+}
+
 // ============================================================================
 // Forward
 // ============================================================================
-template <int DH>
+// KT keys per tile (32 or 64), ST pipeline stages.
+template <int DH, int KT, int ST>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, float *lse)
 {
-    constexpr int KSTR = DH + 8;    // 16-byte reads, conflict-free per 16 lanes
-    constexpr int VSTR = 160;       // transpose reads, conflict-free per half wave
-    constexpr int NF = DH / 16, NB = DH / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[64 * KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[64 * VSTR];
+    constexpr int NF = DH / 16, NB = DH / 32, KB = KT / 32;
+    constexpr int TE = KT * DH;                          // elements of one tile
+    constexpr int PER = 2 * TileDma<DH, KT, 4>::PER_WAVE;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][K, V]
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-    const int64_t nqt = (a.T + 127) / 128;
-    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t qt = bid % nqt, bh = bid / nqt;
-    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = (int)a.T, W = a.W;
+    const int nqt = (T + 127) / 128;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = bid % nqt, bh = bid / nqt;
+    const int h = bh % a.H;
     const int64_t b = bh / a.H;
-    const int64_t i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
+    const int i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
+    const int tok_stride = a.H * DH;
+    const bf16 *kbase = a.kx + act_row(a, b, 0, h) * DH;
+    const bf16 *vbase = a.vx + act_row(a, b, 0, h) * DH;
+
+    const int klo = i0 - W + 1 > 0 ? i0 - W + 1 : 0;
+    const int khi = i0 + 128 < T ? i0 + 128 : T;
+    const int jstart = (klo / KT) * KT;
+    const int nt = (khi - jstart + KT - 1) / KT;
+    auto issue = [&](int it) {
+        bf16 *kt = lds + (it % ST) * 2 * TE;
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
 
     bf16x8 qf[NF];
-    if (qi < a.T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
+    if (qi < T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
     else zero_frags(qf, NF);
 
     f32x16 acc[NB];
@@ -166,43 +251,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int64_t klo = i0 - a.W + 1 > 0 ? i0 - a.W + 1 : 0;
-    const int64_t khi = i0 + 128 < a.T ? i0 + 128 : a.T;
-    const bool active = qw0 < a.T;
-    const int64_t wlo = qw0 - a.W + 1;
-    const int64_t whi = qw0 + 31 < a.T - 1 ? qw0 + 31 : a.T - 1;
+    const bool active = qw0 < T;
+    const int wlo = qw0 - W + 1;
+    const int whi = qw0 + 31 < T - 1 ? qw0 + 31 : T - 1;
 
-    for (int64_t j0 = (klo / 64) * 64; j0 < khi; j0 += 64) {
-        __syncthreads();
-        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, Ks, Vs, tid);
-        __syncthreads();
-        if (!active || j0 > whi || j0 + 63 < wlo) continue;
+    for (int it = 0; it < nt; ++it) {
+        pipeline_wait<ST, PER>(it, nt);
+        if (it + ST - 1 < nt) issue(it + ST - 1);
+        const int j0 = jstart + it * KT;
+        if (!active || j0 > whi || j0 + KT - 1 < wlo) continue;
+        const bf16 *kt = lds + (it % ST) * 2 * TE, *vt = kt + TE;
 
-        f32x16 sc[2];
+        f32x16 sc[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 kf[NF];   // every LDS read of the block issued before the products
+#pragma unroll
+            for (int s = 0; s < NF; ++s) kf[s] = tile_rows<DH>(kt, kb, s, lane);
 #pragma unroll
             for (int e = 0; e < 16; ++e) sc[kb][e] = 0.0f;
 #pragma unroll
-            for (int s = 0; s < NF; ++s) {
-                const bf16x8 af =
-                    *reinterpret_cast<const bf16x8 *>(Ks + (32 * kb + l32) * KSTR + 16 * s + 8 * g);
-                sc[kb] = mfma32(af, qf[s], sc[kb]);
-            }
+            for (int s = 0; s < NF; ++s) sc[kb] = mfma32(kf[s], qf[s], sc[kb]);
         }
-        const bool inside = (j0 + 63 <= qw0) && (j0 >= qw0 + 31 - a.W + 1) && (j0 + 63 < a.T);
+        const bool inside = (j0 + KT - 1 <= qw0) && (j0 >= qw0 + 31 - W + 1) && (j0 + KT - 1 < T);
         if (!inside) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int64_t key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                    if (key > qi || key < qi - a.W + 1 || key >= a.T) sc[kb][e] = -INFINITY;
+                    const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+                    if (key > qi || key < qi - W + 1 || key >= T) sc[kb][e] = -INFINITY;
                 }
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[kb][e]);
         mx = fmaxf(mx, xor32(mx));
@@ -211,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         const float alpha = exp2f(m_run - m_use);
         float rs = 0.0f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = exp2f(sc[kb][e] - m_use);
@@ -225,16 +308,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         for (int db = 0; db < NB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pf[t] = acc_to_operand(sc[t >> 1], t & 1);
+        bf16x8 pf[2 * KB], vfr[NB][2 * KB];
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[db] = mfma32(tr_operand<VSTR>(Vs, t, db, lane), pf[t], acc[db]);
+            for (int t = 0; t < 2 * KB; ++t) vfr[db][t] = tile_tr<DH>(vt, t, db, lane);
+#pragma unroll
+        for (int t = 0; t < 2 * KB; ++t) pf[t] = acc_to_operand(sc[t >> 1], t & 1);
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+            for (int t = 0; t < 2 * KB; ++t) acc[db] = mfma32(vfr[db][t], pf[t], acc[db]);
     }
 
-    if (qi < a.T) {
+    if (qi < T) {
         const float inv = 1.0f / l_run;
         bf16 *orow = o + act_row(a, b, qi, h) * DH;
 #pragma unroll
@@ -253,61 +340,126 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
 // ============================================================================
 // Backward
 // ============================================================================
-// D[b,h,t] = sum_c dO[b,t,h,c] O[b,t,h,c]
+// Preprocess, one thread per chunk pair (channels 8cc .. +7 and the same + Dh/2)
+// of a (b, t, h) row:
+//   Dp[b,h,t] = sum_c dO[b,t,h,c] O[b,t,h,c], lse2[b,h,t] = lse[b,h,t] log2(e)
+//   (both rows padded with zeros from T to Tp), and the rotated queries qr = R_t q.
 template <int DH>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const bf16 *o, const bf16 *dO, float *D,
-                                                         int64_t rows, int H, int64_t T)
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16 *o, const bf16 *dO, const bf16 *q,
+                                                       const float *lse, const float2 *rope,
+                                                       bf16 *qr, float *Dp, float *lse2,
+                                                       int64_t rows, int H, int64_t T, int64_t Tp,
+                                                       int64_t pos0)
 {
-    constexpr int CH = DH / 8;
+    constexpr int CP = DH / 16;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / CH;   // (b*T + t)*H + h
-    const int ch = (int)(gid % CH);
+    const int64_t row = gid / CP;   // (b*T + t)*H + h
+    const int cc = (int)(gid % CP);
     float d = 0.0f;
     if (row < rows) {
+        const int64_t base = row * DH + 8 * cc;
         float x[8], y[8];
-        load8(o + row * DH + 8 * ch, x);
-        load8(dO + row * DH + 8 * ch, y);
+        load8(o + base, x);
+        load8(dO + base, y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) d += x[e] * y[e];
+        load8(o + base + DH / 2, x);
+        load8(dO + base + DH / 2, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += x[e] * y[e];
+        float lo[8], hi[8];
+        load8(q + base, lo);
+        load8(q + base + DH / 2, hi);
+        if (rope) {
+            const int64_t t = (row / H) % T;
+            rotate8(lo, hi, rope + (pos0 + t) * (DH / 2) + 8 * cc, 1.0f);
+        }
+        store8(qr + base, lo);
+        store8(qr + base + DH / 2, hi);
     }
 #pragma unroll
-    for (int off = CH / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
-    if (row < rows && ch == 0) {
+    for (int off = CP / 2; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+    if (row < rows && cc == 0) {
         const int h = (int)(row % H);
         const int64_t bt = row / H;
-        D[((bt / T) * H + h) * T + (bt % T)] = d;
+        const int64_t t = bt % T;
+        const int64_t bh = (bt / T) * H + h;
+        Dp[bh * Tp + t] = d;
+        lse2[bh * Tp + t] = lse[bh * T + t] * kLog2e;
+        if (t == T - 1)
+            for (int64_t u = T; u < Tp; ++u) Dp[bh * Tp + u] = lse2[bh * Tp + u] = 0.0f;
     }
 }
 
 // Key-stationary pass: each wave owns 32 keys, the workgroup 128; query tiles
-// of 32 stream through LDS. Per tile: S = Q^ K~^T, P = exp(scale S - lse),
-// dP = dO V~^T, dS = P (dP - D); dV~^T += dO^T P, dK~^T += Q^^T dS.
+// of 32 (rotated queries Q^ and dO, with their lse and D) stream through LDS.
+// Per tile: S = Q^ K~^T, P = exp(scale S - lse), dP = dO V~^T,
+// dS = P (dP - D); dV~^T += dO^T P, dK~^T += Q^^T dS.
 // Epilogue: dk = scale R^T dK~, dv = dV~, and the gate partial
 // <kmem, dk> + <vmem, dv> summed over the workgroup's keys.
-template <int DH>
+template <int DH, int ST>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf16 *dO,
-                                                             const float *lse, const float *D,
-                                                             bf16 *dk, bf16 *dv, float *ds_part)
+                                                             const float *lse2, const float *Dp,
+                                                             int64_t Tp, bf16 *dk, bf16 *dv,
+                                                             float *ds_part)
 {
-    constexpr int QSTR = DH + 8;
-    constexpr int NF = DH / 16, NB = DH / 32, CP = DH / 16;
-    __shared__ __attribute__((aligned(16))) bf16 Qs[32 * QSTR];
-    __shared__ __attribute__((aligned(16))) bf16 dOs[32 * QSTR];
-    __shared__ float Ls[32], Ds[32];
+    constexpr int NF = DH / 16, NB = DH / 32;
+    constexpr int QT = 32;
+    constexpr int TE = QT * DH;
+    using Dma = TileDma<DH, QT, 4>;
+    constexpr int PER = 2 * Dma::PER_WAVE + 1;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][Q^, dO]
+    __shared__ __attribute__((aligned(16))) float LD[ST][2 * QT];      // [stage][lse2, D]
     __shared__ float red[4];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-    const int64_t nkt = (a.T + 127) / 128;
-    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t kt = bid % nkt, bh = bid / nkt;
-    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = (int)a.T, W = a.W;
+    const int nkt = (T + 127) / 128;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = bid % nkt, bh = bid / nkt;
+    const int h = bh % a.H;
     const int64_t b = bh / a.H;
-    const int64_t j0 = kt * 128, kw0 = j0 + 32 * w, kj = kw0 + l32;
+    const int j0 = kt * 128, kw0 = j0 + 32 * w, kj = kw0 + l32;
     const float qscale = a.scale * kLog2e;
+    const int tok_stride = a.H * DH;
+    const bf16 *qbase = a.qr + act_row(a, b, 0, h) * DH;
+    const bf16 *obase = dO + act_row(a, b, 0, h) * DH;
+    const float *lrow = lse2 + (int64_t)bh * Tp;
+    const float *drow = Dp + (int64_t)bh * Tp;
+
+    const int qend = j0 + 127 + W < T ? j0 + 127 + W : T;   // exclusive
+    const int nt = (qend - j0 + QT - 1) / QT;
+    auto issue = [&](int it) {
+        const int buf = it % ST;
+        const int i0 = j0 + it * QT;
+        bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+#pragma unroll
+        for (int i = 0; i < Dma::PER_WAVE; ++i) {
+            const int ins = w * Dma::PER_WAVE + i;
+            const int r = Dma::row(ins, lane);
+            const int c = Dma::chunk(r, lane);
+            const int qi = i0 + r;
+            const bool in = qi < T;
+            const int64_t off = (int64_t)qi * tok_stride + c * 8;
+            dma16(in ? qbase + off : g_attn_zero, qt + ins * 512);
+            dma16(in ? obase + off : g_attn_zero, ot + ins * 512);
+        }
+        // lse2 and D of the tile: 16 chunks of 16 bytes, four per wave (rows
+        // are padded to Tp, so the tile never leaves its row).
+        if (lane < 4) {
+            const int q = 4 * w + lane;
+            const float *src = q < 8 ? lrow + i0 + 4 * q : drow + i0 + 4 * (q - 8);
+            dma16(reinterpret_cast<const bf16 *>(src), reinterpret_cast<bf16 *>(&LD[buf][16 * w]));
+        }
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
 
     // This lane's key: k~ and v~ as B operands (fragment s: channels 16 s + 8 g .. +7).
     bf16x8 kf[NF], vf[NF];
-    if (kj < a.T) {
+    if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
 #pragma unroll
         for (int s = 0; s < NF; ++s) {
@@ -325,55 +477,36 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
 #pragma unroll
         for (int e = 0; e < 16; ++e) dva[db][e] = dka[db][e] = 0.0f;
 
-    const int64_t qend = j0 + 127 + a.W < a.T ? j0 + 127 + a.W : a.T;   // exclusive
-    const bool active = kw0 < a.T;
-    for (int64_t i0 = j0; i0 < qend; i0 += 32) {
-        __syncthreads();
-        // stage Q^ (rotated) and dO for queries i0 .. i0+31
-        for (int u = tid; u < 32 * CP; u += 256) {
-            const int qq = u / CP, cc = u % CP;
-            const int64_t i = i0 + qq;
-            float lo[8], hi[8], dlo[8], dhi[8];
-            if (i < a.T) {
-                const int64_t base = act_row(a, b, i, h) * DH + 8 * cc;
-                load8(a.q + base, lo);
-                load8(a.q + base + DH / 2, hi);
-                if (a.rope) rotate8(lo, hi, a.rope + (a.pos0 + i) * (DH / 2) + 8 * cc, 1.0f);
-                load8(dO + base, dlo);
-                load8(dO + base + DH / 2, dhi);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) lo[e] = hi[e] = dlo[e] = dhi[e] = 0.0f;
-            }
-            store8(Qs + qq * QSTR + 8 * cc, lo);
-            store8(Qs + qq * QSTR + DH / 2 + 8 * cc, hi);
-            store8(dOs + qq * QSTR + 8 * cc, dlo);
-            store8(dOs + qq * QSTR + DH / 2 + 8 * cc, dhi);
-        }
-        if (tid < 32) {
-            const int64_t i = i0 + tid;
-            Ls[tid] = i < a.T ? lse[(b * a.H + h) * a.T + i] * kLog2e : 0.0f;
-            Ds[tid] = i < a.T ? D[(b * a.H + h) * a.T + i] : 0.0f;
-        }
-        __syncthreads();
-        if (!active || i0 + 31 < kw0 || i0 > kw0 + 31 + a.W - 1) continue;
+    const bool active = kw0 < T;
+    for (int it = 0; it < nt; ++it) {
+        pipeline_wait<ST, PER>(it, nt);
+        if (it + ST - 1 < nt) issue(it + ST - 1);
+        const int i0 = j0 + it * QT;
+        if (!active || i0 + QT - 1 < kw0 || i0 > kw0 + 31 + W - 1) continue;
+        const int buf = it % ST;
+        const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+        const float *Ls = LD[buf], *Ds = LD[buf] + QT;
 
         f32x16 sc, dp;
+        bf16x8 qa[NF], oa[NF];   // every LDS read of the tile issued before the products
+#pragma unroll
+        for (int s = 0; s < NF; ++s) {
+            qa[s] = tile_rows<DH>(qt, 0, s, lane);
+            oa[s] = tile_rows<DH>(ot, 0, s, lane);
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.0f;
 #pragma unroll
         for (int s = 0; s < NF; ++s) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(Qs + l32 * QSTR + 16 * s + 8 * g);
-            sc = mfma32(qa, kf[s], sc);
-            const bf16x8 da = *reinterpret_cast<const bf16x8 *>(dOs + l32 * QSTR + 16 * s + 8 * g);
-            dp = mfma32(da, vf[s], dp);
+            sc = mfma32(qa[s], kf[s], sc);
+            dp = mfma32(oa[s], vf[s], dp);
         }
         // element e: query i0 + 8(e/4) + 4g + e%4, key kj
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int qq = 8 * (e >> 2) + 4 * g + (e & 3);
-            const int64_t i = i0 + qq;
-            const bool ok = i >= kj && i - kj < a.W && i < a.T;
+            const int i = i0 + qq;
+            const bool ok = i >= kj && i - kj < W && i < T;
             const float p = ok ? exp2f(sc[e] * qscale - Ls[qq]) : 0.0f;
             sc[e] = p;
             dp[e] = p * (dp[e] - Ds[qq]);
@@ -384,15 +517,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
             const bf16x8 dsf = acc_to_operand(dp, t);
 #pragma unroll
             for (int db = 0; db < NB; ++db) {
-                dva[db] = mfma32(tr_operand<QSTR>(dOs, t, db, lane), pf, dva[db]);
-                dka[db] = mfma32(tr_operand<QSTR>(Qs, t, db, lane), dsf, dka[db]);
+                dva[db] = mfma32(tile_tr<DH>(ot, t, db, lane), pf, dva[db]);
+                dka[db] = mfma32(tile_tr<DH>(qt, t, db, lane), dsf, dka[db]);
             }
         }
     }
 
     // Epilogue: element e of block db is channel 32 db + 8(e/4) + 4g + e%4 of key kj.
     float part = 0.0f;
-    if (kj < a.T) {
+    if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
         const float2 *cs = a.rope ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
 #pragma unroll
@@ -435,92 +568,116 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     if (tid == 0) ds_part[(b * a.H + h) * nkt + kt] = red[0] + red[1] + red[2] + red[3];
 }
 
-// Query-stationary pass: each wave owns 32 queries; key tiles of 64 in the
-// band stream through LDS (mixed on load). Per tile: S^T = K~ Q^^T,
-// P^T = exp(scale S^T - lse), dP^T = V~ dO^T, dS^T = P^T (dP^T - D),
-// dQ^^T += K~^T dS^T. Epilogue: dq = scale R^T dQ^.
-template <int DH>
+// Query-stationary pass: each wave owns 32 queries; key tiles of KT in the
+// band stream through LDS. Per tile: S^T = K~ Q^^T, P^T = exp(scale S^T - lse),
+// dP^T = V~ dO^T, dS^T = P^T (dP^T - D), dQ^^T += K~^T dS^T.
+// Epilogue: dq = scale R^T dQ^.
+template <int DH, int KT, int ST>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const bf16 *dO,
-                                                              const float *lse, const float *D,
-                                                              bf16 *dq)
+                                                              const float *lse2, const float *Dp,
+                                                              int64_t Tp, bf16 *dq)
 {
-    constexpr int KSTR = DH + 8, VSTR = DH + 8;
-    constexpr int NF = DH / 16, NB = DH / 32;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[64 * KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vs[64 * VSTR];
+    constexpr int NF = DH / 16, NB = DH / 32, KB = KT / 32;
+    constexpr int TE = KT * DH;
+    constexpr int PER = 2 * TileDma<DH, KT, 4>::PER_WAVE;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][K, V]
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-    const int64_t nqt = (a.T + 127) / 128;
-    const int64_t bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t qt = bid % nqt, bh = bid / nqt;
-    const int h = (int)(bh % a.H);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = (int)a.T, W = a.W;
+    const int nqt = (T + 127) / 128;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = bid % nqt, bh = bid / nqt;
+    const int h = bh % a.H;
     const int64_t b = bh / a.H;
-    const int64_t i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
+    const int i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
+    const int tok_stride = a.H * DH;
+    const bf16 *kbase = a.kx + act_row(a, b, 0, h) * DH;
+    const bf16 *vbase = a.vx + act_row(a, b, 0, h) * DH;
+
+    const int klo = i0 - W + 1 > 0 ? i0 - W + 1 : 0;
+    const int khi = i0 + 128 < T ? i0 + 128 : T;
+    const int jstart = (klo / KT) * KT;
+    const int nt = (khi - jstart + KT - 1) / KT;
+    auto issue = [&](int it) {
+        bf16 *kt = lds + (it % ST) * 2 * TE;
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
 
     bf16x8 qf[NF], df[NF];
-    float lse2 = 0.0f, Dq = 0.0f;
-    if (qi < a.T) {
+    float lse_q = 0.0f, Dq = 0.0f;
+    if (qi < T) {
         const int64_t base = act_row(a, b, qi, h) * DH;
-        token_frags<DH>(a, a.q + base, qi, g, true, a.scale * kLog2e, qf);
+        token_frags<DH>(a, a.qr + base, qi, g, false, 1.0f, qf);
         token_frags<DH>(a, dO + base, qi, g, false, 1.0f, df);
-        lse2 = lse[(b * a.H + h) * a.T + qi] * kLog2e;
-        Dq = D[(b * a.H + h) * a.T + qi];
+        lse_q = lse2[(int64_t)bh * Tp + qi];
+        Dq = Dp[(int64_t)bh * Tp + qi];
     } else {
         zero_frags(qf, NF);
         zero_frags(df, NF);
     }
+    const float qscale = a.scale * kLog2e;
     f32x16 acc[NB];
 #pragma unroll
     for (int db = 0; db < NB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
 
-    const int64_t klo = i0 - a.W + 1 > 0 ? i0 - a.W + 1 : 0;
-    const int64_t khi = i0 + 128 < a.T ? i0 + 128 : a.T;
-    const bool active = qw0 < a.T;
-    const int64_t wlo = qw0 - a.W + 1;
-    const int64_t whi = qw0 + 31 < a.T - 1 ? qw0 + 31 : a.T - 1;
+    const bool active = qw0 < T;
+    const int wlo = qw0 - W + 1;
+    const int whi = qw0 + 31 < T - 1 ? qw0 + 31 : T - 1;
 
-    for (int64_t j0 = (klo / 64) * 64; j0 < khi; j0 += 64) {
-        __syncthreads();
-        stage_kv_tile<DH, KSTR, VSTR>(a, b, h, j0, Ks, Vs, tid);
-        __syncthreads();
-        if (!active || j0 > whi || j0 + 63 < wlo) continue;
+    for (int it = 0; it < nt; ++it) {
+        pipeline_wait<ST, PER>(it, nt);
+        if (it + ST - 1 < nt) issue(it + ST - 1);
+        const int j0 = jstart + it * KT;
+        if (!active || j0 > whi || j0 + KT - 1 < wlo) continue;
+        const bf16 *kt = lds + (it % ST) * 2 * TE, *vt = kt + TE;
 
-        f32x16 sc[2], dp[2];
+        f32x16 sc[KB], dp[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 kf[NF], vf[NF];   // every LDS read of the block issued before the products
+#pragma unroll
+            for (int s = 0; s < NF; ++s) {
+                kf[s] = tile_rows<DH>(kt, kb, s, lane);
+                vf[s] = tile_rows<DH>(vt, kb, s, lane);
+            }
 #pragma unroll
             for (int e = 0; e < 16; ++e) sc[kb][e] = dp[kb][e] = 0.0f;
 #pragma unroll
             for (int s = 0; s < NF; ++s) {
-                const bf16x8 ka =
-                    *reinterpret_cast<const bf16x8 *>(Ks + (32 * kb + l32) * KSTR + 16 * s + 8 * g);
-                sc[kb] = mfma32(ka, qf[s], sc[kb]);
-                const bf16x8 va =
-                    *reinterpret_cast<const bf16x8 *>(Vs + (32 * kb + l32) * VSTR + 16 * s + 8 * g);
-                dp[kb] = mfma32(va, df[s], dp[kb]);
+                sc[kb] = mfma32(kf[s], qf[s], sc[kb]);
+                dp[kb] = mfma32(vf[s], df[s], dp[kb]);
             }
         }
-        const bool inside = (j0 + 63 <= qw0) && (j0 >= qw0 + 31 - a.W + 1) && (j0 + 63 < a.T);
+        const bool inside = (j0 + KT - 1 <= qw0) && (j0 >= qw0 + 31 - W + 1) && (j0 + KT - 1 < T);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                const bool ok = inside || (key <= qi && key > qi - a.W && key < a.T);
-                const float p = ok ? exp2f(sc[kb][e] - lse2) : 0.0f;
+                const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+                const bool ok = inside || (key <= qi && key > qi - W && key < T);
+                const float p = ok ? exp2f(sc[kb][e] * qscale - lse_q) : 0.0f;
                 dp[kb][e] = p * (dp[kb][e] - Dq);
             }
+        bf16x8 ktr[NB][2 * KB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+            for (int t = 0; t < 2 * KB; ++t) ktr[db][t] = tile_tr<DH>(kt, t, db, lane);
+#pragma unroll
+        for (int t = 0; t < 2 * KB; ++t) {
             const bf16x8 dsf = acc_to_operand(dp[t >> 1], t & 1);
 #pragma unroll
-            for (int db = 0; db < NB; ++db) acc[db] = mfma32(tr_operand<KSTR>(Ks, t, db, lane), dsf, acc[db]);
+            for (int db = 0; db < NB; ++db) acc[db] = mfma32(ktr[db][t], dsf, acc[db]);
         }
     }
 
-    if (qi < a.T) {
+    if (qi < T) {
         const int64_t base = act_row(a, b, qi, h) * DH;
         const float2 *cs = a.rope ? a.rope + (a.pos0 + qi) * (DH / 2) : nullptr;
 #pragma unroll
@@ -553,11 +710,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
 // ============================================================================
 // Launchers
 // ============================================================================
-static AttnArgs make_args(const Geom &g, const void *q, const void *kx, const void *vx,
-                          const void *km, const void *vm, const float2 *rope)
+static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const void *kx,
+                          const void *vx, const void *km, const void *vm, const float2 *rope)
 {
     AttnArgs a;
     a.q = static_cast<const bf16 *>(q);
+    a.qr = static_cast<const bf16 *>(qr);
     a.kx = static_cast<const bf16 *>(kx);
     a.vx = static_cast<const bf16 *>(vx);
     a.km = static_cast<const bf16 *>(km);
@@ -567,16 +725,23 @@ static AttnArgs make_args(const Geom &g, const void *q, const void *kx, const vo
     return a;
 }
 
+// Tile shapes and pipeline depths: forward and dQ stream K~/V~ tiles of
+// kFwdKT keys through kFwdST stages; dK/dV streams 32-query tiles through
+// kBwdST stages.
+constexpr int kFwdKT = 32, kFwdST = 4, kDqKT = 32, kDqST = 4, kBwdST = 4;
+
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)
 {
-    const AttnArgs a = make_args(g, q, kx, vx, nullptr, nullptr, rope);
+    const AttnArgs a = make_args(g, q, nullptr, kx, vx, nullptr, nullptr, rope);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     prof::Scope ts("attn_fwd", s);
     if (g.Dh == 128)
-        hipLaunchKernelGGL(attn_fwd_kernel<128>, dim3(nwg), dim3(256), 0, s, a, static_cast<bf16 *>(o), lse);
+        hipLaunchKernelGGL((attn_fwd_kernel<128, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s, a,
+                           static_cast<bf16 *>(o), lse);
     else
-        hipLaunchKernelGGL(attn_fwd_kernel<64>, dim3(nwg), dim3(256), 0, s, a, static_cast<bf16 *>(o), lse);
+        hipLaunchKernelGGL((attn_fwd_kernel<64, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s, a,
+                           static_cast<bf16 *>(o), lse);
 }
 
 int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
@@ -584,21 +749,24 @@ int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
 template <int DH>
 static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, const float *lse,
                               void *dq, void *dk, void *dv, const BwdWorkspace &ws, int64_t rows,
-                              unsigned pre_blocks, unsigned nwg, hipStream_t s)
+                              unsigned nwg, hipStream_t s)
 {
     {
-        prof::Scope ts("attn_bwd_rowdot", s);
-        hipLaunchKernelGGL(bwd_rowdot_kernel<DH>, dim3(pre_blocks), dim3(256), 0, s, o, dO, ws.D,
-                           rows, a.H, a.T);
+        const unsigned pre_blocks = (unsigned)((rows * (DH / 16) + 255) / 256);
+        prof::Scope ts("attn_bwd_prep", s);
+        hipLaunchKernelGGL(bwd_prep_kernel<DH>, dim3(pre_blocks), dim3(256), 0, s, o, dO, a.q, lse,
+                           a.rope, static_cast<bf16 *>(ws.q_rot), ws.Dp, ws.lse2, rows, a.H, a.T,
+                           ws.Tp, a.pos0);
     }
     {
         prof::Scope ts("attn_bwd_dkdv", s);
-        hipLaunchKernelGGL(attn_bwd_dkdv_kernel<DH>, dim3(nwg), dim3(256), 0, s, a, dO, lse, ws.D,
-                           static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), ws.ds_part);
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST>), dim3(nwg), dim3(256), 0, s, a, dO,
+                           ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk), static_cast<bf16 *>(dv),
+                           ws.ds_part);
     }
     prof::Scope ts("attn_bwd_dq", s);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<DH>, dim3(nwg), dim3(256), 0, s, a, dO, lse, ws.D,
-                       static_cast<bf16 *>(dq));
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a, dO,
+                       ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dq));
 }
 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
@@ -607,17 +775,15 @@ void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const vo
                           const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
 {
     (void)gate;
-    const AttnArgs a = make_args(g, q, kx, vx, km, vm, rope);
+    const AttnArgs a = make_args(g, q, ws.q_rot, kx, vx, km, vm, rope);
     const int64_t rows = g.N() * g.H;
-    const int CH = g.Dh / 8;
-    const unsigned pre_blocks = (unsigned)((rows * CH + 255) / 256);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     const bf16 *ob = static_cast<const bf16 *>(o);
     const bf16 *dOb = static_cast<const bf16 *>(dO);
     if (g.Dh == 128)
-        launch_attn_bwd_t<128>(a, ob, dOb, lse, dq, dk, dv, ws, rows, pre_blocks, nwg, s);
+        launch_attn_bwd_t<128>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, s);
     else
-        launch_attn_bwd_t<64>(a, ob, dOb, lse, dq, dk, dv, ws, rows, pre_blocks, nwg, s);
+        launch_attn_bwd_t<64>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, s);
 }
 
 }  // namespace mfma

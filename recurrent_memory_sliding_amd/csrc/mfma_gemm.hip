@@ -55,22 +55,6 @@ __device__ __attribute__((aligned(256))) bf16 g_zero_rows[64] = {};
 
 MAGLEV_DEV bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes from global memory straight into LDS at base + lane * 16.
-MAGLEV_DEV void dma16(const bf16 *src, bf16 *lds_wave_base)
-{
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_wave_base, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
-template <int N>
-MAGLEV_DEV void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <bool KMAJOR, int R>
 MAGLEV_DEV bf16x8 read_frag(const bf16 *lds, int rb, int ks, int lane)
 {

@@ -281,10 +281,19 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base)
     const size_t oS = off; off = align(off + (size_t)BHT * sizeof(float));
     const size_t oW = off; off = align(off + (size_t)2 * g.HD() * g.d * esz);
     const size_t oP = off; off = align(off + (size_t)L->ksplit * 2 * g.HD() * g.d * sizeof(float));
+    const size_t nq = g.dtype == MAGLEV_BF16 ? (size_t)g.N() * g.HD() : 0;
+    const size_t oQ = off; off = align(off + nq * esz);
+    L->Tp = (g.T + 31) / 32 * 32;
+    const size_t npad = g.dtype == MAGLEV_BF16 ? (size_t)g.B * g.H * L->Tp : 0;
+    const size_t oL = off; off = align(off + npad * sizeof(float));
+    const size_t oDp = off; off = align(off + npad * sizeof(float));
     L->D = base ? reinterpret_cast<float *>(base + oD) : nullptr;
     L->ds_part = base ? reinterpret_cast<float *>(base + oS) : nullptr;
     L->W_scaled = base ? static_cast<void *>(base + oW) : nullptr;
     L->dW_part = base ? reinterpret_cast<float *>(base + oP) : nullptr;
+    L->q_rot = base && nq ? static_cast<void *>(base + oQ) : nullptr;
+    L->lse2 = base && npad ? reinterpret_cast<float *>(base + oL) : nullptr;
+    L->Dp = base && npad ? reinterpret_cast<float *>(base + oDp) : nullptr;
     return off;
 }
 
