@@ -156,6 +156,11 @@ MAGLEV_DEV void token_frags(const AttnArgs &a, const bf16 *src, int64_t t, int g
     }
 }
 
+// 2^x by the hardware instruction (v_exp_f32; -inf -> 0). Its inputs here are
+// scaled scores minus a row maximum or log-sum-exp (never large and positive),
+// so the range fix-ups of exp2f are not needed.
+MAGLEV_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 MAGLEV_DEV void zero_frags(bf16x8 *f, int n)
 {
     for (int i = 0; i < n; ++i) f[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
@@ -232,6 +237,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const int khi = i0 + 128 < T ? i0 + 128 : T;
     const int jstart = (klo / KT) * KT;
     const int nt = (khi - jstart + KT - 1) / KT;
+    // The query operands are complete before any tile load is issued (see the
+    // dQ pass for why).
+    bf16x8 qf[NF];
+    if (qi < T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
+    else zero_frags(qf, NF);
+    wait_vmcnt<0>();
+
     auto issue = [&](int it) {
         bf16 *kt = lds + (it % ST) * 2 * TE;
         issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
@@ -239,10 +251,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nt) issue(s0);
-
-    bf16x8 qf[NF];
-    if (qi < T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
-    else zero_frags(qf, NF);
 
     f32x16 acc[NB];
 #pragma unroll
@@ -280,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                    if (key > qi || key < qi - W + 1 || key >= T) sc[kb][e] = -INFINITY;
+                    if ((key > qi) | (key < qi - W + 1) | (key >= T)) sc[kb][e] = -INFINITY;
                 }
         }
         float mx = -INFINITY;
@@ -291,13 +299,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         mx = fmaxf(mx, xor32(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = fast_exp2(m_run - m_use);
         float rs = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = exp2f(sc[kb][e] - m_use);
+                const float p = fast_exp2(sc[kb][e] - m_use);
                 sc[kb][e] = p;
                 rs += p;
             }
@@ -430,6 +438,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
 
     const int qend = j0 + 127 + W < T ? j0 + 127 + W : T;   // exclusive
     const int nt = (qend - j0 + QT - 1) / QT;
+
+    // This lane's key: k~ and v~ as B operands (fragment s: channels 16 s + 8 g .. +7),
+    // loaded and waited for before any tile load is issued: the loop must see
+    // them as complete, or the compiler waits for every load in flight (the
+    // tile loads included) at their first use inside the loop.
+    bf16x8 kf[NF], vf[NF];
+    if (kj < T) {
+        const int64_t base = act_row(a, b, kj, h) * DH;
+#pragma unroll
+        for (int s = 0; s < NF; ++s) {
+            kf[s] = *reinterpret_cast<const bf16x8 *>(a.kx + base + 16 * s + 8 * g);
+            vf[s] = *reinterpret_cast<const bf16x8 *>(a.vx + base + 16 * s + 8 * g);
+        }
+    } else {
+        zero_frags(kf, NF);
+        zero_frags(vf, NF);
+    }
+    wait_vmcnt<0>();
+
     auto issue = [&](int it) {
         const int buf = it % ST;
         const int i0 = j0 + it * QT;
@@ -457,20 +484,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nt) issue(s0);
 
-    // This lane's key: k~ and v~ as B operands (fragment s: channels 16 s + 8 g .. +7).
-    bf16x8 kf[NF], vf[NF];
-    if (kj < T) {
-        const int64_t base = act_row(a, b, kj, h) * DH;
-#pragma unroll
-        for (int s = 0; s < NF; ++s) {
-            kf[s] = *reinterpret_cast<const bf16x8 *>(a.kx + base + 16 * s + 8 * g);
-            vf[s] = *reinterpret_cast<const bf16x8 *>(a.vx + base + 16 * s + 8 * g);
-        }
-    } else {
-        zero_frags(kf, NF);
-        zero_frags(vf, NF);
-    }
-
     f32x16 dva[NB], dka[NB];
 #pragma unroll
     for (int db = 0; db < NB; ++db)
@@ -481,35 +494,41 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     for (int it = 0; it < nt; ++it) {
         pipeline_wait<ST, PER>(it, nt);
         if (it + ST - 1 < nt) issue(it + ST - 1);
+        // Tiles outside this wave's band are not skipped: the mask zeroes them.
+        // A skip path would make the loop-carried dK/dV accumulators merge two
+        // definitions, and the compiler then keeps them in VGPRs and copies all
+        // 128 into accumulation registers on every tile.
         const int i0 = j0 + it * QT;
-        if (!active || i0 + QT - 1 < kw0 || i0 > kw0 + 31 + W - 1) continue;
+        (void)active;
         const int buf = it % ST;
         const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
         const float *Ls = LD[buf], *Ds = LD[buf] + QT;
 
         f32x16 sc, dp;
-        bf16x8 qa[NF], oa[NF];   // every LDS read of the tile issued before the products
-#pragma unroll
-        for (int s = 0; s < NF; ++s) {
-            qa[s] = tile_rows<DH>(qt, 0, s, lane);
-            oa[s] = tile_rows<DH>(ot, 0, s, lane);
-        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) sc[e] = dp[e] = 0.0f;
 #pragma unroll
         for (int s = 0; s < NF; ++s) {
-            sc = mfma32(qa[s], kf[s], sc);
-            dp = mfma32(oa[s], vf[s], dp);
+            sc = mfma32(tile_rows<DH>(qt, 0, s, lane), kf[s], sc);
+            dp = mfma32(tile_rows<DH>(ot, 0, s, lane), vf[s], dp);
         }
-        // element e: query i0 + 8(e/4) + 4g + e%4, key kj
+        // element e: query i0 + 8(e/4) + 4g + e%4, key kj. The lse/D values of
+        // this lane's 16 queries are four 16-byte LDS reads each, read
+        // unconditionally (no per-element branch around an LDS load).
+        f32x4 lv[4], dv4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            lv[q4] = *reinterpret_cast<const f32x4 *>(Ls + 8 * q4 + 4 * g);
+            dv4[q4] = *reinterpret_cast<const f32x4 *>(Ds + 8 * q4 + 4 * g);
+        }
+        const bool interior = (i0 >= kj) & (i0 + QT - 1 - kj < W) & (i0 + QT - 1 < T);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int qq = 8 * (e >> 2) + 4 * g + (e & 3);
-            const int i = i0 + qq;
-            const bool ok = i >= kj && i - kj < W && i < T;
-            const float p = ok ? exp2f(sc[e] * qscale - Ls[qq]) : 0.0f;
-            sc[e] = p;
-            dp[e] = p * (dp[e] - Ds[qq]);
+            const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
+            const bool ok = interior | ((i >= kj) & (i - kj < W) & (i < T));
+            const float p = fast_exp2(sc[e] * qscale - lv[e >> 2][e & 3]);
+            sc[e] = ok ? p : 0.0f;
+            dp[e] = sc[e] * (dp[e] - dv4[e >> 2][e & 3]);
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -599,14 +618,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
     const int khi = i0 + 128 < T ? i0 + 128 : T;
     const int jstart = (klo / KT) * KT;
     const int nt = (khi - jstart + KT - 1) / KT;
-    auto issue = [&](int it) {
-        bf16 *kt = lds + (it % ST) * 2 * TE;
-        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
-    };
-#pragma unroll
-    for (int s0 = 0; s0 < ST - 1; ++s0)
-        if (s0 < nt) issue(s0);
-
+    // This lane's query operands and statistics, waited for before any tile
+    // load is issued: values still in flight at their first use inside the
+    // loop would make the compiler wait for every load there (tiles included).
     bf16x8 qf[NF], df[NF];
     float lse_q = 0.0f, Dq = 0.0f;
     if (qi < T) {
@@ -619,6 +633,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
         zero_frags(qf, NF);
         zero_frags(df, NF);
     }
+    wait_vmcnt<0>();
+
+    auto issue = [&](int it) {
+        bf16 *kt = lds + (it % ST) * 2 * TE;
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
     const float qscale = a.scale * kLog2e;
     f32x16 acc[NB];
 #pragma unroll
@@ -660,9 +683,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                const bool ok = inside || (key <= qi && key > qi - W && key < T);
-                const float p = ok ? exp2f(sc[kb][e] * qscale - lse_q) : 0.0f;
-                dp[kb][e] = p * (dp[kb][e] - Dq);
+                const bool ok = inside | ((key <= qi) & (key > qi - W) & (key < T));
+                const float p = fast_exp2(sc[kb][e] * qscale - lse_q);
+                dp[kb][e] = ok ? p * (dp[kb][e] - Dq) : 0.0f;
             }
         bf16x8 ktr[NB][2 * KB];
 #pragma unroll
@@ -728,7 +751,7 @@ static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const vo
 // Tile shapes and pipeline depths: forward and dQ stream K~/V~ tiles of
 // kFwdKT keys through kFwdST stages; dK/dV streams 32-query tiles through
 // kBwdST stages.
-constexpr int kFwdKT = 32, kFwdST = 4, kDqKT = 32, kDqST = 4, kBwdST = 4;
+constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4;
 
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)

@@ -79,14 +79,16 @@ MAGLEV_DEV bf16x8 read_frag(const bf16 *lds, int rb, int ks, int lane)
 // C[M,N] = sum_k A(m,k) B(n,k) over k in this workgroup's split.
 // P supplies: M, N, K; A_KMAJOR/B_KMAJOR; for a K-major operand x_ptr(row, k),
 // the address of 8 elements along k, linear in k inside segments of x_kseg
-// elements (0: one segment); for an MN-major operand (stored [k][col]) x_lin(k,
-// col), the address of 8 elements along col, rows x_ld elements apart; nullptr
-// marks a chunk outside the matrix (M/N tails). Operands hold no zero rows:
+// elements (0: one segment; otherwise a multiple of BK); for an MN-major
+// operand (stored [k][col]) x_lin(k, col), the address of 8 elements along
+// col, rows x_ld elements apart. The kernel only asks for rows < M / N and
+// column chunks inside the matrix (it clamps); K tails read a zero page.
+// Operands hold no zero rows:
 // the shifts are applied in store(m, t, n, value, split), where t = m mod T.
 // Pipeline: a ring of 3 LDS stages filled by direct global->LDS loads two
 // stages ahead of the MFMA work; one barrier per 64-wide K step.
 template <class Cfg, class P>
-__global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
+__global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int group_m)
 {
     using TA = OpTile<P::A_KMAJOR, Cfg::BM>;
     using TB = OpTile<P::B_KMAJOR, Cfg::BN>;
@@ -101,11 +103,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
     const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t tm = bid / ntn, tn = bid % ntn;
-    if (tm >= ntm) return;
+    // Work item order: split-major; inside a split, groups of group_m tile rows
+    // swept column by column. The dispatcher deals workgroups round-robin to
+    // the 8 XCDs and xcd_remap gives each XCD a contiguous run of items, so
+    // the workgroups resident on one XCD (one L2) share a few rows of A tiles
+    // and a few columns of B tiles, and a split's K range stays on its XCDs.
+    const int64_t item = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t per_split = ntm * ntn;
+    const int split = (int)(item / per_split);
+    const int64_t r = item % per_split;
+    const int64_t gsz = (int64_t)group_m * ntn;
+    const int64_t first_m = (r / gsz) * group_m;
+    const int64_t gm = ntm - first_m < group_m ? ntm - first_m : group_m;
+    const int64_t tm = first_m + (r % gsz) % gm, tn = (r % gsz) / gm;
     const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-    const int64_t kb = (int64_t)blockIdx.z * kper;
+    const int64_t kb = (int64_t)split * kper;
     const int64_t ke = kb + kper < p.K ? kb + kper : p.K;
     const int nk = ke > kb ? (int)((ke - kb + Cfg::BK - 1) / Cfg::BK) : 0;
 
@@ -115,17 +127,30 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
     const bf16 *pa[IA];
     const bf16 *pb[IB];
     int ka[IA], kbk[IB];   // k offset of the chunk inside the 64-wide step
+    // Rows (K-major) or column chunks (MN-major) beyond M / N are clamped to the
+    // last valid one: their products land in accumulator rows/columns the
+    // epilogue never stores, so no lane ever needs a null check.
     auto a_addr = [&](int i, int64_t k0) -> const bf16 * {
         const int row = (wave * IA + i) * TA::ROWS_PER_INSTR + lane / TA::CPR;
         const int c = TA::slot(row, lane % TA::CPR);
-        if constexpr (P::A_KMAJOR) return p.a_ptr(m0 + row, k0 + 8 * c);
-        else return p.a_lin(k0 + row, m0 + 8 * c);
+        if constexpr (P::A_KMAJOR) {
+            const int64_t r = m0 + row < p.M ? m0 + row : p.M - 1;
+            return p.a_ptr(r, k0 + 8 * c);
+        } else {
+            const int64_t col = m0 + 8 * c < p.M ? m0 + 8 * c : p.M - 8;
+            return p.a_lin(k0 + row, col);
+        }
     };
     auto b_addr = [&](int i, int64_t k0) -> const bf16 * {
         const int row = (wave * IB + i) * TB::ROWS_PER_INSTR + lane / TB::CPR;
         const int c = TB::slot(row, lane % TB::CPR);
-        if constexpr (P::B_KMAJOR) return p.b_ptr(n0 + row, k0 + 8 * c);
-        else return p.b_lin(k0 + row, n0 + 8 * c);
+        if constexpr (P::B_KMAJOR) {
+            const int64_t r = n0 + row < p.N ? n0 + row : p.N - 1;
+            return p.b_ptr(r, k0 + 8 * c);
+        } else {
+            const int64_t col = n0 + 8 * c < p.N ? n0 + 8 * c : p.N - 8;
+            return p.b_lin(k0 + row, col);
+        }
     };
 #pragma unroll
     for (int i = 0; i < IA; ++i) {
@@ -141,43 +166,45 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
     }
     const int64_t a_step = P::A_KMAJOR ? Cfg::BK : Cfg::BK * p.a_ld;
     const int64_t b_step = P::B_KMAJOR ? Cfg::BK : Cfg::BK * p.b_ld;
+    // Next K at which an operand stored in segments (a_kseg / b_kseg elements,
+    // multiples of BK) switches segment: its pointers are recomputed there.
+    int64_t a_next = p.a_kseg > 0 ? (kb / p.a_kseg + 1) * p.a_kseg : INT64_MAX;
+    int64_t b_next = p.b_kseg > 0 ? (kb / p.b_kseg + 1) * p.b_kseg : INT64_MAX;
 
     // DMA of K step `it` into stage `buf` (the pointers are at step it), then
-    // advance the pointers. Tails and segment switches take the slow branch.
+    // advance the pointers. Tails read the zero rows past ke.
     auto issue = [&](int it, int buf) {
         const int64_t k0 = kb + (int64_t)it * Cfg::BK;
         bf16 *sa = lds + buf * STAGE;
         bf16 *sb = sa + TA::ELEMS;
         const bool tail = k0 + Cfg::BK > ke;
-        if (p.a_kseg > 0 && it > 0 && (k0 % p.a_kseg) == 0) {
+        if (k0 == a_next) {
 #pragma unroll
             for (int i = 0; i < IA; ++i) pa[i] = a_addr(i, k0);
+            a_next += p.a_kseg;
         }
-        if (p.b_kseg > 0 && it > 0 && (k0 % p.b_kseg) == 0) {
+        if (k0 == b_next) {
 #pragma unroll
             for (int i = 0; i < IB; ++i) pb[i] = b_addr(i, k0);
+            b_next += p.b_kseg;
         }
         if (!tail) {
 #pragma unroll
-            for (int i = 0; i < IA; ++i) dma16(pa[i] ? pa[i] : g_zero_rows, sa + (wave * IA + i) * 512);
+            for (int i = 0; i < IA; ++i) dma16(pa[i], sa + (wave * IA + i) * 512);
 #pragma unroll
-            for (int i = 0; i < IB; ++i) dma16(pb[i] ? pb[i] : g_zero_rows, sb + (wave * IB + i) * 512);
+            for (int i = 0; i < IB; ++i) dma16(pb[i], sb + (wave * IB + i) * 512);
         } else {
 #pragma unroll
-            for (int i = 0; i < IA; ++i) {
-                const bool z = !pa[i] || k0 + ka[i] >= ke;
-                dma16(z ? g_zero_rows : pa[i], sa + (wave * IA + i) * 512);
-            }
+            for (int i = 0; i < IA; ++i)
+                dma16(k0 + ka[i] >= ke ? g_zero_rows : pa[i], sa + (wave * IA + i) * 512);
 #pragma unroll
-            for (int i = 0; i < IB; ++i) {
-                const bool z = !pb[i] || k0 + kbk[i] >= ke;
-                dma16(z ? g_zero_rows : pb[i], sb + (wave * IB + i) * 512);
-            }
+            for (int i = 0; i < IB; ++i)
+                dma16(k0 + kbk[i] >= ke ? g_zero_rows : pb[i], sb + (wave * IB + i) * 512);
         }
 #pragma unroll
-        for (int i = 0; i < IA; ++i) pa[i] = pa[i] ? pa[i] + a_step : nullptr;
+        for (int i = 0; i < IA; ++i) pa[i] += a_step;
 #pragma unroll
-        for (int i = 0; i < IB; ++i) pb[i] = pb[i] ? pb[i] + b_step : nullptr;
+        for (int i = 0; i < IB; ++i) pb[i] += b_step;
     };
 
     f32x16 acc[Cfg::FM][Cfg::FN];
@@ -239,7 +266,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper)
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) {
                 const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
-                if (n < p.N) p.store(m, t, n, acc[i][j][e], blockIdx.z);
+                if (n < p.N) p.store(m, t, n, acc[i][j][e], split);
             }
         }
 }
@@ -266,12 +293,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_bf16(P p)
     for (int64_t k0 = k_lo; k0 < k_hi; k0 += 32) {
         const int64_t k = k0 + kg;
         const bool kin = k < k_hi;
-        const bf16 *bp = kin ? p.b_ptr(n0 + r16, k) : nullptr;
-        const bf16x8 bf = bp ? *reinterpret_cast<const bf16x8 *>(bp) : zero8();
+        const bool nin = kin && n0 + r16 < p.N;
+        const bf16x8 bf = nin ? *reinterpret_cast<const bf16x8 *>(p.b_ptr(n0 + r16, k)) : zero8();
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
-            const bf16 *ap = kin ? p.a_ptr(16 * rb + r16, k) : nullptr;
-            const bf16x8 af = ap ? *reinterpret_cast<const bf16x8 *>(ap) : zero8();
+            const bool min_ = kin && 16 * rb + r16 < p.M;
+            const bf16x8 af = min_ ? *reinterpret_cast<const bf16x8 *>(p.a_ptr(16 * rb + r16, k)) : zero8();
             acc[rb] = mfma16(af, bf, acc[rb]);
         }
     }
@@ -307,13 +334,9 @@ struct ProjFwd {
     int64_t M, N, K, T;
     int HD, shift;
     static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0, b_ld = 0;
-    MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const
-    {
-        return row < M ? m + row * K + k : nullptr;
-    }
+    MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const { return m + row * K + k; }
     MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const
     {
-        if (n >= N) return nullptr;
         return n < HD ? wk + n * K + k : wv + (n - HD) * K + k;
     }
     MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
@@ -345,17 +368,16 @@ struct ProjBwdDm {
     static constexpr int64_t b_kseg = 0, a_ld = 0;
     MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const
     {
-        if (row >= M) return nullptr;
         return k < HD ? dk + row * HD + k : dv + row * HD + (k - HD);
     }
     MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
     MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
-    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const
-    {
-        return n < N ? ws + k * N + n : nullptr;
-    }
+    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const { return ws + k * N + n; }
     MAGLEV_DEV void store(int64_t row, int64_t t, int64_t n, float x, int) const
     {
+        // m'[T-1] feeds no key: its injection gradient is zero (written here
+        // unless accumulating); row t's product lands on m'[t-1].
+        if (t == T - 1 && !acc) dm[row * N + n] = 0.0f;
         if (t == 0) return;
         float *p = dm + (row - 1) * N + n;
         *p = acc ? *p + x : x;
@@ -378,13 +400,9 @@ struct ProjBwdDw {
     MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
     MAGLEV_DEV const bf16 *a_lin(int64_t u, int64_t r) const
     {
-        if (r >= M) return nullptr;
         return r < HD ? dk + (u + 1) * HD + r : dv + (u + 1) * HD + (r - HD);
     }
-    MAGLEV_DEV const bf16 *b_lin(int64_t u, int64_t e) const
-    {
-        return e < N ? m + u * N + e : nullptr;
-    }
+    MAGLEV_DEV const bf16 *b_lin(int64_t u, int64_t e) const { return m + u * N + e; }
     MAGLEV_DEV void store(int64_t r, int64_t, int64_t e, float x, int split) const
     {
         part[((int64_t)split * M + r) * N + e] = x;
@@ -402,13 +420,15 @@ using DwCfg = TileCfg<256, 256, 4, 4, 2>;     // wave tile 64 x 64, split over t
 using WideCfg = TileCfg<64, 128, 1, 4, 2>;    // wave tile 64 x 32
 
 template <class Cfg, class P>
-static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const char *name)
+static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const char *name,
+                     int group_m)
 {
     const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
     const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
+    if (group_m > ntm) group_m = (int)ntm;
     prof::Scope ts(name, s);
-    hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn), 1, ksplit),
-                       dim3(Cfg::NT), 0, s, p, kper);
+    hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn * ksplit)), dim3(Cfg::NT), 0, s,
+                       p, kper, group_m);
 }
 
 void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
@@ -423,13 +443,13 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
     p.M = g.N(); p.N = 2 * (int64_t)g.HD(); p.K = g.d; p.T = g.T;
     p.HD = g.HD(); p.shift = shift;
     if (p.M <= 64 && p.N >= 8192) {
-        run_gemm<WideCfg>(p, 1, p.K, s, "proj_fwd_wide");
+        run_gemm<WideCfg>(p, 1, p.K, s, "proj_fwd_wide", 1);
     } else if (p.M <= 64) {
         prof::Scope ts("proj_fwd_skinny", s);
         hipLaunchKernelGGL(gemm_skinny_bf16<ProjFwd>, dim3((unsigned)((p.N + 15) / 16)), dim3(256), 0,
                            s, p);
     } else {
-        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_fwd");
+        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_fwd", 16);
     }
 }
 
@@ -453,23 +473,42 @@ __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate,
 
 // dW = s_h * (sum over splits, fixed order, minus the sequence-boundary pairs
 // G[bT]^T m'[bT-1], b = 1..B-1), optionally added to the output.
-__global__ void dw_reduce(const float *part, int ksplit, int HD, int Dh, int d, int64_t B,
-                          int64_t T, const bf16 *dk, const bf16 *dv, const bf16 *m,
-                          const float *gate, float *dwk, float *dwv, bool acc)
+// dW = s_h (sum of the split partials - boundary pairs), 8 columns a thread:
+// the boundary pairs are G[bT]^T m'[bT-1] for b = 1 .. B-1 (the shifted
+// product pairs the first token of a sequence with the last memory row of the
+// previous one).
+__global__ __launch_bounds__(256) void dw_reduce(const float *part, int ksplit, int HD, int Dh,
+                                                 int d, int64_t B, int64_t T, const bf16 *dk,
+                                                 const bf16 *dv, const bf16 *m,
+                                                 const float *gate, float *dwk, float *dwv,
+                                                 bool acc)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i8 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tot = 2 * (int64_t)HD * d;
-    if (i >= tot) return;
-    float x = 0.0f;
-    for (int sp = 0; sp < ksplit; ++sp) x += part[sp * tot + i];
-    const int64_t r = i / d, e = i % d;
+    if (i8 * 8 >= tot) return;
+    const int64_t i = i8 * 8;
+    const int64_t r = i / d, e = i % d;   // d is a multiple of 16: the 8 columns share row r
+    float x[8], y[8];
+    load8(part + i, x);
+    for (int sp = 1; sp < ksplit; ++sp) {
+        load8(part + sp * tot + i, y);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] += y[u];
+    }
     const int rr = (int)(r < HD ? r : r - HD);
     const bf16 *G = r < HD ? dk : dv;
-    for (int64_t b = 1; b < B; ++b)
-        x -= bf2f(G[(b * T) * HD + rr]) * bf2f(m[(b * T - 1) * d + e]);
-    x *= gate_sigmoid(gate[rr / Dh]);
+    for (int64_t b = 1; b < B; ++b) {
+        const float gv = bf2f(G[(b * T) * HD + rr]);
+        load8(m + (b * T - 1) * d + e, y);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] -= gv * y[u];
+    }
+    const float sg = gate_sigmoid(gate[rr / Dh]);
     float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d + e;
-    *out = acc ? *out + x : x;
+    if (acc) load8(out, y);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = acc ? y[u] + x[u] * sg : x[u] * sg;
+    store8(out, x);
 }
 
 int dw_ksplit(const Geom &g)
@@ -511,7 +550,7 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         p.acc = (acc & 1u) != 0;
         p.a_kseg = HD;
         p.b_ld = g.d;
-        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm");
+        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm", 16);
     }
     {
         ProjBwdDw p;
@@ -526,10 +565,10 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         const int ks = ws.ksplit;
         int64_t kper = (p.K + ks - 1) / ks;
         kper = (kper + 63) / 64 * 64;
-        run_gemm<DwCfg>(p, ks, kper, s, "proj_bwd_dw");
-        const int64_t tot = 2 * (int64_t)HD * g.d;
+        run_gemm<DwCfg>(p, ks, kper, s, "proj_bwd_dw", 1 << 20);
+        const int64_t tot8 = 2 * (int64_t)HD * g.d / 8;
         prof::Scope ts("proj_bwd_dw_reduce", s);
-        hipLaunchKernelGGL(dw_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s,
+        hipLaunchKernelGGL(dw_reduce, dim3((unsigned)((tot8 + 255) / 256)), dim3(256), 0, s,
                            ws.dW_part, ks, HD, g.Dh, g.d, g.B, g.T, p.dk, p.dv, p.m, gate, dWk,
                            dWv, (acc & 2u) != 0);
     }

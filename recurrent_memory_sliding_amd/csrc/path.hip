@@ -331,7 +331,7 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *
         hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,
                            gate, dgate, acc);
     }
-    if (!(acc & 1u)) {
+    if (!(acc & 1u) && g.dtype != MAGLEV_BF16) {   // the bf16 dm' GEMM writes these rows itself
         prof::Scope ts("zero_last_rows", s);
         hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
     }
