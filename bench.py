@@ -87,7 +87,7 @@ def kernel_work(sh: wl.LayerShape) -> dict:
         "proj_fwd": (proj, mem + wts + 2 * act),
         "mix": (0.0, 6 * act),                                  # k v kmem vmem -> kmix vmix
         "attn_fwd": (2 * attn, 4 * act + rowf),                 # q kmix vmix -> o, lse
-        "attn_bwd_rowdot": (0.0, 2 * act + rowf),               # o dO -> D
+        "attn_bwd_prep": (0.0, 4 * act + 3 * rowf),             # o dO q lse -> D, qr, lse2
         "attn_bwd_dkdv": (3 * attn, 8 * act + 2 * rowf + 4.0 * B * H * ((T + 127) // 128)),
         "attn_bwd_dq": (attn, 5 * act + 2 * rowf),              # q dO kmix vmix -> dq
         "proj_bwd_scale_w": (0.0, 2 * wts),
@@ -372,7 +372,7 @@ def main():
             "algorithmic_GB_per_step": round(dbytes / 1e9, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
-            "graph": "one HIP graph per step (20 x (projection + decode + combine) + advance)",
+            "graph": "one HIP graph per step: one projection of m_{t-1} by all layers' stacked weights, 20 decode steps, advance",
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh)
