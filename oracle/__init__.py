@@ -65,6 +65,18 @@ def _load():
         L.oracle_swa_inject_fwd_rows.restype = None
         L.oracle_mixed_entries.argtypes = [I64, I64, I32, I32, I64, D, P, P, P, P, P, P, P]
         L.oracle_mixed_entries.restype = None
+        L.oracle_gated_entries.argtypes = [I64, I64, I32, I32, I64, D, D,
+                                           P, P, P, P, P, P, P, P, P, P]
+        L.oracle_gated_entries.restype = None
+        L.oracle_swa_attend_fwd.argtypes = [I64, I64, I32, I32, I64, I64, D, D, P, P, P, P, P]
+        L.oracle_swa_attend_fwd.restype = None
+        L.oracle_swa_inject_bwd_gated.argtypes = [I64, I64, I32, I32, I32, I64, I64, D, D, D,
+                                                  P, P, P, P, P, P, P, P, P, P, P,
+                                                  P, P, P, P, P, P, P, P, P, P]
+        L.oracle_swa_inject_bwd_gated.restype = None
+        L.oracle_decode_step_gated.argtypes = [I64, I32, I32, I64, D, D, D, I32,
+                                               P, P, P, P, P, P, P, P, P, P, P, PI64, P]
+        L.oracle_decode_step_gated.restype = None
         _lib = L
     return _lib
 
@@ -185,6 +197,108 @@ def decode_step(q, k, v, kmem, vmem, gate_logit, kcache: np.ndarray, vcache: np.
     _load().oracle_decode_step(Bs, H, Dh, W, float(rope_base), float(scale), int(bool(ring_bf16)),
                                _p(q), _p(k), _p(v), _p(km), _p(vm), _p(g), _p(kcache), _p(vcache),
                                pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(o))
+    return o
+
+
+# ----------------------------------------------------------------------------
+# gated variant: k~ = g_kl R k + g_kr R RMSNorm(W_Km m'), v~ = g_vl v + g_vr W_Vm m',
+# g = 2 sigmoid(a), four channel-wise logit vectors [H*Dh] in the order
+# (a_kl, a_kr, a_vl, a_vr).
+# ----------------------------------------------------------------------------
+GATE_NAMES = ("a_kl", "a_kr", "a_vl", "a_vr")
+RMS_EPS = 1e-6
+
+
+def _gates(gates, HD: int):
+    if isinstance(gates, dict):
+        gates = [gates[n] for n in GATE_NAMES]
+    out = [f64(g).reshape(-1) for g in gates]
+    if len(out) != 4 or any(g.size != HD for g in out):
+        raise ValueError("four gate logit vectors of H*Dh entries expected")
+    return out
+
+
+def gated_entries(k, v, kproj, vmem, gates, pos0: int = 0, rope_base: float = 10000.0,
+                  eps: float = RMS_EPS):
+    """Gated mixed entries kmix, vmix [B,T,H,Dh] from the pre-norm key projection."""
+    k, v, kp, vm = (f64(a) for a in (k, v, kproj, vmem))
+    B, T, H, Dh = k.shape
+    if Dh > 512 or H * Dh > 4096:
+        raise ValueError("Dh above 512 or H*Dh above 4096")
+    g = _gates(gates, H * Dh)
+    kx = np.empty((B, T, H, Dh))
+    vx = np.empty((B, T, H, Dh))
+    _load().oracle_gated_entries(B, T, H, Dh, int(pos0), float(rope_base), float(eps), _p(k),
+                                 _p(v), _p(kp), _p(vm), *(_p(a) for a in g), _p(kx), _p(vx))
+    return kx, vx
+
+
+def swa_attend_fwd(q, kmix, vmix, W: int, pos0: int = 0, rope_base: float = 10000.0,
+                   scale: float = 0.0):
+    """O [B,T,H,Dh] and lse [B,H,T] of the rotated queries over given mixed entries."""
+    q, kx, vx = (f64(a) for a in (q, kmix, vmix))
+    B, T, H, Dh = q.shape
+    o = np.empty((B, T, H, Dh))
+    lse = np.empty((B, H, T))
+    _load().oracle_swa_attend_fwd(B, T, H, Dh, int(W), int(pos0), float(rope_base),
+                                  float(scale), _p(q), _p(kx), _p(vx), _p(o), _p(lse))
+    return o, lse
+
+
+def swa_inject_fwd_gated(q, k, v, m_prime, W_Km, W_Vm, gates, W: int, pos0: int = 0,
+                         rope_base: float = 10000.0, scale: float = 0.0, eps: float = RMS_EPS):
+    """Forward of the gated layer path: projection of the shifted memory, the
+    gated mix, attention. Returns (o, lse)."""
+    H, Dh = q.shape[2], q.shape[3]
+    kp, vm = mem_project(m_prime, W_Km, W_Vm, H, Dh, shift=1)
+    kx, vx = gated_entries(k, v, kp, vm, gates, pos0=pos0, rope_base=rope_base, eps=eps)
+    return swa_attend_fwd(q, kx, vx, W, pos0=pos0, rope_base=rope_base, scale=scale)
+
+
+def swa_inject_bwd_gated(q, k, v, m_prime, W_Km, W_Vm, gates, dO, W: int, pos0: int = 0,
+                         rope_base: float = 10000.0, scale: float = 0.0,
+                         eps: float = RMS_EPS):
+    """Gradients of the gated layer path. Returns dict with dq, dk, dv,
+    dm_prime, dW_Km, dW_Vm and the four gate-logit gradients (a_* names)."""
+    q, k, v, mp, WK, WV, dO = (f64(a) for a in (q, k, v, m_prime, W_Km, W_Vm, dO))
+    B, T, H, Dh = q.shape
+    d = mp.shape[-1]
+    if Dh > 512 or H * Dh > 4096:
+        raise ValueError("Dh above 512 or H*Dh above 4096")
+    g = _gates(gates, H * Dh)
+    out = {
+        "dq": np.empty_like(q), "dk": np.empty_like(q), "dv": np.empty_like(q),
+        "dm_prime": np.empty((B, T, d)), "dW_Km": np.empty((H * Dh, d)),
+        "dW_Vm": np.empty((H * Dh, d)),
+    }
+    for n in GATE_NAMES:
+        out["d" + n] = np.empty((H * Dh,))
+    _load().oracle_swa_inject_bwd_gated(
+        B, T, H, Dh, d, int(W), int(pos0), float(rope_base), float(scale), float(eps),
+        _p(q), _p(k), _p(v), _p(mp), _p(WK), _p(WV), *(_p(a) for a in g), _p(dO),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dm_prime"]), _p(out["dW_Km"]),
+        _p(out["dW_Vm"]), *(_p(out["d" + n]) for n in GATE_NAMES))
+    return out
+
+
+def decode_step_gated(q, k, v, kproj, vmem, gates, kcache: np.ndarray, vcache: np.ndarray,
+                      pos, rope_base: float = 10000.0, scale: float = 0.0,
+                      eps: float = RMS_EPS, ring_bf16: bool = True):
+    """One gated decode step (kproj is W_Km m_{t-1} before the norm); the
+    float64 caches [Bs,H,W,Dh] are updated in place. Returns o [Bs,H,Dh]."""
+    q, k, v, kp, vm = (f64(a) for a in (q, k, v, kproj, vmem))
+    assert kcache.dtype == np.float64 and kcache.flags.c_contiguous
+    assert vcache.dtype == np.float64 and vcache.flags.c_contiguous
+    Bs, H, W, Dh = kcache.shape
+    if Dh > 512 or H * Dh > 4096:
+        raise ValueError("Dh above 512 or H*Dh above 4096")
+    g = _gates(gates, H * Dh)
+    pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int64).reshape(Bs))
+    o = np.empty((Bs, H, Dh))
+    _load().oracle_decode_step_gated(Bs, H, Dh, W, float(rope_base), float(scale), float(eps),
+                                     int(bool(ring_bf16)), _p(q), _p(k), _p(v), _p(kp), _p(vm),
+                                     *(_p(a) for a in g), _p(kcache), _p(vcache),
+                                     pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(o))
     return o
 
 

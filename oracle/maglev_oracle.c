@@ -31,6 +31,8 @@
  * form open; this oracle implements the form the library fixes:
  *     k~_j = R_j k_j + s_h * R_j (W_Km m'_{j-1}),   v~_j = v_j + s_h * W_Vm m'_{j-1},
  *     s_h  = 1 / (1 + exp(-g_h)), one gate logit per head.
+ * The gated variant that [R-step] prints (channel-wise 2*sigma gates on both
+ * terms, RMSNorm on the projected memory key) follows at the end of the file.
  *
  * Conventions where the pages are silent (each listed with its reading in the
  * design notes): RoPE pairs channel i with i + Dh/2, theta_i = base^(-2i/Dh),
@@ -542,4 +544,372 @@ ORACLE_API void oracle_swa_inject_fwd_rows(int64_t B, int64_t T, int H, int Dh, 
         if (lse_rows) lse_rows[n] = mx + log(sum);
         free(kt); free(vt); free(qh); free(rk); free(p);
     }
+}
+
+/* ===========================================================================
+ * Gated variant ([R-step], the printed per-layer form):
+ *     k^rec_t = RMSNorm(W_Km m'_{t-1}),       v^rec_t = W_Vm m'_{t-1},
+ *     k~_t = g_kl (.) R_t k_t + g_kr (.) R_t k^rec_t,
+ *     v~_t = g_vl (.) v_t     + g_vr (.) v^rec_t,
+ *     g = 2 sigma(a)  (a = 0 gives the neutral value 1),
+ * with one logit per channel of the H*Dh-wide key/value row for each of the
+ * four gates. Readings where the page is silent: the RMSNorm runs over the
+ * whole H*Dh projected row, has no learned scale of its own (the channel-wise
+ * recurrent gate follows it) and adds eps inside the square root; the gates
+ * multiply after the rotation, since the page rotates both kinds of key
+ * before they are mixed ([R-bg]).
+ * Gate vectors a_* are [H*Dh]; kproj is the pre-norm projection W_Km m'.
+ * ========================================================================= */
+
+/* Channel gate g = 2 sigma(a). */
+static double gate_two_sigmoid(double a) { return 2.0 / (1.0 + exp(-a)); }
+
+/* 1 / sqrt(mean(x^2) + eps) over n channels: the RMSNorm divisor's inverse. */
+static double rms_inverse(const double *x, int n, double eps)
+{
+    return 1.0 / sqrt(dot(x, x, n) / (double)n + eps);
+}
+
+/* Mixed entries of one row (b, t): kmix/vmix [H*Dh] from k, v, kproj, vmem
+ * rows of the same width; p is the absolute position. When rk_out/rn_out are
+ * not NULL they receive R k and R RMSNorm(kproj) (both [H*Dh]). */
+static void gated_row(int H, int Dh, double p, double base, double eps, const double *k,
+                      const double *v, const double *kproj, const double *vmem,
+                      const double *a_kl, const double *a_kr, const double *a_vl,
+                      const double *a_vr, double *kmix, double *vmix, double *rk_out,
+                      double *rn_out)
+{
+    const int HD = H * Dh;
+    const double r = rms_inverse(kproj, HD, eps);
+    double rk[512], rn[512];
+    for (int h = 0; h < H; ++h) {
+        const int o = h * Dh;
+        memcpy(rk, k + o, (size_t)Dh * sizeof(double));
+        rope_rotate(rk, Dh, p, base, 0);
+        for (int c = 0; c < Dh; ++c) rn[c] = kproj[o + c] * r;
+        rope_rotate(rn, Dh, p, base, 0);
+        for (int c = 0; c < Dh; ++c) {
+            kmix[o + c] = gate_two_sigmoid(a_kl[o + c]) * rk[c] +
+                          gate_two_sigmoid(a_kr[o + c]) * rn[c];
+            vmix[o + c] = gate_two_sigmoid(a_vl[o + c]) * v[o + c] +
+                          gate_two_sigmoid(a_vr[o + c]) * vmem[o + c];
+            if (rk_out) rk_out[o + c] = rk[c];
+            if (rn_out) rn_out[o + c] = rn[c];
+        }
+    }
+}
+
+/* Gated mixed entries of every position; all activations [B,T,H,Dh]. */
+ORACLE_API void oracle_gated_entries(int64_t B, int64_t T, int H, int Dh, int64_t pos0,
+                                     double base, double eps, const double *k, const double *v,
+                                     const double *kproj, const double *vmem,
+                                     const double *a_kl, const double *a_kr,
+                                     const double *a_vl, const double *a_vr, double *kmix,
+                                     double *vmix)
+{
+    const int64_t HD = (int64_t)H * Dh;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t off = (b * T + t) * HD;
+            gated_row(H, Dh, (double)(pos0 + t), base, eps, k + off, v + off, kproj + off,
+                      vmem + off, a_kl, a_kr, a_vl, a_vr, kmix + off, vmix + off, NULL, NULL);
+        }
+    }
+}
+
+/* q^ = R q and the given mixed entries of sequence (b, h), as a head view. */
+static void head_view_entries(head_view *hv, int64_t b, int h, int64_t T, int H, int Dh,
+                              int64_t pos0, double base, const double *q, const double *kmix,
+                              const double *vmix)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t off = ((b * T + t) * H + h) * Dh;
+        double *qh = hv->qh + t * Dh;
+        memcpy(qh, q + off, (size_t)Dh * sizeof(double));
+        rope_rotate(qh, Dh, (double)(pos0 + t), base, 0);
+        memcpy(hv->kt + t * Dh, kmix + off, (size_t)Dh * sizeof(double));
+        memcpy(hv->vt + t * Dh, vmix + off, (size_t)Dh * sizeof(double));
+    }
+}
+
+/* Sliding-window attention of the rotated queries over given mixed entries
+ * (already rotated, already mixed): the attention half of the layer, whatever
+ * the mixing form. o [B,T,H,Dh]; lse [B,H,T] (may be NULL). */
+ORACLE_API void oracle_swa_attend_fwd(int64_t B, int64_t T, int H, int Dh, int64_t W,
+                                      int64_t pos0, double rope_base, double scale,
+                                      const double *q, const double *kmix, const double *vmix,
+                                      double *o, double *lse)
+{
+    scale = default_scale(scale, Dh);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int h = 0; h < H; ++h) {
+            head_view hv;
+            double *p = malloc((size_t)(W < T ? W : T) * sizeof(double));
+            if (!head_view_alloc(&hv, T, Dh) || !p) abort();
+            head_view_entries(&hv, b, h, T, H, Dh, pos0, rope_base, q, kmix, vmix);
+            for (int64_t i = 0; i < T; ++i) {
+                double l;
+                const int64_t lo = window_softmax(&hv, i, W, Dh, scale, p, &l);
+                double *oi = o + ((b * T + i) * H + h) * Dh;
+                for (int c = 0; c < Dh; ++c) oi[c] = 0.0;
+                for (int64_t j = lo; j <= i; ++j)
+                    for (int c = 0; c < Dh; ++c) oi[c] += p[j - lo] * hv.vt[j * Dh + c];
+                if (lse) lse[((int64_t)b * H + h) * T + i] = l;
+            }
+            free(p);
+            head_view_free(&hv);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Backward of the gated layer path (shift, projection, RMSNorm, gated mix,
+ * attention), by the chain rule:
+ *   outputs dq, dk, dv [B,T,H,Dh]; dm' [B,T,d]; dW_Km, dW_Vm [H*Dh,d];
+ *           da_kl, da_kr, da_vl, da_vr [H*Dh] (summed over batch and time).
+ * ------------------------------------------------------------------------- */
+ORACLE_API void oracle_swa_inject_bwd_gated(int64_t B, int64_t T, int H, int Dh, int d,
+                                            int64_t W, int64_t pos0, double rope_base,
+                                            double scale, double eps, const double *q,
+                                            const double *k, const double *v,
+                                            const double *m_prime, const double *W_Km,
+                                            const double *W_Vm, const double *a_kl,
+                                            const double *a_kr, const double *a_vl,
+                                            const double *a_vr, const double *dO, double *dq,
+                                            double *dk, double *dv, double *dm_prime,
+                                            double *dW_Km, double *dW_Vm, double *da_kl,
+                                            double *da_kr, double *da_vl, double *da_vr)
+{
+    scale = default_scale(scale, Dh);
+    const int HD = H * Dh;
+    const size_t nact = (size_t)B * (size_t)T * (size_t)HD;
+    double *kproj = malloc(nact * sizeof(double));
+    double *vmem = malloc(nact * sizeof(double));
+    double *kmix = malloc(nact * sizeof(double));
+    double *vmix = malloc(nact * sizeof(double));
+    double *dkmix = malloc(nact * sizeof(double));   /* d loss / d k~ (rotated frame) */
+    double *dvmix = malloc(nact * sizeof(double));   /* d loss / d v~ */
+    double *rk = malloc(nact * sizeof(double));      /* R k */
+    double *rn = malloc(nact * sizeof(double));      /* R RMSNorm(kproj) */
+    double *dkp = malloc(nact * sizeof(double));     /* d loss / d kproj */
+    double *dvmem = malloc(nact * sizeof(double));   /* d loss / d vmem */
+    if (!kproj || !vmem || !kmix || !vmix || !dkmix || !dvmix || !rk || !rn || !dkp || !dvmem)
+        abort();
+
+    oracle_mem_project(B, T, H, Dh, d, 1, m_prime, W_Km, W_Vm, kproj, vmem);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t off = (b * T + t) * HD;
+            gated_row(H, Dh, (double)(pos0 + t), rope_base, eps, k + off, v + off, kproj + off,
+                      vmem + off, a_kl, a_kr, a_vl, a_vr, kmix + off, vmix + off, rk + off,
+                      rn + off);
+        }
+    }
+
+    /* attention: dq = R^T dq^, and the gradients of the mixed entries */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int h = 0; h < H; ++h) {
+            head_view hv;
+            const int64_t wmax = W < T ? W : T;
+            double *p = malloc((size_t)wmax * sizeof(double));
+            double *dp = malloc((size_t)wmax * sizeof(double));
+            double *dqh = calloc((size_t)T * Dh, sizeof(double));
+            double *dkt = calloc((size_t)T * Dh, sizeof(double));
+            double *dvt = calloc((size_t)T * Dh, sizeof(double));
+            if (!head_view_alloc(&hv, T, Dh) || !p || !dp || !dqh || !dkt || !dvt) abort();
+            head_view_entries(&hv, b, h, T, H, Dh, pos0, rope_base, q, kmix, vmix);
+            for (int64_t i = 0; i < T; ++i) {
+                const int64_t lo = window_softmax(&hv, i, W, Dh, scale, p, NULL);
+                const double *dOi = dO + ((b * T + i) * H + h) * Dh;
+                double Di = 0.0;
+                for (int64_t j = lo; j <= i; ++j) {
+                    dp[j - lo] = dot(dOi, hv.vt + j * Dh, Dh);
+                    Di += p[j - lo] * dp[j - lo];
+                }
+                for (int64_t j = lo; j <= i; ++j) {
+                    const double pij = p[j - lo];
+                    const double dsij = pij * (dp[j - lo] - Di);
+                    for (int c = 0; c < Dh; ++c) {
+                        dqh[i * Dh + c] += scale * dsij * hv.kt[j * Dh + c];
+                        dkt[j * Dh + c] += scale * dsij * hv.qh[i * Dh + c];
+                        dvt[j * Dh + c] += pij * dOi[c];
+                    }
+                }
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t off = ((b * T + t) * H + h) * Dh;
+                rope_rotate(dqh + t * Dh, Dh, (double)(pos0 + t), rope_base, 1);
+                memcpy(dq + off, dqh + t * Dh, (size_t)Dh * sizeof(double));
+                memcpy(dkmix + off, dkt + t * Dh, (size_t)Dh * sizeof(double));
+                memcpy(dvmix + off, dvt + t * Dh, (size_t)Dh * sizeof(double));
+            }
+            free(p); free(dp); free(dqh); free(dkt); free(dvt);
+            head_view_free(&hv);
+        }
+    }
+
+    /* gated mix and RMSNorm, row by row:
+     *   dk   = R^T (g_kl (.) dk~),   dkn = R^T (g_kr (.) dk~)  (kn = kproj / rms)
+     *   dkproj = (dkn - kn * mean(dkn (.) kn)) / rms           over the H*Dh row
+     *   dv   = g_vl (.) dv~,         dvmem = g_vr (.) dv~ */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t off = (b * T + t) * HD;
+            const double pos = (double)(pos0 + t);
+            const double r = rms_inverse(kproj + off, HD, eps);
+            double tmp[512], dkn[4096];
+            if (HD > 4096) abort();
+            double mu = 0.0;
+            for (int h = 0; h < H; ++h) {
+                const int o = h * Dh;
+                for (int c = 0; c < Dh; ++c) tmp[c] = gate_two_sigmoid(a_kl[o + c]) * dkmix[off + o + c];
+                rope_rotate(tmp, Dh, pos, rope_base, 1);
+                memcpy(dk + off + o, tmp, (size_t)Dh * sizeof(double));
+                for (int c = 0; c < Dh; ++c) tmp[c] = gate_two_sigmoid(a_kr[o + c]) * dkmix[off + o + c];
+                rope_rotate(tmp, Dh, pos, rope_base, 1);
+                memcpy(dkn + o, tmp, (size_t)Dh * sizeof(double));
+                for (int c = 0; c < Dh; ++c) {
+                    dv[off + o + c] = gate_two_sigmoid(a_vl[o + c]) * dvmix[off + o + c];
+                    dvmem[off + o + c] = gate_two_sigmoid(a_vr[o + c]) * dvmix[off + o + c];
+                }
+            }
+            for (int c = 0; c < HD; ++c) mu += dkn[c] * kproj[off + c] * r;
+            mu /= (double)HD;
+            for (int c = 0; c < HD; ++c) dkp[off + c] = (dkn[c] - kproj[off + c] * r * mu) * r;
+        }
+    }
+
+    /* gates: g = 2 sigma(a)  =>  dg/da = 2 sigma(a) (1 - sigma(a));
+     *   d/dg_kl = sum dk~ (.) R k,   d/dg_kr = sum dk~ (.) R kn,
+     *   d/dg_vl = sum dv~ (.) v,     d/dg_vr = sum dv~ (.) vmem  (over b, t) */
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < HD; ++c) {
+        double gkl = 0.0, gkr = 0.0, gvl = 0.0, gvr = 0.0;
+        for (int64_t n = 0; n < B * T; ++n) {
+            const int64_t i = n * HD + c;
+            gkl += dkmix[i] * rk[i];
+            gkr += dkmix[i] * rn[i];
+            gvl += dvmix[i] * v[i];
+            gvr += dvmix[i] * vmem[i];
+        }
+        const double skl = gate_sigmoid(a_kl[c]), skr = gate_sigmoid(a_kr[c]);
+        const double svl = gate_sigmoid(a_vl[c]), svr = gate_sigmoid(a_vr[c]);
+        da_kl[c] = 2.0 * skl * (1.0 - skl) * gkl;
+        da_kr[c] = 2.0 * skr * (1.0 - skr) * gkr;
+        da_vl[c] = 2.0 * svl * (1.0 - svl) * gvl;
+        da_vr[c] = 2.0 * svr * (1.0 - svr) * gvr;
+    }
+
+    /* shift and projection, as in the ungated backward: row t of the
+     * projection input is m'[t-1]; dm'[T-1] = 0 */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t t = 0; t < T; ++t) {
+            double *out = dm_prime + (b * T + t) * d;
+            if (t == T - 1) {
+                for (int e = 0; e < d; ++e) out[e] = 0.0;
+                continue;
+            }
+            const double *gk = dkp + (b * T + t + 1) * HD;
+            const double *gv = dvmem + (b * T + t + 1) * HD;
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0;
+                for (int r = 0; r < HD; ++r)
+                    acc += gk[r] * W_Km[(int64_t)r * d + e] + gv[r] * W_Vm[(int64_t)r * d + e];
+                out[e] = acc;
+            }
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < HD; ++r) {
+        for (int e = 0; e < d; ++e) {
+            double ak = 0.0, av = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                for (int64_t t = 1; t < T; ++t) {
+                    const double x = m_prime[(b * T + t - 1) * d + e];
+                    ak += dkp[(b * T + t) * HD + r] * x;
+                    av += dvmem[(b * T + t) * HD + r] * x;
+                }
+            }
+            dW_Km[(int64_t)r * d + e] = ak;
+            dW_Vm[(int64_t)r * d + e] = av;
+        }
+    }
+    free(kproj); free(vmem); free(kmix); free(vmix); free(dkmix); free(dvmix);
+    free(rk); free(rn); free(dkp); free(dvmem);
+}
+
+/* ---------------------------------------------------------------------------
+ * One recurrent decode step of the gated variant on a W-slot ring: the new
+ * entry of stream b is the gated mix of its row (kproj = W_Km m_{t-1} before
+ * the norm, vmem = W_Vm m_{t-1}) at position pos[b], written to slot
+ * pos mod W (bf16-rounded when ring_bf16 != 0); then the rotated query
+ * attends over the valid slots, as in the ungated step.
+ * q,k,v,kproj,vmem,o [Bs,H,Dh]; caches [Bs,H,W,Dh] (in/out).
+ * ------------------------------------------------------------------------- */
+ORACLE_API void oracle_decode_step_gated(int64_t Bs, int H, int Dh, int64_t W, double rope_base,
+                                         double scale, double eps, int ring_bf16,
+                                         const double *q, const double *k, const double *v,
+                                         const double *kproj, const double *vmem,
+                                         const double *a_kl, const double *a_kr,
+                                         const double *a_vl, const double *a_vr,
+                                         double *kcache, double *vcache, const int64_t *pos,
+                                         double *o)
+{
+    scale = default_scale(scale, Dh);
+    const int HD = H * Dh;
+    double *kn = malloc((size_t)Bs * HD * sizeof(double));
+    double *vn = malloc((size_t)Bs * HD * sizeof(double));
+    if (!kn || !vn) abort();
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < Bs; ++b) {
+        const int64_t off = b * HD;
+        gated_row(H, Dh, (double)pos[b], rope_base, eps, k + off, v + off, kproj + off,
+                  vmem + off, a_kl, a_kr, a_vl, a_vr, kn + off, vn + off, NULL, NULL);
+    }
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t b = 0; b < Bs; ++b) {
+        for (int h = 0; h < H; ++h) {
+            double *qh = malloc((size_t)Dh * sizeof(double));
+            double *sc = malloc((size_t)W * sizeof(double));
+            if (!qh || !sc) abort();
+            const int64_t p = pos[b];
+            const int64_t slot = p % W;
+            const int64_t off = (b * H + h) * Dh;
+            double *kc = kcache + (b * H + h) * W * Dh;
+            double *vc = vcache + (b * H + h) * W * Dh;
+            for (int c = 0; c < Dh; ++c) {
+                double ke = kn[off + c], ve = vn[off + c];
+                if (ring_bf16) { ke = oracle_round_bf16(ke); ve = oracle_round_bf16(ve); }
+                kc[slot * Dh + c] = ke;
+                vc[slot * Dh + c] = ve;
+            }
+            memcpy(qh, q + off, (size_t)Dh * sizeof(double));
+            rope_rotate(qh, Dh, (double)p, rope_base, 0);
+            double mx = -INFINITY;
+            for (int64_t sl = 0; sl < W; ++sl) {
+                const int64_t back = ((p - sl) % W + W) % W;
+                if (p - back < 0) { sc[sl] = -INFINITY; continue; }
+                sc[sl] = scale * dot(qh, kc + sl * Dh, Dh);
+                if (sc[sl] > mx) mx = sc[sl];
+            }
+            double sum = 0.0;
+            for (int64_t sl = 0; sl < W; ++sl) {
+                sc[sl] = (sc[sl] == -INFINITY) ? 0.0 : exp(sc[sl] - mx);
+                sum += sc[sl];
+            }
+            for (int c = 0; c < Dh; ++c) o[off + c] = 0.0;
+            for (int64_t sl = 0; sl < W; ++sl) {
+                if (sc[sl] == 0.0) continue;
+                for (int c = 0; c < Dh; ++c) o[off + c] += sc[sl] / sum * vc[sl * Dh + c];
+            }
+            free(qh); free(sc);
+        }
+    }
+    free(kn); free(vn);
 }

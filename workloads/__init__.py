@@ -145,6 +145,13 @@ def decode_initial_memory(shape: DecodeShape, seed: int) -> torch.Tensor:
     return _normal(g, (shape.Bs, shape.d)).to(torch_dtype(shape.dtype))
 
 
+def gate_vectors(H: int, Dh: int, seed: int, std: float = 0.5) -> dict:
+    """Four channel-wise gate logit vectors [H*Dh] ~ N(0, std^2) in float32,
+    named a_kl, a_kr, a_vl, a_vr (local/recurrent key, local/recurrent value)."""
+    g = torch.Generator().manual_seed(int(seed) * 7919 + 17)
+    return {n: _normal(g, (H * Dh,), std) for n in ("a_kl", "a_kr", "a_vl", "a_vr")}
+
+
 def marker_values(rows: torch.Tensor, Dh: int, tag: float = 0.0) -> torch.Tensor:
     """Integer-valued markers [len(rows), Dh], exact in bf16 (every value is
     below 256): row i encodes rows[i] in base 64 (channel 0 = high digit + 1,
