@@ -33,6 +33,9 @@
  *   O_i    = sum_{j = max(0, i-W+1)}^{i} softmax_j(scale <R_i q_i, k~_j>) v~_j.
  * The mixed entries k~, v~ are formed once per token by maglev_mem_project
  * and read by the attention forward and backward.
+ * The gated form that [R-step] prints is available as well (the *_gated
+ * calls below): channel-wise gates g = 2 sigmoid(a) on both the local and the
+ * recurrent term, and an RMSNorm on the projected memory key.
  * R_p rotates channel pair (c, c + Dh/2) by angle p * base^(-2c/Dh) (p = pos0 + t).
  *
  * Common conventions
@@ -70,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MAGLEV_ABI_VERSION 3
+#define MAGLEV_ABI_VERSION 4
 
 typedef enum {
     MAGLEV_OK = 0,
@@ -209,6 +212,72 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
                                    const float *gate_logit, void *kcache, void *vcache,
                                    const int64_t *pos, void *o, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Gated mixing form ([R-step]: the recurrent key is RMSNorm(W_k^rec m'_{t-1}),
+ * the recurrent value W_v^rec m'_{t-1}; each layer mixes them with the local
+ * features through channel-wise gates g = 2 sigmoid(a), neutral value 1 at
+ * a = 0; [R-bg]: both keys are rotated before the mix):
+ *   kp_j  = W_Km m'_{j-1},  vmem_j = W_Vm m'_{j-1}          (m'_{-1} := 0)
+ *   kn_j  = kp_j / sqrt(mean_c kp_j[c]^2 + eps)             (over all H*Dh channels)
+ *   k~_j  = g_kl (.) R_j k_j + g_kr (.) R_j kn_j,   v~_j = g_vl (.) v_j + g_vr (.) vmem_j
+ * gates: float32 [4][H*Dh] logits in the order a_kl, a_kr, a_vl, a_vr; channel
+ * c = h*Dh + i of a row. The norm has no learned scale (the recurrent gate
+ * follows it). eps >= 0, finite. The gated calls need H*Dh <= 4096.
+ * Attention over the gated entries is maglev_swa_inject_fwd, unchanged.
+ * ------------------------------------------------------------------------- */
+
+/* Projection with the shift (as maglev_mem_project) and the gated mix.
+ *   m [B,T,d], W_Km, W_Vm [H*Dh,d], k, v [B,T,H,Dh]: dtype, read;
+ *   kproj, vmem [B,T,H,Dh] dtype, written: the projections before the norm
+ *     (the backward reads them);
+ *   kmix, vmix [B,T,H,Dh] dtype, written: the gated entries above.
+ * Every pointer is required (16-byte aligned) except for B*T == 0. */
+maglev_status_t maglev_mem_project_gated(const maglev_geom_t *g, int shift, const void *m,
+                                         const void *W_Km, const void *W_Vm, const void *k,
+                                         const void *v, const float *gates, float eps,
+                                         void *kproj, void *vmem, void *kmix, void *vmix,
+                                         hipStream_t stream);
+
+/* Bytes of device workspace maglev_swa_inject_bwd_gated needs (0 on invalid
+ * geometry or H*Dh > 4096). It holds, besides the attention scratch, the
+ * gradients of the two projections (2 * B*T*H*Dh dtype elements) and
+ * per-workgroup gate partial sums. */
+size_t maglev_swa_inject_bwd_gated_workspace(const maglev_geom_t *g);
+
+/* Backward of the gated layer path: attention, gated mix, norm, shift and
+ * projection (the chain rule through the forward above).
+ * Inputs: q; kmix, vmix, kproj, vmem from maglev_mem_project_gated (shift 1);
+ *   the local k, v; gates, eps; the forward's o and lse; dO; m_prime (unshifted);
+ *   W_Km, W_Vm.
+ * Outputs: dq, dk, dv [B,T,H,Dh] dtype (overwritten); dm_prime [B,T,d] float32
+ *   (row T-1 gets no injection gradient); dW_Km, dW_Vm [H*Dh,d] float32;
+ *   dgates [4][H*Dh] float32, the gradients of the four logit vectors.
+ * accumulate: bit 0 dm_prime +=, bit 1 dW +=, bit 2 dgates +=.
+ * workspace: at least maglev_swa_inject_bwd_gated_workspace(g) bytes.
+ * Deterministic: partial sums are combined in a fixed order, no atomics. */
+maglev_status_t maglev_swa_inject_bwd_gated(
+    const maglev_geom_t *g, const void *q, const void *kmix, const void *vmix, const void *k,
+    const void *v, const void *kproj, const void *vmem, const float *gates, float eps,
+    const void *o, const float *lse, const void *dO, const void *m_prime, const void *W_Km,
+    const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime, float *dW_Km, float *dW_Vm,
+    float *dgates, unsigned accumulate, void *workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/* One decode step of the gated form: as maglev_decode_step, with the new entry
+ *   k~ = g_kl R_p k + g_kr R_p RMSNorm(kproj),  v~ = g_vl v + g_vr vmem,
+ * where kproj, vmem are W_Km m_{t-1}, W_Vm m_{t-1} before the norm
+ * (maglev_mem_project with shift = 0), stream b's H*Dh row starting at element
+ * b * mem_stride (0 selects H*Dh), and the norm runs over that whole row.
+ * gates [4][H*Dh] float32 logits; eps >= 0. Workspace as maglev_decode_step. */
+maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
+                                         float rope_base, float scale, int32_t dtype,
+                                         const void *q, const void *k, const void *v,
+                                         const void *kproj, const void *vmem, int64_t mem_stride,
+                                         const float *gates, float eps, void *kcache,
+                                         void *vcache, const int64_t *pos, void *o,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
 
 /* pos[b] += 1 for b < Bs on the device (moves every stream to its next ring
  * slot; kept separate so one decode step can be captured and replayed). */

@@ -73,6 +73,13 @@ def lib() -> ctypes.CDLL:
             "maglev_decode_step": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
                                    + [vp] * 5 + [vp, sz, vp], i32),
             "maglev_decode_advance": ([i32, vp, vp], i32),
+            "maglev_mem_project_gated": ([G, ctypes.c_int] + [vp] * 6 + [f32] + [vp] * 4 + [vp],
+                                         i32),
+            "maglev_swa_inject_bwd_gated_workspace": ([G], sz),
+            "maglev_swa_inject_bwd_gated": ([G] + [vp] * 8 + [f32] + [vp] * 13 + [u32, vp, sz, vp],
+                                            i32),
+            "maglev_decode_step_gated": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
+                                         + [vp, f32] + [vp] * 4 + [vp, sz, vp], i32),
             "maglev_prepare": ([i32, f32, i64], i32),
             "maglev_status_string": ([i32], ctypes.c_char_p),
             "maglev_last_error": ([], ctypes.c_char_p),
@@ -325,6 +332,122 @@ def maglev_decode_step(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o=N
                                     _ptr(o), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(),
                                     _stream(stream)), "maglev_decode_step")
+    return o
+
+
+# ----------------------------------------------------------------------------
+# Gated form: k~ = g_kl R k + g_kr R RMSNorm(W_Km m'), v~ = g_vl v + g_vr W_Vm m',
+# g = 2 sigmoid(a); gates are float32 [4, H*Dh] logits (a_kl, a_kr, a_vl, a_vr).
+# ----------------------------------------------------------------------------
+GATE_NAMES = ("a_kl", "a_kr", "a_vl", "a_vr")
+RMS_EPS = 1e-6
+
+
+def gate_tensor(gates, HD: int, device) -> torch.Tensor:
+    """The [4, HD] float32 logit tensor the gated calls take, from a tensor or
+    a mapping of the four names."""
+    if not isinstance(gates, torch.Tensor):
+        gates = torch.stack([torch.as_tensor(gates[n], dtype=torch.float32).reshape(-1)
+                             for n in GATE_NAMES])
+    gates = gates.to(device=device, dtype=torch.float32).reshape(4, HD).contiguous()
+    return gates
+
+
+def maglev_mem_project_gated(m, W_Km, W_Vm, H: int, Dh: int, k, v, gates, eps: float = RMS_EPS,
+                             shift: int = 1, pos0: int = 0, rope_base: float = 10000.0,
+                             kproj=None, vmem=None, kmix=None, vmix=None, stream=None):
+    """(kproj, vmem, kmix, vmix): the projections of the shifted memory before
+    the norm, and the gated mixed entries, all [B,T,H,Dh]."""
+    B, T, d = m.shape
+    gates = gate_tensor(gates, H * Dh, m.device)
+    _dev(m, W_Km, W_Vm, k, v, gates, kproj, vmem, kmix, vmix)
+    _same(m, W_Km, W_Vm, k, v, kproj, vmem, kmix, vmix)
+    if tuple(W_Km.shape) != (H * Dh, d) or tuple(W_Vm.shape) != (H * Dh, d):
+        raise MaglevError("W_Km / W_Vm must be [H*Dh, d]")
+    shp = (B, T, H, Dh)
+    if tuple(k.shape) != shp or tuple(v.shape) != shp:
+        raise MaglevError("k / v must be [B,T,H,Dh]")
+    new = lambda t: torch.empty(shp, dtype=m.dtype, device=m.device) if t is None else t
+    kproj, vmem, kmix, vmix = new(kproj), new(vmem), new(kmix), new(vmix)
+    g = make_geom(B, T, H, Dh, d, 1, pos0, rope_base, 0.0, _dtype_code(m))
+    _check(lib().maglev_mem_project_gated(ctypes.byref(g), shift, _ptr(m), _ptr(W_Km), _ptr(W_Vm),
+                                          _ptr(k), _ptr(v), _ptr(gates), float(eps), _ptr(kproj),
+                                          _ptr(vmem), _ptr(kmix), _ptr(vmix), _stream(stream)),
+           "maglev_mem_project_gated")
+    return kproj, vmem, kmix, vmix
+
+
+def maglev_swa_inject_bwd_gated_workspace(B, T, H, Dh, d, W, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, d, W, dtype=dtype)
+    return int(lib().maglev_swa_inject_bwd_gated_workspace(ctypes.byref(g)))
+
+
+def maglev_swa_inject_bwd_gated(q, kmix, vmix, k, v, kproj, vmem, gates, o, lse, dO, m_prime,
+                                W_Km, W_Vm, W: int, eps: float = RMS_EPS, pos0: int = 0,
+                                rope_base: float = 10000.0, scale: float = 0.0,
+                                accumulate: int = 0, out: Optional[dict] = None, workspace=None,
+                                stream=None) -> dict:
+    """Gradients dq, dk, dv (activation dtype), dm_prime, dW_Km, dW_Vm and
+    dgates [4, H*Dh] (float32) of the gated layer path."""
+    B, T, H, Dh = q.shape
+    d = m_prime.shape[-1]
+    dev = q.device
+    gates = gate_tensor(gates, H * Dh, dev)
+    _dev(q, kmix, vmix, k, v, kproj, vmem, gates, o, lse, dO, m_prime, W_Km, W_Vm, workspace)
+    _same(q, kmix, vmix, k, v, kproj, vmem, o, dO, m_prime, W_Km, W_Vm)
+    if out is None:
+        out = {}
+    f32 = torch.float32
+    out.setdefault("dq", torch.empty_like(q))
+    out.setdefault("dk", torch.empty_like(q))
+    out.setdefault("dv", torch.empty_like(q))
+    out.setdefault("dm_prime", torch.empty((B, T, d), dtype=f32, device=dev))
+    out.setdefault("dW_Km", torch.empty((H * Dh, d), dtype=f32, device=dev))
+    out.setdefault("dW_Vm", torch.empty((H * Dh, d), dtype=f32, device=dev))
+    out.setdefault("dgates", torch.empty((4, H * Dh), dtype=f32, device=dev))
+    _dev(*out.values())
+    g = make_geom(B, T, H, Dh, d, W, pos0, rope_base, scale, _dtype_code(q))
+    need = int(lib().maglev_swa_inject_bwd_gated_workspace(ctypes.byref(g)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().maglev_swa_inject_bwd_gated(
+        ctypes.byref(g), _ptr(q), _ptr(kmix), _ptr(vmix), _ptr(k), _ptr(v), _ptr(kproj),
+        _ptr(vmem), _ptr(gates), float(eps), _ptr(o), _ptr(lse), _ptr(dO), _ptr(m_prime),
+        _ptr(W_Km), _ptr(W_Vm), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dm_prime"]), _ptr(out["dW_Km"]), _ptr(out["dW_Vm"]), _ptr(out["dgates"]),
+        accumulate, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "maglev_swa_inject_bwd_gated")
+    return out
+
+
+def maglev_decode_step_gated(q, k, v, kproj, vmem, gates, kcache, vcache, pos, o=None,
+                             eps: float = RMS_EPS, rope_base: float = 10000.0, scale: float = 0.0,
+                             workspace=None, mem_stride: int = 0, stream=None):
+    """One decode step of the gated form (kproj = W_Km m_{t-1} before the norm);
+    kcache/vcache are updated in place. Returns o [Bs,H,Dh]."""
+    Bs, H, W, Dh = kcache.shape
+    gates = gate_tensor(gates, H * Dh, q.device)
+    _dev(q, k, v, gates, kcache, vcache, pos, o, workspace)
+    _same(q, k, v, kproj, vmem, kcache, vcache, o)
+    if pos.dtype != torch.int64 or pos.numel() != Bs:
+        raise MaglevError("pos must be int64 [Bs]")
+    stride = mem_stride or H * Dh
+    for t in (kproj, vmem):
+        if not t.is_cuda:
+            raise MaglevError("tensors must be on the GPU")
+        span = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+        if Bs > 0 and span < (Bs - 1) * stride + H * Dh:
+            raise MaglevError("kproj/vmem too small for Bs x mem_stride")
+    o = torch.empty_like(q) if o is None else o
+    if workspace is None:
+        need = int(lib().maglev_decode_workspace(Bs, H, Dh, W))
+        workspace = torch.zeros((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().maglev_decode_step_gated(Bs, H, Dh, W, rope_base, scale, _dtype_code(q), _ptr(q),
+                                          _ptr(k), _ptr(v), _ptr(kproj), _ptr(vmem),
+                                          int(mem_stride), _ptr(gates), float(eps), _ptr(kcache),
+                                          _ptr(vcache), _ptr(pos), _ptr(o), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          _stream(stream)), "maglev_decode_step_gated")
     return o
 
 

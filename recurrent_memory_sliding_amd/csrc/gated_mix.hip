@@ -1,0 +1,424 @@
+// gated_mix.hip -- the gated mixing form and its backward.
+//
+// Method: Maglev summary on paper.rainbus.top ("Maglev：滑动窗口循环记忆"),
+// section 方法步骤详情: the recurrent key is the RMS-normalised projection of
+// the shifted memory, and each layer mixes it with the local features through
+// channel-wise gates g = 2 sigmoid(a) (neutral value 1 at a = 0); section
+// 前置知识: both keys are rotated before the mix. Per token row of H*Dh
+// channels (p = pos0 + t, kp = W_Km m'_{t-1}, rms = sqrt(mean(kp^2) + eps)):
+//   kn   = kp / rms
+//   k~   = g_kl (.) R_p k + g_kr (.) R_p kn,     v~ = g_vl (.) v + g_vr (.) vmem
+// Backward, from the gradients dk~, dv~ of the mixed entries:
+//   dk   = R_p^T (g_kl (.) dk~),   dkn = R_p^T (g_kr (.) dk~)
+//   dkp  = (dkn - kn mean(dkn (.) kn)) / rms      (mean over the H*Dh row)
+//   dv   = g_vl (.) dv~,           dvmem = g_vr (.) dv~
+//   d/da = 2 sigmoid(a)(1 - sigmoid(a)) * sum over tokens of
+//          dk~ (.) R k | dk~ (.) R kn | dv~ (.) v | dv~ (.) vmem.
+//
+// Layout of the work: one workgroup walks a contiguous range of token rows;
+// each thread owns one chunk pair of the row (8 channels c..c+7 of a head and
+// their rotation partners c+Dh/2..; H*Dh <= 4096, so at most 256 threads) for
+// the whole range, so it keeps its gate-gradient
+// partial sums in registers (the gate values sit in LDS). The two row
+// reductions (sum of squares, mean of dkn*kn) are workgroup sums.
+// Everything is HBM-bound streaming: 16-byte loads and stores per lane.
+#include "common.hpp"
+#include "internal.hpp"
+#include "profile.hpp"
+
+namespace maglev {
+
+namespace {
+
+constexpr int kGatedFwdRows = 4;   // token rows per workgroup in the forward mix
+
+MAGLEV_DEV float two_sigmoid(float a) { return 2.0f / (1.0f + __expf(-a)); }
+
+// Sum over the workgroup (nw waves); every thread receives the total. `red`
+// holds one float per wave; callers alternate buffers between consecutive
+// sums so that one barrier per sum suffices.
+MAGLEV_DEV float group_sum(float x, float *red, int nw)
+{
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    float t = 0.0f;
+    for (int i = 0; i < nw; ++i) t += red[i];
+    return t;
+}
+
+// Rotation of the 8 pairs (lo[e], hi[e]) by the table entries cs[0..7];
+// inverse applies R^T.
+MAGLEV_DEV void rotate_pairs(float *lo, float *hi, const float2 *cs, bool inverse)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float c = cs[e].x, sn = inverse ? -cs[e].y : cs[e].y;
+        const float x0 = lo[e], x1 = hi[e];
+        lo[e] = x0 * c - x1 * sn;
+        hi[e] = x0 * sn + x1 * c;
+    }
+}
+
+// Channel geometry of thread `cp`'s chunk pair inside an H*Dh row.
+template <int DH>
+struct ChunkPair {
+    int j;          // chunk index inside the half head (rotation-table offset 8j)
+    int64_t lo, hi; // first channel of the low and the high half
+    MAGLEV_DEV explicit ChunkPair(int cp)
+    {
+        constexpr int PER_HEAD = DH / 16;
+        j = cp % PER_HEAD;
+        lo = (int64_t)(cp / PER_HEAD) * DH + 8 * j;
+        hi = lo + DH / 2;
+    }
+};
+
+// The workgroup's copy of the gate values g = 2 sigmoid(a), [4][HD] floats in
+// LDS (dynamic shared memory, 16 HD bytes): computed once, read per row, so
+// that the gates do not occupy 64 registers per thread.
+MAGLEV_DEV void stage_gates(const float *logits, int n, float *gsh)
+{
+    for (int i = threadIdx.x; i < n; i += blockDim.x) gsh[i] = two_sigmoid(logits[i]);
+    __syncthreads();
+}
+
+MAGLEV_DEV void lds8(const float *p, float *out)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+}
+
+struct GatedArgs {
+    int64_t N, Tlen, pos0;
+    int HD, rows_per_block;
+    float eps;
+    const float2 *rope;   // [pos][Dh/2] or nullptr
+    const float *gates;   // [4][HD] logits: a_kl, a_kr, a_vl, a_vr
+};
+
+// ---------------------------------------------------------------------------
+// Forward: mixed entries kx, vx from k, v, kp (pre-norm), vm.
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, const T *v,
+                                                      const T *kp, const T *vm, T *kx, T *vx)
+{
+    __shared__ float red[2][4];
+    extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD]
+    const int tid = threadIdx.x, nw = blockDim.x >> 6;
+    const bool act = tid < a.HD / 16;
+    const ChunkPair<DH> cp(act ? tid : 0);
+    stage_gates(a.gates, 4 * a.HD, gsh);
+    const float *gk = gsh, *gv = gsh + 2 * a.HD;   // [2][HD] each: local, recurrent
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+    const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
+    const float inv_hd = 1.0f / (float)a.HD;
+    for (int64_t row = r0; row < r1; ++row) {
+        const int64_t base = row * a.HD;
+        float nl[8] = {}, nh[8] = {};
+        if (act) {
+            load8(kp + base + cp.lo, nl);
+            load8(kp + base + cp.hi, nh);
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += nl[e] * nl[e] + nh[e] * nh[e];
+        const float rs = rsqrtf(group_sum(ss, red[row & 1], nw) * inv_hd + a.eps);
+        if (!act) continue;
+        float kl[8], kh[8];
+        load8(k + base + cp.lo, kl);
+        load8(k + base + cp.hi, kh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }
+        if (a.rope) {
+            const float2 *cs = a.rope + (a.pos0 + row % a.Tlen) * (DH / 2) + 8 * cp.j;
+            rotate_pairs(kl, kh, cs, false);
+            rotate_pairs(nl, nh, cs, false);
+        }
+        {
+            float ga[8], gb[8];
+            lds8(gk + cp.lo, ga);
+            lds8(gk + a.HD + cp.lo, gb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kl[e] = ga[e] * kl[e] + gb[e] * nl[e];
+            lds8(gk + cp.hi, ga);
+            lds8(gk + a.HD + cp.hi, gb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kh[e] = ga[e] * kh[e] + gb[e] * nh[e];
+        }
+        store8(kx + base + cp.lo, kl);
+        store8(kx + base + cp.hi, kh);
+        float vl[8], vh[8], ml[8], mh[8];
+        load8(v + base + cp.lo, vl);
+        load8(v + base + cp.hi, vh);
+        load8(vm + base + cp.lo, ml);
+        load8(vm + base + cp.hi, mh);
+        {
+            float ga[8], gb[8];
+            lds8(gv + cp.lo, ga);
+            lds8(gv + a.HD + cp.lo, gb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vl[e] = ga[e] * vl[e] + gb[e] * ml[e];
+            lds8(gv + cp.hi, ga);
+            lds8(gv + a.HD + cp.hi, gb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vh[e] = ga[e] * vh[e] + gb[e] * mh[e];
+        }
+        store8(vx + base + cp.lo, vl);
+        store8(vx + base + cp.hi, vh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward. dk/dv hold dk~/dv~ on entry and dk/dv on exit (each thread reads
+// its channels before it overwrites them). dkp, dvm receive the gradients of
+// the projected memory; gpart[block][4][HD] the per-block gate partial sums
+// (before the 2 sigma (1 - sigma) factor).
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, const T *v,
+                                                      const T *kp, const T *vm, T *dk, T *dv,
+                                                      T *dkp, T *dvm, float *gpart)
+{
+    __shared__ float red[2][4];
+    extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD]
+    const int tid = threadIdx.x, nw = blockDim.x >> 6;
+    const bool act = tid < a.HD / 16;
+    const ChunkPair<DH> cp(act ? tid : 0);
+    stage_gates(a.gates, 4 * a.HD, gsh);
+    const float *gkl = gsh, *gkr = gsh + a.HD, *gvl = gsh + 2 * a.HD, *gvr = gsh + 3 * a.HD;
+    float pkl[16] = {}, pkr[16] = {}, pvl[16] = {}, pvr[16] = {};
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+    const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
+    const float inv_hd = 1.0f / (float)a.HD;
+    for (int64_t row = r0; row < r1; ++row) {
+        const int64_t base = row * a.HD;
+        float nl[8] = {}, nh[8] = {};
+        if (act) {
+            load8(kp + base + cp.lo, nl);
+            load8(kp + base + cp.hi, nh);
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += nl[e] * nl[e] + nh[e] * nh[e];
+        const float rs = rsqrtf(group_sum(ss, red[0], nw) * inv_hd + a.eps);
+        float dnl[8] = {}, dnh[8] = {};   // dkn
+        float mu = 0.0f;
+        const float2 *cs = (act && a.rope) ? a.rope + (a.pos0 + row % a.Tlen) * (DH / 2) + 8 * cp.j
+                                           : nullptr;
+        if (act) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }   // kn
+            float gl[8], gh[8], kl[8], kh[8];
+            load8(dk + base + cp.lo, gl);
+            load8(dk + base + cp.hi, gh);
+            load8(k + base + cp.lo, kl);
+            load8(k + base + cp.hi, kh);
+            float rnl[8], rnh[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { rnl[e] = nl[e]; rnh[e] = nh[e]; }
+            if (cs) {
+                rotate_pairs(kl, kh, cs, false);
+                rotate_pairs(rnl, rnh, cs, false);
+            }
+            float ol[8], oh[8];
+            {
+                float ga[8], gb[8], gc[8], gd[8];
+                lds8(gkl + cp.lo, ga);
+                lds8(gkl + cp.hi, gb);
+                lds8(gkr + cp.lo, gc);
+                lds8(gkr + cp.hi, gd);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pkl[e] += gl[e] * kl[e];
+                    pkl[8 + e] += gh[e] * kh[e];
+                    pkr[e] += gl[e] * rnl[e];
+                    pkr[8 + e] += gh[e] * rnh[e];
+                    ol[e] = ga[e] * gl[e];
+                    oh[e] = gb[e] * gh[e];
+                    dnl[e] = gc[e] * gl[e];
+                    dnh[e] = gd[e] * gh[e];
+                }
+            }
+            if (cs) {
+                rotate_pairs(ol, oh, cs, true);
+                rotate_pairs(dnl, dnh, cs, true);
+            }
+            store8(dk + base + cp.lo, ol);
+            store8(dk + base + cp.hi, oh);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mu += dnl[e] * nl[e] + dnh[e] * nh[e];
+
+            float vl[8], vh[8], ml[8], mh[8];
+            load8(dv + base + cp.lo, gl);
+            load8(dv + base + cp.hi, gh);
+            load8(v + base + cp.lo, vl);
+            load8(v + base + cp.hi, vh);
+            load8(vm + base + cp.lo, ml);
+            load8(vm + base + cp.hi, mh);
+            {
+                float ga[8], gb[8], gc[8], gd[8];
+                lds8(gvl + cp.lo, ga);
+                lds8(gvl + cp.hi, gb);
+                lds8(gvr + cp.lo, gc);
+                lds8(gvr + cp.hi, gd);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pvl[e] += gl[e] * vl[e];
+                    pvl[8 + e] += gh[e] * vh[e];
+                    pvr[e] += gl[e] * ml[e];
+                    pvr[8 + e] += gh[e] * mh[e];
+                    vl[e] = ga[e] * gl[e];
+                    vh[e] = gb[e] * gh[e];
+                    ml[e] = gc[e] * gl[e];
+                    mh[e] = gd[e] * gh[e];
+                }
+            }
+            store8(dv + base + cp.lo, vl);
+            store8(dv + base + cp.hi, vh);
+            store8(dvm + base + cp.lo, ml);
+            store8(dvm + base + cp.hi, mh);
+        }
+        mu = group_sum(mu, red[1], nw) * inv_hd;
+        if (!act) continue;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dnl[e] = (dnl[e] - nl[e] * mu) * rs;
+            dnh[e] = (dnh[e] - nh[e] * mu) * rs;
+        }
+        store8(dkp + base + cp.lo, dnl);
+        store8(dkp + base + cp.hi, dnh);
+    }
+    if (!act) return;
+    float *out = gpart + (int64_t)blockIdx.x * 4 * a.HD;
+    const float *parts[4] = {pkl, pkr, pvl, pvr};
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        store8(out + gi * a.HD + cp.lo, parts[gi]);
+        store8(out + gi * a.HD + cp.hi, parts[gi] + 8);
+    }
+}
+
+// dgates[i] (+)= 2 sigmoid(a_i)(1 - sigmoid(a_i)) * sum_b gpart[b][i], the
+// blocks summed in a fixed order. One wave per 64 outputs and per quarter of
+// the blocks; the quarters are combined in order through LDS.
+__global__ __launch_bounds__(256) void gate_grad_reduce(const float *gpart, int nblk, int n,
+                                                        const float *gates, float *dgates,
+                                                        unsigned acc)
+{
+    __shared__ float part[4][64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int i = blockIdx.x * 64 + lane;
+    float s = 0.0f;
+    if (i < n) {
+        const int per = (nblk + 3) / 4;
+        const int b0 = w * per, b1 = b0 + per < nblk ? b0 + per : nblk;
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) s += gpart[(int64_t)b * n + i];
+    }
+    part[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && i < n) {
+        const float tot = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        const float sg = 1.0f / (1.0f + __expf(-gates[i]));
+        const float g = 2.0f * sg * (1.0f - sg) * tot;
+        dgates[i] = acc ? dgates[i] + g : g;
+    }
+}
+
+unsigned row_threads(int HD) { return (unsigned)((HD / 16 + 63) / 64 * 64); }
+size_t gate_lds_bytes(int HD) { return (size_t)4 * HD * sizeof(float); }
+
+GatedArgs gated_args(const Geom &g, const float *gates, float eps, const float2 *rope,
+                     int rows_per_block)
+{
+    GatedArgs a;
+    a.N = g.N(); a.Tlen = g.T; a.pos0 = g.pos0;
+    a.HD = g.HD(); a.rows_per_block = rows_per_block;
+    a.eps = eps; a.rope = rope; a.gates = gates;
+    return a;
+}
+
+template <typename T, int DH>
+void fwd_t(const Geom &g, const void *k, const void *v, const void *kp, const void *vm,
+           const float *gates, float eps, const float2 *rope, void *kx, void *vx, hipStream_t s)
+{
+    const int rpb = kGatedFwdRows;
+    const GatedArgs a = gated_args(g, gates, eps, rope, rpb);
+    const unsigned nblk = (unsigned)((g.N() + rpb - 1) / rpb);
+    prof::Scope ts("gated_mix", s);
+    hipLaunchKernelGGL((gated_mix_fwd<T, DH>), dim3(nblk), dim3(row_threads(g.HD())),
+                       gate_lds_bytes(g.HD()), s, a,
+                       static_cast<const T *>(k), static_cast<const T *>(v),
+                       static_cast<const T *>(kp), static_cast<const T *>(vm),
+                       static_cast<T *>(kx), static_cast<T *>(vx));
+}
+
+template <typename T, int DH>
+void bwd_t(const Geom &g, const void *k, const void *v, const void *kp, const void *vm,
+           const float *gates, float eps, const float2 *rope, void *dk, void *dv,
+           const BwdWorkspace &ws, float *dgates, unsigned acc, hipStream_t s)
+{
+    const GatedArgs a = gated_args(g, gates, eps, rope, ws.g_rows);
+    {
+        prof::Scope ts("gated_mix_bwd", s);
+        hipLaunchKernelGGL((gated_mix_bwd<T, DH>), dim3((unsigned)ws.g_blocks),
+                           dim3(row_threads(g.HD())), gate_lds_bytes(g.HD()), s, a,
+                           static_cast<const T *>(k),
+                           static_cast<const T *>(v), static_cast<const T *>(kp),
+                           static_cast<const T *>(vm), static_cast<T *>(dk), static_cast<T *>(dv),
+                           static_cast<T *>(ws.dkp), static_cast<T *>(ws.dvm), ws.gpart);
+    }
+    const int n = 4 * g.HD();
+    prof::Scope ts("gate_grad_reduce", s);
+    hipLaunchKernelGGL(gate_grad_reduce, dim3((unsigned)((n + 63) / 64)), dim3(256), 0, s, ws.gpart,
+                       ws.g_blocks, n, gates, dgates, (acc & 4u) != 0u);
+}
+
+}  // namespace
+
+void gated_partition(int64_t N, int *rows_per_block, int *blocks)
+{
+    // About 512 workgroups (two per CU), at least 8 rows each so that the
+    // per-block gate partials stay small next to the activations.
+    int64_t rpb = (N + 511) / 512;
+    if (rpb < 8) rpb = 8;
+    int64_t nb = (N + rpb - 1) / rpb;
+    if (nb < 1) nb = 1;
+    *rows_per_block = (int)rpb;
+    *blocks = (int)nb;
+}
+
+hipError_t launch_gated_mix(const Geom &g, const void *k, const void *v, const void *kp,
+                            const void *vm, const float *gates, float eps, const float2 *rope,
+                            void *kx, void *vx, hipStream_t s)
+{
+    if (g.dtype == MAGLEV_BF16) {
+        if (g.Dh == 128) fwd_t<bf16, 128>(g, k, v, kp, vm, gates, eps, rope, kx, vx, s);
+        else fwd_t<bf16, 64>(g, k, v, kp, vm, gates, eps, rope, kx, vx, s);
+    } else {
+        if (g.Dh == 128) fwd_t<float, 128>(g, k, v, kp, vm, gates, eps, rope, kx, vx, s);
+        else fwd_t<float, 64>(g, k, v, kp, vm, gates, eps, rope, kx, vx, s);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gated_mix_bwd(const Geom &g, const void *k, const void *v, const void *kp,
+                                const void *vm, const float *gates, float eps,
+                                const float2 *rope, void *dk, void *dv, const BwdWorkspace &ws,
+                                float *dgates, unsigned acc, hipStream_t s)
+{
+    if (g.dtype == MAGLEV_BF16) {
+        if (g.Dh == 128) bwd_t<bf16, 128>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+        else bwd_t<bf16, 64>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+    } else {
+        if (g.Dh == 128) bwd_t<float, 128>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+        else bwd_t<float, 64>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace maglev

@@ -52,8 +52,13 @@ struct BwdWorkspace {
     int64_t Tp;          // T rounded up to a multiple of 32
     int ksplit;
     int n_key_tiles;
+    // gated form only
+    void *dkp;           // [B,T,H*Dh] dtype: d loss / d (W_Km m'), before the norm
+    void *dvm;           // [B,T,H*Dh] dtype: d loss / d (W_Vm m')
+    float *gpart;        // [g_blocks][4][H*Dh] per-workgroup gate partial sums
+    int g_rows, g_blocks;
 };
-size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base);
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base, bool gated);
 
 hipError_t launch_bwd(const Geom &g, const void *q, const void *kmix, const void *vmix,
                       const void *kmem, const void *vmem, const float *gate, const void *o,
@@ -61,6 +66,25 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kmix, const void
                       const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime,
                       float *dW_Km, float *dW_Vm, float *dgate, unsigned accumulate,
                       const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+
+// ---- gated form: k~ = g_kl R k + g_kr R RMSNorm(kp), v~ = g_vl v + g_vr vm ----
+// gates [4][H*Dh] float32 logits (a_kl, a_kr, a_vl, a_vr), g = 2 sigmoid(a).
+void gated_partition(int64_t N, int *rows_per_block, int *blocks);
+hipError_t launch_gated_mix(const Geom &g, const void *k, const void *v, const void *kproj,
+                            const void *vmem, const float *gates, float eps, const float2 *rope,
+                            void *kmix, void *vmix, hipStream_t s);
+// dk/dv: in = gradients of the mixed entries, out = gradients of k and v.
+hipError_t launch_gated_mix_bwd(const Geom &g, const void *k, const void *v, const void *kproj,
+                                const void *vmem, const float *gates, float eps,
+                                const float2 *rope, void *dk, void *dv, const BwdWorkspace &ws,
+                                float *dgates, unsigned accumulate, hipStream_t s);
+hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kmix, const void *vmix,
+                            const void *k, const void *v, const void *kproj, const void *vmem,
+                            const float *gates, float eps, const void *o, const float *lse,
+                            const void *dO, const void *m_prime, const void *W_Km,
+                            const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime,
+                            float *dW_Km, float *dW_Vm, float *dgates, unsigned accumulate,
+                            const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
 
 // ---- consistency loss -------------------------------------------------------
 size_t loss_workspace_bytes(int64_t N, int d);
@@ -70,10 +94,13 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
 
 // ---- decode -----------------------------------------------------------------
 size_t decode_workspace_bytes(int Bs, int H, int Dh, int W);
+// gates == nullptr: the sigma-gated form with gate [H]; otherwise the gated
+// form with gates [4][H*Dh] and kmem = the pre-norm projection (gate unused).
 hipError_t launch_decode(int Bs, int H, int Dh, int W, float rope_base, float scale, int dtype,
                          const void *q, const void *k, const void *v, const void *kmem,
-                         const void *vmem, int64_t mem_stride, const float *gate, void *kcache,
-                         void *vcache, const int64_t *pos, void *o, void *ws, hipStream_t s);
+                         const void *vmem, int64_t mem_stride, const float *gate,
+                         const float *gates, float eps, void *kcache, void *vcache,
+                         const int64_t *pos, void *o, void *ws, hipStream_t s);
 hipError_t launch_advance(int Bs, int64_t *pos, hipStream_t s);
 
 }  // namespace maglev

@@ -174,12 +174,15 @@ MAGLEV_DEV void merge_state(float &m, float &l, float *a, float m2, float l2, co
     for (int e = 0; e < N; ++e) a[e] = a[e] * f1 + a2[e] * f2;
 }
 
-template <typename T, int DH>
+// GATED = false: k~ = R_p (k + s_h kmem), v~ = v + s_h vmem, s_h = sigmoid(gate[h]).
+// GATED = true:  k~ = g_kl R_p k + g_kr R_p RMSNorm(kmem), v~ = g_vl v + g_vr vmem,
+//   g = 2 sigmoid(gates[..]) per channel of the H*Dh row, the norm over stream
+//   b's whole H*Dh projection row (every workgroup of the stream recomputes it).
+template <typename T, int DH, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     int H, int W, float rope_base, double log2_base, float scale, const T *q, const T *k,
-    const T *v, const T *km,
-    const T *vm, int64_t mem_stride, const float *gate, T *kcache, T *vcache,
-    const int64_t *pos, T *o)
+    const T *v, const T *km, const T *vm, int64_t mem_stride, const float *gate,
+    const float *gates, float eps, T *kcache, T *vcache, const int64_t *pos, T *o)
 {
     constexpr int CH = DH / 8;                   // lanes per slot row
     constexpr int G = 64 / CH;                   // slots per wave pass
@@ -188,6 +191,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     __shared__ float knew[DH], vnew[DH];
     __shared__ float wst[kDecWaves][2];
     __shared__ float wacc[kDecWaves][DH];
+    __shared__ float wred[kDecWaves];
 
     const int64_t row = blockIdx.x;              // b * H + h
     const int h = (int)(row % H);
@@ -214,6 +218,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
     // 2. Position, rotation of position p (double precision: no table bounds
     //    p), rotated query, and the new entry (written by this workgroup only).
+    float rs = 0.0f;   // gated form: 1 / rms of the stream's memory-key row
+    if constexpr (GATED) {
+        const int HD = H * DH;
+        const T *kpr = km + b * mem_stride;
+        float ss = 0.0f;
+        for (int c = tid * 8; c < HD; c += kDecThreads * 8) {
+            float x[8];
+            load8(kpr + c, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) wred[w] = ss;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kDecWaves; ++ww) tot += wred[ww];
+        rs = rsqrtf(tot / (float)HD + eps);
+    }
     const int64_t p = pos[b];
     const int slot_new = (int)(p % W);
     const int nvalid = p + 1 < (int64_t)W ? (int)(p + 1) : W;   // slots 0 .. nvalid-1 hold positions >= 0
@@ -231,19 +254,35 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             r = fma(-kq, 2.4492935982947064e-16, r);                      // 2 pi, remainder
             sincosf((float)r, &sn, &cs);
         }
-        const float sg = gate_sigmoid(gate[h]);        const T *qr = q + row * DH;
+        const T *qr = q + row * DH;
         const float a0 = to_f<T>(qr[i]), a1 = to_f<T>(qr[i + DH / 2]);
         const float ls = scale * kLog2e;
         qh[i] = (a0 * cs - a1 * sn) * ls;
         qh[i + DH / 2] = (a0 * sn + a1 * cs) * ls;
         const int64_t mrow = b * mem_stride + (int64_t)h * DH;
         const T *kk = k + row * DH, *kmr = km + mrow, *vmr = vm + mrow;
-        const float x0 = to_f<T>(kk[i]) + sg * to_f<T>(kmr[i]);
-        const float x1 = to_f<T>(kk[i + DH / 2]) + sg * to_f<T>(kmr[i + DH / 2]);
-        const T k0 = from_f<T>(x0 * cs - x1 * sn);
-        const T k1 = from_f<T>(x0 * sn + x1 * cs);
-        const T v0 = from_f<T>(to_f<T>(v[row * DH + i]) + sg * to_f<T>(vmr[i]));
-        const T v1 = from_f<T>(to_f<T>(v[row * DH + i + DH / 2]) + sg * to_f<T>(vmr[i + DH / 2]));
+        const float l0 = to_f<T>(kk[i]), l1 = to_f<T>(kk[i + DH / 2]);
+        const float m0 = to_f<T>(kmr[i]), m1 = to_f<T>(kmr[i + DH / 2]);
+        const float u0 = to_f<T>(v[row * DH + i]), u1 = to_f<T>(v[row * DH + i + DH / 2]);
+        const float w0 = to_f<T>(vmr[i]), w1 = to_f<T>(vmr[i + DH / 2]);
+        T k0, k1, v0, v1;
+        if constexpr (GATED) {
+            const int HD = H * DH;
+            const int c0 = h * DH + i, c1 = c0 + DH / 2;
+            auto g2 = [&](int which, int c) { return 2.0f * gate_sigmoid(gates[which * HD + c]); };
+            const float n0 = m0 * rs, n1 = m1 * rs;
+            k0 = from_f<T>(g2(0, c0) * (l0 * cs - l1 * sn) + g2(1, c0) * (n0 * cs - n1 * sn));
+            k1 = from_f<T>(g2(0, c1) * (l0 * sn + l1 * cs) + g2(1, c1) * (n0 * sn + n1 * cs));
+            v0 = from_f<T>(g2(2, c0) * u0 + g2(3, c0) * w0);
+            v1 = from_f<T>(g2(2, c1) * u1 + g2(3, c1) * w1);
+        } else {
+            const float sg = gate_sigmoid(gate[h]);
+            const float x0 = l0 + sg * m0, x1 = l1 + sg * m1;
+            k0 = from_f<T>(x0 * cs - x1 * sn);
+            k1 = from_f<T>(x0 * sn + x1 * cs);
+            v0 = from_f<T>(u0 + sg * w0);
+            v1 = from_f<T>(u1 + sg * w1);
+        }
         knew[i] = to_f<T>(k0); knew[i + DH / 2] = to_f<T>(k1);
         vnew[i] = to_f<T>(v0); vnew[i + DH / 2] = to_f<T>(v1);
         // Whatever any wave reads from this slot (old or new contents) is
@@ -337,36 +376,52 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
 }
 
-template <typename T, int DH>
+template <typename T, int DH, bool GATED>
 static void launch_decode_t(int Bs, int H, int W, float rope_base, float scale, const void *q,
                             const void *k, const void *v, const void *km, const void *vm,
-                            int64_t mem_stride, const float *gate, void *kc, void *vc,
-                            const int64_t *pos, void *o, void *, hipStream_t s)
+                            int64_t mem_stride, const float *gate, const float *gates, float eps,
+                            void *kc, void *vc, const int64_t *pos, void *o, hipStream_t s)
 {
-    prof::Scope ts("decode_step", s);
-    hipLaunchKernelGGL((decode_kernel<T, DH>), dim3((unsigned)((int64_t)Bs * H)), dim3(kDecThreads),
-                       0, s, H, W, rope_base, rope_base > 0.0f ? log2((double)rope_base) : 0.0,
-                       scale, static_cast<const T *>(q),
-                       static_cast<const T *>(k), static_cast<const T *>(v),
-                       static_cast<const T *>(km), static_cast<const T *>(vm), mem_stride, gate,
+    prof::Scope ts(GATED ? "decode_step_gated" : "decode_step", s);
+    hipLaunchKernelGGL((decode_kernel<T, DH, GATED>), dim3((unsigned)((int64_t)Bs * H)),
+                       dim3(kDecThreads), 0, s, H, W, rope_base,
+                       rope_base > 0.0f ? log2((double)rope_base) : 0.0, scale,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<const T *>(km),
+                       static_cast<const T *>(vm), mem_stride, gate, gates, eps,
                        static_cast<T *>(kc), static_cast<T *>(vc), pos, static_cast<T *>(o));
+}
+
+template <typename T, int DH>
+static void launch_decode_dt(int Bs, int H, int W, float rope_base, float scale, const void *q,
+                             const void *k, const void *v, const void *km, const void *vm,
+                             int64_t mem_stride, const float *gate, const float *gates, float eps,
+                             void *kc, void *vc, const int64_t *pos, void *o, hipStream_t s)
+{
+    if (gates)
+        launch_decode_t<T, DH, true>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride,
+                                     gate, gates, eps, kc, vc, pos, o, s);
+    else
+        launch_decode_t<T, DH, false>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride,
+                                      gate, gates, eps, kc, vc, pos, o, s);
 }
 
 hipError_t launch_decode(int Bs, int H, int Dh, int W, float rope_base, float scale, int dtype,
                          const void *q, const void *k, const void *v, const void *km,
-                         const void *vm, int64_t mem_stride, const float *gate, void *kc,
-                         void *vc, const int64_t *pos, void *o, void *ws, hipStream_t s)
+                         const void *vm, int64_t mem_stride, const float *gate,
+                         const float *gates, float eps, void *kc, void *vc, const int64_t *pos,
+                         void *o, void *, hipStream_t s)
 {
     if (dtype == MAGLEV_BF16) {
         if (Dh == 128)
-            launch_decode_t<bf16, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
+            launch_decode_dt<bf16, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, gates, eps, kc, vc, pos, o, s);
         else
-            launch_decode_t<bf16, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
+            launch_decode_dt<bf16, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, gates, eps, kc, vc, pos, o, s);
     } else {
         if (Dh == 128)
-            launch_decode_t<float, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
+            launch_decode_dt<float, 128>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, gates, eps, kc, vc, pos, o, s);
         else
-            launch_decode_t<float, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, kc, vc, pos, o, ws, s);
+            launch_decode_dt<float, 64>(Bs, H, W, rope_base, scale, q, k, v, km, vm, mem_stride, gate, gates, eps, kc, vc, pos, o, s);
     }
     return hipGetLastError();
 }

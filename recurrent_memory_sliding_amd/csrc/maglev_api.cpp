@@ -242,7 +242,7 @@ size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g)
     Geom G;
     if (check_geom(g, &G) != MAGLEV_OK) return 0;
     BwdWorkspace layout;
-    return bwd_workspace_bytes(G, &layout, nullptr);
+    return bwd_workspace_bytes(G, &layout, nullptr, false);
 }
 
 maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *kmix,
@@ -266,7 +266,7 @@ maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, con
     if (!gate_logit || !dgate) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit or dgate is NULL");
     if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
     BwdWorkspace layout;
-    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace));
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), false);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (workspace && !aligned16(workspace))
@@ -347,8 +347,124 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
         return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)Dh));
     return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kmem, vmem,
-                                    mem_stride, gate_logit, kcache, vcache, pos, o, workspace,
-                                    stream));
+                                    mem_stride, gate_logit, nullptr, 0.0f, kcache, vcache, pos, o,
+                                    workspace, stream));
+}
+
+// ---- gated mixing form --------------------------------------------------------
+
+namespace {
+maglev_status_t check_gated(const Geom &G, const float *gates, float eps)
+{
+    if (G.HD() > 4096) return fail(MAGLEV_ERR_UNSUPPORTED, "gated form needs H*Dh <= 4096");
+    if (!(eps >= 0.0f) || !(eps < INFINITY))
+        return fail(MAGLEV_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+    if (!gates) return fail(MAGLEV_ERR_INVALID_VALUE, "gates is NULL");
+    return MAGLEV_OK;
+}
+}  // namespace
+
+maglev_status_t maglev_mem_project_gated(const maglev_geom_t *g, int shift, const void *m,
+                                         const void *W_Km, const void *W_Vm, const void *k,
+                                         const void *v, const float *gates, float eps,
+                                         void *kproj, void *vmem, void *kmix, void *vmix,
+                                         hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (shift != 0 && shift != 1) return fail(MAGLEV_ERR_INVALID_VALUE, "shift must be 0 or 1");
+    st = check_gated(G, gates, eps);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0) return MAGLEV_OK;
+    st = check_ptrs({m, W_Km, W_Vm, k, v, kproj, vmem, kmix, vmix});
+    if (st != MAGLEV_OK) return st;
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    hipError_t e = launch_project(G, shift, m, W_Km, W_Vm, kproj, vmem, stream);
+    if (e == hipSuccess)
+        e = launch_gated_mix(G, k, v, kproj, vmem, gates, eps, rope, kmix, vmix, stream);
+    return hip_status(e);
+}
+
+size_t maglev_swa_inject_bwd_gated_workspace(const maglev_geom_t *g)
+{
+    Geom G;
+    if (check_geom(g, &G) != MAGLEV_OK || G.HD() > 4096) return 0;
+    BwdWorkspace layout;
+    return bwd_workspace_bytes(G, &layout, nullptr, true);
+}
+
+maglev_status_t maglev_swa_inject_bwd_gated(
+    const maglev_geom_t *g, const void *q, const void *kmix, const void *vmix, const void *k,
+    const void *v, const void *kproj, const void *vmem, const float *gates, float eps,
+    const void *o, const float *lse, const void *dO, const void *m_prime, const void *W_Km,
+    const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime, float *dW_Km, float *dW_Vm,
+    float *dgates, unsigned accumulate, void *workspace, size_t workspace_bytes,
+    hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    st = check_gated(G, gates, eps);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0)
+        st = check_ptrs({W_Km, W_Vm, dW_Km, dW_Vm});
+    else
+        st = check_ptrs({q, kmix, vmix, k, v, kproj, vmem, o, lse, dO, m_prime, W_Km, W_Vm, dq,
+                         dk, dv, dm_prime, dW_Km, dW_Vm});
+    if (st != MAGLEV_OK) return st;
+    if (!dgates) return fail(MAGLEV_ERR_INVALID_VALUE, "dgates is NULL");
+    if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    BwdWorkspace layout;
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), true);
+    if (G.N() > 0 && (!workspace || workspace_bytes < need))
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (workspace && !aligned16(workspace))
+        return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    return hip_status(launch_bwd_gated(G, q, kmix, vmix, k, v, kproj, vmem, gates, eps, o, lse, dO,
+                                       m_prime, W_Km, W_Vm, dq, dk, dv, dm_prime, dW_Km, dW_Vm,
+                                       dgates, accumulate, layout, rope, stream));
+}
+
+maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
+                                         float rope_base, float scale, int32_t dtype,
+                                         const void *q, const void *k, const void *v,
+                                         const void *kproj, const void *vmem, int64_t mem_stride,
+                                         const float *gates, float eps, void *kcache,
+                                         void *vcache, const int64_t *pos, void *o,
+                                         void *workspace, size_t workspace_bytes,
+                                         hipStream_t stream)
+{
+    if (Bs < 0 || H < 1 || W < 1) return fail(MAGLEV_ERR_INVALID_VALUE, "need Bs >= 0, H >= 1, W >= 1");
+    if (Dh != 64 && Dh != 128) return fail(MAGLEV_ERR_UNSUPPORTED, "Dh must be 64 or 128");
+    if (!(scale == scale) || !(rope_base == rope_base))
+        return fail(MAGLEV_ERR_INVALID_VALUE, "scale and rope_base must not be NaN");
+    if (!(eps >= 0.0f) || !(eps < INFINITY))
+        return fail(MAGLEV_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+    maglev_status_t st = check_dtype(dtype);
+    if (st != MAGLEV_OK) return st;
+    if (mem_stride == 0) mem_stride = (int64_t)H * Dh;
+    if (mem_stride < (int64_t)H * Dh || mem_stride % 8 != 0)
+        return fail(MAGLEV_ERR_INVALID_VALUE, "mem_stride must be 0 or a multiple of 8 >= H*Dh");
+    if (Bs == 0) return MAGLEV_OK;
+    st = check_ptrs({q, k, v, kproj, vmem, kcache, vcache, o});
+    if (st != MAGLEV_OK) return st;
+    if (!gates || !pos) return fail(MAGLEV_ERR_INVALID_VALUE, "gates or pos is NULL");
+    if ((double)Bs * H * W * Dh > 4.0e12) return fail(MAGLEV_ERR_INVALID_VALUE, "ring too large");
+    const size_t need = decode_workspace_bytes(Bs, H, Dh, W);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (workspace && !aligned16(workspace))
+        return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)Dh));
+    return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kproj, vmem,
+                                    mem_stride, nullptr, gates, eps, kcache, vcache, pos, o,
+                                    workspace, stream));
 }
 
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream)

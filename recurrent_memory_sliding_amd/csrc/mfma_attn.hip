@@ -404,8 +404,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16 *o, const bf16
 // Per tile: S = Q^ K~^T, P = exp(scale S - lse), dP = dO V~^T,
 // dS = P (dP - D); dV~^T += dO^T P, dK~^T += Q^^T dS.
 // Epilogue: dk = scale R^T dK~, dv = dV~, and the gate partial
-// <kmem, dk> + <vmem, dv> summed over the workgroup's keys.
-template <int DH, int ST>
+// <kmem, dk> + <vmem, dv> summed over the workgroup's keys. With ENTRIES the
+// epilogue writes the gradients of the mixed entries themselves (scale dK~ in
+// the rotated frame, dV~) and no gate partial: the gated mixing form applies
+// its own gates, rotation and norm backward afterwards.
+template <int DH, int ST, bool ENTRIES>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf16 *dO,
                                                              const float *lse2, const float *Dp,
                                                              int64_t Tp, bf16 *dk, bf16 *dv,
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     float part = 0.0f;
     if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
-        const float2 *cs = a.rope ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
+        const float2 *cs = (a.rope && !ENTRIES) ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
 #pragma unroll
         for (int db = 0; db < NB / 2; ++db)
 #pragma unroll
@@ -568,23 +571,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int c = 32 * db + 8 * i4 + 4 * g;
                 bf16x4 k4, v4;
-                const bf16x4 km4 = *reinterpret_cast<const bf16x4 *>(a.km + base + c);
-                const bf16x4 vm4 = *reinterpret_cast<const bf16x4 *>(a.vm + base + c);
+                if constexpr (ENTRIES) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float dkv = dka[db][4 * i4 + u], dvv = dva[db][4 * i4 + u];
-                    k4[u] = f2bf(dkv);
-                    v4[u] = f2bf(dvv);
-                    part += dkv * bf2f(km4[u]) + dvv * bf2f(vm4[u]);
+                    for (int u = 0; u < 4; ++u) {
+                        k4[u] = f2bf(dka[db][4 * i4 + u]);
+                        v4[u] = f2bf(dva[db][4 * i4 + u]);
+                    }
+                } else {
+                    const bf16x4 km4 = *reinterpret_cast<const bf16x4 *>(a.km + base + c);
+                    const bf16x4 vm4 = *reinterpret_cast<const bf16x4 *>(a.vm + base + c);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float dkv = dka[db][4 * i4 + u], dvv = dva[db][4 * i4 + u];
+                        k4[u] = f2bf(dkv);
+                        v4[u] = f2bf(dvv);
+                        part += dkv * bf2f(km4[u]) + dvv * bf2f(vm4[u]);
+                    }
                 }
                 *reinterpret_cast<bf16x4 *>(dk + base + c) = k4;
                 *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
             }
     }
-    part = wave_sum(part);
-    if (lane == 0) red[w] = part;
-    __syncthreads();
-    if (tid == 0) ds_part[(b * a.H + h) * nkt + kt] = red[0] + red[1] + red[2] + red[3];
+    if constexpr (!ENTRIES) {
+        part = wave_sum(part);
+        if (lane == 0) red[w] = part;
+        __syncthreads();
+        if (tid == 0) ds_part[(b * a.H + h) * nkt + kt] = red[0] + red[1] + red[2] + red[3];
+    }
 }
 
 // Query-stationary pass: each wave owns 32 queries; key tiles of KT in the
@@ -772,7 +785,7 @@ int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
 template <int DH>
 static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, const float *lse,
                               void *dq, void *dk, void *dv, const BwdWorkspace &ws, int64_t rows,
-                              unsigned nwg, hipStream_t s)
+                              unsigned nwg, bool entries, hipStream_t s)
 {
     {
         const unsigned pre_blocks = (unsigned)((rows * (DH / 16) + 255) / 256);
@@ -783,9 +796,14 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
     }
     {
         prof::Scope ts("attn_bwd_dkdv", s);
-        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST>), dim3(nwg), dim3(256), 0, s, a, dO,
-                           ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk), static_cast<bf16 *>(dv),
-                           ws.ds_part);
+        if (entries)
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256), 0, s,
+                               a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
+                               static_cast<bf16 *>(dv), ws.ds_part);
+        else
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256), 0,
+                               s, a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
+                               static_cast<bf16 *>(dv), ws.ds_part);
     }
     prof::Scope ts("attn_bwd_dq", s);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a, dO,
@@ -795,7 +813,7 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const void *km, const void *vm, const float *gate, const void *o,
                           const float *lse, const void *dO, void *dq, void *dk, void *dv,
-                          const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
+                          const BwdWorkspace &ws, const float2 *rope, bool entries, hipStream_t s)
 {
     (void)gate;
     const AttnArgs a = make_args(g, q, ws.q_rot, kx, vx, km, vm, rope);
@@ -804,9 +822,9 @@ void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const vo
     const bf16 *ob = static_cast<const bf16 *>(o);
     const bf16 *dOb = static_cast<const bf16 *>(dO);
     if (g.Dh == 128)
-        launch_attn_bwd_t<128>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, s);
+        launch_attn_bwd_t<128>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, entries, s);
     else
-        launch_attn_bwd_t<64>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, s);
+        launch_attn_bwd_t<64>(a, ob, dOb, lse, dq, dk, dv, ws, rows, nwg, entries, s);
 }
 
 }  // namespace mfma

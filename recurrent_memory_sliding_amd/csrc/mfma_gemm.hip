@@ -13,7 +13,8 @@
 // with the gfx950 transpose read ds_read_b64_tr_b16, so no operand is ever
 // transposed in memory. Shifts and zero rows are folded into the row
 // pointers; the sigma gate is folded into a pre-scaled weight copy (dX) or the
-// epilogue (dW).
+// epilogue (dW). The gated form hands over gradients that already carry its
+// gates and norm (no gate: s = 1).
 #include "common.hpp"
 #include "mfma_kernels.hpp"
 #include "profile.hpp"
@@ -453,7 +454,8 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
     }
 }
 
-// s_h-scaled copy of [W_Km; W_Vm] (bf16), 8 elements per thread.
+// s_h-scaled copy of [W_Km; W_Vm] (bf16; a plain copy when gate is null),
+// 8 elements per thread.
 __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate, bf16 *out,
                               int HD, int Dh, int d)
 {
@@ -463,7 +465,7 @@ __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate,
     const bool second = i >= per;
     const int64_t j = second ? i - per : i;
     const int r = (int)((j * 8) / d);
-    const float sg = gate_sigmoid(gate[r / Dh]);
+    const float sg = gate ? gate_sigmoid(gate[r / Dh]) : 1.0f;
     float x[8];
     load8((second ? wv : wk) + j * 8, x);
 #pragma unroll
@@ -471,12 +473,11 @@ __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate,
     store8(out + i * 8, x);
 }
 
-// dW = s_h * (sum over splits, fixed order, minus the sequence-boundary pairs
-// G[bT]^T m'[bT-1], b = 1..B-1), optionally added to the output.
-// dW = s_h (sum of the split partials - boundary pairs), 8 columns a thread:
-// the boundary pairs are G[bT]^T m'[bT-1] for b = 1 .. B-1 (the shifted
+// dW = s_h (sum of the split partials in fixed order - boundary pairs),
+// optionally added to the output, 8 columns a thread (s_h = 1 when gate is
+// null). The boundary pairs are G[bT]^T m'[bT-1] for b = 1 .. B-1: the shifted
 // product pairs the first token of a sequence with the last memory row of the
-// previous one).
+// previous one.
 __global__ __launch_bounds__(256) void dw_reduce(const float *part, int ksplit, int HD, int Dh,
                                                  int d, int64_t B, int64_t T, const bf16 *dk,
                                                  const bf16 *dv, const bf16 *m,
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(256) void dw_reduce(const float *part, int ksplit, 
 #pragma unroll
         for (int u = 0; u < 8; ++u) x[u] -= gv * y[u];
     }
-    const float sg = gate_sigmoid(gate[rr / Dh]);
+    const float sg = gate ? gate_sigmoid(gate[rr / Dh]) : 1.0f;
     float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d + e;
     if (acc) load8(out, y);
 #pragma unroll

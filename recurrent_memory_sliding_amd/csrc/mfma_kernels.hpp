@@ -17,16 +17,20 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const vo
                           const float2 *rope, void *o, float *lse, hipStream_t s);
 
 // Attention backward: rowsum(dO*O), key-stationary dK/dV pass (with the gate
-// partials), query-stationary dQ pass.
+// partials), query-stationary dQ pass. entries = true: dk/dv receive the
+// gradients of the mixed entries (rotated frame) and no gate partials.
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const void *km, const void *vm, const float *gate, const void *o,
                           const float *lse, const void *dO, void *dq, void *dk, void *dv,
-                          const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+                          const BwdWorkspace &ws, const float2 *rope, bool entries,
+                          hipStream_t s);
 
 // Number of gate partials per (b, h) the dK/dV pass writes.
 int64_t ds_part_per_bh(const Geom &g);
 
-// Projection backward: dm' (shifted back) and dW_Km/dW_Vm (split-K, fixed-order reduction).
+// Projection backward: dm' (shifted back) and dW_Km/dW_Vm (split-K, fixed-order
+// reduction). gate == nullptr: the gradients dk/dv are those of the projected
+// memory itself (no per-head sigma factor).
 void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const void *m_prime,
                           const void *wk, const void *wv, const float *gate, float *dm_prime,
                           float *dWk, float *dWv, unsigned acc, const BwdWorkspace &ws,

@@ -69,7 +69,7 @@ struct DmB {
     __device__ float operator()(int64_t r, int64_t e) const
     {
         const int rr = (int)(r < HD ? r : r - HD);
-        const float s = gate_sigmoid(gate[rr / Dh]);
+        const float s = gate ? gate_sigmoid(gate[rr / Dh]) : 1.0f;
         return s * (r < HD ? to_f<T>(wk[r * d + e]) : to_f<T>(wv[rr * (int64_t)d + e]));
     }
 };
@@ -104,7 +104,7 @@ struct DwStore {
     __device__ void operator()(int64_t r, int64_t e, float x) const
     {
         const int rr = (int)(r < HD ? r : r - HD);
-        x *= gate_sigmoid(gate[rr / Dh]);
+        if (gate) x *= gate_sigmoid(gate[rr / Dh]);
         float *p = (r < HD ? wk : wv) + (int64_t)rr * d + e;
         *p = acc ? *p + x : x;
     }
@@ -187,7 +187,7 @@ void mix_launch(const Geom &g, const void *k, const void *v, const void *km, con
                        static_cast<T *>(kx), static_cast<T *>(vx));
 }
 
-template <typename T, int DH>
+template <typename T, int DH, bool ENTRIES = false>
 void attn_bwd_simt(const Geom &g, const void *q, const void *kx, const void *vx, const void *km,
                    const void *vm, const float *gate, const void *o, const float *lse,
                    const void *dO, void *dq, void *dk, void *dv, const BwdWorkspace &ws,
@@ -201,7 +201,7 @@ void attn_bwd_simt(const Geom &g, const void *q, const void *kx, const void *vx,
                        static_cast<const T *>(q), static_cast<const T *>(kx),
                        static_cast<const T *>(vx), static_cast<const T *>(dO), lse, ws.D,
                        static_cast<T *>(dq));
-    hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH>), grid, dim3(DH), 0, s, a,
+    hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH, ENTRIES>), grid, dim3(DH), 0, s, a,
                        static_cast<const T *>(q), static_cast<const T *>(kx),
                        static_cast<const T *>(vx), static_cast<const T *>(km),
                        static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
@@ -269,7 +269,7 @@ hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kx, const v
     return hipGetLastError();
 }
 
-size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base)
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, bool gated)
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     const size_t esz = g.dtype == MAGLEV_BF16 ? 2 : 4;
@@ -287,6 +287,15 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base)
     const size_t npad = g.dtype == MAGLEV_BF16 ? (size_t)g.B * g.H * L->Tp : 0;
     const size_t oL = off; off = align(off + npad * sizeof(float));
     const size_t oDp = off; off = align(off + npad * sizeof(float));
+    const size_t nact = gated ? (size_t)g.N() * g.HD() : 0;
+    const size_t oKp = off; off = align(off + nact * esz);
+    const size_t oVm = off; off = align(off + nact * esz);
+    L->g_rows = L->g_blocks = 0;
+    if (gated) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
+    const size_t oG = off; off = align(off + (size_t)L->g_blocks * 4 * g.HD() * sizeof(float));
+    L->dkp = base && gated ? static_cast<void *>(base + oKp) : nullptr;
+    L->dvm = base && gated ? static_cast<void *>(base + oVm) : nullptr;
+    L->gpart = base && gated ? reinterpret_cast<float *>(base + oG) : nullptr;
     L->D = base ? reinterpret_cast<float *>(base + oD) : nullptr;
     L->ds_part = base ? reinterpret_cast<float *>(base + oS) : nullptr;
     L->W_scaled = base ? static_cast<void *>(base + oW) : nullptr;
@@ -317,7 +326,8 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *
     }
     int64_t per_bh;
     if (g.dtype == MAGLEV_BF16) {
-        mfma::launch_attn_bwd_bf16(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope,
+                                   false, s);
         per_bh = mfma::ds_part_per_bh(g);
     } else {
         if (g.Dh == 128)
@@ -339,6 +349,53 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *
         mfma::launch_proj_bwd_bf16(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, ws, s);
     else
         proj_bwd_simt<float>(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kx, const void *vx,
+                            const void *k, const void *v, const void *kp, const void *vm,
+                            const float *gates, float eps, const void *o, const float *lse,
+                            const void *dO, const void *m_prime, const void *wk, const void *wv,
+                            void *dq, void *dk, void *dv, float *dm_prime, float *dWk, float *dWv,
+                            float *dgates, unsigned acc, const BwdWorkspace &ws,
+                            const float2 *rope, hipStream_t s)
+{
+    const int HD = g.HD();
+    if (g.N() == 0) {
+        const int64_t nw = (int64_t)HD * g.d;
+        if (!(acc & 2u)) {
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWk, nw);
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWv, nw);
+        }
+        if (!(acc & 4u))
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((4 * HD + 255) / 256)), dim3(256), 0, s,
+                               dgates, (int64_t)4 * HD);
+        return hipGetLastError();
+    }
+    // 1. attention backward: dq, and the gradients of the mixed entries into dk/dv
+    if (g.dtype == MAGLEV_BF16) {
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk, dv,
+                                   ws, rope, true, s);
+    } else if (g.Dh == 128) {
+        attn_bwd_simt<float, 128, true>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk,
+                                        dv, ws, rope, s);
+    } else {
+        attn_bwd_simt<float, 64, true>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk,
+                                       dv, ws, rope, s);
+    }
+    // 2. gates, rotation and norm backward: dk, dv final; gradients of the projection
+    hipError_t e = launch_gated_mix_bwd(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+    if (e != hipSuccess) return e;
+    // 3. shift and projection backward (no further gate factor)
+    if (!(acc & 1u) && g.dtype != MAGLEV_BF16) {
+        prof::Scope ts("zero_last_rows", s);
+        hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
+    }
+    if (g.dtype == MAGLEV_BF16)
+        mfma::launch_proj_bwd_bf16(g, ws.dkp, ws.dvm, m_prime, wk, wv, nullptr, dm_prime, dWk, dWv,
+                                   acc, ws, s);
+    else
+        proj_bwd_simt<float>(g, ws.dkp, ws.dvm, m_prime, wk, wv, nullptr, dm_prime, dWk, dWv, acc, s);
     return hipGetLastError();
 }
 

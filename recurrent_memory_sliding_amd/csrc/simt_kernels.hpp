@@ -163,7 +163,8 @@ __global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T
 //   dk~_j = scale sum_i dS_ij q^_i, dv~_j = sum_i P_ij dO_i,
 //   dk_j = R_j^T dk~_j, dv_j = dv~_j,
 //   ds_part[b,h,j] = <kmem_j, dk_j> + <vmem_j, dv_j>  (d loss / d s_h, this key).
-template <typename T, int DH>
+// ENTRIES: write dk~_j itself (rotated frame) and dv~_j, no gate partial.
+template <typename T, int DH, bool ENTRIES>
 __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const T *kx,
                                                      const T *vx, const T *km, const T *vm,
                                                      const T *dO, const float *lse, const float *D,
@@ -189,6 +190,11 @@ __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const
         const float ds = p * (dp - D[(b * a.H + h) * a.T + i]);
         acck += ds * qh;
         accv += p * dOi;
+    }
+    if constexpr (ENTRIES) {
+        dk[krow * DH + c] = from_f<T>(acck * a.scale);
+        dv[krow * DH + c] = from_f<T>(accv);
+        return;
     }
     dkt[c] = acck * a.scale;
     __syncthreads();

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
-              "maglev_decode_step", "maglev_consistency_loss"]:
+              "maglev_decode_step", "maglev_consistency_loss", "maglev_mem_project_gated",
+              "maglev_swa_inject_bwd_gated", "maglev_decode_step_gated"]:
         assert n in names
 
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.maglev_abi_version() == 3
+    assert L.maglev_abi_version() == 4
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
     assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
     assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
@@ -159,6 +160,69 @@ def test_decode_validation(L):
     assert step(args(Bs=0), stride=20 * 10 * 128) == OK
     assert L.maglev_decode_advance(5, None, None) == INVALID
     assert L.maglev_decode_advance(0, FAKE, None) == OK
+
+
+# ---- gated form -------------------------------------------------------------
+def project_gated(L, g, shift=1, eps=1e-6, ptrs=None, gates=FAKE):
+    p = ptrs or [FAKE] * 5            # m W_Km W_Vm k v
+    out = [FAKE] * 4                  # kproj vmem kmix vmix
+    return L.maglev_mem_project_gated(ctypes.byref(g) if g is not None else None, shift, *p,
+                                      gates, eps, *out, None)
+
+
+def test_gated_projection_validation(L):
+    assert project_gated(L, None) == INVALID
+    assert project_gated(L, geom(), shift=3) == INVALID
+    assert project_gated(L, geom(), gates=None) == INVALID
+    assert project_gated(L, geom(), eps=-1.0) == INVALID
+    assert project_gated(L, geom(), eps=float("nan")) == INVALID
+    assert project_gated(L, geom(), eps=float("inf")) == INVALID
+    assert project_gated(L, geom(H=40, Dh=128)) == UNSUPPORTED     # H*Dh above 4096
+    assert project_gated(L, geom(Dh=96)) == UNSUPPORTED
+    bad = [FAKE] * 5; bad[3] = None                                   # k
+    assert project_gated(L, geom(), ptrs=bad) == INVALID
+    bad = [FAKE] * 5; bad[4] = FAKE_ODD                               # v
+    assert project_gated(L, geom(), ptrs=bad) == MISALIGNED
+    assert project_gated(L, geom(B=0)) == OK                          # empty: nothing read
+
+
+def test_gated_backward_workspace_and_validation(L):
+    g = geom(B=8, T=2048, H=10, Dh=128, d=1280, W=512)
+    base = L.maglev_swa_inject_bwd_workspace(ctypes.byref(g))
+    need = L.maglev_swa_inject_bwd_gated_workspace(ctypes.byref(g))
+    # the two projection gradients (bf16) and the gate partials come on top
+    assert need >= base + 2 * 8 * 2048 * 1280 * 2 + 4 * 1280 * 4
+    assert L.maglev_swa_inject_bwd_gated_workspace(ctypes.byref(geom(H=40))) == 0
+    head = [FAKE] * 8                 # q kmix vmix k v kproj vmem gates
+    tail = [FAKE] * 13                # o lse dO m' W_Km W_Vm dq dk dv dm' dWk dWv dgates
+    call = lambda g, h=head, eps=1e-6, t=tail, acc=0, ws=FAKE, n=need: \
+        L.maglev_swa_inject_bwd_gated(ctypes.byref(g), *h, eps, *t, acc, ws, n, None)
+    assert call(g, ws=None) == WORKSPACE
+    assert call(g, n=need - 1) == WORKSPACE
+    assert call(g, acc=8) == INVALID
+    assert call(g, eps=-1e-3) == INVALID
+    bad = list(head); bad[7] = None   # gates
+    assert call(g, h=bad) == INVALID
+    bad = list(tail); bad[12] = None  # dgates
+    assert call(g, t=bad) == INVALID
+    bad = list(tail); bad[7] = FAKE_ODD  # dk
+    assert call(g, t=bad) == MISALIGNED
+
+
+def test_gated_decode_validation(L):
+    head = [FAKE] * 5                 # q k v kproj vmem
+    tail = [FAKE] * 4                 # kcache vcache pos o
+    a = lambda **kw: [kw.get("Bs", 64), 10, kw.get("Dh", 128), kw.get("W", 512), 1e4, 0.0,
+                      kw.get("dtype", 1)]
+    step = lambda args, stride=0, gates=FAKE, eps=1e-6, t=tail: L.maglev_decode_step_gated(
+        *args, *head, stride, gates, eps, *t, FAKE, 0, None)
+    assert step(a(Dh=48)) == UNSUPPORTED
+    assert step(a(), gates=None) == INVALID
+    assert step(a(), eps=-1.0) == INVALID
+    assert step(a(), stride=10 * 128 - 8) == INVALID
+    bad = list(tail); bad[2] = None   # pos
+    assert step(a(), t=bad) == INVALID
+    assert step(a(Bs=0)) == OK
 
 
 def test_prepare_validation(L):
