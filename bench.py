@@ -68,11 +68,12 @@ def decode_bytes(sh: wl.DecodeShape) -> float:
     return float(per_layer * sh.layers)
 
 
-def kernel_work(sh: wl.LayerShape) -> dict:
+def kernel_work(sh: wl.LayerShape, mix: str = "sigma") -> dict:
     """Algorithmic work of one launch of each kernel of the training step:
     {timing name: (FLOPs, HBM bytes)}. FLOPs count in-window pairs and the
     projection products only; bytes count each tensor the kernel must read or
-    write once (bf16 activations, fp32 lse/D/gradients)."""
+    write once (bf16 activations, fp32 lse/D/gradients). mix = "gated": the
+    gated form's kernels (dK/dV then writes the entry gradients only)."""
     T, W, B, H, Dh, d = sh.T, sh.W, sh.B, sh.H, sh.Dh, sh.d
     N, HD = B * T, H * Dh
     pairs = sum(min(i + 1, W) for i in range(T))
@@ -83,17 +84,35 @@ def kernel_work(sh: wl.LayerShape) -> dict:
     mem = 2.0 * N * d                        # one bf16 [B,T,d] tensor
     wts = 2.0 * 2 * HD * d                   # W_Km and W_Vm, bf16
     f32nd = 4.0 * N * d
+    gblocks = max(1, -(-N // max(8, -(-N // 512))))
+    gpart = 4.0 * gblocks * 4 * HD                         # fp32 gate partials
+    if mix == "gated":
+        return {
+            "proj_fwd": (proj, mem + wts + 2 * act),
+            "gated_mix": (0.0, 6 * act),                       # k v kp vm -> kmix vmix
+            "attn_fwd": (2 * attn, 4 * act + rowf),
+            "attn_bwd_prep": (0.0, 4 * act + 3 * rowf),
+            "attn_bwd_dkdv": (3 * attn, 6 * act + 2 * rowf),   # q^ dO kmix vmix -> dk~ dv~
+            "attn_bwd_dq": (attn, 5 * act + 2 * rowf),
+            "gated_mix_bwd": (0.0, 10 * act + gpart),          # dk~ dv~ k v kp vm -> dk dv dkp dvm
+            "gate_grad_reduce": (0.0, gpart + 2 * 4.0 * 4 * HD),
+            "proj_bwd_scale_w": (0.0, 2 * wts),
+            "proj_bwd_dm": (proj, 2 * act + wts + f32nd),
+            "proj_bwd_dw": (proj, 2 * act + mem),
+            "proj_bwd_dw_reduce": (0.0, 4.0 * 2 * HD * d * 2),
+            "loss_partial": (0.0, 2 * mem + f32nd + 2 * f32nd),
+        }
     return {
         "proj_fwd": (proj, mem + wts + 2 * act),
         "mix": (0.0, 6 * act),                                  # k v kmem vmem -> kmix vmix
         "attn_fwd": (2 * attn, 4 * act + rowf),                 # q kmix vmix -> o, lse
         "attn_bwd_prep": (0.0, 4 * act + 3 * rowf),             # o dO q lse -> D, qr, lse2
-        "attn_bwd_dkdv": (3 * attn, 8 * act + 2 * rowf + 4.0 * B * H * ((T + 127) // 128)),
+        "attn_bwd_dkdv": (3 * attn, 6 * act + 2 * rowf),       # q^ dO kmix vmix -> dk dv
         "attn_bwd_dq": (attn, 5 * act + 2 * rowf),              # q dO kmix vmix -> dq
         "proj_bwd_scale_w": (0.0, 2 * wts),
         "proj_bwd_dm": (proj, 2 * act + wts + f32nd),           # dk dv Ws -> dm'
         "proj_bwd_dw": (proj, 2 * act + mem),                   # partials counted separately
-        "proj_bwd_dw_reduce": (0.0, 4.0 * 2 * HD * d * 2),
+        "proj_bwd_dw_reduce": (0.0, 4.0 * 2 * HD * d * 2 + wts),  # G -> dW, row dots with W
         "loss_partial": (0.0, 2 * mem + f32nd + 2 * f32nd),     # m m' -> dm, dm' +=
     }
 
@@ -101,9 +120,17 @@ def kernel_work(sh: wl.LayerShape) -> dict:
 CALL_KERNELS = {
     "maglev_mem_project": ("proj_fwd", "mix"),
     "maglev_swa_inject_fwd": ("attn_fwd",),
-    "maglev_swa_inject_bwd": ("attn_bwd_rowdot", "attn_bwd_dkdv", "attn_bwd_dq", "dgate_reduce",
+    "maglev_swa_inject_bwd": ("attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "dgate_reduce",
                               "zero_last_rows", "proj_bwd_scale_w", "proj_bwd_dm", "proj_bwd_dw",
                               "proj_bwd_dw_reduce"),
+    "maglev_consistency_loss": ("loss_partial", "loss_final"),
+}
+CALL_KERNELS_GATED = {
+    "maglev_mem_project_gated": ("proj_fwd", "gated_mix"),
+    "maglev_swa_inject_fwd": ("attn_fwd",),
+    "maglev_swa_inject_bwd_gated": ("attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq",
+                                    "gated_mix_bwd", "gate_grad_reduce", "proj_bwd_scale_w",
+                                    "proj_bwd_dm", "proj_bwd_dw", "proj_bwd_dw_reduce"),
     "maglev_consistency_loss": ("loss_partial", "loss_final"),
 }
 
@@ -140,9 +167,12 @@ def measured_traffic(kernel):
     return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
 
 
-def train_setup(sh, seed=2):
+def train_setup(sh, seed=2, mix="sigma"):
     inp = wl.layer_inputs(sh, seed, grads=True)
     g = {k: v.cuda() for k, v in inp.items()}
+    if mix == "gated":
+        gv = wl.gate_vectors(sh.H, sh.Dh, seed)
+        g["gates"] = torch.stack([gv[n] for n in rms.GATE_NAMES]).float().cuda()
     dev = "cuda"
     B, T, H, Dh, d = sh.B, sh.T, sh.H, sh.Dh, sh.d
     bf = torch.bfloat16
@@ -166,12 +196,35 @@ def train_setup(sh, seed=2):
             "dgate": torch.empty((H,), dtype=f32, device=dev),
         },
     }
-    buf["ws_bwd"] = torch.empty((rms.maglev_swa_inject_bwd_workspace(B, T, H, Dh, d, sh.W),),
-                                dtype=torch.uint8, device=dev)
+    wsq = (rms.maglev_swa_inject_bwd_gated_workspace if mix == "gated"
+           else rms.maglev_swa_inject_bwd_workspace)
+    buf["ws_bwd"] = torch.empty((wsq(B, T, H, Dh, d, sh.W),), dtype=torch.uint8, device=dev)
+    if mix == "gated":
+        del buf["grads"]["dgate"]
+        buf["grads"]["dgates"] = torch.empty((4, H * Dh), dtype=f32, device=dev)
     buf["ws_loss"] = torch.empty((rms.maglev_consistency_loss_workspace(B * T, d),),
                                  dtype=torch.uint8, device=dev)
     rms.maglev_prepare(Dh, sh.rope_base, T)
     return g, buf
+
+
+def train_step_gated(sh, g, buf):
+    """The same step with the gated form (channel-wise 2 sigmoid gates, RMSNorm
+    on the projected memory key)."""
+    rms.maglev_mem_project_gated(
+        g["m_prime"], g["W_Km"], g["W_Vm"], sh.H, sh.Dh, g["k"], g["v"], g["gates"],
+        pos0=sh.pos0, rope_base=sh.rope_base, kproj=buf["km"], vmem=buf["vm"], kmix=buf["kx"],
+        vmix=buf["vx"])
+    rms.maglev_swa_inject_fwd(
+        g["q"], buf["kx"], buf["vx"], sh.W, pos0=sh.pos0, rope_base=sh.rope_base, d=sh.d,
+        o=buf["o"], lse=buf["lse"])
+    rms.maglev_swa_inject_bwd_gated(
+        g["q"], buf["kx"], buf["vx"], g["k"], g["v"], buf["km"], buf["vm"], g["gates"], buf["o"],
+        buf["lse"], g["dO"], g["m_prime"], g["W_Km"], g["W_Vm"], sh.W, pos0=sh.pos0,
+        rope_base=sh.rope_base, accumulate=0, out=buf["grads"], workspace=buf["ws_bwd"])
+    rms.maglev_consistency_loss(
+        g["m"], g["m_prime"], sh.lam, loss=buf["loss"], dm=buf["dm"],
+        dm_prime=buf["grads"]["dm_prime"], accumulate=2, workspace=buf["ws_loss"])
 
 
 def train_step(sh, g, buf):
@@ -192,25 +245,26 @@ def train_step(sh, g, buf):
         dm_prime=buf["grads"]["dm_prime"], accumulate=2, workspace=buf["ws_loss"])
 
 
-def bench_train(sh, steps, warmup):
+def bench_train(sh, steps, warmup, mix="sigma"):
     """Wall time per step over the timed steps. Every kernel is timed with HIP
     events during the warmup steps after the first (the per-kernel table); the
     timed steps then record events around the kernel with the most time only."""
-    g, buf = train_setup(sh)
-    train_step(sh, g, buf)
+    g, buf = train_setup(sh, mix=mix)
+    step = train_step_gated if mix == "gated" else train_step
+    step(sh, g, buf)
     torch.cuda.synchronize()
     rms.maglev_profile_enable(True)
     for _ in range(max(warmup - 1, 1)):
-        train_step(sh, g, buf)
+        step(sh, g, buf)
     torch.cuda.synchronize()
     rms.maglev_profile_enable(False)
     survey = rms.maglev_profile_read()
-    work = kernel_work(sh)
+    work = kernel_work(sh, mix)
     dom = max((k for k in survey if k in work), key=lambda k: survey[k][1] / survey[k][0])
     rms.maglev_profile_enable(True, only=dom)
     t0 = time.perf_counter()
     for _ in range(steps):
-        train_step(sh, g, buf)
+        step(sh, g, buf)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     rms.maglev_profile_enable(False)
@@ -221,10 +275,14 @@ def bench_train(sh, steps, warmup):
     return ms, survey, dom, timed[dom]
 
 
-def bench_decode(sh, steps, warmup, seed=4):
+def bench_decode(sh, steps, warmup, seed=4, mix="sigma"):
     params = [wl.decode_layer_params(sh, seed, l) for l in range(sh.layers)]
     weights = [{"W_Km": p["W_Km"].cuda(), "W_Vm": p["W_Vm"].cuda(),
                 "gate_logit": p["gate_logit"].cuda()} for p in params]
+    if mix == "gated":
+        for l, w in enumerate(weights):
+            gv = wl.gate_vectors(sh.H, sh.Dh, seed * 100 + l)
+            w["gates"] = torch.stack([gv[n] for n in rms.GATE_NAMES]).float().cuda()
     kc = [p["kcache"].cuda() for p in params]
     vc = [p["vcache"].cuda() for p in params]
     pools = [(p["q_pool"].cuda(), p["k_pool"].cuda(), p["v_pool"].cuda()) for p in params]
@@ -301,6 +359,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=wl.D20_DECODE.steps)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mix", choices=("sigma", "gated"), default="sigma",
+                    help="mixing form: per-head sigma gate (default) or the gated form with "
+                         "channel-wise 2 sigmoid gates and the normalised memory key")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -315,21 +376,22 @@ def main():
     sh = wl.D20_LAYER
     flops = layer_flops(sh)
     total_flops = sum(flops.values())
-    ms, survey, dom, (n_dom, t_dom) = bench_train(sh, args.steps, args.warmup)
+    ms, survey, dom, (n_dom, t_dom) = bench_train(sh, args.steps, args.warmup, args.mix)
     tokens = sh.B * sh.T
     value = tokens / (ms / 1e3)
     path_tflops = total_flops / (ms / 1e3) / 1e12
 
     # per-kernel averages over the warmup steps; live roofline of the dominant kernel
-    work = kernel_work(sh)
+    work = kernel_work(sh, args.mix)
     per_kernel = {}
     for name, (n, tot) in sorted(survey.items(), key=lambda kv: -kv[1][1]):
         rec = {"launches": n, "avg_us": round(tot * 1e3 / n, 2)}
         if name in work:
             rec["roofline"] = roofline_of(work[name][0], work[name][1], tot / n / 1e3)
         per_kernel[name] = rec
+    call_kernels = CALL_KERNELS_GATED if args.mix == "gated" else CALL_KERNELS
     calls = {c: round(sum(survey[k][1] / survey[k][0] for k in ks if k in survey), 4)
-             for c, ks in CALL_KERNELS.items()}
+             for c, ks in call_kernels.items()}
     roofline = roofline_of(work[dom][0], work[dom][1], t_dom / n_dom / 1e3)
     roofline["traffic"] = measured_traffic(dom)
     roofline["kernel"] = dom
@@ -350,7 +412,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d) weights)",
-        "config": {"workload": "d20 decoder-P layer fwd+bwd + consistency loss",
+        "config": {"workload": "d20 decoder-P layer fwd+bwd + consistency loss"
+                               + (", gated mix (2 sigmoid channel gates, RMSNorm memory key)"
+                                  if args.mix == "gated" else ""),
+                   "mix": args.mix,
                    "B": sh.B, "T": sh.T, "W": sh.W, "d_model": sh.d, "heads": sh.H,
                    "head_dim": sh.Dh, "lambda": sh.lam, "global_batch": sh.B, "seq_len": sh.T,
                    "parallelism": "single GPU"},
@@ -362,7 +427,7 @@ def main():
     }
     if not args.no_decode:
         dsh = wl.D20_DECODE
-        dms = bench_decode(dsh, args.decode_steps, 5)
+        dms = bench_decode(dsh, args.decode_steps, 5, mix=args.mix)
         dbytes = decode_bytes(dsh)
         gbs = dbytes / (dms / 1e3) / 1e9
         result["decode"] = {

@@ -43,7 +43,8 @@ hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kmix, const
 // ---- backward --------------------------------------------------------------
 struct BwdWorkspace {
     float *D;            // [B,H,T]  rowsum(dO * O)
-    float *ds_part;      // [B,H,n_key_tiles] partial d loss / d s_h
+    float *ds_part;      // [B,H,T] per-key d loss / d s_h terms (float32 path)
+    float *rowdot;       // [2*H*Dh] <W[r,:], G[r,:]> per weight row (bf16 path)
     void *W_scaled;      // [2*H*Dh, d] dtype: s_h * [W_Km; W_Vm] (rows scaled)
     float *dW_part;      // [ksplit, 2*H*Dh, d] split-K partials (may be unused)
     void *q_rot;         // [B,T,H,Dh] dtype: rotated queries (bf16 path)

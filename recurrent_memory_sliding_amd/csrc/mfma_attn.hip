@@ -36,7 +36,7 @@ namespace mfma {
 struct AttnArgs {
     const bf16 *q;      // queries before rotation (forward)
     const bf16 *qr;     // rotated queries R q (backward)
-    const bf16 *kx, *vx, *km, *vm;
+    const bf16 *kx, *vx;
     const float2 *rope; // [pos][Dh/2] (cos, sin) or nullptr
     int64_t B, T;
     int H, W;
@@ -399,20 +399,55 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const bf16 *o, const bf16
     }
 }
 
+// acc[db][e] holds channel 32 db + 8(e/4) + 4g + e%4 of one row (g = lane/32);
+// channels c and c + DH/2 (blocks db and db + NB/2) form a rotation pair.
+// Scales by `scale` and applies R^T of the row's table cs (nullptr: no
+// rotation). The branch on cs is taken once and the table is read with
+// 16-byte loads issued together (a per-element branch would make each load
+// wait on its own).
+template <int NB>
+MAGLEV_DEV void scale_rotate_back(f32x16 *acc, const float2 *cs, int g, float scale)
+{
+    if (cs) {
+#pragma unroll
+        for (int db = 0; db < NB / 2; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float *t = reinterpret_cast<const float *>(cs + 32 * db + 8 * q + 4 * g);
+                const f32x4 t0 = *reinterpret_cast<const f32x4 *>(t);
+                const f32x4 t1 = *reinterpret_cast<const f32x4 *>(t + 4);
+                const float cx[4] = {t0[0], t0[2], t1[0], t1[2]};
+                const float sy[4] = {t0[1], t0[3], t1[1], t1[3]};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int e = 4 * q + u;
+                    const float lo = acc[db][e] * scale, hi = acc[db + NB / 2][e] * scale;
+                    acc[db][e] = lo * cx[u] + hi * sy[u];
+                    acc[db + NB / 2][e] = -lo * sy[u] + hi * cx[u];
+                }
+            }
+    } else {
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[db][e] *= scale;
+    }
+}
+
 // Key-stationary pass: each wave owns 32 keys, the workgroup 128; query tiles
 // of 32 (rotated queries Q^ and dO, with their lse and D) stream through LDS.
 // Per tile: S = Q^ K~^T, P = exp(scale S - lse), dP = dO V~^T,
 // dS = P (dP - D); dV~^T += dO^T P, dK~^T += Q^^T dS.
-// Epilogue: dk = scale R^T dK~, dv = dV~, and the gate partial
-// <kmem, dk> + <vmem, dv> summed over the workgroup's keys. With ENTRIES the
-// epilogue writes the gradients of the mixed entries themselves (scale dK~ in
-// the rotated frame, dV~) and no gate partial: the gated mixing form applies
-// its own gates, rotation and norm backward afterwards.
-template <int DH, int ST, bool ENTRIES>
+// Epilogue: dk = scale R^T dK~ and dv = dV~ (with ROTATE false: scale dK~ in
+// the rotated frame and dV~, the gradients of the mixed entries themselves,
+// which the gated mixing form takes through its own gates, rotation and norm).
+// The gate gradient of the sigma-gated form does not need this kernel: it is
+// sum_t <kmem_t, dk_t> + <vmem_t, dv_t> = <W_Km, G_k> + <W_Vm, G_v> with
+// G = sum_t [dk_t | dv_t] x_t^T, the product the dW GEMM computes anyway.
+template <int DH, int ST, bool ROTATE>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf16 *dO,
                                                              const float *lse2, const float *Dp,
-                                                             int64_t Tp, bf16 *dk, bf16 *dv,
-                                                             float *ds_part)
+                                                             int64_t Tp, bf16 *dk, bf16 *dv)
 {
     constexpr int NF = DH / 16, NB = DH / 32;
     constexpr int QT = 32;
@@ -421,7 +456,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     constexpr int PER = 2 * Dma::PER_WAVE + 1;
     __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][Q^, dO]
     __shared__ __attribute__((aligned(16))) float LD[ST][2 * QT];      // [stage][lse2, D]
-    __shared__ float red[4];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -546,57 +580,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     }
 
     // Epilogue: element e of block db is channel 32 db + 8(e/4) + 4g + e%4 of key kj.
-    float part = 0.0f;
     if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
-        const float2 *cs = (a.rope && !ENTRIES) ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
-#pragma unroll
-        for (int db = 0; db < NB / 2; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int c = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                const float lo = dka[db][e] * a.scale, hi = dka[db + NB / 2][e] * a.scale;
-                if (cs) {
-                    const float2 r = cs[c];
-                    dka[db][e] = lo * r.x + hi * r.y;
-                    dka[db + NB / 2][e] = -lo * r.y + hi * r.x;
-                } else {
-                    dka[db][e] = lo;
-                    dka[db + NB / 2][e] = hi;
-                }
-            }
+        const float2 *cs = (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
+        scale_rotate_back<NB>(dka, cs, g, a.scale);
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int c = 32 * db + 8 * i4 + 4 * g;
                 bf16x4 k4, v4;
-                if constexpr (ENTRIES) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        k4[u] = f2bf(dka[db][4 * i4 + u]);
-                        v4[u] = f2bf(dva[db][4 * i4 + u]);
-                    }
-                } else {
-                    const bf16x4 km4 = *reinterpret_cast<const bf16x4 *>(a.km + base + c);
-                    const bf16x4 vm4 = *reinterpret_cast<const bf16x4 *>(a.vm + base + c);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const float dkv = dka[db][4 * i4 + u], dvv = dva[db][4 * i4 + u];
-                        k4[u] = f2bf(dkv);
-                        v4[u] = f2bf(dvv);
-                        part += dkv * bf2f(km4[u]) + dvv * bf2f(vm4[u]);
-                    }
+                for (int u = 0; u < 4; ++u) {
+                    k4[u] = f2bf(dka[db][4 * i4 + u]);
+                    v4[u] = f2bf(dva[db][4 * i4 + u]);
                 }
                 *reinterpret_cast<bf16x4 *>(dk + base + c) = k4;
                 *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
             }
-    }
-    if constexpr (!ENTRIES) {
-        part = wave_sum(part);
-        if (lane == 0) red[w] = part;
-        __syncthreads();
-        if (tid == 0) ds_part[(b * a.H + h) * nkt + kt] = red[0] + red[1] + red[2] + red[3];
     }
 }
 
@@ -716,21 +717,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
     if (qi < T) {
         const int64_t base = act_row(a, b, qi, h) * DH;
         const float2 *cs = a.rope ? a.rope + (a.pos0 + qi) * (DH / 2) : nullptr;
-#pragma unroll
-        for (int db = 0; db < NB / 2; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int c = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                const float lo = acc[db][e] * a.scale, hi = acc[db + NB / 2][e] * a.scale;
-                if (cs) {
-                    const float2 r = cs[c];
-                    acc[db][e] = lo * r.x + hi * r.y;
-                    acc[db + NB / 2][e] = -lo * r.y + hi * r.x;
-                } else {
-                    acc[db][e] = lo;
-                    acc[db + NB / 2][e] = hi;
-                }
-            }
+        scale_rotate_back<NB>(acc, cs, g, a.scale);
 #pragma unroll
         for (int db = 0; db < NB; ++db)
 #pragma unroll
@@ -747,15 +734,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
 // Launchers
 // ============================================================================
 static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const void *kx,
-                          const void *vx, const void *km, const void *vm, const float2 *rope)
+                          const void *vx, const float2 *rope)
 {
     AttnArgs a;
     a.q = static_cast<const bf16 *>(q);
     a.qr = static_cast<const bf16 *>(qr);
     a.kx = static_cast<const bf16 *>(kx);
     a.vx = static_cast<const bf16 *>(vx);
-    a.km = static_cast<const bf16 *>(km);
-    a.vm = static_cast<const bf16 *>(vm);
     a.rope = rope;
     a.B = g.B; a.T = g.T; a.H = g.H; a.W = g.W; a.pos0 = g.pos0; a.scale = g.scale;
     return a;
@@ -769,7 +754,7 @@ constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4;
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)
 {
-    const AttnArgs a = make_args(g, q, nullptr, kx, vx, nullptr, nullptr, rope);
+    const AttnArgs a = make_args(g, q, nullptr, kx, vx, rope);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     prof::Scope ts("attn_fwd", s);
     if (g.Dh == 128)
@@ -779,8 +764,6 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const vo
         hipLaunchKernelGGL((attn_fwd_kernel<64, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s, a,
                            static_cast<bf16 *>(o), lse);
 }
-
-int64_t ds_part_per_bh(const Geom &g) { return (g.T + 127) / 128; }
 
 template <int DH>
 static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, const float *lse,
@@ -797,13 +780,13 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
     {
         prof::Scope ts("attn_bwd_dkdv", s);
         if (entries)
-            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256), 0, s,
-                               a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
-                               static_cast<bf16 *>(dv), ws.ds_part);
-        else
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256), 0,
                                s, a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
-                               static_cast<bf16 *>(dv), ws.ds_part);
+                               static_cast<bf16 *>(dv));
+        else
+            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256), 0, s,
+                               a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
+                               static_cast<bf16 *>(dv));
     }
     prof::Scope ts("attn_bwd_dq", s);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a, dO,
@@ -811,12 +794,11 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
 }
 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
-                          const void *km, const void *vm, const float *gate, const void *o,
-                          const float *lse, const void *dO, void *dq, void *dk, void *dv,
-                          const BwdWorkspace &ws, const float2 *rope, bool entries, hipStream_t s)
+                          const void *o, const float *lse, const void *dO, void *dq, void *dk,
+                          void *dv, const BwdWorkspace &ws, const float2 *rope, bool entries,
+                          hipStream_t s)
 {
-    (void)gate;
-    const AttnArgs a = make_args(g, q, ws.q_rot, kx, vx, km, vm, rope);
+    const AttnArgs a = make_args(g, q, ws.q_rot, kx, vx, rope);
     const int64_t rows = g.N() * g.H;
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
     const bf16 *ob = static_cast<const bf16 *>(o);

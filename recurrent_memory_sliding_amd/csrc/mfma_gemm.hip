@@ -473,43 +473,63 @@ __global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate,
     store8(out + i * 8, x);
 }
 
-// dW = s_h (sum of the split partials in fixed order - boundary pairs),
-// optionally added to the output, 8 columns a thread (s_h = 1 when gate is
-// null). The boundary pairs are G[bT]^T m'[bT-1] for b = 1 .. B-1: the shifted
+// One workgroup per row r of [dW_Km; dW_Vm], 8 columns a thread:
+//   G[r,:] = sum of the split partials (fixed order) - boundary pairs,
+//   dW[r,:] (+)= s_h G[r,:]   (s_h = 1 when gate is null),
+//   rowdot[r] = <W[r,:], G[r,:]>  when rowdot is not null.
+// The boundary pairs are G[bT]^T m'[bT-1] for b = 1 .. B-1: the shifted
 // product pairs the first token of a sequence with the last memory row of the
-// previous one.
+// previous one. rowdot is the row's share of the sigma gate's gradient:
+// sum_t <kmem_t, dk_t> = sum_t <W_Km x_t, dk_t> = <W_Km, sum_t dk_t x_t^T>.
 __global__ __launch_bounds__(256) void dw_reduce(const float *part, int ksplit, int HD, int Dh,
                                                  int d, int64_t B, int64_t T, const bf16 *dk,
-                                                 const bf16 *dv, const bf16 *m,
-                                                 const float *gate, float *dwk, float *dwv,
-                                                 bool acc)
+                                                 const bf16 *dv, const bf16 *m, const bf16 *wk,
+                                                 const bf16 *wv, const float *gate, float *dwk,
+                                                 float *dwv, float *rowdot, bool acc)
 {
-    const int64_t i8 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ float red[4];
+    const int r = blockIdx.x;
     const int64_t tot = 2 * (int64_t)HD * d;
-    if (i8 * 8 >= tot) return;
-    const int64_t i = i8 * 8;
-    const int64_t r = i / d, e = i % d;   // d is a multiple of 16: the 8 columns share row r
-    float x[8], y[8];
-    load8(part + i, x);
-    for (int sp = 1; sp < ksplit; ++sp) {
-        load8(part + sp * tot + i, y);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] += y[u];
-    }
-    const int rr = (int)(r < HD ? r : r - HD);
+    const int rr = r < HD ? r : r - HD;
     const bf16 *G = r < HD ? dk : dv;
-    for (int64_t b = 1; b < B; ++b) {
-        const float gv = bf2f(G[(b * T) * HD + rr]);
-        load8(m + (b * T - 1) * d + e, y);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] -= gv * y[u];
-    }
+    const bf16 *Wr = (r < HD ? wk : wv) + (int64_t)rr * d;
+    float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d;
     const float sg = gate ? gate_sigmoid(gate[rr / Dh]) : 1.0f;
-    float *out = (r < HD ? dwk : dwv) + (int64_t)rr * d + e;
-    if (acc) load8(out, y);
+    float dot = 0.0f;
+    for (int e = threadIdx.x * 8; e < d; e += blockDim.x * 8) {   // d is a multiple of 16
+        const int64_t i = (int64_t)r * d + e;
+        float x[8], y[8];
+        load8(part + i, x);
+        for (int sp = 1; sp < ksplit; ++sp) {
+            load8(part + sp * tot + i, y);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = acc ? y[u] + x[u] * sg : x[u] * sg;
-    store8(out, x);
+            for (int u = 0; u < 8; ++u) x[u] += y[u];
+        }
+        for (int64_t b = 1; b < B; ++b) {
+            const float gv = bf2f(G[(b * T) * HD + rr]);
+            load8(m + (b * T - 1) * d + e, y);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] -= gv * y[u];
+        }
+        if (rowdot) {
+            load8(Wr + e, y);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dot += y[u] * x[u];
+        }
+        if (acc) load8(out + e, y);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = acc ? y[u] + x[u] * sg : x[u] * sg;
+        store8(out + e, x);
+    }
+    if (!rowdot) return;
+    dot = wave_sum(dot);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+        rowdot[r] = t;
+    }
 }
 
 int dw_ksplit(const Geom &g)
@@ -567,11 +587,12 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         int64_t kper = (p.K + ks - 1) / ks;
         kper = (kper + 63) / 64 * 64;
         run_gemm<DwCfg>(p, ks, kper, s, "proj_bwd_dw", 1 << 20);
-        const int64_t tot8 = 2 * (int64_t)HD * g.d / 8;
+        const int per_row = (g.d / 8 + 63) / 64 * 64;
         prof::Scope ts("proj_bwd_dw_reduce", s);
-        hipLaunchKernelGGL(dw_reduce, dim3((unsigned)((tot8 + 255) / 256)), dim3(256), 0, s,
-                           ws.dW_part, ks, HD, g.Dh, g.d, g.B, g.T, p.dk, p.dv, p.m, gate, dWk,
-                           dWv, (acc & 2u) != 0);
+        hipLaunchKernelGGL(dw_reduce, dim3((unsigned)(2 * HD)), dim3(per_row < 256 ? per_row : 256),
+                           0, s, ws.dW_part, ks, HD, g.Dh, g.d, g.B, g.T, p.dk, p.dv, p.m,
+                           static_cast<const bf16 *>(wk), static_cast<const bf16 *>(wv), gate, dWk,
+                           dWv, gate ? ws.rowdot : nullptr, (acc & 2u) != 0);
     }
 }
 

@@ -16,21 +16,19 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s);
 
-// Attention backward: rowsum(dO*O), key-stationary dK/dV pass (with the gate
-// partials), query-stationary dQ pass. entries = true: dk/dv receive the
-// gradients of the mixed entries (rotated frame) and no gate partials.
+// Attention backward: rotated queries and rowsum(dO*O), key-stationary dK/dV
+// pass, query-stationary dQ pass. entries = true: dk/dv receive the gradients
+// of the mixed entries (rotated frame) instead of those of k and v.
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
-                          const void *km, const void *vm, const float *gate, const void *o,
-                          const float *lse, const void *dO, void *dq, void *dk, void *dv,
-                          const BwdWorkspace &ws, const float2 *rope, bool entries,
+                          const void *o, const float *lse, const void *dO, void *dq, void *dk,
+                          void *dv, const BwdWorkspace &ws, const float2 *rope, bool entries,
                           hipStream_t s);
 
-// Number of gate partials per (b, h) the dK/dV pass writes.
-int64_t ds_part_per_bh(const Geom &g);
-
 // Projection backward: dm' (shifted back) and dW_Km/dW_Vm (split-K, fixed-order
-// reduction). gate == nullptr: the gradients dk/dv are those of the projected
-// memory itself (no per-head sigma factor).
+// reduction). With a gate it also writes ws.rowdot[r] = <W[r,:], G[r,:]>, the
+// row's share of the gate gradient (G = sum_t [dk|dv]_t x_t^T before the sigma
+// factor). gate == nullptr: dk/dv are the gradients of the projected memory
+// itself (no per-head sigma factor, no row dots).
 void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const void *m_prime,
                           const void *wk, const void *wv, const float *gate, float *dm_prime,
                           float *dWk, float *dWv, unsigned acc, const BwdWorkspace &ws,

@@ -143,6 +143,23 @@ __global__ __launch_bounds__(256) void dgate_reduce(const float *part, int64_t B
     }
 }
 
+// dgate[h] = s(1-s) * sum over the rows r of head h of rowdot[r] + rowdot[HD + r]
+// (the key and the value weight rows), summed in a fixed order. One wave per head.
+__global__ __launch_bounds__(64) void dgate_from_rows(const float *rowdot, int HD, int Dh,
+                                                      const float *gate, float *dgate,
+                                                      unsigned acc)
+{
+    const int h = blockIdx.x, lane = threadIdx.x;
+    float t = 0.0f;
+    for (int i = lane; i < Dh; i += 64) t += rowdot[h * Dh + i] + rowdot[HD + h * Dh + i];
+    t = wave_sum(t);
+    if (lane == 0) {
+        const float sg = gate_sigmoid(gate[h]);
+        const float g = sg * (1.0f - sg) * t;
+        dgate[h] = (acc & 4u) ? dgate[h] + g : g;
+    }
+}
+
 simt::RowArgs row_args(const Geom &g, const float *gate, const float2 *rope)
 {
     simt::RowArgs a;
@@ -293,6 +310,8 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, bool gate
     L->g_rows = L->g_blocks = 0;
     if (gated) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
     const size_t oG = off; off = align(off + (size_t)L->g_blocks * 4 * g.HD() * sizeof(float));
+    const size_t oR = off; off = align(off + (size_t)2 * g.HD() * sizeof(float));
+    L->rowdot = base ? reinterpret_cast<float *>(base + oR) : nullptr;
     L->dkp = base && gated ? static_cast<void *>(base + oKp) : nullptr;
     L->dvm = base && gated ? static_cast<void *>(base + oVm) : nullptr;
     L->gpart = base && gated ? reinterpret_cast<float *>(base + oG) : nullptr;
@@ -324,31 +343,30 @@ hipError_t launch_bwd(const Geom &g, const void *q, const void *kx, const void *
         if (!(acc & 4u)) hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, s, dgate, (int64_t)g.H);
         return hipGetLastError();
     }
-    int64_t per_bh;
     if (g.dtype == MAGLEV_BF16) {
-        mfma::launch_attn_bwd_bf16(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope,
-                                   false, s);
-        per_bh = mfma::ds_part_per_bh(g);
-    } else {
-        if (g.Dh == 128)
-            attn_bwd_simt<float, 128>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
-        else
-            attn_bwd_simt<float, 64>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
-        per_bh = g.T;
+        // attention, then the projection backward, whose dW reduction also
+        // gives each weight row's share <W[r,:], G[r,:]> of the gate gradient
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, false, s);
+        mfma::launch_proj_bwd_bf16(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, ws, s);
+        prof::Scope ts("dgate_reduce", s);
+        hipLaunchKernelGGL(dgate_from_rows, dim3(g.H), dim3(64), 0, s, ws.rowdot, HD, g.Dh, gate,
+                           dgate, acc);
+        return hipGetLastError();
     }
+    if (g.Dh == 128)
+        attn_bwd_simt<float, 128>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
+    else
+        attn_bwd_simt<float, 64>(g, q, kx, vx, km, vm, gate, o, lse, dO, dq, dk, dv, ws, rope, s);
     {
         prof::Scope ts("dgate_reduce", s);
-        hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, per_bh,
+        hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H, g.T,
                            gate, dgate, acc);
     }
-    if (!(acc & 1u) && g.dtype != MAGLEV_BF16) {   // the bf16 dm' GEMM writes these rows itself
+    if (!(acc & 1u)) {
         prof::Scope ts("zero_last_rows", s);
         hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
     }
-    if (g.dtype == MAGLEV_BF16)
-        mfma::launch_proj_bwd_bf16(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, ws, s);
-    else
-        proj_bwd_simt<float>(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, s);
+    proj_bwd_simt<float>(g, dk, dv, m_prime, wk, wv, gate, dm_prime, dWk, dWv, acc, s);
     return hipGetLastError();
 }
 
@@ -374,8 +392,7 @@ hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kx, const 
     }
     // 1. attention backward: dq, and the gradients of the mixed entries into dk/dv
     if (g.dtype == MAGLEV_BF16) {
-        mfma::launch_attn_bwd_bf16(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk, dv,
-                                   ws, rope, true, s);
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, true, s);
     } else if (g.Dh == 128) {
         attn_bwd_simt<float, 128, true>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk,
                                         dv, ws, rope, s);

@@ -19,14 +19,16 @@ from typing import List
 
 import torch
 
-from . import (maglev_decode_advance, maglev_decode_step, maglev_decode_workspace,
-               maglev_mem_project, maglev_prepare)
+from . import (RMS_EPS, maglev_decode_advance, maglev_decode_step, maglev_decode_step_gated,
+               maglev_decode_workspace, maglev_mem_project, maglev_prepare)
 
 
 class DecodeStack:
     """Ring caches, positions and memory of `Bs` streams through `layers` layers.
 
-    weights: per layer dict with W_Km, W_Vm [H*Dh, d] and gate_logit [H];
+    weights: per layer dict with W_Km, W_Vm [H*Dh, d] and either gate_logit [H]
+      (sigma-gated form) or gates [4, H*Dh] float32 (the gated form with the
+      normalised memory key, maglev_decode_step_gated);
     kcache/vcache: per layer [Bs, H, W, Dh] tensors (updated in place);
     pos: int64 [Bs]; m: [Bs, d] memory of the previous step.
     """
@@ -70,10 +72,17 @@ class DecodeStack:
                            kmem=self.kmem_all, vmem=self.vmem_all)
         stride = self.L * self.HD
         for l in range(self.L):
-            maglev_decode_step(q[l], k[l], v[l], self.kmem[l], self.vmem[l],
-                               self.weights[l]["gate_logit"], self.kcache[l], self.vcache[l],
-                               self.pos, o=self.out[l], rope_base=self.rope_base,
-                               workspace=self.ws, mem_stride=stride)
+            w = self.weights[l]
+            if "gates" in w:
+                maglev_decode_step_gated(q[l], k[l], v[l], self.kmem[l], self.vmem[l], w["gates"],
+                                         self.kcache[l], self.vcache[l], self.pos, o=self.out[l],
+                                         eps=w.get("eps", RMS_EPS), rope_base=self.rope_base,
+                                         workspace=self.ws, mem_stride=stride)
+            else:
+                maglev_decode_step(q[l], k[l], v[l], self.kmem[l], self.vmem[l], w["gate_logit"],
+                                   self.kcache[l], self.vcache[l], self.pos, o=self.out[l],
+                                   rope_base=self.rope_base, workspace=self.ws,
+                                   mem_stride=stride)
         maglev_decode_advance(self.pos)
 
     def step(self, q, k, v):
