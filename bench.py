@@ -313,6 +313,51 @@ def bench_decode(sh, steps, warmup, seed=4, mix="sigma"):
     return ms
 
 
+def bench_prefiller(sh, steps, warmup):
+    """Attention layers of the causal prefiller (no injection) at the layer
+    shape: a sliding-window layer (W = 512) and a full-attention layer (W = T),
+    forward (rotate keys + attention) and backward, timed with HIP events."""
+    inp = wl.layer_inputs(sh, 5, grads=True)
+    g = {n: inp[n].cuda() for n in ("q", "k", "v", "dO")}
+    B, T, H, Dh = sh.B, sh.T, sh.H, sh.Dh
+    out = {}
+    for name, W in (("sliding_window_layer", sh.W), ("full_attention_layer", T)):
+        kr = torch.empty_like(g["k"])
+        o = torch.empty_like(g["q"])
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        dq, dk, dv = (torch.empty_like(g["q"]) for _ in range(3))
+        ws = torch.empty((rms.maglev_attn_bwd_workspace(B, T, H, Dh, W),), dtype=torch.uint8,
+                         device="cuda")
+
+        def step():
+            rms.maglev_attn_fwd(g["q"], g["k"], g["v"], W, rope_base=sh.rope_base, krot=kr, o=o,
+                                lse=lse)
+            rms.maglev_attn_bwd(g["q"], kr, g["v"], o, lse, g["dO"], W, rope_base=sh.rope_base,
+                                dq=dq, dk=dk, dv=dv, workspace=ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        pairs = sum(min(i + 1, W) for i in range(T))
+        flops = 6.0 * 2.0 * pairs * Dh * B * H      # 2 forward + 4 backward contractions
+        out[name] = {"W": W, "ms_per_layer_fwd_bwd": round(ms, 4),
+                     "tokens/s": round(B * T / (ms / 1e3), 1),
+                     "algorithmic_TFLOP": round(flops / 1e12, 4),
+                     "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1),
+                     "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(sh):
     """The oracle, as it stands, on a bounded slice of the training workload:
     sequences 0-5 of 8, all heads, full T. The slice holds 6/8 of the layer's
@@ -359,6 +404,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=wl.D20_DECODE.steps)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefiller", action="store_true")
     ap.add_argument("--mix", choices=("sigma", "gated"), default="sigma",
                     help="mixing form: per-head sigma gate (default) or the gated form with "
                          "channel-wise 2 sigmoid gates and the normalised memory key")
@@ -439,6 +485,11 @@ def main():
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
             "graph": "one HIP graph per step: one projection of m_{t-1} by all layers' stacked weights, 20 decode steps, advance",
         }
+    if not args.no_prefiller:
+        result["prefiller"] = {
+            "workload": "causal prefiller attention without injection, B=8, T=2048, 10x128 "
+                        "heads, bf16: SLSL layers' sliding-window (W=512) and full (W=T) kinds",
+            **bench_prefiller(sh, max(args.steps // 2, 5), 3)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh)
     print(json.dumps(result), flush=True)

@@ -279,6 +279,34 @@ maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int3
                                          void *workspace, size_t workspace_bytes,
                                          hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Attention without injection: the layers of the causal prefiller Q, which
+ * produces the targets m' with interleaved sliding-window and full-attention
+ * layers and no memory term ([R-core], [R-step]: the SLSL pattern, window 512
+ * and full attention over the 2048 training context). A layer is
+ *   O_i = sum_{j = max(0, i-W+1)}^{i} softmax_j(scale <R_i q_i, R_j k_j>) v_j,
+ * a sliding-window layer with W = 512 and a full-attention layer with W >= T.
+ * Forward: krot = maglev_rope_keys(k), then maglev_swa_inject_fwd(q, krot, v)
+ * (the rotated keys and the plain values are the entries attended over).
+ * ------------------------------------------------------------------------- */
+
+/* krot = R_{pos0+t} k, [B,T,H,Dh] dtype (written; must not alias k).
+ * Uses g->B, T, H, Dh, pos0, rope_base, dtype. */
+maglev_status_t maglev_rope_keys(const maglev_geom_t *g, const void *k, void *krot,
+                                 hipStream_t stream);
+
+/* Bytes of device workspace maglev_attn_bwd needs (0 on invalid geometry). */
+size_t maglev_attn_bwd_workspace(const maglev_geom_t *g);
+
+/* Backward of attention without injection: from q, krot (maglev_rope_keys),
+ * v, the forward's o and lse, and dO, writes dq, dk (w.r.t. the unrotated k)
+ * and dv, all [B,T,H,Dh] dtype (overwritten). workspace: at least
+ * maglev_attn_bwd_workspace(g) bytes. g->d is not used (any valid value). */
+maglev_status_t maglev_attn_bwd(const maglev_geom_t *g, const void *q, const void *krot,
+                                const void *v, const void *o, const float *lse, const void *dO,
+                                void *dq, void *dk, void *dv, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* pos[b] += 1 for b < Bs on the device (moves every stream to its next ring
  * slot; kept separate so one decode step can be captured and replayed). */
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream);

@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
             "maglev_swa_inject_bwd_gated_workspace": ([G], sz),
             "maglev_swa_inject_bwd_gated": ([G] + [vp] * 8 + [f32] + [vp] * 13 + [u32, vp, sz, vp],
                                             i32),
+            "maglev_rope_keys": ([G, vp, vp, vp], i32),
+            "maglev_attn_bwd_workspace": ([G], sz),
+            "maglev_attn_bwd": ([G] + [vp] * 9 + [vp, sz, vp], i32),
             "maglev_decode_step_gated": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
                                          + [vp, f32] + [vp] * 4 + [vp, sz, vp], i32),
             "maglev_prepare": ([i32, f32, i64], i32),
@@ -449,6 +452,56 @@ def maglev_decode_step_gated(q, k, v, kproj, vmem, gates, kcache, vcache, pos, o
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream)), "maglev_decode_step_gated")
     return o
+
+
+# ----------------------------------------------------------------------------
+# Attention without injection (the prefiller's sliding-window and full layers)
+# ----------------------------------------------------------------------------
+def maglev_rope_keys(k, pos0: int = 0, rope_base: float = 10000.0, krot=None, stream=None):
+    """krot = R_{pos0+t} k for k [B,T,H,Dh]."""
+    _dev(k, krot)
+    _same(k, krot)
+    B, T, H, Dh = k.shape
+    krot = torch.empty_like(k) if krot is None else krot
+    g = make_geom(B, T, H, Dh, H * Dh, 1, pos0, rope_base, 0.0, _dtype_code(k))
+    _check(lib().maglev_rope_keys(ctypes.byref(g), _ptr(k), _ptr(krot), _stream(stream)),
+           "maglev_rope_keys")
+    return krot
+
+
+def maglev_attn_fwd(q, k, v, W: int, pos0: int = 0, rope_base: float = 10000.0,
+                    scale: float = 0.0, krot=None, o=None, lse=None, stream=None):
+    """Causal attention of window W without injection (W >= T: full causal).
+    Returns (o, lse, krot); krot is what the backward takes."""
+    krot = maglev_rope_keys(k, pos0, rope_base, krot=krot, stream=stream)
+    o, lse = maglev_swa_inject_fwd(q, krot, v, W, pos0=pos0, rope_base=rope_base, scale=scale,
+                                   o=o, lse=lse, stream=stream)
+    return o, lse, krot
+
+
+def maglev_attn_bwd_workspace(B, T, H, Dh, W, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, H * Dh, W, dtype=dtype)
+    return int(lib().maglev_attn_bwd_workspace(ctypes.byref(g)))
+
+
+def maglev_attn_bwd(q, krot, v, o, lse, dO, W: int, pos0: int = 0, rope_base: float = 10000.0,
+                    scale: float = 0.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of attention without injection; dk is w.r.t. the unrotated k."""
+    _dev(q, krot, v, o, lse, dO, dq, dk, dv, workspace)
+    _same(q, krot, v, o, dO, dq, dk, dv)
+    B, T, H, Dh = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    g = make_geom(B, T, H, Dh, H * Dh, W, pos0, rope_base, scale, _dtype_code(q))
+    if workspace is None:
+        need = int(lib().maglev_attn_bwd_workspace(ctypes.byref(g)))
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().maglev_attn_bwd(ctypes.byref(g), _ptr(q), _ptr(krot), _ptr(v), _ptr(o), _ptr(lse),
+                                 _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "maglev_attn_bwd")
+    return dq, dk, dv
 
 
 def maglev_decode_advance(pos, stream=None):

@@ -42,7 +42,7 @@ hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kmix, const
 
 // ---- backward --------------------------------------------------------------
 struct BwdWorkspace {
-    float *D;            // [B,H,T]  rowsum(dO * O)
+    float *D;            // [B,H,T]  rowsum(dO * O) (float32 path)
     float *ds_part;      // [B,H,T] per-key d loss / d s_h terms (float32 path)
     float *rowdot;       // [2*H*Dh] <W[r,:], G[r,:]> per weight row (bf16 path)
     void *W_scaled;      // [2*H*Dh, d] dtype: s_h * [W_Km; W_Vm] (rows scaled)
@@ -59,7 +59,10 @@ struct BwdWorkspace {
     float *gpart;        // [g_blocks][4][H*Dh] per-workgroup gate partial sums
     int g_rows, g_blocks;
 };
-size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base, bool gated);
+// Which backward the workspace serves: the sigma-gated layer path, the gated
+// layer path, or attention alone (no memory term, no projection).
+enum class BwdKind { Sigma, Gated, Attn };
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base, BwdKind kind);
 
 hipError_t launch_bwd(const Geom &g, const void *q, const void *kmix, const void *vmix,
                       const void *kmem, const void *vmem, const float *gate, const void *o,
@@ -86,6 +89,14 @@ hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kmix, cons
                             const void *W_Vm, void *dq, void *dk, void *dv, float *dm_prime,
                             float *dW_Km, float *dW_Vm, float *dgates, unsigned accumulate,
                             const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+
+// ---- attention without injection (the prefiller's layers) ------------------
+// kr = R_{pos0+t} k; the backward gives dq, dk (w.r.t. the unrotated k), dv.
+hipError_t launch_rope_keys(const Geom &g, const void *k, const float2 *rope, void *kr,
+                            hipStream_t s);
+hipError_t launch_attn_bwd(const Geom &g, const void *q, const void *kr, const void *v,
+                           const void *o, const float *lse, const void *dO, void *dq, void *dk,
+                           void *dv, const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
 
 // ---- consistency loss -------------------------------------------------------
 size_t loss_workspace_bytes(int64_t N, int d);

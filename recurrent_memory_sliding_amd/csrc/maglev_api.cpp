@@ -242,7 +242,7 @@ size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g)
     Geom G;
     if (check_geom(g, &G) != MAGLEV_OK) return 0;
     BwdWorkspace layout;
-    return bwd_workspace_bytes(G, &layout, nullptr, false);
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::Sigma);
 }
 
 maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, const void *kmix,
@@ -266,7 +266,7 @@ maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, con
     if (!gate_logit || !dgate) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit or dgate is NULL");
     if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
     BwdWorkspace layout;
-    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), false);
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::Sigma);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (workspace && !aligned16(workspace))
@@ -393,7 +393,7 @@ size_t maglev_swa_inject_bwd_gated_workspace(const maglev_geom_t *g)
     Geom G;
     if (check_geom(g, &G) != MAGLEV_OK || G.HD() > 4096) return 0;
     BwdWorkspace layout;
-    return bwd_workspace_bytes(G, &layout, nullptr, true);
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::Gated);
 }
 
 maglev_status_t maglev_swa_inject_bwd_gated(
@@ -418,7 +418,7 @@ maglev_status_t maglev_swa_inject_bwd_gated(
     if (!dgates) return fail(MAGLEV_ERR_INVALID_VALUE, "dgates is NULL");
     if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
     BwdWorkspace layout;
-    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), true);
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::Gated);
     if (G.N() > 0 && (!workspace || workspace_bytes < need))
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (workspace && !aligned16(workspace))
@@ -465,6 +465,54 @@ maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int3
     return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kproj, vmem,
                                     mem_stride, nullptr, gates, eps, kcache, vcache, pos, o,
                                     workspace, stream));
+}
+
+// ---- attention without injection ---------------------------------------------
+
+maglev_status_t maglev_rope_keys(const maglev_geom_t *g, const void *k, void *krot,
+                                 hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0) return MAGLEV_OK;
+    st = check_ptrs({k, krot});
+    if (st != MAGLEV_OK) return st;
+    if (k == krot) return fail(MAGLEV_ERR_INVALID_VALUE, "krot must not alias k");
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    return hip_status(launch_rope_keys(G, k, rope, krot, stream));
+}
+
+size_t maglev_attn_bwd_workspace(const maglev_geom_t *g)
+{
+    Geom G;
+    if (check_geom(g, &G) != MAGLEV_OK) return 0;
+    BwdWorkspace layout;
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::Attn);
+}
+
+maglev_status_t maglev_attn_bwd(const maglev_geom_t *g, const void *q, const void *krot,
+                                const void *v, const void *o, const float *lse, const void *dO,
+                                void *dq, void *dk, void *dv, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0) return MAGLEV_OK;
+    st = check_ptrs({q, krot, v, o, lse, dO, dq, dk, dv});
+    if (st != MAGLEV_OK) return st;
+    BwdWorkspace layout;
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::Attn);
+    if (!workspace || workspace_bytes < need)
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (!aligned16(workspace)) return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    return hip_status(launch_attn_bwd(G, q, krot, v, o, lse, dO, dq, dk, dv, layout, rope, stream));
 }
 
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream)

@@ -204,7 +204,9 @@ void mix_launch(const Geom &g, const void *k, const void *v, const void *km, con
                        static_cast<T *>(kx), static_cast<T *>(vx));
 }
 
-template <typename T, int DH, bool ENTRIES = false>
+// ROTATE false: dk/dv receive the gradients of the mixed entries; PARTIAL:
+// the per-key gate terms of the sigma form go to ws.ds_part (reads km, vm).
+template <typename T, int DH, bool ROTATE = true, bool PARTIAL = true>
 void attn_bwd_simt(const Geom &g, const void *q, const void *kx, const void *vx, const void *km,
                    const void *vm, const float *gate, const void *o, const float *lse,
                    const void *dO, void *dq, void *dk, void *dv, const BwdWorkspace &ws,
@@ -218,7 +220,7 @@ void attn_bwd_simt(const Geom &g, const void *q, const void *kx, const void *vx,
                        static_cast<const T *>(q), static_cast<const T *>(kx),
                        static_cast<const T *>(vx), static_cast<const T *>(dO), lse, ws.D,
                        static_cast<T *>(dq));
-    hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH, ENTRIES>), grid, dim3(DH), 0, s, a,
+    hipLaunchKernelGGL((simt::bwd_dkdv_rows<T, DH, ROTATE, PARTIAL>), grid, dim3(DH), 0, s, a,
                        static_cast<const T *>(q), static_cast<const T *>(kx),
                        static_cast<const T *>(vx), static_cast<const T *>(km),
                        static_cast<const T *>(vm), static_cast<const T *>(dO), lse, ws.D,
@@ -286,42 +288,52 @@ hipError_t launch_attn_fwd(const Geom &g, const void *q, const void *kx, const v
     return hipGetLastError();
 }
 
-size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, bool gated)
+size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind kind)
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
-    const size_t esz = g.dtype == MAGLEV_BF16 ? 2 : 4;
-    const int64_t BHT = g.B * (int64_t)g.H * g.T;
-    L->n_key_tiles = (int)((g.T + 127) / 128);
-    L->ksplit = g.dtype == MAGLEV_BF16 ? mfma::dw_ksplit(g) : 0;
+    const bool bf = g.dtype == MAGLEV_BF16;
+    const bool proj = kind != BwdKind::Attn;          // a projection backward follows
+    const bool gated = kind == BwdKind::Gated;
+    const size_t esz = bf ? 2 : 4;
+    const size_t BHT = (size_t)g.B * g.H * g.T;
+    const size_t HD = (size_t)g.HD();
     size_t off = 0;
-    const size_t oD = off; off = align(off + (size_t)BHT * sizeof(float));
-    const size_t oS = off; off = align(off + (size_t)BHT * sizeof(float));
-    const size_t oW = off; off = align(off + (size_t)2 * g.HD() * g.d * esz);
-    const size_t oP = off; off = align(off + (size_t)L->ksplit * 2 * g.HD() * g.d * sizeof(float));
-    const size_t nq = g.dtype == MAGLEV_BF16 ? (size_t)g.N() * g.HD() : 0;
-    const size_t oQ = off; off = align(off + nq * esz);
+    auto take = [&](size_t bytes) { const size_t o = off; off = align(off + bytes); return o; };
+    auto at = [&](size_t o, bool used) { return base && used ? base + o : nullptr; };
+    L->n_key_tiles = (int)((g.T + 127) / 128);
+    L->ksplit = bf && proj ? mfma::dw_ksplit(g) : 0;
     L->Tp = (g.T + 31) / 32 * 32;
-    const size_t npad = g.dtype == MAGLEV_BF16 ? (size_t)g.B * g.H * L->Tp : 0;
-    const size_t oL = off; off = align(off + npad * sizeof(float));
-    const size_t oDp = off; off = align(off + npad * sizeof(float));
-    const size_t nact = gated ? (size_t)g.N() * g.HD() : 0;
-    const size_t oKp = off; off = align(off + nact * esz);
-    const size_t oVm = off; off = align(off + nact * esz);
     L->g_rows = L->g_blocks = 0;
     if (gated) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
-    const size_t oG = off; off = align(off + (size_t)L->g_blocks * 4 * g.HD() * sizeof(float));
-    const size_t oR = off; off = align(off + (size_t)2 * g.HD() * sizeof(float));
-    L->rowdot = base ? reinterpret_cast<float *>(base + oR) : nullptr;
-    L->dkp = base && gated ? static_cast<void *>(base + oKp) : nullptr;
-    L->dvm = base && gated ? static_cast<void *>(base + oVm) : nullptr;
-    L->gpart = base && gated ? reinterpret_cast<float *>(base + oG) : nullptr;
-    L->D = base ? reinterpret_cast<float *>(base + oD) : nullptr;
-    L->ds_part = base ? reinterpret_cast<float *>(base + oS) : nullptr;
-    L->W_scaled = base ? static_cast<void *>(base + oW) : nullptr;
-    L->dW_part = base ? reinterpret_cast<float *>(base + oP) : nullptr;
-    L->q_rot = base && nq ? static_cast<void *>(base + oQ) : nullptr;
-    L->lse2 = base && npad ? reinterpret_cast<float *>(base + oL) : nullptr;
-    L->Dp = base && npad ? reinterpret_cast<float *>(base + oDp) : nullptr;
+    // float32 path: row sums D and, for the sigma form, the per-key gate terms
+    const size_t oD = take(bf ? 0 : BHT * sizeof(float));
+    const size_t oS = take(!bf && kind == BwdKind::Sigma ? BHT * sizeof(float) : 0);
+    // bf16 path: rotated queries, padded lse*log2(e) and D
+    const size_t nq = bf ? (size_t)g.N() * HD : 0;
+    const size_t npad = bf ? (size_t)g.B * g.H * L->Tp : 0;
+    const size_t oQ = take(nq * esz);
+    const size_t oL = take(npad * sizeof(float));
+    const size_t oDp = take(npad * sizeof(float));
+    // projection backward (bf16): scaled weight copy, split-K partials, row dots
+    const size_t oW = take(bf && proj ? 2 * HD * g.d * esz : 0);
+    const size_t oP = take((size_t)L->ksplit * 2 * HD * g.d * sizeof(float));
+    const size_t oR = take(bf && kind == BwdKind::Sigma ? 2 * HD * sizeof(float) : 0);
+    // gated form: gradients of the two projections and the gate partials
+    const size_t nact = gated ? (size_t)g.N() * HD : 0;
+    const size_t oKp = take(nact * esz);
+    const size_t oVm = take(nact * esz);
+    const size_t oG = take((size_t)L->g_blocks * 4 * HD * sizeof(float));
+    L->D = reinterpret_cast<float *>(at(oD, !bf));
+    L->ds_part = reinterpret_cast<float *>(at(oS, !bf && kind == BwdKind::Sigma));
+    L->q_rot = at(oQ, bf);
+    L->lse2 = reinterpret_cast<float *>(at(oL, bf));
+    L->Dp = reinterpret_cast<float *>(at(oDp, bf));
+    L->W_scaled = at(oW, bf && proj);
+    L->dW_part = reinterpret_cast<float *>(at(oP, L->ksplit > 0));
+    L->rowdot = reinterpret_cast<float *>(at(oR, bf && kind == BwdKind::Sigma));
+    L->dkp = at(oKp, gated);
+    L->dvm = at(oVm, gated);
+    L->gpart = reinterpret_cast<float *>(at(oG, gated));
     return off;
 }
 
@@ -394,11 +406,11 @@ hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kx, const 
     if (g.dtype == MAGLEV_BF16) {
         mfma::launch_attn_bwd_bf16(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, true, s);
     } else if (g.Dh == 128) {
-        attn_bwd_simt<float, 128, true>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk,
-                                        dv, ws, rope, s);
+        attn_bwd_simt<float, 128, false, false>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO,
+                                                dq, dk, dv, ws, rope, s);
     } else {
-        attn_bwd_simt<float, 64, true>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO, dq, dk,
-                                       dv, ws, rope, s);
+        attn_bwd_simt<float, 64, false, false>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO,
+                                               dq, dk, dv, ws, rope, s);
     }
     // 2. gates, rotation and norm backward: dk, dv final; gradients of the projection
     hipError_t e = launch_gated_mix_bwd(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
@@ -413,6 +425,47 @@ hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kx, const 
                                    acc, ws, s);
     else
         proj_bwd_simt<float>(g, ws.dkp, ws.dvm, m_prime, wk, wv, nullptr, dm_prime, dWk, dWv, acc, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_keys(const Geom &g, const void *k, const float2 *rope, void *kr,
+                            hipStream_t s)
+{
+    const int64_t rows = g.N() * g.H;
+    const int64_t threads = rows * (g.Dh / 16);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    prof::Scope ts("rope_keys", s);
+    if (g.dtype == MAGLEV_BF16) {
+        if (g.Dh == 128)
+            hipLaunchKernelGGL((simt::rope_rows<bf16, 128>), grid, dim3(256), 0, s, rows, g.H, g.T,
+                               g.pos0, rope, static_cast<const bf16 *>(k), static_cast<bf16 *>(kr));
+        else
+            hipLaunchKernelGGL((simt::rope_rows<bf16, 64>), grid, dim3(256), 0, s, rows, g.H, g.T,
+                               g.pos0, rope, static_cast<const bf16 *>(k), static_cast<bf16 *>(kr));
+    } else {
+        if (g.Dh == 128)
+            hipLaunchKernelGGL((simt::rope_rows<float, 128>), grid, dim3(256), 0, s, rows, g.H, g.T,
+                               g.pos0, rope, static_cast<const float *>(k), static_cast<float *>(kr));
+        else
+            hipLaunchKernelGGL((simt::rope_rows<float, 64>), grid, dim3(256), 0, s, rows, g.H, g.T,
+                               g.pos0, rope, static_cast<const float *>(k), static_cast<float *>(kr));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const Geom &g, const void *q, const void *kr, const void *v,
+                           const void *o, const float *lse, const void *dO, void *dq, void *dk,
+                           void *dv, const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
+{
+    if (g.N() == 0) return hipSuccess;
+    if (g.dtype == MAGLEV_BF16)
+        mfma::launch_attn_bwd_bf16(g, q, kr, v, o, lse, dO, dq, dk, dv, ws, rope, false, s);
+    else if (g.Dh == 128)
+        attn_bwd_simt<float, 128, true, false>(g, q, kr, v, nullptr, nullptr, nullptr, o, lse, dO, dq,
+                                               dk, dv, ws, rope, s);
+    else
+        attn_bwd_simt<float, 64, true, false>(g, q, kr, v, nullptr, nullptr, nullptr, o, lse, dO, dq,
+                                              dk, dv, ws, rope, s);
     return hipGetLastError();
 }
 

@@ -163,8 +163,9 @@ __global__ __launch_bounds__(DH) void bwd_dq_rows(RowArgs a, const T *q, const T
 //   dk~_j = scale sum_i dS_ij q^_i, dv~_j = sum_i P_ij dO_i,
 //   dk_j = R_j^T dk~_j, dv_j = dv~_j,
 //   ds_part[b,h,j] = <kmem_j, dk_j> + <vmem_j, dv_j>  (d loss / d s_h, this key).
-// ENTRIES: write dk~_j itself (rotated frame) and dv~_j, no gate partial.
-template <typename T, int DH, bool ENTRIES>
+// ROTATE false: write dk~_j itself (rotated frame) instead of dk_j.
+// PARTIAL false: no gate partial (km, vm, ds_part are not read or written).
+template <typename T, int DH, bool ROTATE, bool PARTIAL>
 __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const T *kx,
                                                      const T *vx, const T *km, const T *vm,
                                                      const T *dO, const float *lse, const float *D,
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const
         acck += ds * qh;
         accv += p * dOi;
     }
-    if constexpr (ENTRIES) {
+    if constexpr (!ROTATE) {
         dk[krow * DH + c] = from_f<T>(acck * a.scale);
         dv[krow * DH + c] = from_f<T>(accv);
         return;
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(DH) void bwd_dkdv_rows(RowArgs a, const T *q, const
     const float dkc = rope_channel_f<DH>(dkt, c, rope_row(a, j, DH), true);
     dk[krow * DH + c] = from_f<T>(dkc);
     dv[krow * DH + c] = from_f<T>(accv);
+    if constexpr (!PARTIAL) return;
     const float part = dkc * to_f<T>(km[krow * DH + c]) + accv * to_f<T>(vm[krow * DH + c]);
     const float tot = block_sum<DH>(part, red);
     if (c == 0) ds_part[(b * a.H + h) * a.T + j] = tot;
@@ -257,6 +259,37 @@ __global__ __launch_bounds__(256) void mix_entries(int64_t rows, int H, int64_t 
     }
     store8(vx + base, lo);
     store8(vx + base + DH / 2, hi);
+}
+
+// ---------------------------------------------------------------------------
+// Rotated keys of attention without injection: kr = R_p k, p = pos0 + t, one
+// 8-channel chunk pair (c, c + Dh/2) per thread.
+// ---------------------------------------------------------------------------
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void rope_rows(int64_t rows, int H, int64_t Tlen, int64_t pos0,
+                                                 const float2 *rope, const T *k, T *kr)
+{
+    constexpr int CP = DH / 16;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / CP;            // (b*T + t)*H + h
+    if (row >= rows) return;
+    const int cc = (int)(gid % CP);
+    const int64_t t = (row / H) % Tlen;
+    const int64_t base = row * DH + 8 * cc;
+    float lo[8], hi[8];
+    load8(k + base, lo);
+    load8(k + base + DH / 2, hi);
+    if (rope) {
+        const float2 *cs = rope + (pos0 + t) * (DH / 2) + 8 * cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = cs[e].x, sn = cs[e].y, x0 = lo[e], x1 = hi[e];
+            lo[e] = x0 * c - x1 * sn;
+            hi[e] = x0 * sn + x1 * c;
+        }
+    }
+    store8(kr + base, lo);
+    store8(kr + base + DH / 2, hi);
 }
 
 // ---------------------------------------------------------------------------

@@ -225,6 +225,25 @@ def test_gated_decode_validation(L):
     assert step(a(Bs=0)) == OK
 
 
+def test_attention_only_validation(L):
+    g = geom(B=8, T=2048, H=10, Dh=128, d=1280, W=2048)
+    need = L.maglev_attn_bwd_workspace(ctypes.byref(g))
+    # rotated queries (bf16) and the padded lse / D rows; no projection scratch
+    assert 8 * 2048 * 1280 * 2 <= need < L.maglev_swa_inject_bwd_workspace(ctypes.byref(g))
+    assert L.maglev_attn_bwd_workspace(ctypes.byref(geom(Dh=96))) == 0
+    assert L.maglev_rope_keys(ctypes.byref(geom(Dh=96)), FAKE, FAKE, None) == UNSUPPORTED
+    assert L.maglev_rope_keys(ctypes.byref(geom()), FAKE, FAKE, None) == INVALID   # aliasing
+    assert L.maglev_rope_keys(ctypes.byref(geom()), FAKE_ODD, FAKE, None) == MISALIGNED
+    assert L.maglev_rope_keys(ctypes.byref(geom(T=0)), None, None, None) == OK
+    ptrs = [FAKE] * 9                 # q krot v o lse dO dq dk dv
+    assert L.maglev_attn_bwd(ctypes.byref(g), *ptrs, None, 0, None) == WORKSPACE
+    assert L.maglev_attn_bwd(ctypes.byref(g), *ptrs, FAKE, need - 1, None) == WORKSPACE
+    assert L.maglev_attn_bwd(ctypes.byref(g), *ptrs, FAKE_ODD, need, None) == MISALIGNED
+    bad = list(ptrs); bad[4] = None   # lse
+    assert L.maglev_attn_bwd(ctypes.byref(g), *bad, FAKE, need, None) == INVALID
+    assert L.maglev_attn_bwd(ctypes.byref(geom(B=0)), *([None] * 9), None, 0, None) == OK
+
+
 def test_prepare_validation(L):
     assert L.maglev_prepare(100, 1e4, 10) == UNSUPPORTED
     assert L.maglev_prepare(128, 1e4, -1) == INVALID
