@@ -29,9 +29,16 @@ FLAGS = [
 ]
 
 
+# Extra compiler options of single translation units. The attention kernels
+# keep their MFMA results in VGPRs: left to its heuristics the allocator put
+# the score accumulators of the dK/dV pass in AGPRs overlapping the dK/dV
+# accumulators and moved 96 registers between the two files on every tile.
+FILE_FLAGS = {"mfma_attn.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
