@@ -174,6 +174,26 @@ def swa_inject_bwd(q, k, v, m_prime, W_Km, W_Vm, gate_logit, dO, W: int, pos0: i
     return out
 
 
+def swa_inject_bwd_shared(layers, m_prime, W_Km, W_Vm, W: int, pos0: int = 0,
+                          rope_base: float = 10000.0, scale: float = 0.0):
+    """Gradients of a stack of layers that share one memory projection
+    (W_Km, W_Vm applied to the same shifted m') and each have their own
+    q, k, v, gate logits and upstream gradient dO: layers is a list of dicts
+    with those keys. The stack's objective is the sum over layers, so by the
+    chain rule each layer contributes its single-layer gradient and the
+    shared parameters and m' collect the sum of the contributions.
+    Returns (per_layer, shared): per_layer[l] holds dq, dk, dv, dgate;
+    shared holds dm_prime, dW_Km, dW_Vm."""
+    per_layer, shared = [], None
+    for x in layers:
+        g = swa_inject_bwd(x["q"], x["k"], x["v"], m_prime, W_Km, W_Vm, x["gate_logit"], x["dO"],
+                           W, pos0=pos0, rope_base=rope_base, scale=scale)
+        per_layer.append({n: g[n] for n in ("dq", "dk", "dv", "dgate")})
+        part = {n: g[n] for n in ("dm_prime", "dW_Km", "dW_Vm")}
+        shared = part if shared is None else {n: shared[n] + part[n] for n in part}
+    return per_layer, shared
+
+
 def consistency_loss(m, m_prime, lam: float):
     """(loss, dm, dm_prime) for L = lam/(N sqrt d) * sum (m - m')^2 over N rows of width d."""
     m, mp = f64(m), f64(m_prime)

@@ -515,3 +515,49 @@ def test_golden_tiny_fp32_unchanged():
     for t, row in stored["o_rows"].items():
         np.testing.assert_allclose(now["o_rows"][t], row, rtol=1e-12, atol=1e-12)
     assert now["loss"] == pytest.approx(stored["loss"], rel=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# layers sharing one memory projection
+# ----------------------------------------------------------------------------
+def _stack_objective(layers, shared, W):
+    H, Dh = layers[0]["q"].shape[2], layers[0]["q"].shape[3]
+    km, vm = oracle.mem_project(shared["m_prime"], shared["W_Km"], shared["W_Vm"], H, Dh, shift=1)
+    tot = 0.0
+    for x in layers:
+        o, _ = oracle.swa_inject_fwd(x["q"], x["k"], x["v"], km, vm, x["gate_logit"], W)
+        tot += float(np.sum(o * x["dO"]))
+    return tot
+
+
+def test_shared_projection_stack_matches_finite_differences():
+    """Two layers, one projection of the same m' by the same weights, their
+    own q, k, v, gates and dO: every gradient of the summed objective."""
+    sh = wl.LayerShape(B=1, T=10, W=3, d=8, H=2, Dh=4, dtype=wl.F32)
+    raws = [wl.layer_inputs(sh, seed=60 + l, grads=True) for l in range(2)]
+    layers = [{n: oracle.f64(r[n]) for n in ("q", "k", "v", "gate_logit", "dO")} for r in raws]
+    shared = {n: oracle.f64(raws[0][n]) for n in ("m_prime", "W_Km", "W_Vm")}
+    per, sg = oracle.swa_inject_bwd_shared(layers, shared["m_prime"], shared["W_Km"],
+                                           shared["W_Vm"], sh.W)
+    h = 1e-6
+
+    def fd(store, name):
+        flat = store[name].reshape(-1)
+        out = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + h
+            fp = _stack_objective(layers, shared, sh.W)
+            flat[i] = keep - h
+            fm = _stack_objective(layers, shared, sh.W)
+            flat[i] = keep
+            out[i] = (fp - fm) / (2 * h)
+        return out.reshape(store[name].shape)
+
+    for name, gname in (("m_prime", "dm_prime"), ("W_Km", "dW_Km"), ("W_Vm", "dW_Vm")):
+        np.testing.assert_allclose(sg[gname], fd(shared, name), rtol=1e-6, atol=1e-7, err_msg=gname)
+    for l in range(2):
+        for name in ("q", "k", "v", "gate_logit"):
+            gname = "dgate" if name == "gate_logit" else "d" + name
+            np.testing.assert_allclose(per[l][gname], fd(layers[l], name), rtol=1e-6, atol=1e-7,
+                                       err_msg="layer %d %s" % (l, gname))
