@@ -358,6 +358,107 @@ def bench_prefiller(sh, steps, warmup):
     return out
 
 
+def bench_stack(sh, layers, steps, warmup):
+    """One lifted pass through a stack of `layers` injected layers at the
+    stack shape (forward of every layer, the consistency loss, backward of
+    every layer), two ways:
+      shared: one memory projection of m' shared by all layers (per-layer
+        mix and gates), its backward once from the summed memory gradients;
+      per_layer: every layer with its own m' and projection weights (its own
+        projection forward and backward).
+    Inputs are drawn on the device from a seeded generator (no parity is
+    checked here). Timed with HIP events around whole passes."""
+    dev, bf, f32 = "cuda", torch.bfloat16, torch.float32
+    B, T, H, Dh, d, W = sh.B, sh.T, sh.H, sh.Dh, sh.d, sh.W
+    HD = H * Dh
+    gen = torch.Generator(device=dev).manual_seed(11)
+
+    def rnd(*shape, std=1.0, dt=bf):
+        return (torch.randn(*shape, generator=gen, device=dev) * std).to(dt)
+
+    act = (B, T, H, Dh)
+    L = [{"q": rnd(*act), "k": rnd(*act), "v": rnd(*act), "dO": rnd(*act),
+          "gate": rnd(H, dt=f32), "mp": rnd(B, T, d), "WK": rnd(HD, d, std=d ** -0.5),
+          "WV": rnd(HD, d, std=d ** -0.5), "kx": torch.empty(act, dtype=bf, device=dev),
+          "vx": torch.empty(act, dtype=bf, device=dev), "km": torch.empty(act, dtype=bf, device=dev),
+          "vm": torch.empty(act, dtype=bf, device=dev), "o": torch.empty(act, dtype=bf, device=dev),
+          "lse": torch.empty((B, H, T), dtype=f32, device=dev),
+          "dgate": torch.empty((H,), dtype=f32, device=dev)} for _ in range(layers)]
+    m = rnd(B, T, d)
+    km, vm = (torch.empty(act, dtype=bf, device=dev) for _ in range(2))
+    dkm, dvm = (torch.empty(act, dtype=f32, device=dev) for _ in range(2))
+    dq, dk, dv = (torch.empty(act, dtype=bf, device=dev) for _ in range(3))
+    dmp = torch.empty((B, T, d), dtype=f32, device=dev)
+    dm = torch.empty((B, T, d), dtype=f32, device=dev)
+    dWk, dWv = (torch.empty((HD, d), dtype=f32, device=dev) for _ in range(2))
+    loss = torch.empty((1,), dtype=f32, device=dev)
+    ws_sh = torch.empty((rms.maglev_swa_inject_bwd_shared_workspace(B, T, H, Dh, W),),
+                        dtype=torch.uint8, device=dev)
+    ws_pb = torch.empty((rms.maglev_mem_project_bwd_workspace(B, T, H, Dh, d),), dtype=torch.uint8,
+                        device=dev)
+    ws_bw = torch.empty((rms.maglev_swa_inject_bwd_workspace(B, T, H, Dh, d, W),),
+                        dtype=torch.uint8, device=dev)
+    ws_ls = torch.empty((rms.maglev_consistency_loss_workspace(B * T, d),), dtype=torch.uint8,
+                        device=dev)
+    grads = {"dq": dq, "dk": dk, "dv": dv, "dm_prime": dmp, "dW_Km": dWk, "dW_Vm": dWv}
+    mp, WK, WV = L[0]["mp"], L[0]["WK"], L[0]["WV"]
+
+    def shared_pass():
+        rms.maglev_mem_project(mp, WK, WV, H, Dh, shift=1, kmem=km, vmem=vm)
+        for x in L:
+            rms.maglev_mix_entries(x["k"], x["v"], km, vm, x["gate"], kmix=x["kx"], vmix=x["vx"])
+            rms.maglev_swa_inject_fwd(x["q"], x["kx"], x["vx"], W, o=x["o"], lse=x["lse"])
+        for i, x in enumerate(reversed(L)):
+            rms.maglev_swa_inject_bwd_shared(x["q"], x["kx"], x["vx"], km, vm, x["gate"], x["o"],
+                                             x["lse"], x["dO"], dkm, dvm, W,
+                                             accumulate=1 if i else 0, dq=dq, dk=dk, dv=dv,
+                                             dgate=x["dgate"], workspace=ws_sh)
+        rms.maglev_mem_project_bwd(dkm, dvm, mp, WK, WV, dm_prime=dmp, dW_Km=dWk, dW_Vm=dWv,
+                                   workspace=ws_pb)
+        rms.maglev_consistency_loss(m, mp, sh.lam, loss=loss, dm=dm, dm_prime=dmp, accumulate=2,
+                                    workspace=ws_ls)
+
+    def per_layer_pass():
+        for x in L:
+            rms.maglev_mem_project(x["mp"], x["WK"], x["WV"], H, Dh, shift=1, kmem=x["km"],
+                                   vmem=x["vm"], k=x["k"], v=x["v"], gate_logit=x["gate"],
+                                   kmix=x["kx"], vmix=x["vx"])
+            rms.maglev_swa_inject_fwd(x["q"], x["kx"], x["vx"], W, o=x["o"], lse=x["lse"])
+        grads["dgate"] = L[0]["dgate"]
+        for x in reversed(L):
+            grads["dgate"] = x["dgate"]
+            rms.maglev_swa_inject_bwd(x["q"], x["kx"], x["vx"], x["km"], x["vm"], x["gate"], x["o"],
+                                      x["lse"], x["dO"], x["mp"], x["WK"], x["WV"], W, out=grads,
+                                      workspace=ws_bw)
+        rms.maglev_consistency_loss(m, L[-1]["mp"], sh.lam, loss=loss, dm=dm, dm_prime=dmp,
+                                    accumulate=2, workspace=ws_ls)
+
+    pairs = sum(min(i + 1, W) for i in range(T))
+    attn = 2.0 * pairs * Dh * B * H
+    proj = 2.0 * B * T * d * 2 * HD
+    out = {}
+    for name, fn, flops in (("shared_projection", shared_pass, layers * 6 * attn + 3 * proj),
+                            ("projection_per_layer", per_layer_pass, layers * (6 * attn + 3 * proj))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name] = {"ms_per_pass": round(ms, 3), "tokens/s": round(B * T / (ms / 1e3), 1),
+                     "algorithmic_TFLOP": round(flops / 1e12, 4),
+                     "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1),
+                     "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del L
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(sh):
     """The oracle, as it stands, on a bounded slice of the training workload:
     sequences 0-5 of 8, all heads, full T. The slice holds 6/8 of the layer's
@@ -405,6 +506,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefiller", action="store_true")
+    ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--mix", choices=("sigma", "gated"), default="sigma",
                     help="mixing form: per-head sigma gate (default) or the gated form with "
                          "channel-wise 2 sigmoid gates and the normalised memory key")
@@ -490,6 +592,14 @@ def main():
             "workload": "causal prefiller attention without injection, B=8, T=2048, 10x128 "
                         "heads, bf16: SLSL layers' sliding-window (W=512) and full (W=T) kinds",
             **bench_prefiller(sh, max(args.steps // 2, 5), 3)}
+    if not args.no_stack:
+        ssh = wl.D20_STACK
+        result["stack"] = {
+            "workload": "one lifted pass through %d injected layers, B=%d, T=%d, W=%d, d=%d, "
+                        "10x128 heads, bf16, consistency loss at the end"
+                        % (wl.D20_STACK_LAYERS, ssh.B, ssh.T, ssh.W, ssh.d),
+            "layers": wl.D20_STACK_LAYERS,
+            **bench_stack(ssh, wl.D20_STACK_LAYERS, 3, 1)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh)
     print(json.dumps(result), flush=True)

@@ -280,6 +280,61 @@ maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int3
                                          hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Layers sharing one memory projection ([R-step]: a shared projection maps
+ * the shifted memory to the recurrent K/V features, each layer mixes them in
+ * through its own gate). Per pass:
+ *   maglev_mem_project(shift = 1, no mixing arguments) once -> kmem, vmem;
+ *   per layer l: maglev_mix_entries(k_l, v_l, kmem, vmem, gate_l) and
+ *     maglev_swa_inject_fwd; backward maglev_swa_inject_bwd_shared, which
+ *     sums s dk and s dv of every layer into float32 dkmem, dvmem;
+ *   maglev_mem_project_bwd once: dm' and dW from the sums.
+ * The stack's objective is the sum over layers, so these are its gradients.
+ * ------------------------------------------------------------------------- */
+
+/* The mix of one layer from given memory terms (the mixing half of
+ * maglev_mem_project): kmix = R_{pos0+t} k + s_h R_{pos0+t} kmem,
+ * vmix = v + s_h vmem. k, v, kmem, vmem, kmix, vmix [B,T,H,Dh] dtype;
+ * gate_logit [H] float32. Uses g->B, T, H, Dh, pos0, rope_base, dtype. */
+maglev_status_t maglev_mix_entries(const maglev_geom_t *g, const void *k, const void *v,
+                                   const void *kmem, const void *vmem, const float *gate_logit,
+                                   void *kmix, void *vmix, hipStream_t stream);
+
+/* Bytes of device workspace maglev_swa_inject_bwd_shared needs (0 on invalid geometry). */
+size_t maglev_swa_inject_bwd_shared_workspace(const maglev_geom_t *g);
+
+/* Backward of one layer whose memory terms come from a shared projection:
+ *   dq, dk, dv [B,T,H,Dh] dtype (overwritten): gradients w.r.t. q, k, v;
+ *   dkmem, dvmem [B,T,H,Dh] float32: s_h dk and s_h dv, the layer's share of
+ *     the gradients of the shared kmem, vmem (accumulate bit 0: added);
+ *   dgate [H] float32 (bit 2: added).
+ * Inputs as maglev_swa_inject_bwd (kmix, vmix from maglev_mix_entries).
+ * accumulate: only bits 0 and 2. Deterministic (fixed-order sums). */
+maglev_status_t maglev_swa_inject_bwd_shared(const maglev_geom_t *g, const void *q,
+                                             const void *kmix, const void *vmix,
+                                             const void *kmem, const void *vmem,
+                                             const float *gate_logit, const void *o,
+                                             const float *lse, const void *dO, void *dq,
+                                             void *dk, void *dv, float *dkmem, float *dvmem,
+                                             float *dgate, unsigned accumulate, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace maglev_mem_project_bwd needs (0 on invalid geometry). */
+size_t maglev_mem_project_bwd_workspace(const maglev_geom_t *g);
+
+/* Backward of the shift and projection from the gradients of the projected
+ * memory: dkmem, dvmem [B,T,H,Dh] float32 (e.g. summed over the layers of a
+ * pass); m_prime [B,T,d] dtype (unshifted); W_Km, W_Vm [H*Dh,d] dtype.
+ *   dm_prime [B,T,d] float32: row t receives the gradient of projection
+ *     input row t+1, row T-1 nothing (accumulate bit 0: added);
+ *   dW_Km, dW_Vm [H*Dh,d] float32 (bit 1: added).
+ * The bf16 path rounds dkmem, dvmem to bf16 once (MFMA operands). */
+maglev_status_t maglev_mem_project_bwd(const maglev_geom_t *g, const float *dkmem,
+                                       const float *dvmem, const void *m_prime, const void *W_Km,
+                                       const void *W_Vm, float *dm_prime, float *dW_Km,
+                                       float *dW_Vm, unsigned accumulate, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Attention without injection: the layers of the causal prefiller Q, which
  * produces the targets m' with interleaved sliding-window and full-attention
  * layers and no memory term ([R-core], [R-step]: the SLSL pattern, window 512

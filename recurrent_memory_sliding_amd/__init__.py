@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
             "maglev_swa_inject_bwd_gated_workspace": ([G], sz),
             "maglev_swa_inject_bwd_gated": ([G] + [vp] * 8 + [f32] + [vp] * 13 + [u32, vp, sz, vp],
                                             i32),
+            "maglev_mix_entries": ([G] + [vp] * 7 + [vp], i32),
+            "maglev_swa_inject_bwd_shared_workspace": ([G], sz),
+            "maglev_swa_inject_bwd_shared": ([G] + [vp] * 15 + [u32, vp, sz, vp], i32),
+            "maglev_mem_project_bwd_workspace": ([G], sz),
+            "maglev_mem_project_bwd": ([G] + [vp] * 8 + [u32, vp, sz, vp], i32),
             "maglev_rope_keys": ([G, vp, vp, vp], i32),
             "maglev_attn_bwd_workspace": ([G], sz),
             "maglev_attn_bwd": ([G] + [vp] * 9 + [vp, sz, vp], i32),
@@ -452,6 +457,93 @@ def maglev_decode_step_gated(q, k, v, kproj, vmem, gates, kcache, vcache, pos, o
                                           workspace.numel() * workspace.element_size(),
                                           _stream(stream)), "maglev_decode_step_gated")
     return o
+
+
+# ----------------------------------------------------------------------------
+# Layers sharing one memory projection: mem_project once per pass, then per
+# layer mix_entries / swa_inject_fwd / swa_inject_bwd_shared (summing the
+# memory gradients), then mem_project_bwd once.
+# ----------------------------------------------------------------------------
+def maglev_mix_entries(k, v, kmem, vmem, gate_logit, pos0: int = 0, rope_base: float = 10000.0,
+                       kmix=None, vmix=None, stream=None):
+    """(kmix, vmix) of one layer from the given (shared) memory terms."""
+    _dev(k, v, kmem, vmem, gate_logit, kmix, vmix)
+    _same(k, v, kmem, vmem, kmix, vmix)
+    B, T, H, Dh = k.shape
+    for t in (v, kmem, vmem):
+        if tuple(t.shape) != tuple(k.shape):
+            raise MaglevError("k, v, kmem, vmem must all be [B,T,H,Dh]")
+    if gate_logit.dtype != torch.float32 or gate_logit.numel() != H:
+        raise MaglevError("gate_logit must be float32 [H]")
+    kmix = torch.empty_like(k) if kmix is None else kmix
+    vmix = torch.empty_like(k) if vmix is None else vmix
+    g = make_geom(B, T, H, Dh, H * Dh, 1, pos0, rope_base, 0.0, _dtype_code(k))
+    _check(lib().maglev_mix_entries(ctypes.byref(g), _ptr(k), _ptr(v), _ptr(kmem), _ptr(vmem),
+                                    _ptr(gate_logit), _ptr(kmix), _ptr(vmix), _stream(stream)),
+           "maglev_mix_entries")
+    return kmix, vmix
+
+
+def maglev_swa_inject_bwd_shared_workspace(B, T, H, Dh, W, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, H * Dh, W, dtype=dtype)
+    return int(lib().maglev_swa_inject_bwd_shared_workspace(ctypes.byref(g)))
+
+
+def maglev_swa_inject_bwd_shared(q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, dkmem, dvmem,
+                                 W: int, pos0: int = 0, rope_base: float = 10000.0,
+                                 scale: float = 0.0, accumulate: int = 0, dq=None, dk=None,
+                                 dv=None, dgate=None, workspace=None, stream=None):
+    """One layer's backward with shared memory terms: returns (dq, dk, dv, dgate);
+    dkmem/dvmem (float32 [B,T,H,Dh]) receive s dk, s dv (added with bit 0)."""
+    _dev(q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, dkmem, dvmem, dq, dk, dv, dgate,
+         workspace)
+    _same(q, kmix, vmix, kmem, vmem, o, dO, dq, dk, dv)
+    B, T, H, Dh = q.shape
+    for t in (dkmem, dvmem):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(q.shape):
+            raise MaglevError("dkmem / dvmem must be float32 [B,T,H,Dh]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    dgate = torch.empty((H,), dtype=torch.float32, device=q.device) if dgate is None else dgate
+    g = make_geom(B, T, H, Dh, H * Dh, W, pos0, rope_base, scale, _dtype_code(q))
+    if workspace is None:
+        need = int(lib().maglev_swa_inject_bwd_shared_workspace(ctypes.byref(g)))
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().maglev_swa_inject_bwd_shared(
+        ctypes.byref(g), _ptr(q), _ptr(kmix), _ptr(vmix), _ptr(kmem), _ptr(vmem), _ptr(gate_logit),
+        _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dkmem), _ptr(dvmem),
+        _ptr(dgate), accumulate, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "maglev_swa_inject_bwd_shared")
+    return dq, dk, dv, dgate
+
+
+def maglev_mem_project_bwd_workspace(B, T, H, Dh, d, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, d, 1, dtype=dtype)
+    return int(lib().maglev_mem_project_bwd_workspace(ctypes.byref(g)))
+
+
+def maglev_mem_project_bwd(dkmem, dvmem, m_prime, W_Km, W_Vm, accumulate: int = 0, dm_prime=None,
+                           dW_Km=None, dW_Vm=None, workspace=None, stream=None):
+    """(dm_prime, dW_Km, dW_Vm), all float32, from float32 dkmem, dvmem [B,T,H,Dh]."""
+    _dev(dkmem, dvmem, m_prime, W_Km, W_Vm, dm_prime, dW_Km, dW_Vm, workspace)
+    _same(m_prime, W_Km, W_Vm)
+    B, T, H, Dh = dkmem.shape
+    d = m_prime.shape[-1]
+    dev = m_prime.device
+    f32 = torch.float32
+    dm_prime = torch.empty((B, T, d), dtype=f32, device=dev) if dm_prime is None else dm_prime
+    dW_Km = torch.empty((H * Dh, d), dtype=f32, device=dev) if dW_Km is None else dW_Km
+    dW_Vm = torch.empty((H * Dh, d), dtype=f32, device=dev) if dW_Vm is None else dW_Vm
+    g = make_geom(B, T, H, Dh, d, 1, 0, 0.0, 0.0, _dtype_code(m_prime))
+    if workspace is None:
+        need = int(lib().maglev_mem_project_bwd_workspace(ctypes.byref(g)))
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().maglev_mem_project_bwd(
+        ctypes.byref(g), _ptr(dkmem), _ptr(dvmem), _ptr(m_prime), _ptr(W_Km), _ptr(W_Vm),
+        _ptr(dm_prime), _ptr(dW_Km), _ptr(dW_Vm), accumulate, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "maglev_mem_project_bwd")
+    return dm_prime, dW_Km, dW_Vm
 
 
 # ----------------------------------------------------------------------------

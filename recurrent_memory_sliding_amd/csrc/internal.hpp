@@ -61,7 +61,10 @@ struct BwdWorkspace {
 };
 // Which backward the workspace serves: the sigma-gated layer path, the gated
 // layer path, or attention alone (no memory term, no projection).
-enum class BwdKind { Sigma, Gated, Attn };
+// Shared: one layer of a stack sharing a projection (attention backward and
+// the memory-gradient accumulation); Proj: that projection's backward alone.
+enum class BwdKind { Sigma, Gated, Attn, Shared, Proj };
+constexpr int kSharedTokens = 128;   // tokens per workgroup of the shared accumulation
 size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base, BwdKind kind);
 
 hipError_t launch_bwd(const Geom &g, const void *q, const void *kmix, const void *vmix,
@@ -97,6 +100,22 @@ hipError_t launch_rope_keys(const Geom &g, const void *k, const float2 *rope, vo
 hipError_t launch_attn_bwd(const Geom &g, const void *q, const void *kr, const void *v,
                            const void *o, const float *lse, const void *dO, void *dq, void *dk,
                            void *dv, const BwdWorkspace &ws, const float2 *rope, hipStream_t s);
+
+// ---- layers sharing one memory projection ------------------------------------
+// Per layer: attention backward (dq, dk, dv) and dkm (+)= s dk, dvm (+)= s dv
+// (float32), dgate (+)= s(1-s) sum <kmem, dk> + <vmem, dv>. accumulate bit 0:
+// dkm/dvm +=, bit 2: dgate +=.
+hipError_t launch_bwd_shared(const Geom &g, const void *q, const void *kmix, const void *vmix,
+                             const void *kmem, const void *vmem, const float *gate,
+                             const void *o, const float *lse, const void *dO, void *dq,
+                             void *dk, void *dv, float *dkmem, float *dvmem, float *dgate,
+                             unsigned accumulate, const BwdWorkspace &ws, const float2 *rope,
+                             hipStream_t s);
+// Once per pass: dm' and dW from the summed float32 memory gradients.
+hipError_t launch_mem_project_bwd(const Geom &g, const float *dkmem, const float *dvmem,
+                                  const void *m_prime, const void *W_Km, const void *W_Vm,
+                                  float *dm_prime, float *dW_Km, float *dW_Vm, unsigned accumulate,
+                                  const BwdWorkspace &ws, hipStream_t s);
 
 // ---- consistency loss -------------------------------------------------------
 size_t loss_workspace_bytes(int64_t N, int d);

@@ -515,6 +515,100 @@ maglev_status_t maglev_attn_bwd(const maglev_geom_t *g, const void *q, const voi
     return hip_status(launch_attn_bwd(G, q, krot, v, o, lse, dO, dq, dk, dv, layout, rope, stream));
 }
 
+// ---- layers sharing one memory projection ---------------------------------------
+
+maglev_status_t maglev_mix_entries(const maglev_geom_t *g, const void *k, const void *v,
+                                   const void *kmem, const void *vmem, const float *gate_logit,
+                                   void *kmix, void *vmix, hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0) return MAGLEV_OK;
+    st = check_ptrs({k, v, kmem, vmem, kmix, vmix});
+    if (st != MAGLEV_OK) return st;
+    if (!gate_logit) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit is NULL");
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    return hip_status(launch_mix(G, k, v, kmem, vmem, gate_logit, rope, kmix, vmix, stream));
+}
+
+size_t maglev_swa_inject_bwd_shared_workspace(const maglev_geom_t *g)
+{
+    Geom G;
+    if (check_geom(g, &G) != MAGLEV_OK) return 0;
+    BwdWorkspace layout;
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::Shared);
+}
+
+maglev_status_t maglev_swa_inject_bwd_shared(const maglev_geom_t *g, const void *q,
+                                             const void *kmix, const void *vmix,
+                                             const void *kmem, const void *vmem,
+                                             const float *gate_logit, const void *o,
+                                             const float *lse, const void *dO, void *dq,
+                                             void *dk, void *dv, float *dkmem, float *dvmem,
+                                             float *dgate, unsigned accumulate, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (!gate_logit || !dgate) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit or dgate is NULL");
+    if (accumulate & ~5u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    if (G.N() > 0) {
+        st = check_ptrs({q, kmix, vmix, kmem, vmem, o, lse, dO, dq, dk, dv, dkmem, dvmem});
+        if (st != MAGLEV_OK) return st;
+    }
+    BwdWorkspace layout;
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::Shared);
+    if (G.N() > 0 && (!workspace || workspace_bytes < need))
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (workspace && !aligned16(workspace))
+        return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    const float2 *rope = nullptr;
+    if (G.N() > 0) {
+        st = table_for(G, stream, &rope);
+        if (st != MAGLEV_OK) return st;
+    }
+    return hip_status(launch_bwd_shared(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, dq,
+                                        dk, dv, dkmem, dvmem, dgate, accumulate, layout, rope,
+                                        stream));
+}
+
+size_t maglev_mem_project_bwd_workspace(const maglev_geom_t *g)
+{
+    Geom G;
+    if (check_geom(g, &G) != MAGLEV_OK) return 0;
+    BwdWorkspace layout;
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::Proj);
+}
+
+maglev_status_t maglev_mem_project_bwd(const maglev_geom_t *g, const float *dkmem,
+                                       const float *dvmem, const void *m_prime, const void *W_Km,
+                                       const void *W_Vm, float *dm_prime, float *dW_Km,
+                                       float *dW_Vm, unsigned accumulate, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    if (accumulate & ~3u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    if (G.N() == 0)
+        st = check_ptrs({W_Km, W_Vm, dW_Km, dW_Vm});
+    else
+        st = check_ptrs({dkmem, dvmem, m_prime, W_Km, W_Vm, dm_prime, dW_Km, dW_Vm});
+    if (st != MAGLEV_OK) return st;
+    BwdWorkspace layout;
+    const size_t need = bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::Proj);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (workspace && !aligned16(workspace))
+        return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    return hip_status(launch_mem_project_bwd(G, dkmem, dvmem, m_prime, W_Km, W_Vm, dm_prime, dW_Km,
+                                             dW_Vm, accumulate, layout, stream));
+}
+
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream)
 {
     if (Bs < 0) return fail(MAGLEV_ERR_INVALID_VALUE, "Bs must be >= 0");

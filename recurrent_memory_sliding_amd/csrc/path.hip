@@ -160,6 +160,60 @@ __global__ __launch_bounds__(64) void dgate_from_rows(const float *rowdot, int H
     }
 }
 
+// One layer's contribution to the gradients of a memory projection shared by
+// several layers: dkm (+)= s_h dk, dvm (+)= s_h dv (float32 [B,T,H,Dh]), and
+// part[(b H + h) nblk + tb] = sum over this block's tokens of
+// <kmem, dk> + <vmem, dv> (the gate terms of head h). One workgroup per
+// (token block, b, h); 16 bytes a lane.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void shared_mem_grad(int64_t Tlen, int H, int tokens,
+                                                       const float *gate, const T *dk, const T *dv,
+                                                       const T *km, const T *vm, float *dkm,
+                                                       float *dvm, float *part, unsigned acc)
+{
+    constexpr int CPT = DH / 8;           // 8-channel chunks of one token's head row
+    constexpr int TPP = 256 / CPT;        // tokens per pass
+    __shared__ float red[4];
+    const int bh = blockIdx.y, h = bh % H;
+    const int64_t b = bh / H;
+    const int c = threadIdx.x % CPT, tl = threadIdx.x / CPT;
+    const float sg = gate_sigmoid(gate[h]);
+    const int64_t t0 = (int64_t)blockIdx.x * tokens;
+    const int64_t t1 = t0 + tokens < Tlen ? t0 + tokens : Tlen;
+    float p = 0.0f;
+    for (int64_t t = t0 + tl; t < t1; t += TPP) {
+        const int64_t off = ((b * Tlen + t) * H + h) * DH + 8 * c;
+        float x[8], y[8], z[8];
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            load8((pass ? dv : dk) + off, x);
+            load8((pass ? vm : km) + off, y);
+            float *dst = (pass ? dvm : dkm) + off;
+            if (acc) load8(dst, z);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                p += x[e] * y[e];
+                z[e] = acc ? z[e] + sg * x[e] : sg * x[e];
+            }
+            store8(dst, z);
+        }
+    }
+    p = wave_sum(p);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = p;
+    __syncthreads();
+    if (threadIdx.x == 0) part[(int64_t)bh * gridDim.x + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+// float32 -> bf16, 8 elements a thread (n a multiple of 8).
+__global__ void to_bf16(const float *x, bf16 *y, int64_t n8)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    float v[8];
+    load8(x + 8 * i, v);
+    store8(y + 8 * i, v);
+}
+
 simt::RowArgs row_args(const Geom &g, const float *gate, const float2 *rope)
 {
     simt::RowArgs a;
@@ -292,8 +346,11 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
 {
     auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
     const bool bf = g.dtype == MAGLEV_BF16;
-    const bool proj = kind != BwdKind::Attn;          // a projection backward follows
+    // a projection backward follows (sigma, gated) or is the whole call (proj)
+    const bool proj = kind == BwdKind::Sigma || kind == BwdKind::Gated || kind == BwdKind::Proj;
+    const bool attn = kind != BwdKind::Proj;          // an attention backward runs
     const bool gated = kind == BwdKind::Gated;
+    const bool shared = kind == BwdKind::Shared;
     const size_t esz = bf ? 2 : 4;
     const size_t BHT = (size_t)g.B * g.H * g.T;
     const size_t HD = (size_t)g.HD();
@@ -305,12 +362,15 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     L->Tp = (g.T + 31) / 32 * 32;
     L->g_rows = L->g_blocks = 0;
     if (gated) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
-    // float32 path: row sums D and, for the sigma form, the per-key gate terms
-    const size_t oD = take(bf ? 0 : BHT * sizeof(float));
-    const size_t oS = take(!bf && kind == BwdKind::Sigma ? BHT * sizeof(float) : 0);
+    // float32 path: row sums D and, for the sigma form, the per-key gate terms;
+    // a layer of a shared projection: per-block gate terms (both paths)
+    const size_t nsp = (size_t)g.B * g.H * ((g.T + kSharedTokens - 1) / kSharedTokens);
+    const size_t oD = take(!bf && attn ? BHT * sizeof(float) : 0);
+    const size_t oS = take(!bf && kind == BwdKind::Sigma ? BHT * sizeof(float)
+                           : shared ? nsp * sizeof(float) : 0);
     // bf16 path: rotated queries, padded lse*log2(e) and D
-    const size_t nq = bf ? (size_t)g.N() * HD : 0;
-    const size_t npad = bf ? (size_t)g.B * g.H * L->Tp : 0;
+    const size_t nq = bf && attn ? (size_t)g.N() * HD : 0;
+    const size_t npad = bf && attn ? (size_t)g.B * g.H * L->Tp : 0;
     const size_t oQ = take(nq * esz);
     const size_t oL = take(npad * sizeof(float));
     const size_t oDp = take(npad * sizeof(float));
@@ -318,21 +378,22 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     const size_t oW = take(bf && proj ? 2 * HD * g.d * esz : 0);
     const size_t oP = take((size_t)L->ksplit * 2 * HD * g.d * sizeof(float));
     const size_t oR = take(bf && kind == BwdKind::Sigma ? 2 * HD * sizeof(float) : 0);
-    // gated form: gradients of the two projections and the gate partials
-    const size_t nact = gated ? (size_t)g.N() * HD : 0;
+    // gated form: gradients of the two projections and the gate partials; the
+    // shared projection's backward (bf16): its float32 gradients rounded to bf16
+    const size_t nact = gated || (bf && kind == BwdKind::Proj) ? (size_t)g.N() * HD : 0;
     const size_t oKp = take(nact * esz);
     const size_t oVm = take(nact * esz);
     const size_t oG = take((size_t)L->g_blocks * 4 * HD * sizeof(float));
-    L->D = reinterpret_cast<float *>(at(oD, !bf));
-    L->ds_part = reinterpret_cast<float *>(at(oS, !bf && kind == BwdKind::Sigma));
-    L->q_rot = at(oQ, bf);
-    L->lse2 = reinterpret_cast<float *>(at(oL, bf));
-    L->Dp = reinterpret_cast<float *>(at(oDp, bf));
+    L->D = reinterpret_cast<float *>(at(oD, !bf && attn));
+    L->ds_part = reinterpret_cast<float *>(at(oS, (!bf && kind == BwdKind::Sigma) || shared));
+    L->q_rot = at(oQ, nq > 0);
+    L->lse2 = reinterpret_cast<float *>(at(oL, npad > 0));
+    L->Dp = reinterpret_cast<float *>(at(oDp, npad > 0));
     L->W_scaled = at(oW, bf && proj);
     L->dW_part = reinterpret_cast<float *>(at(oP, L->ksplit > 0));
     L->rowdot = reinterpret_cast<float *>(at(oR, bf && kind == BwdKind::Sigma));
-    L->dkp = at(oKp, gated);
-    L->dvm = at(oVm, gated);
+    L->dkp = at(oKp, nact > 0);
+    L->dvm = at(oVm, nact > 0);
     L->gpart = reinterpret_cast<float *>(at(oG, gated));
     return off;
 }
@@ -466,6 +527,79 @@ hipError_t launch_attn_bwd(const Geom &g, const void *q, const void *kr, const v
     else
         attn_bwd_simt<float, 64, true, false>(g, q, kr, v, nullptr, nullptr, nullptr, o, lse, dO, dq,
                                               dk, dv, ws, rope, s);
+    return hipGetLastError();
+}
+
+template <typename T, int DH>
+static void shared_grad_t(const Geom &g, const float *gate, const void *dk, const void *dv,
+                          const void *km, const void *vm, float *dkm, float *dvm, float *part,
+                          unsigned acc, hipStream_t s)
+{
+    const dim3 grid((unsigned)((g.T + kSharedTokens - 1) / kSharedTokens), (unsigned)(g.B * g.H));
+    prof::Scope ts("shared_mem_grad", s);
+    hipLaunchKernelGGL((shared_mem_grad<T, DH>), grid, dim3(256), 0, s, g.T, g.H, kSharedTokens,
+                       gate, static_cast<const T *>(dk), static_cast<const T *>(dv),
+                       static_cast<const T *>(km), static_cast<const T *>(vm), dkm, dvm, part, acc);
+}
+
+hipError_t launch_bwd_shared(const Geom &g, const void *q, const void *kx, const void *vx,
+                             const void *km, const void *vm, const float *gate, const void *o,
+                             const float *lse, const void *dO, void *dq, void *dk, void *dv,
+                             float *dkm, float *dvm, float *dgate, unsigned acc,
+                             const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
+{
+    if (g.N() == 0) {
+        if (!(acc & 4u)) hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, s, dgate, (int64_t)g.H);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_attn_bwd(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, s);
+    if (e != hipSuccess) return e;
+    const unsigned a1 = acc & 1u;
+    if (g.dtype == MAGLEV_BF16) {
+        if (g.Dh == 128) shared_grad_t<bf16, 128>(g, gate, dk, dv, km, vm, dkm, dvm, ws.ds_part, a1, s);
+        else shared_grad_t<bf16, 64>(g, gate, dk, dv, km, vm, dkm, dvm, ws.ds_part, a1, s);
+    } else {
+        if (g.Dh == 128) shared_grad_t<float, 128>(g, gate, dk, dv, km, vm, dkm, dvm, ws.ds_part, a1, s);
+        else shared_grad_t<float, 64>(g, gate, dk, dv, km, vm, dkm, dvm, ws.ds_part, a1, s);
+    }
+    prof::Scope ts("dgate_reduce", s);
+    hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H,
+                       (int64_t)((g.T + kSharedTokens - 1) / kSharedTokens), gate, dgate, acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_mem_project_bwd(const Geom &g, const float *dkm, const float *dvm,
+                                  const void *m_prime, const void *wk, const void *wv,
+                                  float *dm_prime, float *dWk, float *dWv, unsigned acc,
+                                  const BwdWorkspace &ws, hipStream_t s)
+{
+    const int HD = g.HD();
+    if (g.N() == 0) {
+        const int64_t nw = (int64_t)HD * g.d;
+        if (!(acc & 2u)) {
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWk, nw);
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, dWv, nw);
+        }
+        return hipGetLastError();
+    }
+    if (g.dtype == MAGLEV_BF16) {
+        const int64_t n8 = g.N() * (int64_t)HD / 8;
+        {
+            prof::Scope ts("proj_bwd_to_bf16", s);
+            hipLaunchKernelGGL(to_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, dkm,
+                               static_cast<bf16 *>(ws.dkp), n8);
+            hipLaunchKernelGGL(to_bf16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, dvm,
+                               static_cast<bf16 *>(ws.dvm), n8);
+        }
+        mfma::launch_proj_bwd_bf16(g, ws.dkp, ws.dvm, m_prime, wk, wv, nullptr, dm_prime, dWk, dWv,
+                                   acc, ws, s);
+        return hipGetLastError();
+    }
+    if (!(acc & 1u)) {
+        prof::Scope ts("zero_last_rows", s);
+        hipLaunchKernelGGL(zero_last_rows, dim3(g.B), dim3(256), 0, s, dm_prime, g.B, g.T, g.d);
+    }
+    proj_bwd_simt<float>(g, dkm, dvm, m_prime, wk, wv, nullptr, dm_prime, dWk, dWv, acc, s);
     return hipGetLastError();
 }
 

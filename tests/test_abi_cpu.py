@@ -244,6 +244,33 @@ def test_attention_only_validation(L):
     assert L.maglev_attn_bwd(ctypes.byref(geom(B=0)), *([None] * 9), None, 0, None) == OK
 
 
+def test_shared_projection_validation(L):
+    g = geom(B=4, T=2048, H=10, Dh=128, d=1280, W=512)
+    args = [FAKE] * 7                 # k v kmem vmem gate kmix vmix
+    assert L.maglev_mix_entries(ctypes.byref(geom(Dh=96)), *args, None) == UNSUPPORTED
+    bad = list(args); bad[4] = None   # gate
+    assert L.maglev_mix_entries(ctypes.byref(g), *bad, None) == INVALID
+    bad = list(args); bad[2] = FAKE_ODD
+    assert L.maglev_mix_entries(ctypes.byref(g), *bad, None) == MISALIGNED
+    need = L.maglev_swa_inject_bwd_shared_workspace(ctypes.byref(g))
+    assert need >= L.maglev_attn_bwd_workspace(ctypes.byref(g))
+    ptrs = [FAKE] * 15                # q kmix vmix kmem vmem gate o lse dO dq dk dv dkmem dvmem dgate
+    call = lambda p=ptrs, acc=0, ws=FAKE, n=need: L.maglev_swa_inject_bwd_shared(
+        ctypes.byref(g), *p, acc, ws, n, None)
+    assert call(acc=2) == INVALID     # only bits 0 and 2
+    assert call(ws=None) == WORKSPACE
+    assert call(n=need - 1) == WORKSPACE
+    bad = list(ptrs); bad[12] = None  # dkmem
+    assert call(p=bad) == INVALID
+    pneed = L.maglev_mem_project_bwd_workspace(ctypes.byref(g))
+    assert pneed >= 2 * 4 * 2048 * 1280 * 2   # the bf16 roundings of dkmem, dvmem
+    pp = [FAKE] * 8                   # dkmem dvmem m' W_Km W_Vm dm' dWk dWv
+    assert L.maglev_mem_project_bwd(ctypes.byref(g), *pp, 4, FAKE, pneed, None) == INVALID
+    assert L.maglev_mem_project_bwd(ctypes.byref(g), *pp, 0, None, 0, None) == WORKSPACE
+    bad = list(pp); bad[2] = None     # m'
+    assert L.maglev_mem_project_bwd(ctypes.byref(g), *bad, 0, FAKE, pneed, None) == INVALID
+
+
 def test_prepare_validation(L):
     assert L.maglev_prepare(100, 1e4, 10) == UNSUPPORTED
     assert L.maglev_prepare(128, 1e4, -1) == INVALID
