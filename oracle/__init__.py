@@ -77,6 +77,10 @@ def _load():
         L.oracle_decode_step_gated.argtypes = [I64, I32, I32, I64, D, D, D, I32,
                                                P, P, P, P, P, P, P, P, P, P, P, PI64, P]
         L.oracle_decode_step_gated.restype = None
+        L.oracle_lm_head.argtypes = [I64, I32, I64, D, D, D, P, P, PI64, P, P, P, P]
+        L.oracle_lm_head.restype = D
+        L.oracle_lm_head_rows.argtypes = [I64, PI64, I32, I64, D, D, I64, P, P, PI64, P, P, P]
+        L.oracle_lm_head_rows.restype = None
         _lib = L
     return _lib
 
@@ -320,6 +324,49 @@ def decode_step_gated(q, k, v, kproj, vmem, gates, kcache: np.ndarray, vcache: n
                                      *(_p(a) for a in g), _p(kcache), _p(vcache),
                                      pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _p(o))
     return o
+
+
+LM_CAP = 15.0
+
+
+def lm_head(h, U, targets, m_prime=None, lam: float = 0.0, cap: float = LM_CAP,
+            eps: float = RMS_EPS, grads: bool = True):
+    """Loss head: m = RMSNorm(h), capped logits cap tanh(U m / cap), mean CE over
+    all positions (targets outside [0, V) ignored) + lam / (N sqrt d) sum ||m - m'||^2.
+    Returns dict with loss, m [N,d] and (grads) dh [N,d], dU [V,d]."""
+    h, U = f64(h), f64(U)
+    d = h.shape[-1]
+    hs = h.reshape(-1, d)
+    N, V = hs.shape[0], U.shape[0]
+    tg = np.ascontiguousarray(np.asarray(targets, dtype=np.int64).reshape(N))
+    mp = f64(m_prime).reshape(N, d) if m_prime is not None else None
+    out = {"m": np.empty((N, d))}
+    if grads:
+        out["dh"] = np.empty((N, d))
+        out["dU"] = np.empty((V, d))
+    PI = ctypes.POINTER(ctypes.c_int64)
+    out["loss"] = float(_load().oracle_lm_head(
+        N, d, V, float(cap), float(eps), float(lam), _p(hs), _p(U), tg.ctypes.data_as(PI),
+        _p(mp) if mp is not None else None, _p(out["m"]), _p(out["dh"]) if grads else None,
+        _p(out["dU"]) if grads else None))
+    return out
+
+
+def lm_head_rows(h, U, targets, rows, cap: float = LM_CAP, eps: float = RMS_EPS):
+    """(lse, ce, dm_head) of the listed rows only: log-sum-exp, CE term and
+    U^T dz of each row (dz already carrying 1/N)."""
+    h, U = f64(h), f64(U)
+    d = h.shape[-1]
+    hs = h.reshape(-1, d)
+    N, V = hs.shape[0], U.shape[0]
+    tg = np.ascontiguousarray(np.asarray(targets, dtype=np.int64).reshape(N))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    n = rows.size
+    lse, ce, dm = np.empty(n), np.empty(n), np.empty((n, d))
+    PI = ctypes.POINTER(ctypes.c_int64)
+    _load().oracle_lm_head_rows(n, rows.ctypes.data_as(PI), d, V, float(cap), float(eps), N,
+                                _p(hs), _p(U), tg.ctypes.data_as(PI), _p(lse), _p(ce), _p(dm))
+    return lse, ce, dm
 
 
 def omp_threads() -> int:

@@ -913,3 +913,130 @@ ORACLE_API void oracle_decode_step_gated(int64_t Bs, int H, int Dh, int64_t W, d
     }
     free(kn); free(vn);
 }
+
+/* ===========================================================================
+ * Loss head ([R-step]: the output state m_t feeds the LM head
+ * p(x_{t+1} | x_{<=t}) = softmax(cap * tanh(U m_t / cap)) with cap = 15, and
+ * the loss is the mean over positions of CE + lambda ||m_t - m'_t||^2 / sqrt(d);
+ * the targets m' are states after the final RMSNorm, so m_t is taken as the
+ * final RMSNorm of the decoder's last hidden state h_t).
+ *   m_n   = h_n / sqrt(mean(h_n^2) + eps)            (no learned scale)
+ *   c_nv  = cap tanh((U m_n)_v / cap)
+ *   CE_n  = log sum_v exp(c_nv) - c_n,target_n        (0 when the target is
+ *           outside [0, V): the position is ignored; N still divides)
+ *   loss  = sum_n CE_n / N + lambda / (N sqrt(d)) sum_n ||m_n - m'_n||^2
+ * Gradients by the chain rule: dc = (softmax(c) - onehot) / N,
+ *   dz = dc (1 - tanh^2), dm = U^T dz + 2 lambda (m - m') / (N sqrt d),
+ *   dU = sum_n dz_n m_n^T, dh = r (dm - m mean(dm (.) m)), r = 1 / rms(h).
+ * h, m, m' [N,d]; U [V,d]; targets [N]; dh [N,d]; dU [V,d] (may be NULL);
+ * m_prime may be NULL (no consistency term). Returns the loss.
+ * ========================================================================= */
+ORACLE_API double oracle_lm_head(int64_t N, int d, int64_t V, double cap, double eps,
+                                 double lambda, const double *h, const double *U,
+                                 const int64_t *targets, const double *m_prime, double *m_out,
+                                 double *dh, double *dU)
+{
+    double *m = malloc((size_t)N * d * sizeof(double));
+    double *rr = malloc((size_t)N * sizeof(double));
+    double *ce = malloc((size_t)N * sizeof(double));
+    double *dz = dU ? malloc((size_t)N * V * sizeof(double)) : NULL;
+    if (!m || !rr || !ce || (dU && !dz)) abort();
+    const double cons = m_prime ? lambda / ((double)N * sqrt((double)d)) : 0.0;
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t n = 0; n < N; ++n) {
+        const double *hn = h + n * d;
+        double *mn = m + n * d;
+        const double r = 1.0 / sqrt(dot(hn, hn, d) / (double)d + eps);
+        rr[n] = r;
+        for (int e = 0; e < d; ++e) mn[e] = hn[e] * r;
+        double *c = malloc((size_t)V * sizeof(double));
+        double *dm = malloc((size_t)d * sizeof(double));
+        if (!c || !dm) abort();
+        double mx = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            c[v] = cap * tanh(dot(U + v * d, mn, d) / cap);
+            if (c[v] > mx) mx = c[v];
+        }
+        double sum = 0.0;
+        for (int64_t v = 0; v < V; ++v) sum += exp(c[v] - mx);
+        const double lse = mx + log(sum);
+        const int64_t tgt = targets[n];
+        const int valid = tgt >= 0 && tgt < V;
+        ce[n] = valid ? lse - c[tgt] : 0.0;
+        /* dm = U^T dz (+ consistency) */
+        for (int e = 0; e < d; ++e)
+            dm[e] = m_prime ? 2.0 * cons * (mn[e] - m_prime[n * d + e]) : 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            const double t = c[v] / cap;
+            double g = valid ? (exp(c[v] - lse) - (v == tgt ? 1.0 : 0.0)) / (double)N : 0.0;
+            g *= (1.0 - t * t);
+            if (dz) dz[n * V + v] = g;
+            for (int e = 0; e < d; ++e) dm[e] += g * U[v * d + e];
+        }
+        if (dh) {
+            const double mu = dot(dm, mn, d) / (double)d;
+            for (int e = 0; e < d; ++e) dh[n * d + e] = r * (dm[e] - mn[e] * mu);
+        }
+        free(c); free(dm);
+    }
+    if (dU) {
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v)
+            for (int e = 0; e < d; ++e) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += dz[n * V + v] * m[n * d + e];
+                dU[v * d + e] = acc;
+            }
+    }
+    double loss = 0.0;
+    for (int64_t n = 0; n < N; ++n) loss += ce[n];
+    loss /= (double)N;
+    if (m_prime)
+        for (int64_t i = 0; i < N * (int64_t)d; ++i) {
+            const double diff = m[i] - m_prime[i];
+            loss += cons * diff * diff;
+        }
+    if (m_out) memcpy(m_out, m, (size_t)N * d * sizeof(double));
+    free(m); free(rr); free(ce); free(dz);
+    return loss;
+}
+
+/* Per-row quantities of the loss head for listed rows only (for large
+ * shapes): the log-sum-exp of row n's capped logits, its CE term and the
+ * head's part of dm_n (U^T dz_n, no consistency term), for rows[i]. */
+ORACLE_API void oracle_lm_head_rows(int64_t nrows, const int64_t *rows, int d, int64_t V,
+                                    double cap, double eps, int64_t N, const double *h,
+                                    const double *U, const int64_t *targets, double *lse_out,
+                                    double *ce_out, double *dm_out)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t n = rows[i];
+        const double *hn = h + n * d;
+        double *mn = malloc((size_t)d * sizeof(double));
+        double *c = malloc((size_t)V * sizeof(double));
+        if (!mn || !c) abort();
+        const double r = 1.0 / sqrt(dot(hn, hn, d) / (double)d + eps);
+        for (int e = 0; e < d; ++e) mn[e] = hn[e] * r;
+        double mx = -INFINITY;
+        for (int64_t v = 0; v < V; ++v) {
+            c[v] = cap * tanh(dot(U + v * d, mn, d) / cap);
+            if (c[v] > mx) mx = c[v];
+        }
+        double sum = 0.0;
+        for (int64_t v = 0; v < V; ++v) sum += exp(c[v] - mx);
+        const double lse = mx + log(sum);
+        const int64_t tgt = targets[n];
+        const int valid = tgt >= 0 && tgt < V;
+        lse_out[i] = lse;
+        ce_out[i] = valid ? lse - c[tgt] : 0.0;
+        for (int e = 0; e < d; ++e) dm_out[i * d + e] = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            const double t = c[v] / cap;
+            const double g = valid ? (exp(c[v] - lse) - (v == tgt ? 1.0 : 0.0)) / (double)N
+                                       * (1.0 - t * t) : 0.0;
+            for (int e = 0; e < d; ++e) dm_out[i * d + e] += g * U[v * d + e];
+        }
+        free(mn); free(c);
+    }
+}

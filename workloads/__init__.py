@@ -145,6 +145,18 @@ def decode_initial_memory(shape: DecodeShape, seed: int) -> torch.Tensor:
     return _normal(g, (shape.Bs, shape.d)).to(torch_dtype(shape.dtype))
 
 
+def head_inputs(N: int, d: int, V: int, seed: int, dtype: str = BF16) -> dict:
+    """Loss-head inputs: the decoder's last hidden state h ~ N(0, 1) [N, d],
+    the targets m' ~ N(0, 1) [N, d] (unit RMS, like a final-RMSNorm state),
+    the head U ~ N(0, 1/d) [V, d] and next-token targets uniform in [0, V)."""
+    g = torch.Generator().manual_seed(int(seed) * 104729 + 5)
+    dt = torch_dtype(dtype)
+    out = {"h": _normal(g, (N, d)).to(dt), "m_prime": _normal(g, (N, d)).to(dt),
+           "U": _normal(g, (V, d), 1.0 / math.sqrt(d)).to(dt)}
+    out["targets"] = torch.randint(0, V, (N,), generator=g, dtype=torch.int64)
+    return out
+
+
 def gate_vectors(H: int, Dh: int, seed: int, std: float = 0.5) -> dict:
     """Four channel-wise gate logit vectors [H*Dh] ~ N(0, std^2) in float32,
     named a_kl, a_kr, a_vl, a_vr (local/recurrent key, local/recurrent value)."""
