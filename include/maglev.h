@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MAGLEV_ABI_VERSION 4
+#define MAGLEV_ABI_VERSION 5
 
 typedef enum {
     MAGLEV_OK = 0,
@@ -361,6 +361,41 @@ maglev_status_t maglev_attn_bwd(const maglev_geom_t *g, const void *q, const voi
                                 const void *v, const void *o, const float *lse, const void *dO,
                                 void *dq, void *dk, void *dv, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace maglev_lm_head needs (0 on invalid sizes). The
+ * float32 logits [N, V] dominate: 4 N V bytes, plus the dz buffer (N V
+ * elements of dtype) and O(N d) more. */
+size_t maglev_lm_head_workspace(int64_t N, int32_t d, int64_t V, int32_t dtype);
+
+/* Loss head of the lifted pass ([R-step]: the output state m_t feeds the
+ * soft-capped LM head, and the loss averages the cross-entropy and the
+ * consistency term over the positions; [R-bg]: the targets m' are states
+ * after the final RMSNorm):
+ *   m_n    = h_n / sqrt(mean_e h_ne^2 + eps)        (RMSNorm, no learned scale)
+ *   c_nv   = cap tanh((U m_n)_v / cap)
+ *   CE_n   = logsumexp_v c_nv - c_n,target_n  (0 when target_n is outside [0, V))
+ *   loss   = sum_n CE_n / N + lambda / (N sqrt(d)) sum_n ||m_n - m'_n||^2
+ * Inputs: h [N, d] dtype (the decoder's last hidden state, one row per
+ *   position); U [V, d] dtype (the head's weight, one row per vocabulary
+ *   entry); targets [N] int64 (device); m_prime [N, d] dtype or NULL (then
+ *   the consistency term is left out and lambda is unused).
+ * Outputs: m [N, d] dtype = RMSNorm(h) (overwritten); loss: device float32
+ *   scalar; dh [N, d] float32 and dU [V, d] float32, each optional (NULL:
+ *   not computed; with both NULL no backward work is done): the gradients of
+ *   loss w.r.t. h and U.
+ * accumulate: bit 0 -> dh +=, bit 1 -> dU +=, bit 2 -> loss +=; a clear bit
+ *   overwrites. Every position counts in N, also one whose target is ignored.
+ * Constraints: N >= 1 (the mean over no positions is undefined), d a multiple
+ *   of 16, V a multiple of 8 and >= 16, cap > 0 and finite, eps >= 0 and
+ *   finite, lambda not NaN.
+ * workspace: at least maglev_lm_head_workspace(N, d, V, dtype) bytes, owned by
+ *   the caller, 16-byte aligned; contents are scratch on return. No
+ *   floating-point atomics: the result is deterministic. */
+maglev_status_t maglev_lm_head(int64_t N, int32_t d, int64_t V, float cap, float eps,
+                               float lambda, int32_t dtype, const void *h, const void *U,
+                               const int64_t *targets, const void *m_prime, void *m, float *loss,
+                               float *dh, float *dU, unsigned accumulate, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* pos[b] += 1 for b < Bs on the device (moves every stream to its next ring
  * slot; kept separate so one decode step can be captured and replayed). */

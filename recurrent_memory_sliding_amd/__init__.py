@@ -25,7 +25,7 @@ __all__ = [
     "maglev_swa_inject_bwd_workspace", "maglev_consistency_loss",
     "maglev_consistency_loss_workspace", "maglev_decode_step", "maglev_decode_workspace",
     "maglev_decode_advance", "maglev_prepare", "maglev_abi_version", "maglev_profile_enable",
-    "maglev_profile_read",
+    "maglev_profile_read", "maglev_lm_head", "maglev_lm_head_workspace", "LM_CAP",
 ]
 
 MAGLEV_F32 = 0
@@ -88,6 +88,9 @@ def lib() -> ctypes.CDLL:
             "maglev_attn_bwd": ([G] + [vp] * 9 + [vp, sz, vp], i32),
             "maglev_decode_step_gated": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
                                          + [vp, f32] + [vp] * 4 + [vp, sz, vp], i32),
+            "maglev_lm_head_workspace": ([i64, i32, i64, i32], sz),
+            "maglev_lm_head": ([i64, i32, i64, f32, f32, f32, i32] + [vp] * 8 + [u32, vp, sz, vp],
+                               i32),
             "maglev_prepare": ([i32, f32, i64], i32),
             "maglev_status_string": ([i32], ctypes.c_char_p),
             "maglev_last_error": ([], ctypes.c_char_p),
@@ -303,6 +306,47 @@ def maglev_consistency_loss(m, m_prime, lam: float, loss=None, dm=None, dm_prime
                                          workspace.numel() * workspace.element_size(),
                                          _stream(stream)), "maglev_consistency_loss")
     return loss, dm, dm_prime
+
+
+LM_CAP = 15.0   # soft cap of the LM head's logits
+
+
+def maglev_lm_head_workspace(N: int, d: int, V: int, dtype=torch.bfloat16) -> int:
+    return int(lib().maglev_lm_head_workspace(N, d, V, _DT[dtype]))
+
+
+def maglev_lm_head(h, U, targets, m_prime=None, lam: float = 0.0, cap: float = LM_CAP,
+                   eps: float = 1e-6, want_grads: bool = True, m=None, loss=None, dh=None,
+                   dU=None, accumulate: int = 0, workspace=None, stream=None):
+    """Loss head: (loss [1] float32, m = RMSNorm(h) [..., d] dtype, dh [..., d]
+    float32 or None, dU [V, d] float32 or None). targets: int64, h's leading
+    shape; entries outside [0, V) are ignored."""
+    _dev(h, U, targets, m_prime, m, loss, dh, dU, workspace)
+    _same(h, U, m_prime, m)
+    d = h.shape[-1]
+    N = h.numel() // d
+    V = U.shape[0]
+    if U.dim() != 2 or U.shape[1] != d:
+        raise MaglevError("U must be [V, d]")
+    if targets.dtype != torch.int64 or targets.numel() != N or not targets.is_contiguous():
+        raise MaglevError("targets must be contiguous int64 with one entry per row of h")
+    if m_prime is not None and m_prime.shape != h.shape:
+        raise MaglevError("m_prime must have h's shape")
+    dev = h.device
+    m = torch.empty_like(h) if m is None else m
+    loss = torch.empty((1,), dtype=torch.float32, device=dev) if loss is None else loss
+    if want_grads:
+        dh = torch.empty(h.shape, dtype=torch.float32, device=dev) if dh is None else dh
+        dU = torch.empty(U.shape, dtype=torch.float32, device=dev) if dU is None else dU
+    need = int(lib().maglev_lm_head_workspace(N, d, V, _dtype_code(h)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _check(lib().maglev_lm_head(N, d, V, cap, eps, lam, _dtype_code(h), _ptr(h), _ptr(U),
+                                _ptr(targets), _ptr(m_prime), _ptr(m), _ptr(loss), _ptr(dh),
+                                _ptr(dU), accumulate, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream)),
+           "maglev_lm_head")
+    return loss, m, dh, dU
 
 
 def maglev_decode_workspace(Bs: int, H: int, Dh: int, W: int) -> int:

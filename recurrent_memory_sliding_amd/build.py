@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmaglev.so")
 SOURCES = ["maglev_api.cpp", "profile.cpp", "path.hip", "mfma_gemm.hip", "mfma_attn.hip",
-           "loss_decode.hip", "gated_mix.hip"]
+           "loss_decode.hip", "gated_mix.hip", "loss_head.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-x", "hip", "-std=c++17", "-O3", "-fPIC", "--offload-arch=gfx950",

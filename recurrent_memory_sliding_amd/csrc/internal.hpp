@@ -123,6 +123,23 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
                        const void *mp, float *loss, float *dm, float *dmp, unsigned accumulate,
                        void *ws, hipStream_t s);
 
+// ---- loss head -----------------------------------------------------------
+struct HeadWorkspace {
+    float *rstd = nullptr;     // [N] 1 / rms of each row of h
+    float *ce = nullptr;       // [N] per-position cross-entropy
+    float *logits = nullptr;   // [N, V] capped logits
+    void *dz = nullptr;        // [N, V] dtype, gradient w.r.t. the raw logits
+    float *dm = nullptr;       // [N, d] gradient w.r.t. m
+    void *loss_ws = nullptr;   // consistency-loss partial sums
+};
+// Bytes of workspace; with base != nullptr, also carves it into *L.
+size_t lm_head_workspace_bytes(int64_t N, int d, int64_t V, int dtype, HeadWorkspace *L,
+                               char *base);
+hipError_t launch_lm_head(int64_t N, int d, int64_t V, float cap, float eps, float lambda,
+                          int dtype, const void *h, const void *U, const int64_t *targets,
+                          const void *m_prime, void *m, float *loss, float *dh, float *dU,
+                          unsigned acc, const HeadWorkspace &ws, hipStream_t s);
+
 // ---- decode -----------------------------------------------------------------
 size_t decode_workspace_bytes(int Bs, int H, int Dh, int W);
 // gates == nullptr: the sigma-gated form with gate [H]; otherwise the gated

@@ -312,6 +312,50 @@ maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int3
                                   workspace, stream));
 }
 
+static bool head_sizes_ok(int64_t N, int32_t d, int64_t V)
+{
+    return N >= 1 && N <= INT32_MAX && d >= 16 && (d % 16) == 0 && V >= 16 && (V % 8) == 0 &&
+           V <= INT32_MAX;
+}
+
+size_t maglev_lm_head_workspace(int64_t N, int32_t d, int64_t V, int32_t dtype)
+{
+    if (!head_sizes_ok(N, d, V) || (dtype != MAGLEV_F32 && dtype != MAGLEV_BF16)) return 0;
+    HeadWorkspace L;
+    return lm_head_workspace_bytes(N, d, V, dtype, &L, nullptr);
+}
+
+maglev_status_t maglev_lm_head(int64_t N, int32_t d, int64_t V, float cap, float eps,
+                               float lambda, int32_t dtype, const void *h, const void *U,
+                               const int64_t *targets, const void *m_prime, void *m, float *loss,
+                               float *dh, float *dU, unsigned accumulate, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    if (!head_sizes_ok(N, d, V))
+        return fail(MAGLEV_ERR_INVALID_VALUE,
+                    "need N >= 1, d a multiple of 16, V a multiple of 8 and >= 16");
+    if (!(cap > 0.0f) || !isfinite(cap)) return fail(MAGLEV_ERR_INVALID_VALUE, "cap must be finite and > 0");
+    if (!(eps >= 0.0f) || !isfinite(eps)) return fail(MAGLEV_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+    if (!(lambda == lambda)) return fail(MAGLEV_ERR_INVALID_VALUE, "lambda is NaN");
+    maglev_status_t st = check_dtype(dtype);
+    if (st != MAGLEV_OK) return st;
+    st = check_ptrs({h, U, m});
+    if (st != MAGLEV_OK) return st;
+    if (!targets) return fail(MAGLEV_ERR_INVALID_VALUE, "targets is NULL");
+    if (!loss) return fail(MAGLEV_ERR_INVALID_VALUE, "loss is NULL");
+    if ((m_prime && !aligned16(m_prime)) || (dh && !aligned16(dh)) || (dU && !aligned16(dU)))
+        return fail(MAGLEV_ERR_MISALIGNED, "m_prime / dh / dU not 16-byte aligned");
+    if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    HeadWorkspace L;
+    const size_t need = lm_head_workspace_bytes(N, d, V, dtype, &L, nullptr);
+    if (!workspace || workspace_bytes < need)
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (!aligned16(workspace)) return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    lm_head_workspace_bytes(N, d, V, dtype, &L, static_cast<char *>(workspace));
+    return hip_status(launch_lm_head(N, d, V, cap, eps, lambda, dtype, h, U, targets, m_prime, m,
+                                     loss, dh, dU, accumulate, L, stream));
+}
+
 size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W)
 {
     if (Bs < 0 || H < 1 || (Dh != 64 && Dh != 128) || W < 1) return 0;

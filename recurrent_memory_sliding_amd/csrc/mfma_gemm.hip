@@ -410,6 +410,58 @@ struct ProjBwdDw {
     }
 };
 
+// Loss-head products ([V, d] head U, N_tok rows):
+//   logits  C[n, v] = cap tanh((m U^T)[n, v] / cap)    A = m [N,d], B = U [V,d], both K-major
+//   dm      dm[n, e] = sum_v dz[n, v] U[v, e]           A = dz [N,V] K-major, B = U MN-major
+//   dU      dU[v, e] (+)= sum_n dz[n, v] m[n, e]        A = dz MN-major, B = m MN-major
+struct LmLogits {
+    static constexpr bool A_KMAJOR = true, B_KMAJOR = true;
+    const bf16 *m, *u;
+    float *out;
+    int64_t M, N, K, T;
+    float cap;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0, b_ld = 0;
+    MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const { return m + row * K + k; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const { return u + n * K + k; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV void store(int64_t row, int64_t, int64_t n, float x, int) const
+    {
+        out[row * N + n] = cap * tanhf(x / cap);
+    }
+};
+struct LmDm {
+    static constexpr bool A_KMAJOR = true, B_KMAJOR = false;
+    const bf16 *dz, *u;
+    float *dm;
+    int64_t M, N, K, T;
+    int64_t b_ld;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0;
+    MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const { return dz + row * K + k; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const { return u + k * b_ld + n; }
+    MAGLEV_DEV void store(int64_t row, int64_t, int64_t n, float x, int) const { dm[row * N + n] = x; }
+};
+struct LmDu {
+    static constexpr bool A_KMAJOR = false, B_KMAJOR = false;
+    const bf16 *dz, *m;
+    float *du;
+    int64_t M, N, K, T;
+    int64_t a_ld, b_ld;
+    bool acc;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0;
+    MAGLEV_DEV const bf16 *a_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t k, int64_t col) const { return dz + k * a_ld + col; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t col) const { return m + k * b_ld + col; }
+    MAGLEV_DEV void store(int64_t r, int64_t, int64_t e, float x, int) const
+    {
+        float *p = du + r * N + e;
+        *p = acc ? *p + x : x;
+    }
+};
+
 // Tile configurations, chosen by timing the three products at the d20 shape
 // (N_tok = 16384, d = 1280, 10 x 128 heads): two LDS stages and 8 or 16 waves
 // per workgroup, so that each SIMD has several waves to cover LDS and barrier
@@ -430,6 +482,39 @@ static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const 
     prof::Scope ts(name, s);
     hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn * ksplit)), dim3(Cfg::NT), 0, s,
                        p, kper, group_m);
+}
+
+void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m, const void *u,
+                           float *logits, hipStream_t s)
+{
+    LmLogits p;
+    p.m = static_cast<const bf16 *>(m);
+    p.u = static_cast<const bf16 *>(u);
+    p.out = logits;
+    p.M = N; p.N = V; p.K = d; p.T = 0; p.cap = cap;
+    run_gemm<ProjCfg>(p, 1, p.K, s, "lm_logits", 16);
+}
+
+void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,
+                       hipStream_t s)
+{
+    LmDm p;
+    p.dz = static_cast<const bf16 *>(dz);
+    p.u = static_cast<const bf16 *>(u);
+    p.dm = dm;
+    p.M = N; p.N = d; p.K = V; p.T = 0; p.b_ld = d;
+    run_gemm<ProjCfg>(p, 1, p.K, s, "lm_dm", 16);
+}
+
+void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *m, float *du,
+                       bool acc, hipStream_t s)
+{
+    LmDu p;
+    p.dz = static_cast<const bf16 *>(dz);
+    p.m = static_cast<const bf16 *>(m);
+    p.du = du;
+    p.M = V; p.N = d; p.K = N; p.T = 0; p.a_ld = V; p.b_ld = d; p.acc = acc;
+    run_gemm<DwCfg>(p, 1, p.K, s, "lm_du", 1 << 20);
 }
 
 void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,

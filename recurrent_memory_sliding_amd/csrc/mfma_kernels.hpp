@@ -34,6 +34,15 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
                           float *dWk, float *dWv, unsigned acc, const BwdWorkspace &ws,
                           hipStream_t s);
 
+// Loss-head products: logits = cap tanh(m U^T / cap) (float32 [N,V]),
+// dm = dz U (float32 [N,d]), dU (+)= dz^T m (float32 [V,d]).
+void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m, const void *u,
+                           float *logits, hipStream_t s);
+void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,
+                       hipStream_t s);
+void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *m, float *du,
+                       bool acc, hipStream_t s);
+
 // Split-K factor the dW GEMM uses for this geometry (workspace sizing).
 int dw_ksplit(const Geom &g);
 

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
               "maglev_decode_step", "maglev_consistency_loss", "maglev_mem_project_gated",
-              "maglev_swa_inject_bwd_gated", "maglev_decode_step_gated"]:
+              "maglev_swa_inject_bwd_gated", "maglev_decode_step_gated", "maglev_lm_head"]:
         assert n in names
 
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.maglev_abi_version() == 4
+    assert L.maglev_abi_version() == 5
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
     assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
     assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
@@ -269,6 +269,44 @@ def test_shared_projection_validation(L):
     assert L.maglev_mem_project_bwd(ctypes.byref(g), *pp, 0, None, 0, None) == WORKSPACE
     bad = list(pp); bad[2] = None     # m'
     assert L.maglev_mem_project_bwd(ctypes.byref(g), *bad, 0, FAKE, pneed, None) == INVALID
+
+
+def test_loss_head_workspace_and_validation(L):
+    need = L.maglev_lm_head_workspace(16384, 1280, 65536, 1)
+    # float32 logits and bf16 dz dominate: 6 N V bytes
+    assert need >= 6 * 16384 * 65536
+    assert L.maglev_lm_head_workspace(16384, 1280, 65536, 0) > need
+    for bad in [(0, 64, 64, 1), (4, 40, 64, 1), (4, 64, 12, 1), (4, 64, 8, 1), (4, 64, 64, 3)]:
+        assert L.maglev_lm_head_workspace(*bad) == 0
+    w = L.maglev_lm_head_workspace(4, 64, 64, 1)
+    # h U targets m_prime m loss dh dU
+    ptrs = [FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None]
+
+    def call(N=4, d=64, V=64, cap=15.0, eps=1e-6, lam=0.0, dtype=1, p=None, acc=0, ws=FAKE,
+             wsb=None):
+        return L.maglev_lm_head(N, d, V, cap, eps, lam, dtype, *(p or ptrs), acc, ws,
+                                w if wsb is None else wsb, None)
+
+    assert call(N=0) == INVALID
+    assert call(d=40) == INVALID
+    assert call(V=12) == INVALID
+    assert call(V=8) == INVALID
+    assert call(cap=0.0) == INVALID
+    assert call(cap=float("inf")) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(lam=float("nan")) == INVALID
+    assert call(dtype=4) == INVALID
+    assert call(acc=8) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=w - 1) == WORKSPACE
+    assert call(ws=FAKE_ODD) == MISALIGNED
+    for i, status in [(0, INVALID), (1, INVALID), (2, INVALID), (4, INVALID), (5, INVALID)]:
+        bad = list(ptrs); bad[i] = None
+        assert call(p=bad) == status, i
+    for i in (0, 1, 3, 4, 6, 7):
+        bad = list(ptrs); bad[i] = FAKE_ODD
+        assert call(p=bad) == MISALIGNED, i
 
 
 def test_prepare_validation(L):
