@@ -459,6 +459,67 @@ def bench_stack(sh, layers, steps, warmup):
     return out
 
 
+def bench_loss_head(N, d, V, steps, warmup):
+    """The loss head at the last hidden state of a batch: final RMSNorm,
+    soft-capped LM head (V entries), mean cross-entropy, consistency term
+    (lambda 0.5) and the gradients w.r.t. h and U, one C-ABI call per step,
+    timed with HIP events; a second timed pass records each kernel's average
+    duration for its roofline."""
+    x = wl.head_inputs(N, d, V, 12, wl.BF16)
+    g = {n: t.cuda() for n, t in x.items()}
+    m = torch.empty_like(g["h"])
+    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+    dh = torch.empty(g["h"].shape, dtype=torch.float32, device="cuda")
+    dU = torch.empty(g["U"].shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty((rms.maglev_lm_head_workspace(N, d, V),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        rms.maglev_lm_head(g["h"], g["U"], g["targets"], m_prime=g["m_prime"], lam=0.5, m=m,
+                           loss=loss, dh=dh, dU=dU, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    rms.maglev_profile_enable(True)
+    for _ in range(max(steps // 2, 2)):
+        step()
+    torch.cuda.synchronize()
+    rms.maglev_profile_enable(False)
+    survey = rms.maglev_profile_read()
+    gemm = 2.0 * N * V * d
+    nd = 2.0 * N * d   # one bf16 [N, d] tensor
+    work = {  # (algorithmic flops, algorithmic bytes) per launch
+        "lm_logits": (gemm, nd + 2.0 * V * d + 4.0 * N * V),
+        "head_ce": (0.0, 4.0 * N * V + 2.0 * N * V + 8.0 * N),
+        "lm_dm": (gemm, 2.0 * N * V + 2.0 * V * d + 4.0 * N * d),
+        "lm_du": (gemm, 2.0 * N * V + nd + 4.0 * V * d),
+        "head_norm": (0.0, 2.0 * nd + 4.0 * N),
+        "head_norm_bwd": (0.0, nd + 8.0 * N * d + 4.0 * N),
+    }
+    kernels = {}
+    for name, (n, tot) in sorted(survey.items(), key=lambda kv: -kv[1][1]):
+        rec = {"launches": n, "avg_us": round(tot * 1e3 / n, 2)}
+        if name in work:
+            rec["roofline"] = roofline_of(work[name][0], work[name][1], tot / n / 1e3)
+        kernels[name] = rec
+    flops = 3.0 * gemm
+    del g, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tokens/s": round(N / (ms / 1e3), 1),
+            "algorithmic_TFLOP": round(flops / 1e12, 4),
+            "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1),
+            "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": kernels}
+
+
 def cpu_baseline(sh):
     """The oracle, as it stands, on a bounded slice of the training workload:
     sequences 0-5 of 8, all heads, full T. The slice holds 6/8 of the layer's
@@ -507,6 +568,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefiller", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--no-head", action="store_true")
     ap.add_argument("--mix", choices=("sigma", "gated"), default="sigma",
                     help="mixing form: per-head sigma gate (default) or the gated form with "
                          "channel-wise 2 sigmoid gates and the normalised memory key")
@@ -600,6 +662,13 @@ def main():
                         % (wl.D20_STACK_LAYERS, ssh.B, ssh.T, ssh.W, ssh.d),
             "layers": wl.D20_STACK_LAYERS,
             **bench_stack(ssh, wl.D20_STACK_LAYERS, 3, 1)}
+    if not args.no_head:
+        N, d, V = sh.B * sh.T, sh.d, wl.D20_VOCAB
+        result["loss_head"] = {
+            "workload": "loss head over %d positions (B=%d x T=%d), d=%d, V=%d, bf16: final "
+                        "RMSNorm, 15-capped LM head, mean CE + consistency, dh and dU"
+                        % (N, sh.B, sh.T, d, V),
+            **bench_loss_head(N, d, V, max(args.steps // 2, 5), 2)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sh)
     print(json.dumps(result), flush=True)

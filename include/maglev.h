@@ -386,8 +386,9 @@ size_t maglev_lm_head_workspace(int64_t N, int32_t d, int64_t V, int32_t dtype);
  * accumulate: bit 0 -> dh +=, bit 1 -> dU +=, bit 2 -> loss +=; a clear bit
  *   overwrites. Every position counts in N, also one whose target is ignored.
  * Constraints: N >= 1 (the mean over no positions is undefined), d a multiple
- *   of 16, V a multiple of 8 and >= 16, cap > 0 and finite, eps >= 0 and
- *   finite, lambda not NaN.
+ *   of 16, V a multiple of 8 and >= 16, 0 < cap <= 64 (the log-sum-exp is
+ *   taken without a running maximum, which needs exp(cap) V finite in
+ *   float32), eps >= 0 and finite, lambda not NaN.
  * workspace: at least maglev_lm_head_workspace(N, d, V, dtype) bytes, owned by
  *   the caller, 16-byte aligned; contents are scratch on return. No
  *   floating-point atomics: the result is deterministic. */

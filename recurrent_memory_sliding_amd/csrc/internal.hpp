@@ -128,6 +128,7 @@ struct HeadWorkspace {
     float *rstd = nullptr;     // [N] 1 / rms of each row of h
     float *ce = nullptr;       // [N] per-position cross-entropy
     float *logits = nullptr;   // [N, V] capped logits
+    float *rowsum = nullptr;   // [N, column tiles] partial sums of exp(logit)
     void *dz = nullptr;        // [N, V] dtype, gradient w.r.t. the raw logits
     float *dm = nullptr;       // [N, d] gradient w.r.t. m
     void *loss_ws = nullptr;   // consistency-loss partial sums

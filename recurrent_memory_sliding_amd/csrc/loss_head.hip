@@ -13,7 +13,8 @@
 //   dm = dz U + consistency term,  dU (+)= dz^T m,  dh = r (dm - m mean(dm m))
 // The capped logits are materialised in float32 ([N, V]) by the head GEMM's
 // epilogue; one workgroup per row then forms lse, CE and dz (three passes
-// over the row, the second and third mostly from L2); dz (activation dtype)
+// with the per-row sums of exp(c) over each column tile; one workgroup per row
+// then forms lse, CE and dz in one pass over the row; dz (activation dtype)
 // is the A operand of the two gradient products.
 #include "common.hpp"
 #include "internal.hpp"
@@ -85,16 +86,6 @@ __global__ __launch_bounds__(256) void head_norm_bwd(int64_t N, int d, const T *
     }
 }
 
-MAGLEV_DEV float block_max(float x, float *red)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-
 MAGLEV_DEV float block_total(float x, float *red)
 {
     x = wave_sum(x);
@@ -105,32 +96,32 @@ MAGLEV_DEV float block_total(float x, float *red)
 }
 
 // One workgroup (256 threads) per row n of the capped logits c [N, V]:
-// lse_n, CE_n (0 for a target outside [0, V)), and, when dz is not null,
-// dz[n, :] as above. V is a multiple of 8.
+// lse_n = log sum_v exp(c_nv) (no running maximum: |c| <= cap <= 64 keeps
+// every exp(c) finite and normal in float32), CE_n (0 for a target outside
+// [0, V)), and, when dz is not null, dz[n, :] as above. The row's sum comes
+// from the ntn per-tile partial sums the head product wrote (rowsum != null)
+// or from a pass over the row. V is a multiple of 8.
 template <typename T>
 __global__ __launch_bounds__(256) void head_ce(int64_t N, int64_t V, float cap, const float *c,
+                                               const float *rowsum, int64_t ntn,
                                                const int64_t *targets, float *ce, T *dz)
 {
     __shared__ float red[4];
     const int64_t n = blockIdx.x;
     const float *row = c + n * V;
-    float mx = -INFINITY;
-    for (int64_t v = 8 * (int64_t)threadIdx.x; v < V; v += 2048) {
-        float x[8];
-        load8(row + v, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    }
-    mx = block_max(mx, red);
     float sum = 0.0f;
-    for (int64_t v = 8 * (int64_t)threadIdx.x; v < V; v += 2048) {
-        float x[8];
-        load8(row + v, x);
+    if (rowsum) {
+        for (int64_t t = threadIdx.x; t < ntn; t += 256) sum += rowsum[n * ntn + t];
+    } else {
+        for (int64_t v = 8 * (int64_t)threadIdx.x; v < V; v += 2048) {
+            float x[8];
+            load8(row + v, x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum += __expf(x[e] - mx);
+            for (int e = 0; e < 8; ++e) sum += __expf(x[e]);
+        }
     }
     sum = block_total(sum, red);
-    const float lse = mx + __logf(sum);
+    const float lse = __logf(sum);
     const int64_t tgt = targets[n];
     const bool valid = tgt >= 0 && tgt < V;
     if (threadIdx.x == 0) ce[n] = valid ? lse - row[tgt] : 0.0f;
@@ -211,12 +202,14 @@ size_t lm_head_workspace_bytes(int64_t N, int d, int64_t V, int dtype, HeadWorks
     const size_t oR = take((size_t)N * sizeof(float));
     const size_t oC = take((size_t)N * sizeof(float));
     const size_t oL = take((size_t)N * V * sizeof(float));
+    const size_t oP = take((size_t)N * mfma::lm_logits_col_tiles(V) * sizeof(float));
     const size_t oZ = take((size_t)N * V * esz);
     const size_t oM = take((size_t)N * d * sizeof(float));
     const size_t oS = take(loss_workspace_bytes(N, d));
     L->rstd = base ? reinterpret_cast<float *>(base + oR) : nullptr;
     L->ce = base ? reinterpret_cast<float *>(base + oC) : nullptr;
     L->logits = base ? reinterpret_cast<float *>(base + oL) : nullptr;
+    L->rowsum = base ? reinterpret_cast<float *>(base + oP) : nullptr;
     L->dz = base ? static_cast<void *>(base + oZ) : nullptr;
     L->dm = base ? reinterpret_cast<float *>(base + oM) : nullptr;
     L->loss_ws = base ? static_cast<void *>(base + oS) : nullptr;
@@ -238,7 +231,7 @@ static hipError_t lm_head_t(int64_t N, int d, int64_t V, float cap, float eps, f
                            h, m, ws.rstd);
     }
     if constexpr (sizeof(T) == 2) {
-        mfma::launch_lm_logits_bf16(N, V, d, cap, m, Uv, ws.logits, s);
+        mfma::launch_lm_logits_bf16(N, V, d, cap, m, Uv, ws.logits, ws.rowsum, s);
     } else {
         prof::Scope ts("lm_logits", s);
         simt::gemm_tiled<F32Rows, F32RowsT, CapStore><<<dim3((unsigned)((V + 63) / 64),
@@ -249,8 +242,10 @@ static hipError_t lm_head_t(int64_t N, int d, int64_t V, float cap, float eps, f
     }
     {
         prof::Scope ts("head_ce", s);
+        const bool sums = sizeof(T) == 2;   // the MFMA head product writes row sums
         hipLaunchKernelGGL(head_ce<T>, dim3((unsigned)N), dim3(256), 0, s, N, V, cap, ws.logits,
-                           targets, ws.ce, grads ? static_cast<T *>(ws.dz) : nullptr);
+                           sums ? ws.rowsum : nullptr, mfma::lm_logits_col_tiles(V), targets,
+                           ws.ce, grads ? static_cast<T *>(ws.dz) : nullptr);
         hipLaunchKernelGGL(head_loss, dim3(1), dim3(256), 0, s, N, ws.ce, loss, acc & 4u);
     }
     if (grads) {

@@ -334,7 +334,7 @@ maglev_status_t maglev_lm_head(int64_t N, int32_t d, int64_t V, float cap, float
     if (!head_sizes_ok(N, d, V))
         return fail(MAGLEV_ERR_INVALID_VALUE,
                     "need N >= 1, d a multiple of 16, V a multiple of 8 and >= 16");
-    if (!(cap > 0.0f) || !isfinite(cap)) return fail(MAGLEV_ERR_INVALID_VALUE, "cap must be finite and > 0");
+    if (!(cap > 0.0f && cap <= 64.0f)) return fail(MAGLEV_ERR_INVALID_VALUE, "cap must be in (0, 64]");
     if (!(eps >= 0.0f) || !isfinite(eps)) return fail(MAGLEV_ERR_INVALID_VALUE, "eps must be finite and >= 0");
     if (!(lambda == lambda)) return fail(MAGLEV_ERR_INVALID_VALUE, "lambda is NaN");
     maglev_status_t st = check_dtype(dtype);

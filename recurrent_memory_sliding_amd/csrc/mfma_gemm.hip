@@ -15,6 +15,9 @@
 // pointers; the sigma gate is folded into a pre-scaled weight copy (dX) or the
 // epilogue (dW). The gated form hands over gradients that already carry its
 // gates and norm (no gate: s = 1).
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "mfma_kernels.hpp"
 #include "profile.hpp"
@@ -75,6 +78,36 @@ MAGLEV_DEV bf16x8 read_frag(const bf16 *lds, int rb, int ks, int lane)
         const i16x4 hi = lds_read_tr16(lds + kb * R + L::slot(kb, c) * 8 + e);
         return join_tr(lo, hi);
     }
+}
+
+// A problem with a `rowsum` member also wants, for every row, the sum over
+// this tile's columns of the value its store_sum(m, n, x) returns; the tile
+// writes it to rowsum[m * rs_ld + column tile].
+template <class P, class = void>
+struct HasRowSum : std::false_type {};
+template <class P>
+struct HasRowSum<P, std::void_t<decltype(std::declval<const P &>().rowsum)>> : std::true_type {};
+
+// Sums v[k] (k < 32) over the 32 lanes of each half wave with 31 exchanges:
+// at distance D a lane keeps the half of its C live values selected by lane
+// bit D and adds the partner's copy of that half. Afterwards v[0] of lane l
+// holds the sum of value index l & 31. (One template level per distance, so
+// every register index is a constant.)
+template <int D, int C>
+MAGLEV_DEV void transpose_sum_level(float (&v)[32], int lane)
+{
+    const bool hi = (lane & D) != 0;
+#pragma unroll
+    for (int k = 0; k < C / 2; ++k) {
+        const float send = hi ? v[k] : v[C / 2 + k];
+        const float keep = hi ? v[C / 2 + k] : v[k];
+        v[k] = keep + __shfl_xor(send, D, 64);
+    }
+    if constexpr (D > 1) transpose_sum_level<D / 2, C / 2>(v, lane);
+}
+MAGLEV_DEV void half_wave_transpose_sum(float (&v)[32], int lane)
+{
+    transpose_sum_level<16, 32>(v, lane);
 }
 
 // C[M,N] = sum_k A(m,k) B(n,k) over k in this workgroup's split.
@@ -169,8 +202,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
     const int64_t b_step = P::B_KMAJOR ? Cfg::BK : Cfg::BK * p.b_ld;
     // Next K at which an operand stored in segments (a_kseg / b_kseg elements,
     // multiples of BK) switches segment: its pointers are recomputed there.
-    int64_t a_next = p.a_kseg > 0 ? (kb / p.a_kseg + 1) * p.a_kseg : INT64_MAX;
-    int64_t b_next = p.b_kseg > 0 ? (kb / p.b_kseg + 1) * p.b_kseg : INT64_MAX;
+    const int64_t a_seg = p.a_kseg > 0 ? p.a_kseg : 1, b_seg = p.b_kseg > 0 ? p.b_kseg : 1;
+    int64_t a_next = p.a_kseg > 0 ? (kb / a_seg + 1) * a_seg : INT64_MAX;
+    int64_t b_next = p.b_kseg > 0 ? (kb / b_seg + 1) * b_seg : INT64_MAX;
 
     // DMA of K step `it` into stage `buf` (the pointers are at step it), then
     // advance the pointers. Tails read the zero rows past ke.
@@ -254,22 +288,65 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
 
     // Epilogue: row index m and its position t = m mod T (from m0 mod T).
     const int g = lane >> 5;
-    const int64_t t0 = p.T > 0 ? m0 % p.T : 0;
+    if constexpr (HasRowSum<P>::value) {
+        // stores, and the per-row sums of store_sum's values over the tile's
+        // valid columns: in-lane over j, across the half wave, across the WN
+        // waves of a row band through LDS (the stages are no longer read once
+        // every wave has passed the barrier)
+        static_assert(Cfg::FM == 2, "row sums take 64 rows per wave");
+        float v[32];
+        auto values = [&](auto edge) {
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i)
+            for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = (wm * Cfg::FM + i) * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-            const int64_t m = m0 + r;
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t m = m0 + (wm * Cfg::FM + i) * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < Cfg::FN; ++j) {
+                        const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
+                        if (!decltype(edge)::value || (m < p.M && n < p.N))
+                            sum += p.store_sum(m, n, acc[i][j][e]);
+                    }
+                    v[i * 16 + e] = sum;
+                }
+        };
+        // a tile inside the matrix stores without per-element checks
+        if (m0 + Cfg::BM <= p.M && n0 + Cfg::BN <= p.N) values(std::false_type{});
+        else values(std::true_type{});
+        half_wave_transpose_sum(v, lane);
+        __syncthreads();
+        float *rs = reinterpret_cast<float *>(lds);   // [WN][BM]
+        const int k = lane & 31;
+        const int r = (wm * Cfg::FM + (k >> 4)) * 32 + 8 * ((k >> 2) & 3) + 4 * g + (k & 3);
+        rs[wn * Cfg::BM + r] = v[0];
+        __syncthreads();
+        for (int rr = tid; rr < Cfg::BM; rr += Cfg::NT) {
+            const int64_t m = m0 + rr;
             if (m >= p.M) continue;
-            int64_t t = t0 + r;
-            if (p.T > 0) while (t >= p.T) t -= p.T;
+            float sum = 0.0f;
 #pragma unroll
-            for (int j = 0; j < Cfg::FN; ++j) {
-                const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
-                if (n < p.N) p.store(m, t, n, acc[i][j][e], split);
-            }
+            for (int w = 0; w < Cfg::WN; ++w) sum += rs[w * Cfg::BM + rr];
+            p.rowsum[m * p.rs_ld + tn] = sum;
         }
+    } else {
+        const int64_t t0 = p.T > 0 ? m0 % p.T : 0;
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = (wm * Cfg::FM + i) * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                const int64_t m = m0 + r;
+                if (m >= p.M) continue;
+                int64_t t = t0 + r;
+                if (p.T > 0) while (t >= p.T) t -= p.T;
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j) {
+                    const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + (lane & 31);
+                    if (n < p.N) p.store(m, t, n, acc[i][j][e], split);
+                }
+            }
+    }
 }
 
 // Skinny product for M <= 64 rows (the decode step projects one memory row per
@@ -414,20 +491,29 @@ struct ProjBwdDw {
 //   logits  C[n, v] = cap tanh((m U^T)[n, v] / cap)    A = m [N,d], B = U [V,d], both K-major
 //   dm      dm[n, e] = sum_v dz[n, v] U[v, e]           A = dz [N,V] K-major, B = U MN-major
 //   dU      dU[v, e] (+)= sum_n dz[n, v] m[n, e]        A = dz MN-major, B = m MN-major
+//   the logits product also sums exp(c) over each tile's columns per row: c
+//   lies in [-cap, cap] with cap <= 64, so exp(c) is finite and normal in
+//   float32 and the row's log-sum-exp needs no running maximum.
 struct LmLogits {
     static constexpr bool A_KMAJOR = true, B_KMAJOR = true;
     const bf16 *m, *u;
     float *out;
+    float *rowsum;
+    int64_t rs_ld;
     int64_t M, N, K, T;
-    float cap;
+    float cap, inv_cap2;   // cap, 2 / cap
     static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0, b_ld = 0;
     MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const { return m + row * K + k; }
     MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const { return u + n * K + k; }
     MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
     MAGLEV_DEV const bf16 *b_lin(int64_t, int64_t) const { return nullptr; }
-    MAGLEV_DEV void store(int64_t row, int64_t, int64_t n, float x, int) const
+    // c = cap tanh(x / cap), tanh(y) = 1 - 2 / (exp(2y) + 1) (exp(2y) may
+    // overflow to inf for large y, which gives tanh = 1 exactly); returns exp(c)
+    MAGLEV_DEV float store_sum(int64_t row, int64_t n, float x) const
     {
-        out[row * N + n] = cap * tanhf(x / cap);
+        const float c = cap - 2.0f * cap * __builtin_amdgcn_rcpf(__expf(x * inv_cap2) + 1.0f);
+        out[row * N + n] = c;
+        return __expf(c);
     }
 };
 struct LmDm {
@@ -484,15 +570,21 @@ static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const 
                        p, kper, group_m);
 }
 
+using LmLogitsCfg = DwCfg;
+
+int64_t lm_logits_col_tiles(int64_t V) { return (V + LmLogitsCfg::BN - 1) / LmLogitsCfg::BN; }
+
 void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m, const void *u,
-                           float *logits, hipStream_t s)
+                           float *logits, float *rowsum, hipStream_t s)
 {
     LmLogits p;
     p.m = static_cast<const bf16 *>(m);
     p.u = static_cast<const bf16 *>(u);
     p.out = logits;
-    p.M = N; p.N = V; p.K = d; p.T = 0; p.cap = cap;
-    run_gemm<ProjCfg>(p, 1, p.K, s, "lm_logits", 16);
+    p.rowsum = rowsum;
+    p.rs_ld = lm_logits_col_tiles(V);
+    p.M = N; p.N = V; p.K = d; p.T = 0; p.cap = cap; p.inv_cap2 = 2.0f / cap;
+    run_gemm<LmLogitsCfg>(p, 1, p.K, s, "lm_logits", 16);
 }
 
 void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,

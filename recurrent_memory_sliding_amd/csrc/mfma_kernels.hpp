@@ -34,10 +34,13 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
                           float *dWk, float *dWv, unsigned acc, const BwdWorkspace &ws,
                           hipStream_t s);
 
-// Loss-head products: logits = cap tanh(m U^T / cap) (float32 [N,V]),
-// dm = dz U (float32 [N,d]), dU (+)= dz^T m (float32 [V,d]).
+// Loss-head products: logits = cap tanh(m U^T / cap) (float32 [N,V]) with
+// rowsum[n, t] = sum of exp(logit) over column tile t of row n (float32
+// [N, lm_logits_col_tiles(V)], cap <= 64), dm = dz U (float32 [N,d]),
+// dU (+)= dz^T m (float32 [V,d]).
+int64_t lm_logits_col_tiles(int64_t V);
 void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m, const void *u,
-                           float *logits, hipStream_t s);
+                           float *logits, float *rowsum, hipStream_t s);
 void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,
                        hipStream_t s);
 void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *m, float *du,

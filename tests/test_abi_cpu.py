@@ -293,6 +293,8 @@ def test_loss_head_workspace_and_validation(L):
     assert call(V=8) == INVALID
     assert call(cap=0.0) == INVALID
     assert call(cap=float("inf")) == INVALID
+    assert call(cap=64.5) == INVALID
+    assert call(cap=float("nan")) == INVALID
     assert call(eps=-1.0) == INVALID
     assert call(eps=float("nan")) == INVALID
     assert call(lam=float("nan")) == INVALID

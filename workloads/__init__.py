@@ -76,6 +76,9 @@ TINY_FP32 = LayerShape(B=1, T=256, W=32, d=64, H=1, Dh=64, dtype=F32, lam=1.0)
 D20_LAYER = LayerShape(B=8, T=2048, W=512, d=1280, H=10, Dh=128, dtype=BF16, lam=0.1)
 D20_STACK = LayerShape(B=4, T=2048, W=512, d=1280, H=10, Dh=128, dtype=BF16, lam=0.1)
 D20_STACK_LAYERS = 20
+# LM-head vocabulary: the pages build on the nanochat stack and its tokenizer
+# without printing a size; 2^16 entries is that tokenizer's default.
+D20_VOCAB = 65536
 D20_DECODE = DecodeShape(layers=20, Bs=64, W=512, d=1280, H=10, Dh=128, steps=4096)
 
 
