@@ -570,7 +570,13 @@ static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const 
                        p, kper, group_m);
 }
 
-using LmLogitsCfg = DwCfg;
+// Loss-head products, timed at N = 16384, d = 1280, V = 65536: 256 x 256
+// tiles with 8 waves (a 128 x 64 or 64 x 128 block per wave) for the logits
+// and dU, 128 x 128 for dm (d = 1280 gives only 320 tiles of 256 x 256); all
+// three sweep small groups of tile rows (4 to 8) so that the workgroups on one
+// XCD share their A and B tiles in its L2.
+using LmLogitsCfg = TileCfg<256, 256, 4, 2, 2>;
+using LmDuCfg = TileCfg<256, 256, 2, 4, 2>;
 
 int64_t lm_logits_col_tiles(int64_t V) { return (V + LmLogitsCfg::BN - 1) / LmLogitsCfg::BN; }
 
@@ -584,7 +590,7 @@ void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m
     p.rowsum = rowsum;
     p.rs_ld = lm_logits_col_tiles(V);
     p.M = N; p.N = V; p.K = d; p.T = 0; p.cap = cap; p.inv_cap2 = 2.0f / cap;
-    run_gemm<LmLogitsCfg>(p, 1, p.K, s, "lm_logits", 16);
+    run_gemm<LmLogitsCfg>(p, 1, p.K, s, "lm_logits", 8);
 }
 
 void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,
@@ -595,7 +601,7 @@ void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *
     p.u = static_cast<const bf16 *>(u);
     p.dm = dm;
     p.M = N; p.N = d; p.K = V; p.T = 0; p.b_ld = d;
-    run_gemm<ProjCfg>(p, 1, p.K, s, "lm_dm", 16);
+    run_gemm<ProjCfg>(p, 1, p.K, s, "lm_dm", 4);
 }
 
 void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *m, float *du,
@@ -606,7 +612,7 @@ void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *
     p.m = static_cast<const bf16 *>(m);
     p.du = du;
     p.M = V; p.N = d; p.K = N; p.T = 0; p.a_ld = V; p.b_ld = d; p.acc = acc;
-    run_gemm<DwCfg>(p, 1, p.K, s, "lm_du", 1 << 20);
+    run_gemm<LmDuCfg>(p, 1, p.K, s, "lm_du", 4);
 }
 
 void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk, const void *wv,
@@ -748,7 +754,7 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
         p.acc = (acc & 1u) != 0;
         p.a_kseg = HD;
         p.b_ld = g.d;
-        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm", 16);
+        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm", 2);
     }
     {
         ProjBwdDw p;
