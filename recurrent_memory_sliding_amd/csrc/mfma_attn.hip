@@ -49,6 +49,9 @@ MAGLEV_DEV int64_t act_row(const AttnArgs &a, int64_t b, int64_t t, int h)
     return (b * a.T + t) * a.H + h;
 }
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;
+
 // Source of tile rows outside the sequence.
 __device__ __attribute__((aligned(256))) bf16 g_attn_zero[128] = {};
 
@@ -558,14 +561,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
             lv[q4] = *reinterpret_cast<const f32x4 *>(Ls + 8 * q4 + 4 * g);
             dv4[q4] = *reinterpret_cast<const f32x4 *>(Ds + 8 * q4 + 4 * g);
         }
-        const bool interior = (i0 >= kj) & (i0 + QT - 1 - kj < W) & (i0 + QT - 1 < T);
+        // A tile whose every (query, key) pair of this wave lies in the band
+        // (the usual case) takes the branch without the per-element mask; the
+        // condition is uniform over the wave.
+        const bool interior = (i0 >= kw0 + 31) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
+        if (interior) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
-            const bool ok = interior | ((i >= kj) & (i - kj < W) & (i < T));
-            const float p = fast_exp2(sc[e] * qscale - lv[e >> 2][e & 3]);
-            sc[e] = ok ? p : 0.0f;
-            dp[e] = sc[e] * (dp[e] - dv4[e >> 2][e & 3]);
+            for (int e = 0; e < 16; ++e) {
+                sc[e] = fast_exp2(sc[e] * qscale - lv[e >> 2][e & 3]);
+                dp[e] = sc[e] * (dp[e] - dv4[e >> 2][e & 3]);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                const bool ok = (i >= kj) & (i - kj < W) & (i < T);
+                const float p = fast_exp2(sc[e] * qscale - lv[e >> 2][e & 3]);
+                sc[e] = ok ? p : 0.0f;
+                dp[e] = sc[e] * (dp[e] - dv4[e >> 2][e & 3]);
+            }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -594,6 +608,268 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
                 for (int u = 0; u < 4; ++u) {
                     k4[u] = f2bf(dka[db][4 * i4 + u]);
                     v4[u] = f2bf(dva[db][4 * i4 + u]);
+                }
+                *reinterpret_cast<bf16x4 *>(dk + base + c) = k4;
+                *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
+            }
+    }
+}
+
+// Scale and inverse rotation of one channel-pair block: lo holds channels
+// c = c0 + 8(e/4) + 4g + e%4 of one key, hi the channels c + DH/2; cs is the
+// key's rotation table at entry c0 (nullptr: scale only).
+MAGLEV_DEV void scale_rotate_pair(f32x16 &lo, f32x16 &hi, const float2 *cs, int g, float scale)
+{
+    if (cs) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float *t = reinterpret_cast<const float *>(cs + 8 * q + 4 * g);
+            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(t);
+            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(t + 4);
+            const float cx[4] = {t0[0], t0[2], t1[0], t1[2]};
+            const float sy[4] = {t0[1], t0[3], t1[1], t1[3]};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = 4 * q + u;
+                const float x = lo[e] * scale, y = hi[e] * scale;
+                lo[e] = x * cx[u] + y * sy[u];
+                hi[e] = -x * sy[u] + y * cx[u];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            lo[e] *= scale;
+            hi[e] *= scale;
+        }
+    }
+}
+
+// Key-stationary pass with each 32-key block split over a pair of waves
+// (Dh = 128): four waves, two pairs, 64 keys a workgroup; 32-query tiles of
+// Q^ and dO stream through LDS in ST stages. Per tile, the pair's first wave
+// forms S = Q^ K~^T and P = exp(scale S - lse), its second wave
+// dP - D = dO V~^T - D; they swap P and dP - D through LDS (one barrier a
+// tile, which also publishes the next tile's stage), both form
+// dS = P (dP - D), and each
+// accumulates dV~^T += dO^T P and dK~^T += Q^^T dS for its half of the
+// channels: blocks hf and hf + 2 of 32 channels (hf = the wave's place in
+// the pair), so that the rotation pairs (c, c + 64) stay in one wave. A wave
+// holds one of K~, V~ and a quarter of the accumulators, and a workgroup
+// needs 80 KB of LDS, so two workgroups share a CU: they run out of step, and
+// one's MFMA work covers the other's softmax, exchange and barrier. Each
+// phase issues all of its LDS operand reads before its first product (one
+// read in flight per product left every product waiting for LDS latency).
+// The lse (first wave) or D (second wave) values of the next tile are loaded
+// into registers while the current one is used (issued before the DMA that
+// follows them, so the in-order count of vector memory operations tells when
+// they have arrived).
+template <int ST, bool ROTATE>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, const bf16 *dO,
+                                                                     const float *lse2,
+                                                                     const float *Dp, int64_t Tp,
+                                                                     bf16 *dk, bf16 *dv)
+{
+    static_assert(ST >= 3, "the next tile is published one tile ahead");
+    constexpr int DH = 128, NF = DH / 16, NPAIR = 2, KB = 32 * NPAIR;
+    constexpr int QT = 32;
+    constexpr int TE = QT * DH;
+    using Dma = TileDma<DH, QT, 2 * NPAIR>;
+    constexpr int PER = 2 * Dma::PER_WAVE;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][Q^, dO]
+    // [tile parity][pair][role][quad][lane]: P (role 0) and dP - D (role 1) in
+    // the accumulator layout, four 16-byte groups a lane
+    __shared__ __attribute__((aligned(16))) f32x4 X[2][NPAIR][2][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pr = w >> 1, hf = w & 1;
+    const int T = (int)a.T, W = a.W;
+    const int nkt = (T + KB - 1) / KB;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = bid % nkt, bh = bid / nkt;
+    const int h = bh % a.H;
+    const int64_t b = bh / a.H;
+    const int j0 = kt * KB, kw0 = j0 + 32 * pr, kj = kw0 + l32;
+    const float qscale = a.scale * kLog2e;
+    const int tok_stride = a.H * DH;
+    const bf16 *qbase = a.qr + act_row(a, b, 0, h) * DH;
+    const bf16 *obase = dO + act_row(a, b, 0, h) * DH;
+    const float *lrow = lse2 + (int64_t)bh * Tp;
+    const float *drow = Dp + (int64_t)bh * Tp;
+
+    const int qend = j0 + KB - 1 + W < T ? j0 + KB - 1 + W : T;   // exclusive
+    const int nt = (qend - j0 + QT - 1) / QT;
+
+    // This lane's key row of K~ (first wave) or V~ (second wave) as B
+    // operands, complete before any tile load is issued.
+    bf16x8 kvf[NF];
+    if (kj < T) {
+        const bf16 *src = (hf ? a.vx : a.kx) + act_row(a, b, kj, h) * DH;
+#pragma unroll
+        for (int s = 0; s < NF; ++s) kvf[s] = *reinterpret_cast<const bf16x8 *>(src + 16 * s + 8 * g);
+    } else {
+        zero_frags(kvf, NF);
+    }
+    wait_vmcnt<0>();
+
+    auto issue = [&](int it) {
+        const int buf = it % ST;
+        const int i0 = j0 + it * QT;
+        bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+#pragma unroll
+        for (int i = 0; i < Dma::PER_WAVE; ++i) {
+            const int ins = w * Dma::PER_WAVE + i;
+            const int r = Dma::row(ins, lane);
+            const int c = Dma::chunk(r, lane);
+            const int qi = i0 + r;
+            const bool in = qi < T;
+            const int64_t off = (int64_t)qi * tok_stride + c * 8;
+            dma16(in ? qbase + off : g_attn_zero, qt + ins * 512);
+            dma16(in ? obase + off : g_attn_zero, ot + ins * 512);
+        }
+    };
+    // The statistic of this lane's 16 queries of tile it that the wave's role
+    // needs: lse2 (first wave, for P) or D (second wave, which sends dP - D).
+    // Rows are padded to Tp, so a tile never leaves its row. Two register
+    // sets, one per tile parity, so that no copy (and no wait for the loads
+    // behind them) is needed.
+    struct Stats {
+        f32x4 v[4];
+    };
+    const float *srow = hf ? drow : lrow;
+    auto load_stats = [&](int it, Stats &st) {
+        const int i0 = j0 + it * QT;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            st.v[q4] = *reinterpret_cast<const f32x4 *>(srow + i0 + 8 * q4 + 4 * g);
+    };
+    Stats sa, sb;
+    // Tiles 0 .. ST-2 and the statistics of tile 0 in flight; all landed and
+    // tile 0 visible to every wave.
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
+    load_stats(0, sa);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    f32x16 dva[2], dka[2];   // blocks hf and hf + 2 of 32 channels
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dva[lb][e] = dka[lb][e] = 0.0f;
+
+    auto tile_step = [&](int it, const Stats &cur, Stats &next) {
+        const int i0 = j0 + it * QT;
+        const int buf = it % ST;
+        const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+
+        // S (first wave) or dP (second wave); element e: query
+        // i0 + 8(e/4) + 4g + e%4, key kj
+        const bf16 *rt = hf ? ot : qt;
+        f32x16 mine;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mine[e] = 0.0f;
+        bf16x8 rows[NF];
+#pragma unroll
+        for (int s = 0; s < NF; ++s) rows[s] = tile_rows<DH>(rt, 0, s, lane);
+#pragma unroll
+        for (int s = 0; s < NF; ++s) mine = mfma32(rows[s], kvf[s], mine);
+        // all eight operand reads are issued before the first product waits
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NF, 0);
+        // this tile's statistics: loaded before the last DMA issued
+        if (it + ST - 2 < nt) wait_vmcnt<PER>();
+        else wait_vmcnt<0>();
+        if (hf == 0) {
+            // every (query, key) pair of this block in the band: no mask
+            const bool interior = (i0 >= kw0 + 31) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
+            if (interior) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    mine[e] = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool ok = (i >= kj) & (i - kj < W) & (i < T);
+                    const float p = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
+                    mine[e] = ok ? p : 0.0f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mine[e] -= cur.v[e >> 2][e & 3];
+        }
+        const int par = it & 1;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            X[par][pr][hf][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
+        // the next tile's stage (issued one iteration ago) lands before the
+        // barrier publishes it
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (it + 1 < nt) load_stats(it + 1, next);
+        if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
+
+        // the transposed operands of this tile's eight products, read before
+        // the exchange so that their latency overlaps the dS arithmetic
+        bf16x8 trv[2][2], trq[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int lb = 0; lb < 2; ++lb) {
+                trv[t][lb] = tile_tr<DH>(ot, t, hf + 2 * lb, lane);
+                trq[t][lb] = tile_tr<DH>(qt, t, hf + 2 * lb, lane);
+            }
+        f32x16 P, dS;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 o = X[par][pr][hf ^ 1][q4][lane];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = 4 * q4 + u;
+                P[e] = hf ? o[u] : mine[e];
+                dS[e] = P[e] * (hf ? mine[e] : o[u]);   // P (dP - D)
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16x8 pf = acc_to_operand(P, t);
+            const bf16x8 dsf = acc_to_operand(dS, t);
+#pragma unroll
+            for (int lb = 0; lb < 2; ++lb) {
+                dva[lb] = mfma32(trv[t][lb], pf, dva[lb]);
+                dka[lb] = mfma32(trq[t][lb], dsf, dka[lb]);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 20, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
+    };
+    for (int it = 0; it < nt; it += 2) {
+        tile_step(it, sa, sb);
+        if (it + 1 < nt) tile_step(it + 1, sb, sa);
+    }
+
+    // Epilogue: element e of local block lb is channel 32 (hf + 2 lb) +
+    // 8(e/4) + 4g + e%4 of key kj.
+    if (kj < T) {
+        const int64_t base = act_row(a, b, kj, h) * DH;
+        const float2 *cs =
+            (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) + 32 * hf : nullptr;
+        scale_rotate_pair(dka[0], dka[1], cs, g, a.scale);
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int c = 32 * (hf + 2 * lb) + 8 * i4 + 4 * g;
+                bf16x4 k4, v4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    k4[u] = f2bf(dka[lb][4 * i4 + u]);
+                    v4[u] = f2bf(dva[lb][4 * i4 + u]);
                 }
                 *reinterpret_cast<bf16x4 *>(dk + base + c) = k4;
                 *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
@@ -748,8 +1024,8 @@ static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const vo
 
 // Tile shapes and pipeline depths: forward and dQ stream K~/V~ tiles of
 // kFwdKT keys through kFwdST stages; dK/dV streams 32-query tiles through
-// kBwdST stages.
-constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4;
+// kBwdST stages (kPairST in the wave-pair pass used for Dh = 128).
+constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4, kPairST = 3;
 
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)
@@ -779,14 +1055,26 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
     }
     {
         prof::Scope ts("attn_bwd_dkdv", s);
-        if (entries)
+        if constexpr (DH == 128) {
+            // one workgroup per 64 keys of a (sequence, head)
+            const unsigned npw = (unsigned)(a.B * a.H * ((a.T + 63) / 64));
+            if (entries)
+                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, false>), dim3(npw),
+                                   dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
+                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
+            else
+                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, true>), dim3(npw),
+                                   dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
+                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
+        } else if (entries) {
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256), 0,
                                s, a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
                                static_cast<bf16 *>(dv));
-        else
+        } else {
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256), 0, s,
                                a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
                                static_cast<bf16 *>(dv));
+        }
     }
     prof::Scope ts("attn_bwd_dq", s);
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a, dO,
