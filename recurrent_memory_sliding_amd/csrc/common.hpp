@@ -148,11 +148,13 @@ MAGLEV_DEV void wait_vmcnt()
 }
 
 // Map a linear workgroup id so that consecutive logical tiles share an XCD
-// (workgroups are dispatched round-robin over the 8 XCDs, each with its own L2).
+// (workgroups are dispatched round-robin over the 8 XCDs, each with its own
+// L2): XCD x receives the nwg/8 (+1 for x < nwg mod 8) consecutive items from
+// x * (nwg/8) + min(x, nwg mod 8), in dispatch order.
 MAGLEV_DEV int xcd_remap(int wg, int nwg)
 {
-    if ((nwg & 7) != 0) return wg;
-    return (wg & 7) * (nwg >> 3) + (wg >> 3);
+    const int q = nwg >> 3, r = nwg & 7, x = wg & 7;
+    return x * q + (x < r ? x : r) + (wg >> 3);
 }
 
 }  // namespace maglev
