@@ -30,7 +30,7 @@ namespace maglev {
 
 namespace {
 
-constexpr int kGatedFwdRows = 4;   // token rows per workgroup in the forward mix
+constexpr int kGatedFwdRows = 8;   // token rows per workgroup in the forward mix
 
 MAGLEV_DEV float two_sigmoid(float a) { return 2.0f / (1.0f + __expf(-a)); }
 
@@ -99,8 +99,40 @@ struct GatedArgs {
     const float *gates;   // [4][HD] logits: a_kl, a_kr, a_vl, a_vr
 };
 
+// Eight elements as loaded (bf16 kept packed, converted when used), so that a
+// row's loads can all be in flight in few registers.
+template <typename T> struct Chunk8;
+template <> struct Chunk8<bf16> {
+    u32x4 x;
+    MAGLEV_DEV void load(const bf16 *p) { x = *reinterpret_cast<const u32x4 *>(p); }
+    MAGLEV_DEV void zero() { x = u32x4{0u, 0u, 0u, 0u}; }
+    MAGLEV_DEV void get(float *out) const
+    {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+    }
+};
+template <> struct Chunk8<float> {
+    f32x4 a, b;
+    MAGLEV_DEV void load(const float *p)
+    {
+        a = *reinterpret_cast<const f32x4 *>(p);
+        b = *reinterpret_cast<const f32x4 *>(p + 4);
+    }
+    MAGLEV_DEV void zero() { a = b = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    MAGLEV_DEV void get(float *out) const
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Forward: mixed entries kx, vx from k, v, kp (pre-norm), vm.
+// A row's eight loads go out together, and the next row's before the current
+// one is reduced and mixed (the row norm's workgroup sum is the only step that
+// waits on other threads).
 // ---------------------------------------------------------------------------
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, const T *v,
@@ -111,26 +143,42 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
     const int tid = threadIdx.x, nw = blockDim.x >> 6;
     const bool act = tid < a.HD / 16;
     const ChunkPair<DH> cp(act ? tid : 0);
-    stage_gates(a.gates, 4 * a.HD, gsh);
-    const float *gk = gsh, *gv = gsh + 2 * a.HD;   // [2][HD] each: local, recurrent
     const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
     const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
-    const float inv_hd = 1.0f / (float)a.HD;
-    for (int64_t row = r0; row < r1; ++row) {
+    // [kp, k, v, vm][low, high half]
+    using RowIn = Chunk8<T>[4][2];
+    auto load_row = [&](int64_t row, RowIn &d) {
         const int64_t base = row * a.HD;
-        float nl[8] = {}, nh[8] = {};
-        if (act) {
-            load8(kp + base + cp.lo, nl);
-            load8(kp + base + cp.hi, nh);
+        const T *src[4] = {kp, k, v, vm};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (act) {
+                d[t][0].load(src[t] + base + cp.lo);
+                d[t][1].load(src[t] + base + cp.hi);
+            } else {
+                d[t][0].zero();
+                d[t][1].zero();
+            }
         }
+    };
+    RowIn ia, ib;
+    if (r0 < r1) load_row(r0, ia);
+    stage_gates(a.gates, 4 * a.HD, gsh);
+    const float *gk = gsh, *gv = gsh + 2 * a.HD;   // [2][HD] each: local, recurrent
+    const float inv_hd = 1.0f / (float)a.HD;
+    auto mix_row = [&](int64_t row, const RowIn &d) {
+        const int64_t base = row * a.HD;
+        float nl[8], nh[8];
+        d[0][0].get(nl);
+        d[0][1].get(nh);
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += nl[e] * nl[e] + nh[e] * nh[e];
         const float rs = rsqrtf(group_sum(ss, red[row & 1], nw) * inv_hd + a.eps);
-        if (!act) continue;
+        if (!act) return;
         float kl[8], kh[8];
-        load8(k + base + cp.lo, kl);
-        load8(k + base + cp.hi, kh);
+        d[1][0].get(kl);
+        d[1][1].get(kh);
 #pragma unroll
         for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }
         if (a.rope) {
@@ -152,10 +200,10 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
         store8(kx + base + cp.lo, kl);
         store8(kx + base + cp.hi, kh);
         float vl[8], vh[8], ml[8], mh[8];
-        load8(v + base + cp.lo, vl);
-        load8(v + base + cp.hi, vh);
-        load8(vm + base + cp.lo, ml);
-        load8(vm + base + cp.hi, mh);
+        d[2][0].get(vl);
+        d[2][1].get(vh);
+        d[3][0].get(ml);
+        d[3][1].get(mh);
         {
             float ga[8], gb[8];
             lds8(gv + cp.lo, ga);
@@ -169,6 +217,14 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
         }
         store8(vx + base + cp.lo, vl);
         store8(vx + base + cp.hi, vh);
+    };
+    for (int64_t row = r0; row < r1; row += 2) {
+        if (row + 1 < r1) load_row(row + 1, ib);
+        mix_row(row, ia);
+        if (row + 1 < r1) {
+            if (row + 2 < r1) load_row(row + 2, ia);
+            mix_row(row + 1, ib);
+        }
     }
 }
 
