@@ -233,113 +233,86 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
 // its channels before it overwrites them). dkp, dvm receive the gradients of
 // the projected memory; gpart[block][4][HD] the per-block gate partial sums
 // (before the 2 sigma (1 - sigma) factor).
+// dkn = R^T (g_kr (.) dk~) does not depend on the norm, and
+// mean(dkn (.) kn) = rs * mean(dkn (.) kp) with rs = 1/rms, so both row sums
+// (of kp^2 and of dkn (.) kp) come out of one workgroup reduction.
+// A row's twelve loads go out together; for bf16 the next row's are in flight
+// while the current one is reduced and written.
 // ---------------------------------------------------------------------------
+MAGLEV_DEV float2 group_sum2(float x, float y, float2 *red, int nw)
+{
+    x = wave_sum(x);
+    y = wave_sum(y);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(x, y);
+    __syncthreads();
+    float2 t = make_float2(0.0f, 0.0f);
+    for (int i = 0; i < nw; ++i) { t.x += red[i].x; t.y += red[i].y; }
+    return t;
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, const T *v,
                                                       const T *kp, const T *vm, T *dk, T *dv,
                                                       T *dkp, T *dvm, float *gpart)
 {
-    __shared__ float red[2][4];
+    __shared__ float2 red[2][4];
     extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD]
     const int tid = threadIdx.x, nw = blockDim.x >> 6;
     const bool act = tid < a.HD / 16;
     const ChunkPair<DH> cp(act ? tid : 0);
+    const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
+    const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
+    // [kp, dk~, k, dv~, v, vm][low, high half]
+    using RowIn = Chunk8<T>[6][2];
+    auto load_row = [&](int64_t row, RowIn &d) {
+        const int64_t base = row * a.HD;
+        const T *src[6] = {kp, dk, k, dv, v, vm};
+#pragma unroll
+        for (int t = 0; t < 6; ++t) {
+            if (act) {
+                d[t][0].load(src[t] + base + cp.lo);
+                d[t][1].load(src[t] + base + cp.hi);
+            } else {
+                d[t][0].zero();
+                d[t][1].zero();
+            }
+        }
+    };
+    RowIn ia, ib;
+    if (r0 < r1) load_row(r0, ia);
     stage_gates(a.gates, 4 * a.HD, gsh);
     const float *gkl = gsh, *gkr = gsh + a.HD, *gvl = gsh + 2 * a.HD, *gvr = gsh + 3 * a.HD;
     float pkl[16] = {}, pkr[16] = {}, pvl[16] = {}, pvr[16] = {};
-    const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
-    const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
     const float inv_hd = 1.0f / (float)a.HD;
-    for (int64_t row = r0; row < r1; ++row) {
+    auto grad_row = [&](int64_t row, const RowIn &d) {
         const int64_t base = row * a.HD;
-        float nl[8] = {}, nh[8] = {};
-        if (act) {
-            load8(kp + base + cp.lo, nl);
-            load8(kp + base + cp.hi, nh);
-        }
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += nl[e] * nl[e] + nh[e] * nh[e];
-        const float rs = rsqrtf(group_sum(ss, red[0], nw) * inv_hd + a.eps);
-        float dnl[8] = {}, dnh[8] = {};   // dkn
-        float mu = 0.0f;
         const float2 *cs = (act && a.rope) ? a.rope + (a.pos0 + row % a.Tlen) * (DH / 2) + 8 * cp.j
                                            : nullptr;
-        if (act) {
+        float nl[8], nh[8], gl[8], gh[8], dnl[8], dnh[8];
+        d[0][0].get(nl);
+        d[0][1].get(nh);
+        d[1][0].get(gl);
+        d[1][1].get(gh);
+        {
+            float gc[8], gd[8];
+            lds8(gkr + cp.lo, gc);
+            lds8(gkr + cp.hi, gd);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }   // kn
-            float gl[8], gh[8], kl[8], kh[8];
-            load8(dk + base + cp.lo, gl);
-            load8(dk + base + cp.hi, gh);
-            load8(k + base + cp.lo, kl);
-            load8(k + base + cp.hi, kh);
-            float rnl[8], rnh[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { rnl[e] = nl[e]; rnh[e] = nh[e]; }
-            if (cs) {
-                rotate_pairs(kl, kh, cs, false);
-                rotate_pairs(rnl, rnh, cs, false);
-            }
-            float ol[8], oh[8];
-            {
-                float ga[8], gb[8], gc[8], gd[8];
-                lds8(gkl + cp.lo, ga);
-                lds8(gkl + cp.hi, gb);
-                lds8(gkr + cp.lo, gc);
-                lds8(gkr + cp.hi, gd);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pkl[e] += gl[e] * kl[e];
-                    pkl[8 + e] += gh[e] * kh[e];
-                    pkr[e] += gl[e] * rnl[e];
-                    pkr[8 + e] += gh[e] * rnh[e];
-                    ol[e] = ga[e] * gl[e];
-                    oh[e] = gb[e] * gh[e];
-                    dnl[e] = gc[e] * gl[e];
-                    dnh[e] = gd[e] * gh[e];
-                }
-            }
-            if (cs) {
-                rotate_pairs(ol, oh, cs, true);
-                rotate_pairs(dnl, dnh, cs, true);
-            }
-            store8(dk + base + cp.lo, ol);
-            store8(dk + base + cp.hi, oh);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mu += dnl[e] * nl[e] + dnh[e] * nh[e];
-
-            float vl[8], vh[8], ml[8], mh[8];
-            load8(dv + base + cp.lo, gl);
-            load8(dv + base + cp.hi, gh);
-            load8(v + base + cp.lo, vl);
-            load8(v + base + cp.hi, vh);
-            load8(vm + base + cp.lo, ml);
-            load8(vm + base + cp.hi, mh);
-            {
-                float ga[8], gb[8], gc[8], gd[8];
-                lds8(gvl + cp.lo, ga);
-                lds8(gvl + cp.hi, gb);
-                lds8(gvr + cp.lo, gc);
-                lds8(gvr + cp.hi, gd);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pvl[e] += gl[e] * vl[e];
-                    pvl[8 + e] += gh[e] * vh[e];
-                    pvr[e] += gl[e] * ml[e];
-                    pvr[8 + e] += gh[e] * mh[e];
-                    vl[e] = ga[e] * gl[e];
-                    vh[e] = gb[e] * gh[e];
-                    ml[e] = gc[e] * gl[e];
-                    mh[e] = gd[e] * gh[e];
-                }
-            }
-            store8(dv + base + cp.lo, vl);
-            store8(dv + base + cp.hi, vh);
-            store8(dvm + base + cp.lo, ml);
-            store8(dvm + base + cp.hi, mh);
+            for (int e = 0; e < 8; ++e) { dnl[e] = gc[e] * gl[e]; dnh[e] = gd[e] * gh[e]; }
         }
-        mu = group_sum(mu, red[1], nw) * inv_hd;
-        if (!act) continue;
+        if (cs) rotate_pairs(dnl, dnh, cs, true);   // dkn
+        float ss = 0.0f, sd = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ss += nl[e] * nl[e] + nh[e] * nh[e];
+            sd += dnl[e] * nl[e] + dnh[e] * nh[e];
+        }
+        const float2 t = group_sum2(ss, sd, red[row & 1], nw);
+        const float rs = rsqrtf(t.x * inv_hd + a.eps);
+        const float mu = t.y * rs * inv_hd;   // mean(dkn (.) kn)
+        if (!act) return;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }   // kn
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             dnl[e] = (dnl[e] - nl[e] * mu) * rs;
@@ -347,6 +320,77 @@ __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, co
         }
         store8(dkp + base + cp.lo, dnl);
         store8(dkp + base + cp.hi, dnh);
+        float kl[8], kh[8];
+        d[2][0].get(kl);
+        d[2][1].get(kh);
+        if (cs) {
+            rotate_pairs(kl, kh, cs, false);
+            rotate_pairs(nl, nh, cs, false);
+        }
+        float ol[8], oh[8];
+        {
+            float ga[8], gb[8];
+            lds8(gkl + cp.lo, ga);
+            lds8(gkl + cp.hi, gb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pkl[e] += gl[e] * kl[e];
+                pkl[8 + e] += gh[e] * kh[e];
+                pkr[e] += gl[e] * nl[e];
+                pkr[8 + e] += gh[e] * nh[e];
+                ol[e] = ga[e] * gl[e];
+                oh[e] = gb[e] * gh[e];
+            }
+        }
+        if (cs) rotate_pairs(ol, oh, cs, true);
+        store8(dk + base + cp.lo, ol);
+        store8(dk + base + cp.hi, oh);
+
+        float vl[8], vh[8], ml[8], mh[8];
+        d[3][0].get(gl);
+        d[3][1].get(gh);
+        d[4][0].get(vl);
+        d[4][1].get(vh);
+        d[5][0].get(ml);
+        d[5][1].get(mh);
+        {
+            float ga[8], gb[8], gc[8], gd[8];
+            lds8(gvl + cp.lo, ga);
+            lds8(gvl + cp.hi, gb);
+            lds8(gvr + cp.lo, gc);
+            lds8(gvr + cp.hi, gd);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pvl[e] += gl[e] * vl[e];
+                pvl[8 + e] += gh[e] * vh[e];
+                pvr[e] += gl[e] * ml[e];
+                pvr[8 + e] += gh[e] * mh[e];
+                vl[e] = ga[e] * gl[e];
+                vh[e] = gb[e] * gh[e];
+                ml[e] = gc[e] * gl[e];
+                mh[e] = gd[e] * gh[e];
+            }
+        }
+        store8(dv + base + cp.lo, vl);
+        store8(dv + base + cp.hi, vh);
+        store8(dvm + base + cp.lo, ml);
+        store8(dvm + base + cp.hi, mh);
+    };
+    if constexpr (sizeof(T) == 2) {
+        for (int64_t row = r0; row < r1; row += 2) {
+            if (row + 1 < r1) load_row(row + 1, ib);
+            grad_row(row, ia);
+            if (row + 1 < r1) {
+                if (row + 2 < r1) load_row(row + 2, ia);
+                grad_row(row + 1, ib);
+            }
+        }
+    } else {
+        // float rows are twice as large: one row in flight at a time
+        for (int64_t row = r0; row < r1; ++row) {
+            if (row > r0) load_row(row, ia);
+            grad_row(row, ia);
+        }
     }
     if (!act) return;
     float *out = gpart + (int64_t)blockIdx.x * 4 * a.HD;
