@@ -45,7 +45,7 @@ struct BwdWorkspace {
     float *D;            // [B,H,T]  rowsum(dO * O) (float32 path)
     float *ds_part;      // [B,H,T] per-key d loss / d s_h terms (float32 path)
     float *rowdot;       // [2*H*Dh] <W[r,:], G[r,:]> per weight row (bf16 path)
-    void *W_scaled;      // [2*H*Dh, d] dtype: s_h * [W_Km; W_Vm] (rows scaled)
+    void *W_scaled;      // [d, 2*H*Dh] dtype: (s_h * [W_Km; W_Vm])^T (rows scaled, then transposed)
     float *dW_part;      // [ksplit, 2*H*Dh, d] split-K partials (may be unused)
     void *q_rot;         // [B,T,H,Dh] dtype: rotated queries (bf16 path)
     float *lse2;         // [B*H, Tp] lse * log2(e), zero beyond T (bf16 path)

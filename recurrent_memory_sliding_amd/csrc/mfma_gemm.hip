@@ -25,7 +25,11 @@
 namespace maglev {
 namespace mfma {
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_ = 3>
+// PIPE selects the main loop: true reads each K step's first fragments
+// during the previous step's last MFMAs (one barrier inside the step); false
+// keeps one barrier at the top of each step and fewer registers live, which
+// the widest wave tiles need to stay within 256 VGPRs.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_ = 3, bool PIPE_ = true>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, BK = 64, WM = WM_, WN = WN_;
     static constexpr int NT = WM_ * WN_ * 64;
@@ -33,6 +37,7 @@ struct TileCfg {
     static constexpr int FM = BM_ / WM_ / 32;   // 32x32 blocks per wave along M
     static constexpr int FN = BN_ / WN_ / 32;
     static constexpr int STAGES = STAGES_;
+    static constexpr bool PIPE = PIPE_;
 };
 
 // LDS layout of one operand tile, no padding, 16-byte chunks XOR-swizzled so
@@ -53,6 +58,11 @@ struct OpTile {
         return KMAJOR ? (c ^ ((row >> 1) & 7)) : (c ^ ((row & 3) << 2));
     }
 };
+
+constexpr int kGemmSchedMfma = 0x8, kGemmSchedDsRead = 0x100;   // sched_group_barrier masks
+
+// s_waitcnt lgkmcnt(0) with the other counters left alone (gfx9 encoding).
+MAGLEV_DEV void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
 // Source of rows that must read as zero (the shift's first row, K tails).
 __device__ __attribute__((aligned(256))) bf16 g_zero_rows[64] = {};
@@ -250,39 +260,116 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    constexpr int AHEAD = Cfg::STAGES - 1;         // K steps in flight ahead of the MFMA work
-#pragma unroll
-    for (int s0 = 0; s0 < AHEAD; ++s0)
-        if (s0 < nk) issue(s0, s0);
-    for (int it = 0; it < nk; ++it) {
-        // stage it has landed once at most (AHEAD - 1) later stages are still in flight
-        if (AHEAD >= 2 && it + 1 < nk) wait_vmcnt<(AHEAD >= 2 ? PER_STAGE : 0)>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();                // every wave's share of stage it is in LDS,
-                                                     // and stage it-1 is no longer being read
-        if (it + AHEAD < nk) issue(it + AHEAD, (it + AHEAD) % Cfg::STAGES);
-        const bf16 *la = lds + (it % Cfg::STAGES) * STAGE;
-        const bf16 *lb = la + TA::ELEMS;
+    if constexpr (Cfg::PIPE) {
+        // Fragment reads of sub-step ks (16 of the stage's 64 k) into buffer b.
         bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
+        auto read_ks = [&](const bf16 *la, int ks, int b) {
+            const bf16 *lb = la + TA::ELEMS;
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) af[0][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, 0, lane);
+            for (int i = 0; i < Cfg::FM; ++i)
+                af[b][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, ks, lane);
 #pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) bfr[0][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, 0, lane);
-#pragma unroll
-        for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
-            const int cur = ks & 1;
-            if (ks + 1 < Cfg::BK / 16) {
-#pragma unroll
-                for (int i = 0; i < Cfg::FM; ++i)
-                    af[cur ^ 1][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, ks + 1, lane);
-#pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j)
-                    bfr[cur ^ 1][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, ks + 1, lane);
-            }
+            for (int j = 0; j < Cfg::FN; ++j)
+                bfr[b][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, ks, lane);
+        };
+        // The MFMAs of one sub-step with the reads of the next interleaved: two
+        // LDS instructions (ds_read_b128, or one transpose-read pair) ahead of
+        // each MFMA until the reads are out, so that they land while the rest of
+        // the sub-step computes.
+        constexpr int NREAD = Cfg::FM * (P::A_KMAJOR ? 1 : 2) + Cfg::FN * (P::B_KMAJOR ? 1 : 2);
+        constexpr int NMFMA = Cfg::FM * Cfg::FN;
+        auto mfma_ks = [&](int b) {
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[cur][i], bfr[cur][j], acc[i][j]);
+                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[b][i], bfr[b][j], acc[i][j]);
+#pragma unroll
+            for (int g = 0; g < (NREAD + 1) / 2 && g < NMFMA; ++g) {
+                __builtin_amdgcn_sched_group_barrier(kGemmSchedDsRead, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kGemmSchedMfma, 1, 0);
+            }
+            if constexpr (NMFMA > (NREAD + 1) / 2)
+                __builtin_amdgcn_sched_group_barrier(kGemmSchedMfma, NMFMA - (NREAD + 1) / 2, 0);
+        };
+
+        // Pipeline: step s is loaded into stage s mod STAGES; the loads run
+        // STAGES - 1 steps ahead of the MFMA work. The barrier of step it sits in
+        // its last sub-step: there every wave's loads of step it+1 have landed
+        // and no wave reads stage it any more, so it is refilled (step
+        // it+STAGES) and the first fragments of step it+1 are read while the
+        // last MFMAs of step it run.
+#pragma unroll
+        for (int s0 = 0; s0 < Cfg::STAGES; ++s0)
+            if (s0 < nk) issue(s0, s0);
+        if (nk > 0) {
+            if (Cfg::STAGES >= 2 && nk >= Cfg::STAGES) wait_vmcnt<PER_STAGE * (Cfg::STAGES - 1)>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            read_ks(lds, 0, 0);
+        }
+        // (The last step is peeled off so that no join in the loop body makes the
+        // compiler wait for the next step's fragments before this step's MFMAs.)
+        auto step = [&](int it, auto last) {
+            const bf16 *la = lds + (it % Cfg::STAGES) * STAGE;
+#pragma unroll
+            for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
+                const int cur = ks & 1;
+                if (ks + 1 < Cfg::BK / 16) {
+                    read_ks(la, ks + 1, cur ^ 1);
+                } else if constexpr (!decltype(last)::value) {
+                    // stage it+1 landed once at most the loads of steps
+                    // it+2 .. it+STAGES-1 are in flight; this wave's reads of
+                    // stage it have returned
+                    if (Cfg::STAGES >= 3 && it + Cfg::STAGES - 1 < nk)
+                        wait_vmcnt<PER_STAGE * (Cfg::STAGES >= 3 ? Cfg::STAGES - 2 : 0)>();
+                    else wait_vmcnt<0>();
+                    wait_lgkmcnt0();
+                    __builtin_amdgcn_s_barrier();
+                    if (it + Cfg::STAGES < nk) issue(it + Cfg::STAGES, it % Cfg::STAGES);
+                    read_ks(lds + ((it + 1) % Cfg::STAGES) * STAGE, 0, cur ^ 1);
+                }
+                mfma_ks(cur);
+            }
+        };
+        for (int it = 0; it + 1 < nk; ++it) step(it, std::false_type{});
+        if (nk > 0) step(nk - 1, std::true_type{});
+    } else {
+        constexpr int AHEAD = Cfg::STAGES - 1;     // K steps in flight ahead of the MFMA work
+#pragma unroll
+        for (int s0 = 0; s0 < AHEAD; ++s0)
+            if (s0 < nk) issue(s0, s0);
+        for (int it = 0; it < nk; ++it) {
+            // stage it has landed once at most (AHEAD - 1) later stages are still in flight
+            if (AHEAD >= 2 && it + 1 < nk) wait_vmcnt<(AHEAD >= 2 ? PER_STAGE : 0)>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();            // every wave's share of stage it is in LDS,
+                                                     // and stage it-1 is no longer being read
+            if (it + AHEAD < nk) issue(it + AHEAD, (it + AHEAD) % Cfg::STAGES);
+            const bf16 *la = lds + (it % Cfg::STAGES) * STAGE;
+            const bf16 *lb = la + TA::ELEMS;
+            bf16x8 af[2][Cfg::FM], bfr[2][Cfg::FN];
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+                af[0][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, 0, lane);
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+                bfr[0][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, 0, lane);
+#pragma unroll
+            for (int ks = 0; ks < Cfg::BK / 16; ++ks) {
+                const int cur = ks & 1;
+                if (ks + 1 < Cfg::BK / 16) {
+#pragma unroll
+                    for (int i = 0; i < Cfg::FM; ++i)
+                        af[cur ^ 1][i] = read_frag<P::A_KMAJOR, Cfg::BM>(la, wm * Cfg::FM + i, ks + 1, lane);
+#pragma unroll
+                    for (int j = 0; j < Cfg::FN; ++j)
+                        bfr[cur ^ 1][j] = read_frag<P::B_KMAJOR, Cfg::BN>(lb, wn * Cfg::FN + j, ks + 1, lane);
+                }
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[cur][i], bfr[cur][j], acc[i][j]);
+            }
         }
     }
 
@@ -433,24 +520,25 @@ struct ProjFwd {
 };
 
 // dX [N_tok, d] = G [N_tok, 2HD] * Ws [2HD, d], G = [dk | dv] (k segments of
-// HD), Ws = s_h-scaled [W_Km; W_Vm] stored [k][d]. dX row (b,t) is the
-// gradient of the memory row m'[b,t-1] (t >= 1).
+// HD), Ws = s_h-scaled [W_Km; W_Vm] stored transposed, [d][2HD], so that both
+// operands are K-major. dX row (b,t) is the gradient of the memory row
+// m'[b,t-1] (t >= 1).
 struct ProjBwdDm {
-    static constexpr bool A_KMAJOR = true, B_KMAJOR = false;
-    const bf16 *dk, *dv, *ws;
+    static constexpr bool A_KMAJOR = true, B_KMAJOR = true;
+    const bf16 *dk, *dv, *wt;
     float *dm;
     int64_t M, N, K, T;
     int HD;
     bool acc;
-    int64_t a_kseg, b_ld;
-    static constexpr int64_t b_kseg = 0, a_ld = 0;
+    int64_t a_kseg;
+    static constexpr int64_t b_kseg = 0, a_ld = 0, b_ld = 0;
     MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const
     {
         return k < HD ? dk + row * HD + k : dv + row * HD + (k - HD);
     }
-    MAGLEV_DEV const bf16 *b_ptr(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const { return wt + n * K + k; }
     MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
-    MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const { return ws + k * N + n; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t, int64_t) const { return nullptr; }
     MAGLEV_DEV void store(int64_t row, int64_t t, int64_t n, float x, int) const
     {
         // m'[T-1] feeds no key: its injection gradient is zero (written here
@@ -549,14 +637,27 @@ struct LmDu {
 };
 
 // Tile configurations, chosen by timing the three products at the d20 shape
-// (N_tok = 16384, d = 1280, 10 x 128 heads): two LDS stages and 8 or 16 waves
-// per workgroup, so that each SIMD has several waves to cover LDS and barrier
-// latency (one wave per SIMD left the matrix cores idle most of the time).
-using ProjCfg = TileCfg<128, 128, 2, 4, 2>;   // wave tile 64 x 32, 2 workgroups per CU
-using DwCfg = TileCfg<256, 256, 4, 4, 2>;     // wave tile 64 x 64, split over tokens
+// (N_tok = 16384, d = 1280, 10 x 128 heads) with random operands: two LDS
+// stages and 8 waves per workgroup, so that each SIMD has two or more waves to
+// cover LDS and barrier latency (one wave per SIMD left the matrix cores idle
+// most of the time).
+// The projection and dX have a short reduction (1280, 2560), so per-tile
+// start-up and stores weigh: 256 x 320 tiles (wave tile 64 x 160, 0.7 KB of
+// LDS reads per MFMA) make exactly two rounds of the 256 CUs for the
+// projection (N = 2560) and one for dX (N = 1280). Smaller problems, which
+// would leave CUs idle with them, take 128 x 128 tiles (two workgroups a CU).
+using ProjBigCfg = TileCfg<256, 320, 4, 2, 2, false>;
+using ProjCfg = TileCfg<128, 128, 2, 4, 2>;    // wave tile 64 x 32
+using DwCfg = TileCfg<256, 256, 2, 4, 2>;      // wave tile 128 x 64, split over tokens
 // At most 64 rows (decode: one memory row per stream) against many output
 // columns (every layer's stacked weights): one 64-row tile, weights streamed once.
-using WideCfg = TileCfg<64, 128, 1, 4, 2>;    // wave tile 64 x 32
+using WideCfg = TileCfg<64, 128, 1, 4, 2, false>;   // wave tile 64 x 32
+
+// Whether an M x N product fills at least one round of the CUs with 256 x 320 tiles.
+bool proj_big_tiles(int64_t M, int64_t N)
+{
+    return ((M + ProjBigCfg::BM - 1) / ProjBigCfg::BM) * ((N + ProjBigCfg::BN - 1) / ProjBigCfg::BN) >= 256;
+}
 
 template <class Cfg, class P>
 static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const char *name,
@@ -632,28 +733,51 @@ void launch_project_bf16(const Geom &g, int shift, const void *m, const void *wk
         prof::Scope ts("proj_fwd_skinny", s);
         hipLaunchKernelGGL(gemm_skinny_bf16<ProjFwd>, dim3((unsigned)((p.N + 15) / 16)), dim3(256), 0,
                            s, p);
+    } else if (proj_big_tiles(p.M, p.N)) {
+        run_gemm<ProjBigCfg>(p, 1, p.K, s, "proj_fwd", 4);
     } else {
         run_gemm<ProjCfg>(p, 1, p.K, s, "proj_fwd", 16);
     }
 }
 
-// s_h-scaled copy of [W_Km; W_Vm] (bf16; a plain copy when gate is null),
-// 8 elements per thread.
-__global__ void scale_weights(const bf16 *wk, const bf16 *wv, const float *gate, bf16 *out,
-                              int HD, int Dh, int d)
+// Transposed s_h-scaled copy of [W_Km; W_Vm]: out[e][r] = s_h(r) W[r][e]
+// (rows r < HD from W_Km, the rest from W_Vm; s_h = 1 when gate is null).
+// One workgroup per 64 x 64 block (2HD is a multiple of 128, d of 16), staged
+// through LDS so that both the reads and the writes are 16-byte runs.
+__global__ __launch_bounds__(256) void scale_weights_t(const bf16 *wk, const bf16 *wv,
+                                                       const float *gate, bf16 *out, int HD,
+                                                       int Dh, int d)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // chunk index
-    const int64_t per = (int64_t)HD * d / 8;
-    if (i >= 2 * per) return;
-    const bool second = i >= per;
-    const int64_t j = second ? i - per : i;
-    const int r = (int)((j * 8) / d);
-    const float sg = gate ? gate_sigmoid(gate[r / Dh]) : 1.0f;
-    float x[8];
-    load8((second ? wv : wk) + j * 8, x);
+    __shared__ float tile[64][65];
+    const int r0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+    const int R = 2 * HD;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= sg;
-    store8(out + i * 8, x);
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q;   // 512 chunks of 8: row c / 8, chunk c % 8
+        const int rr = c >> 3, e = e0 + 8 * (c & 7);
+        const int r = r0 + rr;
+        float x[8] = {};
+        if (e < d) {
+            const bf16 *src = r < HD ? wk + (int64_t)r * d : wv + (int64_t)(r - HD) * d;
+            load8(src + e, x);
+            const float sg = gate ? gate_sigmoid(gate[(r < HD ? r : r - HD) / Dh]) : 1.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] *= sg;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tile[8 * (c & 7) + u][rr] = x[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q;   // output row e0 + c / 8, chunk c % 8 of r
+        const int ee = c >> 3, e = e0 + ee;
+        if (e >= d) continue;
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = tile[ee][8 * (c & 7) + u];
+        store8(out + (int64_t)e * R + r0 + 8 * (c & 7), x);
+    }
 }
 
 // One workgroup per row r of [dW_Km; dW_Vm], 8 columns a thread:
@@ -737,24 +861,23 @@ void launch_proj_bwd_bf16(const Geom &g, const void *dk, const void *dv, const v
     const int HD = g.HD();
     bf16 *wsc = static_cast<bf16 *>(ws.W_scaled);
     {
-        const int64_t chunks = 2 * (int64_t)HD * g.d / 8;
         prof::Scope ts("proj_bwd_scale_w", s);
-        hipLaunchKernelGGL(scale_weights, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                           static_cast<const bf16 *>(wk), static_cast<const bf16 *>(wv), gate, wsc,
-                           HD, g.Dh, g.d);
+        hipLaunchKernelGGL(scale_weights_t, dim3((unsigned)((g.d + 63) / 64), (unsigned)(2 * HD / 64)),
+                           dim3(256), 0, s, static_cast<const bf16 *>(wk),
+                           static_cast<const bf16 *>(wv), gate, wsc, HD, g.Dh, g.d);
     }
     {
         ProjBwdDm p;
         p.dk = static_cast<const bf16 *>(dk);
         p.dv = static_cast<const bf16 *>(dv);
-        p.ws = wsc;
+        p.wt = wsc;
         p.dm = dm_prime;
         p.M = g.N(); p.N = g.d; p.K = 2 * (int64_t)HD; p.T = g.T;
         p.HD = HD;
         p.acc = (acc & 1u) != 0;
         p.a_kseg = HD;
-        p.b_ld = g.d;
-        run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm", 2);
+        if (proj_big_tiles(p.M, p.N)) run_gemm<ProjBigCfg>(p, 1, p.K, s, "proj_bwd_dm", 4);
+        else run_gemm<ProjCfg>(p, 1, p.K, s, "proj_bwd_dm", 2);
     }
     {
         ProjBwdDw p;
