@@ -98,6 +98,17 @@ struct HasRowSum : std::false_type {};
 template <class P>
 struct HasRowSum<P, std::void_t<decltype(std::declval<const P &>().rowsum)>> : std::true_type {};
 
+// A problem with store4(m, t, n, v, split), which stores columns n .. n+3 of
+// row m (N a multiple of 4), gets its accumulators transposed: the MFMA is
+// issued with the operands swapped, so that a lane holds one row of each
+// 32 x 32 block and runs of four consecutive columns (entries 4q .. 4q+3 are
+// columns 8q + 4(lane / 32) + 0..3), and stores 8 or 16 bytes at a time.
+template <class P, class = void>
+struct HasStore4 : std::false_type {};
+template <class P>
+struct HasStore4<P, std::void_t<decltype(std::declval<const P &>().store4(
+                        int64_t(), int64_t(), int64_t(), f32x4(), 0))>> : std::true_type {};
+
 // Sums v[k] (k < 32) over the 32 lanes of each half wave with 31 exchanges:
 // at distance D a lane keeps the half of its C live values selected by lane
 // bit D and adds the partner's copy of that half. Afterwards v[0] of lane l
@@ -252,6 +263,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
         for (int i = 0; i < IB; ++i) pb[i] += b_step;
     };
 
+    constexpr bool TR = HasStore4<P>::value;   // accumulators hold row-per-lane blocks
     f32x16 acc[Cfg::FM][Cfg::FN];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
@@ -282,7 +294,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-                for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[b][i], bfr[b][j], acc[i][j]);
+                for (int j = 0; j < Cfg::FN; ++j)
+                    acc[i][j] = TR ? mfma32(bfr[b][j], af[b][i], acc[i][j]) : mfma32(af[b][i], bfr[b][j], acc[i][j]);
 #pragma unroll
             for (int g = 0; g < (NREAD + 1) / 2 && g < NMFMA; ++g) {
                 __builtin_amdgcn_sched_group_barrier(kGemmSchedDsRead, 2, 0);
@@ -368,7 +381,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
 #pragma unroll
                 for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
-                    for (int j = 0; j < Cfg::FN; ++j) acc[i][j] = mfma32(af[cur][i], bfr[cur][j], acc[i][j]);
+                    for (int j = 0; j < Cfg::FN; ++j)
+                        acc[i][j] = TR ? mfma32(bfr[cur][j], af[cur][i], acc[i][j])
+                                       : mfma32(af[cur][i], bfr[cur][j], acc[i][j]);
             }
         }
     }
@@ -415,6 +430,24 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_bf16(P p, int64_t kper, int grou
 #pragma unroll
             for (int w = 0; w < Cfg::WN; ++w) sum += rs[w * Cfg::BM + rr];
             p.rowsum[m * p.rs_ld + tn] = sum;
+        }
+    } else if constexpr (TR) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const int64_t m = m0 + (wm * Cfg::FM + i) * 32 + (lane & 31);
+            if (m >= p.M) continue;
+            const int64_t t = p.T > 0 ? m % p.T : 0;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = n0 + (wn * Cfg::FN + j) * 32 + 8 * q + 4 * g;
+                    if (n < p.N)
+                        p.store4(m, t, n,
+                                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                       acc[i][j][4 * q + 3]},
+                                 split);
+                }
         }
     } else {
         const int64_t t0 = p.T > 0 ? m0 % p.T : 0;
@@ -517,6 +550,19 @@ struct ProjFwd {
             out[row * HD + c] = f2bf(x);
         }
     }
+    // four columns n .. n+3 (HD is a multiple of 4: they lie on one side)
+    MAGLEV_DEV void store4(int64_t row, int64_t t, int64_t n, f32x4 x, int) const
+    {
+        bf16 *out = n < HD ? km : vm;
+        const int64_t c = n < HD ? n : n - HD;
+        const bf16x4 v{f2bf(x[0]), f2bf(x[1]), f2bf(x[2]), f2bf(x[3])};
+        if (shift) {
+            if (t == 0) *reinterpret_cast<bf16x4 *>(out + row * HD + c) = bf16x4{};
+            if (t + 1 < T) *reinterpret_cast<bf16x4 *>(out + (row + 1) * HD + c) = v;
+        } else {
+            *reinterpret_cast<bf16x4 *>(out + row * HD + c) = v;
+        }
+    }
 };
 
 // dX [N_tok, d] = G [N_tok, 2HD] * Ws [2HD, d], G = [dk | dv] (k segments of
@@ -548,6 +594,13 @@ struct ProjBwdDm {
         float *p = dm + (row - 1) * N + n;
         *p = acc ? *p + x : x;
     }
+    MAGLEV_DEV void store4(int64_t row, int64_t t, int64_t n, f32x4 x, int) const
+    {
+        if (t == T - 1 && !acc) *reinterpret_cast<f32x4 *>(dm + row * N + n) = f32x4{};
+        if (t == 0) return;
+        f32x4 *p = reinterpret_cast<f32x4 *>(dm + (row - 1) * N + n);
+        *p = acc ? *p + x : x;
+    }
 };
 
 // dW partial [2HD, d] = sum over tokens u of G[u+1]^T m'[u] (u = 0 .. N_tok-2),
@@ -572,6 +625,10 @@ struct ProjBwdDw {
     MAGLEV_DEV void store(int64_t r, int64_t, int64_t e, float x, int split) const
     {
         part[((int64_t)split * M + r) * N + e] = x;
+    }
+    MAGLEV_DEV void store4(int64_t r, int64_t, int64_t e, f32x4 x, int split) const
+    {
+        *reinterpret_cast<f32x4 *>(part + ((int64_t)split * M + r) * N + e) = x;
     }
 };
 
@@ -616,6 +673,10 @@ struct LmDm {
     MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
     MAGLEV_DEV const bf16 *b_lin(int64_t k, int64_t n) const { return u + k * b_ld + n; }
     MAGLEV_DEV void store(int64_t row, int64_t, int64_t n, float x, int) const { dm[row * N + n] = x; }
+    MAGLEV_DEV void store4(int64_t row, int64_t, int64_t n, f32x4 x, int) const
+    {
+        *reinterpret_cast<f32x4 *>(dm + row * N + n) = x;
+    }
 };
 struct LmDu {
     static constexpr bool A_KMAJOR = false, B_KMAJOR = false;
@@ -632,6 +693,11 @@ struct LmDu {
     MAGLEV_DEV void store(int64_t r, int64_t, int64_t e, float x, int) const
     {
         float *p = du + r * N + e;
+        *p = acc ? *p + x : x;
+    }
+    MAGLEV_DEV void store4(int64_t r, int64_t, int64_t e, f32x4 x, int) const
+    {
+        f32x4 *p = reinterpret_cast<f32x4 *>(du + r * N + e);
         *p = acc ? *p + x : x;
     }
 };
