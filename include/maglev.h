@@ -204,7 +204,9 @@ size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W);
  *   that overlap in time need their own workspaces).
  * The ring holds dtype values: the new entry is rounded once (ties to even).
  * The RoPE angle of the new position is evaluated on the device in double
- * precision, so no table bounds the position. Positions must be >= 0. */
+ * precision, so no table bounds the position. Positions must be >= 0.
+ * Bs*H must be below 2^31 (one workgroup per stream and head), else
+ * MAGLEV_ERR_INVALID_VALUE. */
 maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
                                    float rope_base, float scale, int32_t dtype, const void *q,
                                    const void *k, const void *v, const void *kmem,

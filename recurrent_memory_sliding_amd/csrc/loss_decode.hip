@@ -219,9 +219,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     __shared__ float wacc[kDecWaves][DH];
     __shared__ float wred[kDecWaves];
 
-    const int64_t row = blockIdx.x;              // b * H + h
-    const int h = (int)(row % H);
-    const int64_t b = row / H;
+    const int row32 = blockIdx.x;                // b * H + h (Bs * H < 2^31)
+    const int64_t row = row32;
+    const int h = row32 % H;
+    const int64_t b = row32 / H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane / CH, ch = lane % CH;

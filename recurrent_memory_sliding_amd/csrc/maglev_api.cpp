@@ -384,6 +384,7 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
     if (st != MAGLEV_OK) return st;
     if (!gate_logit || !pos) return fail(MAGLEV_ERR_INVALID_VALUE, "gate_logit or pos is NULL");
     if ((double)Bs * H * W * Dh > 4.0e12) return fail(MAGLEV_ERR_INVALID_VALUE, "ring too large");
+    if ((int64_t)Bs * H > 2147483647) return fail(MAGLEV_ERR_INVALID_VALUE, "Bs*H must be below 2^31");
     const size_t need = decode_workspace_bytes(Bs, H, Dh, W);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
@@ -500,6 +501,7 @@ maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int3
     if (st != MAGLEV_OK) return st;
     if (!gates || !pos) return fail(MAGLEV_ERR_INVALID_VALUE, "gates or pos is NULL");
     if ((double)Bs * H * W * Dh > 4.0e12) return fail(MAGLEV_ERR_INVALID_VALUE, "ring too large");
+    if ((int64_t)Bs * H > 2147483647) return fail(MAGLEV_ERR_INVALID_VALUE, "Bs*H must be below 2^31");
     const size_t need = decode_workspace_bytes(Bs, H, Dh, W);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");

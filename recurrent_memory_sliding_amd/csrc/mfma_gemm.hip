@@ -716,8 +716,11 @@ using ProjBigCfg = TileCfg<256, 320, 4, 2, 2, false>;
 using ProjCfg = TileCfg<128, 128, 2, 4, 2>;    // wave tile 64 x 32
 using DwCfg = TileCfg<256, 256, 2, 4, 2>;      // wave tile 128 x 64, split over tokens
 // At most 64 rows (decode: one memory row per stream) against many output
-// columns (every layer's stacked weights): one 64-row tile, weights streamed once.
-using WideCfg = TileCfg<64, 128, 1, 4, 2, false>;   // wave tile 64 x 32
+// columns (every layer's stacked weights): one 64-row tile, weights streamed
+// once. The product is bound by the latency of the weight loads: three stages
+// of 64 x 256 tiles (one workgroup a CU) stream the 131 MB of 20 d20 layers
+// in 30 µs, two stages of 64 x 128 (three a CU) in 32.5 µs.
+using WideCfg = TileCfg<64, 256, 1, 4, 3, false>;   // wave tile 64 x 64
 
 // Whether an M x N product fills at least one round of the CUs with 256 x 320 tiles.
 bool proj_big_tiles(int64_t M, int64_t N)
