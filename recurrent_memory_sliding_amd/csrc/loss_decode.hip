@@ -132,6 +132,7 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kBatchPasses = 4;
+constexpr int kDecBuffers = 2;   // batches in flight per wave
 
 size_t decode_workspace_bytes(int, int, int, int) { return 0; }
 
@@ -247,12 +248,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     if constexpr (GATED) {
         if (tid * 8 < H * DH) load8(km + b * mem_stride + tid * 8, gx);
     }
-    // Two batch buffers: the next batch is in flight while one is reduced.
-    // Every issue is unconditional (slots past the ring's end re-read its
-    // last slot, and are never used), so the count of loads in flight is the
-    // same on every path and no join makes a wait cover the next batch.
+    // kDecBuffers batch buffers in rotation: the next batches are in flight
+    // while one is reduced. Every issue is unconditional (slots past the
+    // ring's end re-read its last slot, and are never used), so the count of
+    // loads in flight is the same on every path and no join makes a wait
+    // cover the next batch.
     using Batch = Raw8<T>[2][kBatchPasses];   // [K, V][pass]
-    Batch buf0, buf1;
+    Batch bufs[kDecBuffers];
     auto issue = [&](int j, Batch &bf) {
 #pragma unroll
         for (int ps = 0; ps < kBatchPasses; ++ps) {
@@ -262,8 +264,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             bf[1][ps].load(vring + (int64_t)sl * DH);
         }
     };
-    issue(w, buf0);
-    issue(w + kDecWaves, buf1);
+#pragma unroll
+    for (int u = 0; u < kDecBuffers; ++u) issue(w + u * kDecWaves, bufs[u]);
 
     // 2. Rotation of position p (double precision: no table bounds p),
     //    rotated query, and the new entry (written by this workgroup only).
@@ -390,11 +392,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
         m_run = mn;
     };
-    for (int j = w; j < nbatch; j += 2 * kDecWaves) {
-        batch(j, buf0);
-        issue(j + 2 * kDecWaves, buf0);
-        if (j + kDecWaves < nbatch) batch(j + kDecWaves, buf1);
-        issue(j + 3 * kDecWaves, buf1);
+    for (int j = w; j < nbatch; j += kDecBuffers * kDecWaves) {
+#pragma unroll
+        for (int u = 0; u < kDecBuffers; ++u) {
+            if (j + u * kDecWaves < nbatch) batch(j + u * kDecWaves, bufs[u]);
+            issue(j + (u + kDecBuffers) * kDecWaves, bufs[u]);
+        }
     }
 
     // 4. Merge the lane groups of the wave (same channels, other slots), then the waves.
