@@ -8,7 +8,8 @@ inputs (a query's output needs only its W keys and the memory row before them;
 a key's gradient needs only the W queries after it and their windows), at the
 named-workload bar: 2e-2 max-abs for the activations. Gradients that sum over
 every token (dm', dW, dgate) are also checked through identities that hold at
-any size, computed in float64 on the CPU from the GPU's own dk/dv."""
+any size, computed in float64 on the CPU from the GPU's own dk/dv, over every
+row and column; so are the memory projections (kmem, vmem) of the forward."""
 import numpy as np
 import pytest
 import torch
@@ -95,12 +96,28 @@ def check_forward_samples(sh, inp, g, km, vm, o, lse):
     return worst
 
 
+def shifted_projection(inp, sh):
+    """kmem, vmem [B,T,H,Dh] of the whole batch in float64 (row t from m'[t-1],
+    row 0 zero): the definition the projection product computes."""
+    mp = inp["m_prime"].double()
+    prev = torch.zeros_like(mp)
+    prev[:, 1:] = mp[:, :-1]
+    shape = (sh.B, sh.T, sh.H, sh.Dh)
+    return ((prev @ inp["W_Km"].double().T).reshape(shape).numpy(),
+            (prev @ inp["W_Vm"].double().T).reshape(shape).numpy())
+
+
 def test_d20_layer_forward_fullsize():
+    """Sampled outputs against the oracle, and every kmem/vmem entry (the
+    256 x 320-tile projection this size launches) against the float64 product."""
     sh = wl.D20_LAYER
     flush("d20 layer forward, B=8 T=2048 W=512")
     inp = wl.layer_inputs(sh, 1)
     g, km, vm, o, lse = run_forward_fullsize(sh, inp)
     flush("  worst o error %.3e" % check_forward_samples(sh, inp, g, km, vm, o, lse))
+    rk, rv = shifted_projection(inp, sh)
+    check("kmem (all)", km, rk, TOL, max_scale(rk))
+    check("vmem (all)", vm, rv, TOL, max_scale(rv))
 
 
 def backward_fullsize(sh, seed, keys):
@@ -121,22 +138,20 @@ def backward_fullsize(sh, seed, keys):
     WK, WV = inp["W_Km"].double(), inp["W_Vm"].double()
     mp = inp["m_prime"].double()
     HD = sh.H * sh.Dh
-    rng = np.random.default_rng(seed)
-    for b, t in [(0, 0), (sh.B - 1, sh.T - 2), (1 % sh.B, 777)] + [(int(rng.integers(sh.B)), int(rng.integers(sh.T - 1))) for _ in range(4)]:
-        sk = (dk[b, t + 1] * s[:, None]).reshape(HD)
-        sv = (dv[b, t + 1] * s[:, None]).reshape(HD)
-        want = sk @ WK + sv @ WV
-        check("dm'[%d,%d]" % (b, t), gr["dm_prime"][b, t], want.numpy(), TOL)
+    # every row of dm' and every entry of dW (the products this size launches)
+    sk = (dk[:, 1:] * s[None, None, :, None]).reshape(sh.B, sh.T - 1, HD)
+    sv = (dv[:, 1:] * s[None, None, :, None]).reshape(sh.B, sh.T - 1, HD)
+    want = (sk @ WK + sv @ WV).numpy()
+    check("dm' (all rows)", gr["dm_prime"][:, :-1], want, TOL, max_scale(want))
+    del sk, sv, want
     assert gr["dm_prime"][:, -1].abs().max().item() == 0.0
-    cols = rng.choice(sh.d, 6, replace=False)
     prev = torch.zeros_like(mp)
     prev[:, 1:] = mp[:, :-1]
-    X = prev[:, :, cols].reshape(-1, len(cols))                  # [N, 6]
-    for name, grad, W_ in (("dW_Km", dk, "K"), ("dW_Vm", dv, "V")):
+    X = prev.reshape(-1, sh.d)                                   # [N, d]
+    for name, grad in (("dW_Km", dk), ("dW_Vm", dv)):
         G = (grad * s[None, None, :, None]).reshape(-1, HD)      # [N, HD]
         want = (G.T @ X).numpy()
-        got = gr[name][:, cols]
-        check(name, got, want, TOL, max_scale(want))
+        check(name + " (all)", gr[name], want, TOL, max_scale(want))
     kmc, vmc = km.cpu().double(), vm.cpu().double()
     terms = (kmc * dk + vmc * dv).sum(dim=(0, 1, 3))
     want = (s * (1 - s) * terms).numpy()
