@@ -19,8 +19,9 @@
 // each thread owns one chunk pair of the row (8 channels c..c+7 of a head and
 // their rotation partners c+Dh/2..; H*Dh <= 4096, so at most 256 threads) for
 // the whole range, so it keeps its gate-gradient
-// partial sums in registers (the gate values sit in LDS). The two row
-// reductions (sum of squares, mean of dkn*kn) are workgroup sums.
+// partial sums in registers (the gate values sit in LDS). The row reductions
+// (sum of squares; in the backward also mean of dkn*kn, in the same pass) are
+// workgroup sums.
 // Everything is HBM-bound streaming: 16-byte loads and stores per lane.
 #include "common.hpp"
 #include "internal.hpp"

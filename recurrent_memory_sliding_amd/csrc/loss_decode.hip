@@ -125,10 +125,10 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
 // is read by Dh/8 lanes with 16-byte loads, so each wave instruction reads
 // 64/(Dh/8) consecutive slots contiguously. The ring is cut into batches of
 // kBatchPasses wave passes; batch j goes to wave j mod 4, which keeps an
-// online softmax state per lane group. The loads of a wave's first batch do
-// not depend on the position (the slot about to be overwritten is read and
-// discarded), so they are issued before pos[b] arrives and before the
-// rotation of the new position is evaluated.
+// online softmax state per lane group and kDecBuffers batches in flight. The
+// loads of a wave's first batches do not depend on the position (the slot
+// about to be overwritten is read and discarded), so they are issued before
+// pos[b] arrives and before the rotation of the new position is evaluated.
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kBatchPasses = 4;
