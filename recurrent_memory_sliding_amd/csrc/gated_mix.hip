@@ -31,7 +31,8 @@ namespace maglev {
 
 namespace {
 
-constexpr int kGatedFwdRows = 8;   // token rows per workgroup in the forward mix
+constexpr int kGatedFwdRows = 16;  // token rows per workgroup in the forward mix (d20: 1024
+                                    // workgroups, all resident at once; 74 µs against 85 at 8 rows)
 
 MAGLEV_DEV float two_sigmoid(float a) { return 2.0f / (1.0f + __expf(-a)); }
 
