@@ -96,6 +96,7 @@ MAGLEV_DEV void lds8(const float *p, float *out)
 struct GatedArgs {
     int64_t N, Tlen, pos0;
     int HD, rows_per_block;
+    int row_threads;      // threads a row takes (a multiple of 64)
     float eps;
     const float2 *rope;   // [pos][Dh/2] or nullptr
     const float *gates;   // [4][HD] logits: a_kl, a_kr, a_vl, a_vr
@@ -237,15 +238,17 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
 // (before the 2 sigma (1 - sigma) factor).
 // dkn = R^T (g_kr (.) dk~) does not depend on the norm, and
 // mean(dkn (.) kn) = rs * mean(dkn (.) kp) with rs = 1/rms, so both row sums
-// (of kp^2 and of dkn (.) kp) come out of one workgroup reduction.
-// A row's twelve loads go out together; for bf16 the next row's are in flight
-// while the current one is reduced and written.
+// (of kp^2 and of dkn (.) kp) come out of one reduction. A row's twelve loads
+// go out together.
 // ---------------------------------------------------------------------------
-MAGLEV_DEV float2 group_sum2(float x, float y, float2 *red, int nw)
+// Sums of x and y over the nw waves of one row group (red: one slot per wave
+// of the group, wave index wi inside it); every thread of the workgroup must
+// call it, since it holds the workgroup barrier.
+MAGLEV_DEV float2 group_sum2(float x, float y, float2 *red, int nw, int wi)
 {
     x = wave_sum(x);
     y = wave_sum(y);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(x, y);
+    if ((threadIdx.x & 63) == 0) red[wi] = make_float2(x, y);
     __syncthreads();
     float2 t = make_float2(0.0f, 0.0f);
     for (int i = 0; i < nw; ++i) { t.x += red[i].x; t.y += red[i].y; }
@@ -253,17 +256,27 @@ MAGLEV_DEV float2 group_sum2(float x, float y, float2 *red, int nw)
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, const T *v,
+__global__ __launch_bounds__(256, 2) void gated_mix_bwd(GatedArgs a, const T *k, const T *v,
                                                       const T *kp, const T *vm, T *dk, T *dv,
                                                       T *dkp, T *dvm, float *gpart)
 {
-    __shared__ float2 red[2][4];
-    extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD]
-    const int tid = threadIdx.x, nw = blockDim.x >> 6;
-    const bool act = tid < a.HD / 16;
-    const ChunkPair<DH> cp(act ? tid : 0);
+    // The workgroup is nh row groups of rt threads (nh = 2 when a row needs at
+    // most 128 threads): group h takes rows r0 + h, r0 + h + nh, ..., so that
+    // two waves a SIMD work while the per-block gate partials stay as few as
+    // with one group. Both groups run the same number of iterations (a group
+    // past the block's last row runs one without loads or stores), since the
+    // row reductions hold workgroup barriers.
+    __shared__ float2 red[2][2][4];   // [iteration parity][group][wave of the group]
+    extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD] gates, [64][rt] partials
+    const int rt = a.row_threads, nh = blockDim.x / rt;
+    const int tid = threadIdx.x, grp = tid / rt, tig = tid - grp * rt;
+    const int nwg = rt >> 6, wig = tig >> 6;
+    const bool act = tig < a.HD / 16;
+    const ChunkPair<DH> cp(act ? tig : 0);
     const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
     const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
+    const int64_t niter = r1 > r0 ? (r1 - r0 + nh - 1) / nh : 0;
+    auto row_of = [&](int64_t it) { return r0 + it * nh + grp; };
     // [kp, dk~, k, dv~, v, vm][low, high half]
     using RowIn = Chunk8<T>[6][2];
     auto load_row = [&](int64_t row, RowIn &d) {
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, co
         const T *src[6] = {kp, dk, k, dv, v, vm};
 #pragma unroll
         for (int t = 0; t < 6; ++t) {
-            if (act) {
+            if (act && row < r1) {
                 d[t][0].load(src[t] + base + cp.lo);
                 d[t][1].load(src[t] + base + cp.hi);
             } else {
@@ -280,16 +293,18 @@ __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, co
             }
         }
     };
-    RowIn ia, ib;
-    if (r0 < r1) load_row(r0, ia);
+    RowIn ia;
+    if (niter > 0) load_row(row_of(0), ia);
     stage_gates(a.gates, 4 * a.HD, gsh);
     const float *gkl = gsh, *gkr = gsh + a.HD, *gvl = gsh + 2 * a.HD, *gvr = gsh + 3 * a.HD;
     float pkl[16] = {}, pkr[16] = {}, pvl[16] = {}, pvr[16] = {};
     const float inv_hd = 1.0f / (float)a.HD;
-    auto grad_row = [&](int64_t row, const RowIn &d) {
+    auto grad_row = [&](int64_t it, const RowIn &d) {
+        const int64_t row = row_of(it);
+        const bool live = act && row < r1;
         const int64_t base = row * a.HD;
-        const float2 *cs = (act && a.rope) ? a.rope + (a.pos0 + row % a.Tlen) * (DH / 2) + 8 * cp.j
-                                           : nullptr;
+        const float2 *cs = (live && a.rope) ? a.rope + (a.pos0 + row % a.Tlen) * (DH / 2) + 8 * cp.j
+                                            : nullptr;
         float nl[8], nh[8], gl[8], gh[8], dnl[8], dnh[8];
         d[0][0].get(nl);
         d[0][1].get(nh);
@@ -309,10 +324,10 @@ __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, co
             ss += nl[e] * nl[e] + nh[e] * nh[e];
             sd += dnl[e] * nl[e] + dnh[e] * nh[e];
         }
-        const float2 t = group_sum2(ss, sd, red[row & 1], nw);
+        const float2 t = group_sum2(ss, sd, red[it & 1][grp], nwg, wig);
         const float rs = rsqrtf(t.x * inv_hd + a.eps);
         const float mu = t.y * rs * inv_hd;   // mean(dkn (.) kn)
-        if (!act) return;
+        if (!live) return;
 #pragma unroll
         for (int e = 0; e < 8; ++e) { nl[e] *= rs; nh[e] *= rs; }   // kn
 #pragma unroll
@@ -378,25 +393,34 @@ __global__ __launch_bounds__(256) void gated_mix_bwd(GatedArgs a, const T *k, co
         store8(dvm + base + cp.lo, ml);
         store8(dvm + base + cp.hi, mh);
     };
-    if constexpr (sizeof(T) == 2) {
-        for (int64_t row = r0; row < r1; row += 2) {
-            if (row + 1 < r1) load_row(row + 1, ib);
-            grad_row(row, ia);
-            if (row + 1 < r1) {
-                if (row + 2 < r1) load_row(row + 2, ia);
-                grad_row(row + 1, ib);
-            }
+    // One row in flight per group: the second group is what overlaps a row's
+    // loads with another's reduction (a prefetched row per group costs the
+    // registers of two waves a SIMD: 107 µs at d20 against 139 µs).
+    for (int64_t it = 0; it < niter; ++it) {
+        if (it > 0) load_row(row_of(it), ia);
+        grad_row(it, ia);
+    }
+    float *parts[4] = {pkl, pkr, pvl, pvr};
+    if (nh > 1) {
+        // group 1 hands its partial sums to group 0 through LDS ([64][rt]
+        // after the gates), which adds them in a fixed order
+        float *pp = gsh + 4 * a.HD;
+        if (grp == 1 && act) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) pp[(gi * 16 + e) * rt + tig] = parts[gi][e];
         }
-    } else {
-        // float rows are twice as large: one row in flight at a time
-        for (int64_t row = r0; row < r1; ++row) {
-            if (row > r0) load_row(row, ia);
-            grad_row(row, ia);
+        __syncthreads();
+        if (grp == 0 && act) {
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) parts[gi][e] += pp[(gi * 16 + e) * rt + tig];
         }
     }
-    if (!act) return;
+    if (grp != 0 || !act) return;
     float *out = gpart + (int64_t)blockIdx.x * 4 * a.HD;
-    const float *parts[4] = {pkl, pkr, pvl, pvr};
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
         store8(out + gi * a.HD + cp.lo, parts[gi]);
@@ -440,6 +464,7 @@ GatedArgs gated_args(const Geom &g, const float *gates, float eps, const float2 
     GatedArgs a;
     a.N = g.N(); a.Tlen = g.T; a.pos0 = g.pos0;
     a.HD = g.HD(); a.rows_per_block = rows_per_block;
+    a.row_threads = (int)row_threads(g.HD());
     a.eps = eps; a.rope = rope; a.gates = gates;
     return a;
 }
@@ -466,9 +491,12 @@ void bwd_t(const Geom &g, const void *k, const void *v, const void *kp, const vo
 {
     const GatedArgs a = gated_args(g, gates, eps, rope, ws.g_rows);
     {
+        // two row groups a workgroup when a row takes at most 128 threads
+        const unsigned rt = row_threads(g.HD()), nh = rt <= 128 ? 2u : 1u;
+        const size_t lds = gate_lds_bytes(g.HD()) + (nh > 1 ? (size_t)64 * rt * sizeof(float) : 0);
         prof::Scope ts("gated_mix_bwd", s);
-        hipLaunchKernelGGL((gated_mix_bwd<T, DH>), dim3((unsigned)ws.g_blocks),
-                           dim3(row_threads(g.HD())), gate_lds_bytes(g.HD()), s, a,
+        hipLaunchKernelGGL((gated_mix_bwd<T, DH>), dim3((unsigned)ws.g_blocks), dim3(nh * rt), lds,
+                           s, a,
                            static_cast<const T *>(k),
                            static_cast<const T *>(v), static_cast<const T *>(kp),
                            static_cast<const T *>(vm), static_cast<T *>(dk), static_cast<T *>(dv),
