@@ -32,17 +32,19 @@ namespace maglev {
 namespace {
 
 constexpr int kGatedFwdRows = 16;  // token rows per workgroup in the forward mix (d20: 1024
-                                    // workgroups, all resident at once; 74 µs against 85 at 8 rows)
+                                    // workgroups, all resident at once)
 
 MAGLEV_DEV float two_sigmoid(float a) { return 2.0f / (1.0f + __expf(-a)); }
 
-// Sum over the workgroup (nw waves); every thread receives the total. `red`
-// holds one float per wave; callers alternate buffers between consecutive
-// sums so that one barrier per sum suffices.
-MAGLEV_DEV float group_sum(float x, float *red, int nw)
+// Sum over one row group of nw waves (wi: this wave's index inside it); every
+// thread of the group receives the total. `red` holds one float per wave;
+// callers alternate buffers between consecutive sums so that one barrier per
+// sum suffices, and every thread of the workgroup calls it (it holds the
+// workgroup barrier).
+MAGLEV_DEV float group_sum(float x, float *red, int nw, int wi)
 {
     x = wave_sum(x);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    if ((threadIdx.x & 63) == 0) red[wi] = x;
     __syncthreads();
     float t = 0.0f;
     for (int i = 0; i < nw; ++i) t += red[i];
@@ -133,21 +135,27 @@ template <> struct Chunk8<float> {
 
 // ---------------------------------------------------------------------------
 // Forward: mixed entries kx, vx from k, v, kp (pre-norm), vm.
-// A row's eight loads go out together, and the next row's before the current
-// one is reduced and mixed (the row norm's workgroup sum is the only step that
-// waits on other threads).
+// A row's eight loads go out together; two row groups a workgroup keep two
+// rows in flight (the row norm's sum is the only step that waits on other
+// threads).
 // ---------------------------------------------------------------------------
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, const T *v,
                                                       const T *kp, const T *vm, T *kx, T *vx)
 {
-    __shared__ float red[2][4];
+    // Row groups as in the backward: nh groups of rt threads, group h taking
+    // rows r0 + h, r0 + h + nh, ..., one row in flight each.
+    __shared__ float red[2][2][4];   // [iteration parity][group][wave of the group]
     extern __shared__ __attribute__((aligned(16))) float gsh[];   // [4][HD]
-    const int tid = threadIdx.x, nw = blockDim.x >> 6;
-    const bool act = tid < a.HD / 16;
-    const ChunkPair<DH> cp(act ? tid : 0);
+    const int rt = a.row_threads, nh = blockDim.x / rt;
+    const int tid = threadIdx.x, grp = tid / rt, tig = tid - grp * rt;
+    const int nwg = rt >> 6, wig = tig >> 6;
+    const bool act = tig < a.HD / 16;
+    const ChunkPair<DH> cp(act ? tig : 0);
     const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_block;
     const int64_t r1 = r0 + a.rows_per_block < a.N ? r0 + a.rows_per_block : a.N;
+    const int64_t niter = r1 > r0 ? (r1 - r0 + nh - 1) / nh : 0;
+    auto row_of = [&](int64_t it) { return r0 + it * nh + grp; };
     // [kp, k, v, vm][low, high half]
     using RowIn = Chunk8<T>[4][2];
     auto load_row = [&](int64_t row, RowIn &d) {
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
         const T *src[4] = {kp, k, v, vm};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            if (act) {
+            if (act && row < r1) {
                 d[t][0].load(src[t] + base + cp.lo);
                 d[t][1].load(src[t] + base + cp.hi);
             } else {
@@ -164,12 +172,13 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
             }
         }
     };
-    RowIn ia, ib;
-    if (r0 < r1) load_row(r0, ia);
+    RowIn ia;
+    if (niter > 0) load_row(row_of(0), ia);
     stage_gates(a.gates, 4 * a.HD, gsh);
     const float *gk = gsh, *gv = gsh + 2 * a.HD;   // [2][HD] each: local, recurrent
     const float inv_hd = 1.0f / (float)a.HD;
-    auto mix_row = [&](int64_t row, const RowIn &d) {
+    auto mix_row = [&](int64_t it, const RowIn &d) {
+        const int64_t row = row_of(it);
         const int64_t base = row * a.HD;
         float nl[8], nh[8];
         d[0][0].get(nl);
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
         float ss = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += nl[e] * nl[e] + nh[e] * nh[e];
-        const float rs = rsqrtf(group_sum(ss, red[row & 1], nw) * inv_hd + a.eps);
-        if (!act) return;
+        const float rs = rsqrtf(group_sum(ss, red[it & 1][grp], nwg, wig) * inv_hd + a.eps);
+        if (!act || row >= r1) return;
         float kl[8], kh[8];
         d[1][0].get(kl);
         d[1][1].get(kh);
@@ -221,13 +230,9 @@ __global__ __launch_bounds__(256) void gated_mix_fwd(GatedArgs a, const T *k, co
         store8(vx + base + cp.lo, vl);
         store8(vx + base + cp.hi, vh);
     };
-    for (int64_t row = r0; row < r1; row += 2) {
-        if (row + 1 < r1) load_row(row + 1, ib);
-        mix_row(row, ia);
-        if (row + 1 < r1) {
-            if (row + 2 < r1) load_row(row + 2, ia);
-            mix_row(row + 1, ib);
-        }
+    for (int64_t it = 0; it < niter; ++it) {
+        if (it > 0) load_row(row_of(it), ia);
+        mix_row(it, ia);
     }
 }
 
@@ -476,9 +481,9 @@ void fwd_t(const Geom &g, const void *k, const void *v, const void *kp, const vo
     const int rpb = kGatedFwdRows;
     const GatedArgs a = gated_args(g, gates, eps, rope, rpb);
     const unsigned nblk = (unsigned)((g.N() + rpb - 1) / rpb);
+    const unsigned rt = row_threads(g.HD()), nh = rt <= 128 ? 2u : 1u;
     prof::Scope ts("gated_mix", s);
-    hipLaunchKernelGGL((gated_mix_fwd<T, DH>), dim3(nblk), dim3(row_threads(g.HD())),
-                       gate_lds_bytes(g.HD()), s, a,
+    hipLaunchKernelGGL((gated_mix_fwd<T, DH>), dim3(nblk), dim3(nh * rt), gate_lds_bytes(g.HD()), s, a,
                        static_cast<const T *>(k), static_cast<const T *>(v),
                        static_cast<const T *>(kp), static_cast<const T *>(vm),
                        static_cast<T *>(kx), static_cast<T *>(vx));
