@@ -156,6 +156,7 @@ def test_decode_validation(L):
     assert step(args(), t=bad) == INVALID
     assert step(args(), stride=10 * 128 - 8) == INVALID   # below H*Dh
     assert step(args(), stride=10 * 128 + 4) == INVALID   # not a multiple of 8
+    assert step(args(Bs=2 ** 30, W=1)) == INVALID        # Bs*H at or above 2^31 workgroups
     assert step(args(Bs=0)) == OK
     assert step(args(Bs=0), stride=20 * 10 * 128) == OK
     assert L.maglev_decode_advance(5, None, None) == INVALID
@@ -222,6 +223,7 @@ def test_gated_decode_validation(L):
     assert step(a(), stride=10 * 128 - 8) == INVALID
     bad = list(tail); bad[2] = None   # pos
     assert step(a(), t=bad) == INVALID
+    assert step(a(Bs=2 ** 30, W=1)) == INVALID   # Bs*H at or above 2^31 workgroups
     assert step(a(Bs=0)) == OK
 
 
