@@ -156,6 +156,16 @@ def test_gated_bf16_ten_heads_two_waves_per_row():
     run_case(shape(B=1, T=130, W=40, H=10, Dh=128, d=256), 63)
 
 
+def test_gated_bf16_wide_rows_one_group_per_workgroup():
+    """H*Dh = 2560: a row takes 192 threads, so the mix kernels run one row
+    group a workgroup (narrower rows run two); 41 rows leave a ragged block."""
+    run_case(shape(B=1, T=41, W=20, H=20, Dh=128, d=64), 70)
+
+
+def test_gated_fp32_wide_rows_one_group_per_workgroup():
+    run_case(shape(B=1, T=37, W=16, H=18, Dh=128, d=64, dtype=wl.F32), 71)
+
+
 def test_gated_fp32_exact_algebra():
     run_case(shape(B=2, T=150, W=40, H=2, Dh=64, d=128, dtype=wl.F32), 64)
 
