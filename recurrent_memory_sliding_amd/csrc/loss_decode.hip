@@ -41,9 +41,13 @@ __global__ __launch_bounds__(kLossThreads) void loss_partial(int64_t n8, const T
     float sum = 0.0f;
     const int64_t stride = (int64_t)gridDim.x * kLossThreads;
     for (int64_t i = (int64_t)blockIdx.x * kLossThreads + threadIdx.x; i < n8; i += stride) {
-        float a[8], b[8], g[8];
+        // every load of the chunk is issued before its first store (the
+        // compiler cannot move a load across a store it cannot prove apart)
+        float a[8], b[8], g[8], om[8], op[8];
         load8(m + 8 * i, a);
         load8(mp + 8 * i, b);
+        if (dm && (acc & 1u)) load8(dm + 8 * i, om);
+        if (dmp && (acc & 2u)) load8(dmp + 8 * i, op);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float diff = a[e] - b[e];
@@ -51,18 +55,14 @@ __global__ __launch_bounds__(kLossThreads) void loss_partial(int64_t n8, const T
             g[e] = g2 * diff;
         }
         if (dm) {
-            float out[8];
-            if (acc & 1u) load8(dm + 8 * i, out);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = (acc & 1u) ? out[e] + g[e] : g[e];
-            store8(dm + 8 * i, out);
+            for (int e = 0; e < 8; ++e) om[e] = (acc & 1u) ? om[e] + g[e] : g[e];
+            store8(dm + 8 * i, om);
         }
         if (dmp) {
-            float out[8];
-            if (acc & 2u) load8(dmp + 8 * i, out);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) out[e] = (acc & 2u) ? out[e] - g[e] : -g[e];
-            store8(dmp + 8 * i, out);
+            for (int e = 0; e < 8; ++e) op[e] = (acc & 2u) ? op[e] - g[e] : -g[e];
+            store8(dmp + 8 * i, op);
         }
     }
     sum = wave_sum(sum);
