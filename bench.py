@@ -150,19 +150,22 @@ def roofline_of(flops, nbytes, seconds):
 
 
 def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter runs
+    """HBM bytes per launch of `kernel` (or per step, for a record that spans
+    several kernels) from the committed counter runs
     (profiles/pmc_traffic.json), or None when they are missing or were taken
-    on a different source of that kernel."""
+    on a different source of any kernel the record covers."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)["kernels"][kernel]
-        src = os.path.join(ROOT, "recurrent_memory_sliding_amd", "csrc", rec["source"])
-        with open(src, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-    except (OSError, KeyError, ValueError):
-        return None
-    if sha != rec["source_sha256"]:
+        sources = rec["sources"] if "sources" in rec else [rec["source"]]
+        want = rec["source_sha256"] if "sources" in rec else [rec["source_sha256"]]
+        for name, sha_rec in zip(sources, want):
+            src = os.path.join(ROOT, "recurrent_memory_sliding_amd", "csrc", name)
+            with open(src, "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != sha_rec:
+                    return None
+    except (OSError, KeyError, ValueError, TypeError):
         return None
     return float(rec["fetch_bytes"]) + float(rec["write_bytes"])
 
@@ -646,7 +649,8 @@ def main():
             "tokens/s": round(dsh.Bs / (dms / 1e3), 1),
             "algorithmic_GB_per_step": round(dbytes / 1e9, 4),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic("decode_step") if args.mix == "sigma" else None},
             "graph": "one HIP graph per step: one projection of m_{t-1} by all layers' stacked weights, 20 decode steps, advance",
         }
     if not args.no_prefiller:
