@@ -392,10 +392,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
         m_run = mn;
     };
+    // The same for a batch whose slots all hold positions >= 0 and none of
+    // which is the new entry's (all batches of a full ring but one): no
+    // per-slot tests. Which form a batch takes is the same on the whole wave,
+    // so the choice is a scalar branch; the per-slot tests of the general
+    // form made divergent branches around every slot and cost about 4 % of
+    // a decode step.
+    const int jnew = slot_new / SB;
+    auto batch_full = [&](const Batch &cur) {
+        float sc[kBatchPasses];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int ps = 0; ps < kBatchPasses; ++ps) {
+            float kv[8];
+            cur[0][ps].get(kv);
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qv[e] * kv[e];
+            sc[ps] = group_sum_dpp<CH>(d);
+            bmax = fmaxf(bmax, sc[ps]);
+        }
+        const float mn = fmaxf(m_run, bmax);
+        const float corr = m_run == -INFINITY ? 0.0f : exp2f(m_run - mn);
+        l_run *= corr;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= corr;
+#pragma unroll
+        for (int ps = 0; ps < kBatchPasses; ++ps) {
+            const float pr = exp2f(sc[ps] - mn);
+            float vv[8];
+            cur[1][ps].get(vv);
+            l_run += pr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += pr * vv[e];
+        }
+        m_run = mn;
+    };
     for (int j = w; j < nbatch; j += kDecBuffers * kDecWaves) {
 #pragma unroll
         for (int u = 0; u < kDecBuffers; ++u) {
-            if (j + u * kDecWaves < nbatch) batch(j + u * kDecWaves, bufs[u]);
+            const int jj = j + u * kDecWaves;
+            if (jj < nbatch) {
+                if (jj != jnew && (jj + 1) * SB <= nvalid) batch_full(bufs[u]);
+                else batch(jj, bufs[u]);
+            }
             issue(j + (u + kDecBuffers) * kDecWaves, bufs[u]);
         }
     }
