@@ -241,11 +241,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const int jstart = (klo / KT) * KT;
     const int nt = (khi - jstart + KT - 1) / KT;
     // The query operands are complete before any tile load is issued (see the
-    // dQ pass for why).
+    // dQ pass for why). They are bf16(R q) unscaled, the operand the backward
+    // recomputes the scores from, so that its probabilities are the ones whose
+    // log-sum-exp this pass records; the softmax scale (times log2 e) is
+    // applied to the float32 scores inside the exponent's fma.
     bf16x8 qf[NF];
-    if (qi < T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, a.scale * kLog2e, qf);
+    if (qi < T) token_frags<DH>(a, a.q + act_row(a, b, qi, h) * DH, qi, g, true, 1.0f, qf);
     else zero_frags(qf, NF);
     wait_vmcnt<0>();
+    const float c2 = a.scale * kLog2e;   // scores -> log2 units
 
     auto issue = [&](int it) {
         bf16 *kt = lds + (it % ST) * 2 * TE;
@@ -294,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
                     if ((key > qi) | (key < qi - W + 1) | (key >= T)) sc[kb][e] = -INFINITY;
                 }
         }
+        // running maximum of the raw scores (c2 > 0 keeps the order)
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -302,13 +307,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         mx = fmaxf(mx, xor32(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        const float alpha = fast_exp2((m_run - m_use) * c2);
+        const float mc = m_use * c2;
         float rs = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float p = fast_exp2(sc[kb][e] - m_use);
+                const float p = fast_exp2(fmaf(sc[kb][e], c2, -mc));
                 sc[kb][e] = p;
                 rs += p;
             }
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
                 for (int u = 0; u < 4; ++u) v4[u] = f2bf(acc[db][4 * i4 + u] * inv);
                 *reinterpret_cast<bf16x4 *>(orow + 32 * db + 8 * i4 + 4 * g) = v4;
             }
-        if (g == 0 && lse) lse[(b * a.H + h) * a.T + qi] = (m_run + log2f(l_run)) * kLn2;
+        if (g == 0 && lse) lse[(b * a.H + h) * a.T + qi] = (m_run * c2 + log2f(l_run)) * kLn2;
     }
 }
 
