@@ -146,6 +146,20 @@ def _same(ref: torch.Tensor, *ts):
             raise MaglevError("mixed activation dtypes")
 
 
+def _decode_shapes(kcache, vcache, q, k, v, o, gate, gated):
+    """Shapes one decode step's kernel assumes: rings [Bs,H,W,Dh] alike,
+    q/k/v/o [Bs,H,Dh], gate logits [H] (sigma form) or [4,H*Dh] (gated)."""
+    if kcache.dim() != 4 or tuple(vcache.shape) != tuple(kcache.shape):
+        raise MaglevError("kcache and vcache must both be [Bs,H,W,Dh]")
+    Bs, H, _, Dh = kcache.shape
+    gate_numel = 4 * H * Dh if gated else H
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t is not None and tuple(t.shape) != (Bs, H, Dh):
+            raise MaglevError("%s must be [Bs,H,Dh] = %s" % (name, (Bs, H, Dh)))
+    if gate.numel() != gate_numel:
+        raise MaglevError("gate logits must have %d entries" % gate_numel)
+
+
 def make_geom(B, T, H, Dh, d, W, pos0=0, rope_base=10000.0, scale=0.0, dtype=MAGLEV_BF16) -> Geom:
     return Geom(B, T, H, Dh, d, W, pos0, rope_base, scale, dtype)
 
@@ -364,6 +378,9 @@ def maglev_decode_step(q, k, v, kmem, vmem, gate_logit, kcache, vcache, pos, o=N
     leave it so)."""
     _dev(q, k, v, gate_logit, kcache, vcache, pos, o, workspace)
     _same(q, k, v, kmem, vmem, kcache, vcache, o)
+    _decode_shapes(kcache, vcache, q, k, v, o, gate_logit, False)
+    if gate_logit.dtype != torch.float32:
+        raise MaglevError("gate_logit must be float32")
     Bs, H, W, Dh = kcache.shape
     if pos.dtype != torch.int64 or pos.numel() != Bs:
         raise MaglevError("pos must be int64 [Bs]")
@@ -477,10 +494,13 @@ def maglev_decode_step_gated(q, k, v, kproj, vmem, gates, kcache, vcache, pos, o
                              workspace=None, mem_stride: int = 0, stream=None):
     """One decode step of the gated form (kproj = W_Km m_{t-1} before the norm);
     kcache/vcache are updated in place. Returns o [Bs,H,Dh]."""
+    if kcache.dim() != 4:
+        raise MaglevError("kcache must be [Bs,H,W,Dh]")
     Bs, H, W, Dh = kcache.shape
     gates = gate_tensor(gates, H * Dh, q.device)
     _dev(q, k, v, gates, kcache, vcache, pos, o, workspace)
     _same(q, k, v, kproj, vmem, kcache, vcache, o)
+    _decode_shapes(kcache, vcache, q, k, v, o, gates, True)
     if pos.dtype != torch.int64 or pos.numel() != Bs:
         raise MaglevError("pos must be int64 [Bs]")
     stride = mem_stride or H * Dh

@@ -266,6 +266,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     };
 #pragma unroll
     for (int u = 0; u < kDecBuffers; ++u) issue(w + u * kDecWaves, bufs[u]);
+    // A stream with a negative position has no slot: it is skipped whole (ring
+    // and o untouched). p is the same on every thread of the workgroup, so the
+    // whole workgroup leaves before its first barrier.
+    if (p < 0) return;
 
     // 2. Rotation of position p (double precision: no table bounds p),
     //    rotated query, and the new entry (written by this workgroup only).

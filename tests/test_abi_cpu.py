@@ -325,3 +325,30 @@ def test_binding_fails_loudly_without_gpu_tensors():
     x = torch.zeros(2, 4, 64)
     with pytest.raises(rms.MaglevError):
         rms.maglev_mem_project(x, torch.zeros(64, 64), torch.zeros(64, 64), 1, 64)
+
+
+def test_decode_binding_checks_every_shape_the_kernel_assumes():
+    """The decode binding's shape checks (pure host logic, run before any
+    launch): rings alike, q/k/v/o [Bs,H,Dh], gate logits [H] or [4,H*Dh]."""
+    import torch
+
+    chk = rms._decode_shapes
+    Bs, H, W, Dh = 3, 2, 8, 64
+    ring = torch.zeros(Bs, H, W, Dh)
+    row = torch.zeros(Bs, H, Dh)
+    gate = torch.zeros(H)
+    chk(ring, ring, row, row, row, None, gate, False)                  # valid
+    chk(ring, ring, row, row, row, row, torch.zeros(4, H * Dh), True)  # valid, gated
+    bad = [
+        (ring, torch.zeros(Bs, H, W + 1, Dh), row, row, row, None, gate, False),
+        (torch.zeros(Bs, H, W), ring, row, row, row, None, gate, False),
+        (ring, ring, torch.zeros(Bs, H, Dh + 1), row, row, None, gate, False),
+        (ring, ring, row, torch.zeros(Bs + 1, H, Dh), row, None, gate, False),
+        (ring, ring, row, row, torch.zeros(Bs * H * Dh), None, gate, False),
+        (ring, ring, row, row, row, torch.zeros(Bs, H, 2 * Dh), gate, False),
+        (ring, ring, row, row, row, None, torch.zeros(H + 1), False),
+        (ring, ring, row, row, row, None, gate, True),
+    ]
+    for args in bad:
+        with pytest.raises(rms.MaglevError):
+            chk(*args)

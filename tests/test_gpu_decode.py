@@ -236,3 +236,26 @@ def test_graph_replay_matches_eager_steps():
         for l in range(L):
             assert torch.equal(eager.kcache[l], graphed.kcache[l])
         assert torch.equal(eager.pos, graphed.pos)
+
+
+def test_negative_position_stream_is_skipped():
+    """A stream whose position is negative writes nothing (ring and o keep
+    their contents); the other streams of the same call are unaffected."""
+    Bs, H, Dh, W = 3, 2, 128, 24
+    gen = torch.Generator().manual_seed(90)
+    rnd = lambda *s: torch.randn(*s, generator=gen).bfloat16()
+    q, k, v, km, vm = (rnd(Bs, H, Dh) for _ in range(5))
+    kc0, vc0 = rnd(Bs, H, W, Dh), rnd(Bs, H, W, Dh)
+    gate = torch.randn(H, generator=gen)
+    kc, vc = kc0.cuda(), vc0.cuda()
+    o = torch.full((Bs, H, Dh), 7.0, dtype=torch.bfloat16, device="cuda")
+    pos = torch.tensor([W + 5, -1, 3], dtype=torch.int64, device="cuda")
+    rms.maglev_decode_step(q.cuda(), k.cuda(), v.cuda(), km.cuda(), vm.cuda(), gate.cuda(), kc,
+                           vc, pos, o=o)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[1].cpu(), kc0[1]) and torch.equal(vc[1].cpu(), vc0[1])
+    assert torch.all(o[1].cpu() == 7.0)
+    okc, ovc = oracle.f64(kc0[[0, 2]]), oracle.f64(vc0[[0, 2]])
+    ro = oracle.decode_step(q[[0, 2]], k[[0, 2]], v[[0, 2]], km[[0, 2]], vm[[0, 2]], gate, okc,
+                            ovc, np.array([W + 5, 3]))
+    check("o of the other streams", o[[0, 2]], ro, 2e-2)
