@@ -18,7 +18,7 @@ import oracle
 import recurrent_memory_sliding_amd as rms
 import workloads as wl
 from recurrent_memory_sliding_amd.decode import DecodeStack
-from layer_util import check, flush, gpu, gpu_project, max_scale
+from layer_util import check, check_act, flush, gpu, gpu_project, max_scale
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -86,7 +86,7 @@ def check_forward_samples(sh, inp, g, km, vm, o, lse):
     worst = 0.0
     for b, h, i in sample_queries(sh):
         ro, rl, rkm, rvm, rkx, rvx, t0 = oracle_query_row(inp, sh, b, h, i)
-        worst = max(worst, check("o[%d,%d,%d]" % (b, i, h), o[b, i, h], ro, TOL))
+        worst = max(worst, check_act("o[%d,%d,%d]" % (b, i, h), o[b, i, h], ro, sh.dtype))
         check("lse", lse[b, h, i], rl, TOL)
         check("kmem rows", km[b, t0:i + 1, h], rkm, TOL)
         check("vmem rows", vm[b, t0:i + 1, h], rvm, TOL)
@@ -128,9 +128,9 @@ def backward_fullsize(sh, seed, keys):
     torch.cuda.synchronize()
     for b, h, j in keys:
         rdq, rdk, rdv = oracle_key_grads(inp, sh, b, h, j)
-        check("dq[%d,%d,%d]" % (b, j, h), gr["dq"][b, j, h], rdq, TOL)
-        check("dk[%d,%d,%d]" % (b, j, h), gr["dk"][b, j, h], rdk, TOL)
-        check("dv[%d,%d,%d]" % (b, j, h), gr["dv"][b, j, h], rdv, TOL)
+        check_act("dq[%d,%d,%d]" % (b, j, h), gr["dq"][b, j, h], rdq, sh.dtype)
+        check_act("dk[%d,%d,%d]" % (b, j, h), gr["dk"][b, j, h], rdk, sh.dtype)
+        check_act("dv[%d,%d,%d]" % (b, j, h), gr["dv"][b, j, h], rdv, sh.dtype)
     # identities of the projection backward, from the GPU's own dk, dv (float64, CPU)
     dk = gr["dk"].cpu().double()
     dv = gr["dv"].cpu().double()

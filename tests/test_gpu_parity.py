@@ -39,12 +39,12 @@ def run_fwd_case(sh, seed, grads=False, mutate=None):
     res = gpu_forward(inp, sh)
     torch.cuda.synchronize()
     ref = oracle_forward(inp, sh)
-    errs = check_forward(sh, inp, res, ref)
+    errs, op = check_forward(sh, inp, res, ref)
     if grads:
         g, km, vm, o, lse = res
         gr = gpu_backward(g, km, vm, o, lse, sh)
         torch.cuda.synchronize()
-        errs.update(check_backward(sh, inp, gr, oracle_backward(inp, sh), ref[0], ref[1]))
+        errs.update(check_backward(sh, inp, gr, oracle_backward(inp, sh), ref[0], ref[1], op))
     flush("  errors %s" % {k: "%.2e" % v for k, v in errs.items()})
     return inp, res, errs
 
