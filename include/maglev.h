@@ -181,6 +181,23 @@ maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int3
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* The consistency loss above for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving or training loops, harnesses
+ * that forbid allocation): the same kernels and the same result bits, with
+ * the partial sums in a device array of the library (2048 floats, 8 KB per
+ * GPU, held until the process ends) instead of a workspace. Arguments and
+ * accumulate bits as maglev_consistency_loss; nothing is allocated or freed.
+ * The scratch holds the partial sums of every (N, d) (the grid is capped at
+ * 2048 workgroups); a size whose partials would not fit returns
+ * MAGLEV_ERR_UNSUPPORTED. The array's address is looked up on the first call
+ * on a device (maglev_prepare does it ahead of capture). Every call on one
+ * GPU shares the array: calls that overlap in time on one GPU race, so
+ * serialise them (one stream, or events). */
+maglev_status_t maglev_consistency_loss_noalloc(int64_t N, int32_t d, float lambda, int32_t dtype,
+                                                const void *m, const void *m_prime, float *loss,
+                                                float *dm, float *dm_prime, unsigned accumulate,
+                                                hipStream_t stream);
+
 /* Bytes of device workspace maglev_decode_step needs (0 on invalid sizes). */
 size_t maglev_decode_workspace(int32_t Bs, int32_t H, int32_t Dh, int32_t W);
 
@@ -405,8 +422,9 @@ maglev_status_t maglev_lm_head(int64_t N, int32_t d, int64_t V, float cap, float
  * slot; kept separate so one decode step can be captured and replayed). */
 maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stream);
 
-/* Ensure the RoPE table for (Dh, rope_base) covers positions [0, max_pos) on
- * the current device. Synchronous; call before HIP-graph capture. */
+/* Set-up of the current device: ensure the RoPE table for (Dh, rope_base)
+ * covers positions [0, max_pos), and look up the device scratch of
+ * maglev_consistency_loss_noalloc. Synchronous; call before HIP-graph capture. */
 maglev_status_t maglev_prepare(int32_t Dh, float rope_base, int64_t max_pos);
 
 /* Human-readable name of a status code (static storage). */

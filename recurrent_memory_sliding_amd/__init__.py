@@ -23,6 +23,7 @@ __all__ = [
     "MaglevError", "MAGLEV_F32", "MAGLEV_BF16", "lib", "library_path",
     "maglev_mem_project", "maglev_swa_inject_fwd", "maglev_swa_inject_bwd",
     "maglev_swa_inject_bwd_workspace", "maglev_consistency_loss",
+    "maglev_consistency_loss_noalloc",
     "maglev_consistency_loss_workspace", "maglev_decode_step", "maglev_decode_workspace",
     "maglev_decode_advance", "maglev_prepare", "maglev_abi_version", "maglev_profile_enable",
     "maglev_profile_read", "maglev_lm_head", "maglev_lm_head_workspace", "LM_CAP",
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
             "maglev_swa_inject_bwd": ([G] + [vp] * 19 + [u32, vp, sz, vp], i32),
             "maglev_consistency_loss_workspace": ([i64, i32], sz),
             "maglev_consistency_loss": ([i64, i32, f32, i32, vp, vp, vp, vp, vp, u32, vp, sz, vp], i32),
+            "maglev_consistency_loss_noalloc": ([i64, i32, f32, i32, vp, vp, vp, vp, vp, u32, vp],
+                                                i32),
             "maglev_decode_workspace": ([i32, i32, i32, i32], sz),
             "maglev_decode_step": ([i32, i32, i32, i32, f32, f32, i32] + [vp] * 5 + [i64]
                                    + [vp] * 5 + [vp, sz, vp], i32),
@@ -319,6 +322,27 @@ def maglev_consistency_loss(m, m_prime, lam: float, loss=None, dm=None, dm_prime
                                          _ptr(workspace),
                                          workspace.numel() * workspace.element_size(),
                                          _stream(stream)), "maglev_consistency_loss")
+    return loss, dm, dm_prime
+
+
+def maglev_consistency_loss_noalloc(m, m_prime, lam: float, loss, dm=None, dm_prime=None,
+                                    accumulate: int = 0, stream=None):
+    """The consistency loss with the library's device scratch instead of a
+    workspace: the caller passes every output (loss [1] float32; dm,
+    dm_prime [..., d] float32 or None) and nothing is allocated."""
+    _dev(m, m_prime, loss, dm, dm_prime)
+    _same(m, m_prime)
+    d = m.shape[-1]
+    N = m.numel() // d
+    for t in (dm, dm_prime):
+        if t is not None and (t.dtype != torch.float32 or t.shape != m.shape):
+            raise MaglevError("dm / dm_prime must be float32 with m's shape")
+    if loss.dtype != torch.float32 or loss.numel() < 1:
+        raise MaglevError("loss must be a float32 tensor of at least one element")
+    _check(lib().maglev_consistency_loss_noalloc(N, d, lam, _dtype_code(m), _ptr(m),
+                                                 _ptr(m_prime), _ptr(loss), _ptr(dm),
+                                                 _ptr(dm_prime), accumulate, _stream(stream)),
+           "maglev_consistency_loss_noalloc")
     return loss, dm, dm_prime
 
 

@@ -122,6 +122,11 @@ size_t loss_workspace_bytes(int64_t N, int d);
 hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
                        const void *mp, float *loss, float *dm, float *dmp, unsigned accumulate,
                        void *ws, hipStream_t s);
+// The allocation-free variant's partial sums: a device array of
+// loss_scratch_bytes() bytes per GPU; its address on the current device
+// (looked up on the first call per device).
+size_t loss_scratch_bytes();
+hipError_t loss_scratch_address(float **addr);
 
 // ---- loss head -----------------------------------------------------------
 struct HeadWorkspace {

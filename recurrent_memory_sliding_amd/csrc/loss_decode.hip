@@ -8,6 +8,8 @@
 // m_t = P(x_{t-W+1:t}, M_{t-1})) and section 前置知识 (KV cache; the memory rides
 // in the existing entries); gist.science summary ("Technische Samenvatting:
 // Maglev - Sliding Recurrent Memory"), section Inferentiemechanisme.
+#include <mutex>
+
 #include "common.hpp"
 #include "internal.hpp"
 #include "profile.hpp"
@@ -114,6 +116,45 @@ hipError_t launch_loss(int64_t N, int d, float lambda, int dtype, const void *m,
     prof::Scope ts("loss_final", s);
     hipLaunchKernelGGL(loss_final, dim3(1), dim3(1024), 0, s, partial, nb, c, loss, acc);
     return hipGetLastError();
+}
+
+// ============================================================================
+// Allocation-free consistency loss: the partial sums in a device array
+// ============================================================================
+// The partial sums of the allocation-free entry point (kLossMaxBlocks floats,
+// 8 KB: the grid never has more workgroups, whatever N and d) live in this
+// file-scope array, one copy per GPU for the life of the process. In host
+// code the name `scratch` is a host-side stand-in, not the device address:
+// the address is looked up once per device, with that device current, and
+// only that address is handed to kernels. Every call on one GPU shares the
+// array, so calls that overlap in time on one GPU race; each call writes
+// every partial it reads, so nothing needs clearing between calls.
+static __device__ __align__(256) float scratch[kLossMaxBlocks];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_addr[kScratchDevices] = {};   // per device: the address of `scratch` there
+}  // namespace
+
+size_t loss_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t loss_scratch_address(float **addr)
+{
+    *addr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = static_cast<float *>(p);
+    }
+    *addr = g_scratch_addr[dev];
+    return hipSuccess;
 }
 
 // ============================================================================

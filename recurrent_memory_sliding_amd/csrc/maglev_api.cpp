@@ -188,6 +188,11 @@ maglev_status_t maglev_prepare(int32_t Dh, float rope_base, int64_t max_pos)
 {
     if (Dh != 64 && Dh != 128) return fail(MAGLEV_ERR_UNSUPPORTED, "Dh must be 64 or 128");
     if (max_pos < 0) return fail(MAGLEV_ERR_INVALID_VALUE, "max_pos must be >= 0");
+    // set-up of the current device: the address of the allocation-free
+    // loss's scratch array, then the RoPE table
+    float *scr = nullptr;
+    maglev_status_t st = hip_status(loss_scratch_address(&scr));
+    if (st != MAGLEV_OK) return st;
     const float2 *t = nullptr;
     return rope_table(Dh, rope_base, max_pos, &t);
 }
@@ -285,11 +290,10 @@ size_t maglev_consistency_loss_workspace(int64_t N, int32_t d)
     return loss_workspace_bytes(N, d);
 }
 
-maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int32_t dtype,
-                                        const void *m, const void *m_prime, float *loss,
-                                        float *dm, float *dm_prime, unsigned accumulate,
-                                        void *workspace, size_t workspace_bytes,
-                                        hipStream_t stream)
+static maglev_status_t check_loss_args(int64_t N, int32_t d, float lambda, int32_t dtype,
+                                       const void *m, const void *m_prime, const float *loss,
+                                       const float *dm, const float *dm_prime,
+                                       unsigned accumulate)
 {
     if (N < 0) return fail(MAGLEV_ERR_INVALID_VALUE, "N must be >= 0");
     if (d < 8 || (d % 8) != 0) return fail(MAGLEV_ERR_INVALID_VALUE, "d must be a positive multiple of 8");
@@ -304,12 +308,42 @@ maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int3
     if ((dm && !aligned16(dm)) || (dm_prime && !aligned16(dm_prime)))
         return fail(MAGLEV_ERR_MISALIGNED, "dm / dm_prime not 16-byte aligned");
     if (accumulate & ~7u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    return MAGLEV_OK;
+}
+
+maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int32_t dtype,
+                                        const void *m, const void *m_prime, float *loss,
+                                        float *dm, float *dm_prime, unsigned accumulate,
+                                        void *workspace, size_t workspace_bytes,
+                                        hipStream_t stream)
+{
+    maglev_status_t st =
+        check_loss_args(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate);
+    if (st != MAGLEV_OK) return st;
     const size_t need = loss_workspace_bytes(N, d);
     if (!workspace || workspace_bytes < need)
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (!aligned16(workspace)) return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     return hip_status(launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
                                   workspace, stream));
+}
+
+maglev_status_t maglev_consistency_loss_noalloc(int64_t N, int32_t d, float lambda,
+                                                int32_t dtype, const void *m,
+                                                const void *m_prime, float *loss, float *dm,
+                                                float *dm_prime, unsigned accumulate,
+                                                hipStream_t stream)
+{
+    maglev_status_t st =
+        check_loss_args(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate);
+    if (st != MAGLEV_OK) return st;
+    if (loss_workspace_bytes(N, d) > loss_scratch_bytes())
+        return fail(MAGLEV_ERR_UNSUPPORTED, "the partial sums exceed the library's device scratch");
+    float *scr = nullptr;
+    st = hip_status(loss_scratch_address(&scr));
+    if (st != MAGLEV_OK) return st;
+    return hip_status(launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
+                                  scr, stream));
 }
 
 static bool head_sizes_ok(int64_t N, int32_t d, int64_t V)

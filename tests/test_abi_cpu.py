@@ -316,8 +316,11 @@ def test_loss_head_workspace_and_validation(L):
 def test_prepare_validation(L):
     assert L.maglev_prepare(100, 1e4, 10) == UNSUPPORTED
     assert L.maglev_prepare(128, 1e4, -1) == INVALID
-    # rope_base <= 0 disables the rotation: nothing to allocate
-    assert L.maglev_prepare(128, 0.0, 1000) == OK
+    # rope_base <= 0 disables the rotation: nothing to allocate; the set-up
+    # still looks up the allocation-free loss's scratch on the current
+    # device, which a host without a GPU does not have
+    import torch
+    assert L.maglev_prepare(128, 0.0, 1000) == (OK if torch.cuda.device_count() > 0 else HIP)
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
@@ -352,3 +355,29 @@ def test_decode_binding_checks_every_shape_the_kernel_assumes():
     for args in bad:
         with pytest.raises(rms.MaglevError):
             chk(*args)
+
+
+def test_no_alloc_loss_validation(L):
+    """The allocation-free loss rejects what the workspace call rejects,
+    before any device work (the scratch address is only looked up after)."""
+    f = L.maglev_consistency_loss_noalloc
+    f.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int32] + \
+        [ctypes.c_void_p] * 5 + [ctypes.c_uint, ctypes.c_void_p]
+    f.restype = ctypes.c_int32
+    ok = dict(N=4, d=64, lam=0.1, dtype=1, m=FAKE, mp=FAKE, loss=FAKE, dm=None, dmp=None, acc=0)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["N"], a["d"], a["lam"], a["dtype"], a["m"], a["mp"], a["loss"], a["dm"],
+                 a["dmp"], a["acc"], None)
+
+    assert call(N=-1) == INVALID
+    assert call(d=12) == INVALID
+    assert call(lam=float("nan")) == INVALID
+    assert call(dtype=7) == INVALID
+    assert call(m=None) == INVALID
+    assert call(loss=None) == INVALID
+    assert call(mp=FAKE_ODD) == MISALIGNED
+    assert call(dm=FAKE_ODD) == MISALIGNED
+    assert call(acc=8) == INVALID
