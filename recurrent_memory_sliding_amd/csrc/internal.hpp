@@ -53,6 +53,14 @@ struct BwdWorkspace {
     int64_t Tp;          // T rounded up to a multiple of 32
     int ksplit;
     int n_key_tiles;
+    // bf16 path, Dh = 128: dS = P (dP - D) of every in-band 32 x 32 tile as the
+    // dK/dV pass rounded it for its dK product, [B*H][nt32][ds_tiles][32 k][32 q],
+    // tile (kt, j) covering keys 32 kt.. and queries 32 (kt + j)..; the dQ pass
+    // reads it instead of recomputing the scores (null: dQ recomputes).
+    void *ds;
+    int nt32;            // ceil(T / 32)
+    int ds_tiles;        // query tiles stored per key tile
+
     // gated form only
     void *dkp;           // [B,T,H*Dh] dtype: d loss / d (W_Km m'), before the norm
     void *dvm;           // [B,T,H*Dh] dtype: d loss / d (W_Vm m')

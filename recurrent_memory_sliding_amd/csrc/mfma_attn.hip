@@ -52,6 +52,15 @@ MAGLEV_DEV int64_t act_row(const AttnArgs &a, int64_t b, int64_t t, int h)
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;
 
+// Third dword of a raw buffer descriptor for untyped buffer instructions on
+// gfx9-family chips: a valid 32-bit data format, no swizzle, no index
+// stride (offsets at or beyond num_records are dropped stores).
+constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of a buffer access: nontemporal (streamed past the caches the
+// re-read tiles live in).
+constexpr int kNontemporal = 2;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
 // Source of tile rows outside the sequence.
 __device__ __attribute__((aligned(256))) bf16 g_attn_zero[128] = {};
 
@@ -674,7 +683,8 @@ template <int ST, bool ROTATE>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, const bf16 *dO,
                                                                      const float *lse2,
                                                                      const float *Dp, int64_t Tp,
-                                                                     bf16 *dk, bf16 *dv)
+                                                                     bf16 *dk, bf16 *dv, bf16 *dso,
+                                                                     int nK, int nt32)
 {
     static_assert(ST >= 3, "the next tile is published one tile ahead");
     constexpr int DH = 128, NF = DH / 16, NPAIR = 2, KB = 32 * NPAIR;
@@ -738,8 +748,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     // The statistic of this lane's 16 queries of tile it that the wave's role
     // needs: lse2 (first wave, for P) or D (second wave, which sends dP - D).
     // Rows are padded to Tp, so a tile never leaves its row. Two register
-    // sets, one per tile parity, so that no copy (and no wait for the loads
-    // behind them) is needed.
+    // sets, one per tile parity, so that no copy is needed. (The compiler
+    // cannot count the tile loads, which are inline assembly, so its wait
+    // for these loads also covers the tile loads issued after them; staging
+    // the statistics in LDS instead would need more LDS than two workgroups
+    // a CU leave.)
     struct Stats {
         f32x4 v[4];
     };
@@ -766,6 +779,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
 #pragma unroll
         for (int e = 0; e < 16; ++e) dva[lb][e] = dka[lb][e] = 0.0f;
 
+    // this lane's byte offset in a stored dS tile: key row l32, queries 4 g..
+    const int ds_voff = l32 * 64 + 8 * g;
     auto tile_step = [&](int it, const Stats &cur, Stats &next) {
         const int i0 = j0 + it * QT;
         const int buf = it % ST;
@@ -816,8 +831,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // barrier publishes it
         wait_vmcnt<0>();
         __syncthreads();
-        if (it + 1 < nt) load_stats(it + 1, next);
-        if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
 
         // the transposed operands of this tile's eight products, read before
         // the exchange so that their latency overlaps the dS arithmetic
@@ -840,16 +853,47 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
                 dS[e] = P[e] * (hf ? mine[e] : o[u]);   // P (dP - D)
             }
         }
+        bf16x8 pf[2], dsf[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const bf16x8 pf = acc_to_operand(P, t);
-            const bf16x8 dsf = acc_to_operand(dS, t);
-#pragma unroll
-            for (int lb = 0; lb < 2; ++lb) {
-                dva[lb] = mfma32(trv[t][lb], pf, dva[lb]);
-                dka[lb] = mfma32(trq[t][lb], dsf, dka[lb]);
+            pf[t] = acc_to_operand(P, t);
+            dsf[t] = acc_to_operand(dS, t);
+        }
+        // dS of this 32 x 32 tile as the dK product takes it (the bf16 operand
+        // registers themselves), for the dQ pass: [key][query] tiles of
+        // 64-byte rows. Lane l32 holds key kw0 + l32; operand t holds queries
+        // i0 + 16t + 4g + (0..3) and i0 + 16t + 8 + 4g + (0..3), bytes
+        // 32t + 8g and 32t + 16 + 8g of the row: four 8-byte buffer stores
+        // from the pair's first wave, through a per-tile descriptor (uniform
+        // registers) and one 32-bit lane offset, so that they take no
+        // registers the loop needs. Tiles outside the stored range (a query
+        // tile before the keys, or beyond the window) are not stored. The
+        // stores go out before this step's statistics and tile loads: the
+        // vector memory counter counts stores too, and the next step's waits
+        // for those loads would otherwise wait for the younger stores.
+        if (dso && hf == 0) {
+            const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
+            if (jj >= 0 && jj < nK) {
+                bf16 *tile = dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024;
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
+                const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
+                const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
             }
         }
+        if (it + 1 < nt) load_stats(it + 1, next);
+        if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int lb = 0; lb < 2; ++lb) {
+                dva[lb] = mfma32(trv[t][lb], pf[t], dva[lb]);
+                dka[lb] = mfma32(trq[t][lb], dsf[t], dka[lb]);
+            }
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 20, 1);
         __builtin_amdgcn_sched_group_barrier(kSchedValu, 64, 1);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
@@ -1012,6 +1056,134 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
     }
 }
 
+// Transposed operand in natural key order: reduction rows 16 tt + 8 g + {0..7}
+// (g = lane / 32), column 32 db + (lane % 32) -- the layout of an operand
+// whose 8 K entries are consecutive rows of the tile.
+MAGLEV_DEV bf16x8 tile_tr_nat(const bf16 *t, int tt, int db, int lane)
+{
+    constexpr int DH = 128;
+    const int g = lane >> 5, j = lane & 15;
+    const int n = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    const int c = n >> 3, e = n & 7;
+    const int ra = 16 * tt + 8 * g + (j >> 2);
+    const i16x4 lo = lds_read_tr16(t + tile_off<DH>(ra, c) + e);
+    const i16x4 hi = lds_read_tr16(t + tile_off<DH>(ra + 4, c) + e);
+    return join_tr(lo, hi);
+}
+
+// Query-stationary dQ pass from the stored dS tiles (Dh = 128): each wave
+// owns 32 queries (one query tile), the workgroup 128; the K~ tiles of the
+// workgroup's band and each wave's own dS tile of the same 32 keys stream
+// through LDS in ST stages. Per tile: dQ^^T += K~^T dS^T (8 products), no
+// scores, no softmax. Epilogue as the recomputing pass: dq = scale R^T dQ^.
+// A dS tile sits in LDS as stored, 32 key rows of 64 bytes; its operand
+// (query column, 8 consecutive keys) comes from transposed reads, whose
+// half-wave passes cover four whole rows, 256 contiguous bytes: every bank
+// once.
+template <int ST>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, const bf16 *ds, int nK,
+                                                                 int nt32, bf16 *dq)
+{
+    constexpr int DH = 128, NB = DH / 32, KT = 32;
+    constexpr int TE = KT * DH;            // K~ tile
+    constexpr int DSE = 32 * 32;           // one wave's dS tile
+    constexpr int SE = TE + 4 * DSE;       // one stage
+    using Dma = TileDma<DH, KT, 4>;
+    constexpr int PER = Dma::PER_WAVE + 2;  // vector memory ops a wave issues per stage
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * SE];
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = (int)a.T, W = a.W;
+    const int nqt = (T + 127) / 128;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt = bid % nqt, bh = bid / nqt;
+    const int h = bh % a.H;
+    const int64_t b = bh / a.H;
+    const int i0 = qt * 128, qw0 = i0 + 32 * w, qi = qw0 + l32;
+    const int wqt = qw0 >> 5;                                          // this wave's query tile
+    const int wkt_lo = (qw0 - W + 1 > 0 ? qw0 - W + 1 : 0) >> 5;     // its first key tile
+    const bool active = qw0 < T;
+    const int tok_stride = a.H * DH;
+    const bf16 *kbase = a.kx + act_row(a, b, 0, h) * DH;
+    const bf16 *dsbase = ds + (int64_t)bh * nt32 * nK * DSE;
+
+    const int klo = i0 - W + 1 > 0 ? i0 - W + 1 : 0;
+    const int khi = i0 + 128 < T ? i0 + 128 : T;
+    const int jstart = (klo / KT) * KT;
+    const int nt = (khi - jstart + KT - 1) / KT;
+
+    // K~ tile of the workgroup (two instructions a wave) and this wave's dS
+    // tile of the same keys (two more: 16 rows of 64 bytes each), read from
+    // the zero page where the wave has no such tile.
+    auto issue = [&](int it) {
+        bf16 *st = lds + (it % ST) * SE;
+        const int j0 = jstart + it * KT;
+#pragma unroll
+        for (int i = 0; i < Dma::PER_WAVE; ++i) {
+            const int ins = w * Dma::PER_WAVE + i;
+            const int r = Dma::row(ins, lane);
+            const int c = Dma::chunk(r, lane);
+            const int j = j0 + r;
+            dma16(j < T ? kbase + (int64_t)j * tok_stride + c * 8 : g_attn_zero, st + ins * 512);
+        }
+        const int kt = j0 >> 5;
+        const bool have = active && kt >= wkt_lo && kt <= wqt;
+        const bf16 *src = dsbase + ((int64_t)kt * nK + (wqt - kt)) * DSE;
+        bf16 *dst = st + TE + w * DSE;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) dma16(have ? src + i * 512 + lane * 8 : g_attn_zero, dst + i * 512);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0)
+        if (s0 < nt) issue(s0);
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int db = 0; db < NB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+
+    for (int it = 0; it < nt; ++it) {
+        pipeline_wait<ST, PER>(it, nt);
+        if (it + ST - 1 < nt) issue(it + ST - 1);
+        const int kt = (jstart >> 5) + it;
+        if (!active || kt < wkt_lo || kt > wqt) continue;
+        const bf16 *kt_lds = lds + (it % ST) * SE;
+        const bf16 *ds_lds = kt_lds + TE + w * DSE;
+        bf16x8 ktr[NB][2], dsf[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            // keys 16t + 8g + (0..3) and (4..7) of query column l32
+            const int j = lane & 15;
+            const bf16 *p = ds_lds + (16 * t + 8 * g + (j >> 2)) * 32 + 16 * ((lane >> 4) & 1) +
+                            4 * (j & 3);
+            dsf[t] = join_tr(lds_read_tr16(p), lds_read_tr16(p + 4 * 32));
+#pragma unroll
+            for (int db = 0; db < NB; ++db) ktr[db][t] = tile_tr_nat(kt_lds, t, db, lane);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < NB; ++db) acc[db] = mfma32(ktr[db][t], dsf[t], acc[db]);
+    }
+
+    if (qi < T) {
+        const int64_t base = act_row(a, b, qi, h) * DH;
+        const float2 *cs = a.rope ? a.rope + (a.pos0 + qi) * (DH / 2) : nullptr;
+        scale_rotate_back<NB>(acc, cs, g, a.scale);
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                bf16x4 v4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v4[u] = f2bf(acc[db][4 * i4 + u]);
+                *reinterpret_cast<bf16x4 *>(dq + base + 32 * db + 8 * i4 + 4 * g) = v4;
+            }
+    }
+}
+
 // ============================================================================
 // Launchers
 // ============================================================================
@@ -1031,7 +1203,8 @@ static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const vo
 // Tile shapes and pipeline depths: forward and dQ stream K~/V~ tiles of
 // kFwdKT keys through kFwdST stages; dK/dV streams 32-query tiles through
 // kBwdST stages (kPairST in the wave-pair pass used for Dh = 128).
-constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4, kPairST = 3;
+constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4, kPairST = 3,
+              kDqDsST = 3;
 
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)
@@ -1064,14 +1237,17 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
         if constexpr (DH == 128) {
             // one workgroup per 64 keys of a (sequence, head)
             const unsigned npw = (unsigned)(a.B * a.H * ((a.T + 63) / 64));
+            bf16 *dso = static_cast<bf16 *>(ws.ds);
             if (entries)
                 hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, false>), dim3(npw),
                                    dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
-                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
+                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), dso,
+                                   ws.ds_tiles, ws.nt32);
             else
                 hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, true>), dim3(npw),
                                    dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
-                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
+                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), dso,
+                                   ws.ds_tiles, ws.nt32);
         } else if (entries) {
             hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256), 0,
                                s, a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
@@ -1083,8 +1259,13 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
         }
     }
     prof::Scope ts("attn_bwd_dq", s);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a, dO,
-                       ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dq));
+    if (DH == 128 && ws.ds)
+        hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<kDqDsST>), dim3(nwg), dim3(256), 0, s, a,
+                           static_cast<const bf16 *>(ws.ds), ws.ds_tiles, ws.nt32,
+                           static_cast<bf16 *>(dq));
+    else
+        hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a,
+                           dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dq));
 }
 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,

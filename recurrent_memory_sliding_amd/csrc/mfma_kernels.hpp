@@ -46,6 +46,10 @@ void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *
 void launch_lm_du_bf16(int64_t N, int64_t V, int d, const void *dz, const void *m, float *du,
                        bool acc, hipStream_t s);
 
+// Widest window (in 32-query tiles per 32-key tile) whose dS tiles the dK/dV
+// pass stores for the dQ pass (Dh = 128); wider windows recompute the scores.
+constexpr int kMaxDsTiles = 80;
+
 // Split-K factor the dW GEMM uses for this geometry (workspace sizing).
 int dw_ksplit(const Geom &g);
 

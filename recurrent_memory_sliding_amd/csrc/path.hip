@@ -374,6 +374,13 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     const size_t oQ = take(nq * esz);
     const size_t oL = take(npad * sizeof(float));
     const size_t oDp = take(npad * sizeof(float));
+    // bf16 path, Dh = 128: the dS tiles the dQ pass reads (windows up to
+    // kMaxDsTiles query tiles a key tile; wider ones make the dQ pass
+    // recompute the scores instead)
+    L->nt32 = (int)((g.T + 31) / 32);
+    L->ds_tiles = (g.W + 30) / 32 + 1 < L->nt32 ? (g.W + 30) / 32 + 1 : L->nt32;
+    const bool ds = bf && attn && g.Dh == 128 && L->ds_tiles <= mfma::kMaxDsTiles;
+    const size_t oDS = take(ds ? (size_t)g.B * g.H * L->nt32 * L->ds_tiles * 1024 * esz : 0);
     // projection backward (bf16): scaled weight copy, split-K partials, row dots
     const size_t oW = take(bf && proj ? 2 * HD * g.d * esz : 0);
     const size_t oP = take((size_t)L->ksplit * 2 * HD * g.d * sizeof(float));
@@ -387,6 +394,7 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     L->D = reinterpret_cast<float *>(at(oD, !bf && attn));
     L->ds_part = reinterpret_cast<float *>(at(oS, (!bf && kind == BwdKind::Sigma) || shared));
     L->q_rot = at(oQ, nq > 0);
+    L->ds = at(oDS, ds);
     L->lse2 = reinterpret_cast<float *>(at(oL, npad > 0));
     L->Dp = reinterpret_cast<float *>(at(oDp, npad > 0));
     L->W_scaled = at(oW, bf && proj);

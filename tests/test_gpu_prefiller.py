@@ -108,3 +108,9 @@ def test_d20_full_attention_layer_fullsize_sampled():
     for n, (b, h, i) in enumerate(rows):
         check_act("o(%d,%d,%d)" % (b, h, i), o[b, i, h], ro[n], sh.dtype)
         check("lse(%d,%d,%d)" % (b, h, i), lse[b, h, i:i + 1], rlse[n:n + 1], tol)
+
+
+def test_full_attention_beyond_stored_score_tiles_dh128():
+    """T = W = 2600 (82 query tiles a key tile, above the 80 whose dS the
+    dK/dV pass stores): the dQ pass recomputes the scores instead."""
+    run_case(shape(B=1, T=2600, W=2600, H=1, Dh=128, d=128), 88)
