@@ -86,6 +86,9 @@ def kernel_work(sh: wl.LayerShape, mix: str = "sigma") -> dict:
     f32nd = 4.0 * N * d
     gblocks = max(1, -(-N // max(8, -(-N // 512))))
     gpart = 4.0 * gblocks * 4 * HD                         # fp32 gate partials
+    # dQ from the dS tiles the dK/dV pass stores (Dh = 128): the band of dS
+    # (bf16), K~ and dq; else the recomputing pass (q^, dO, K~, V~ -> dq)
+    dq_bytes = (2 * act + 2.0 * pairs * B * H) if Dh == 128 else (5 * act + 2 * rowf)
     if mix == "gated":
         return {
             "proj_fwd": (proj, mem + wts + 2 * act),
@@ -93,7 +96,7 @@ def kernel_work(sh: wl.LayerShape, mix: str = "sigma") -> dict:
             "attn_fwd": (2 * attn, 4 * act + rowf),
             "attn_bwd_prep": (0.0, 4 * act + 3 * rowf),
             "attn_bwd_dkdv": (3 * attn, 6 * act + 2 * rowf),   # q^ dO kmix vmix -> dk~ dv~
-            "attn_bwd_dq": (attn, 5 * act + 2 * rowf),
+            "attn_bwd_dq": (attn, dq_bytes),
             "gated_mix_bwd": (0.0, 10 * act + gpart),          # dk~ dv~ k v kp vm -> dk dv dkp dvm
             "gate_grad_reduce": (0.0, gpart + 2 * 4.0 * 4 * HD),
             "proj_bwd_scale_w": (0.0, 2 * wts),
@@ -108,7 +111,7 @@ def kernel_work(sh: wl.LayerShape, mix: str = "sigma") -> dict:
         "attn_fwd": (2 * attn, 4 * act + rowf),                 # q kmix vmix -> o, lse
         "attn_bwd_prep": (0.0, 4 * act + 3 * rowf),             # o dO q lse -> D, qr, lse2
         "attn_bwd_dkdv": (3 * attn, 6 * act + 2 * rowf),       # q^ dO kmix vmix -> dk dv
-        "attn_bwd_dq": (attn, 5 * act + 2 * rowf),              # q dO kmix vmix -> dq
+        "attn_bwd_dq": (attn, dq_bytes),
         "proj_bwd_scale_w": (0.0, 2 * wts),
         "proj_bwd_dm": (proj, 2 * act + wts + f32nd),           # dk dv Ws -> dm'
         "proj_bwd_dw": (proj, 2 * act + mem),                   # partials counted separately
