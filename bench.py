@@ -371,7 +371,10 @@ def bench_stack(sh, layers, steps, warmup):
       shared: one memory projection of m' shared by all layers (per-layer
         mix and gates), its backward once from the summed memory gradients;
       per_layer: every layer with its own m' and projection weights (its own
-        projection forward and backward).
+        projection forward and backward);
+      gated_shared: the gated mix (channel-wise 2 sigmoid gates, RMSNorm on
+        the recurrent key) over one shared projection, its backward once from
+        the summed gradients of the pre-norm projections.
     Inputs are drawn on the device from a seeded generator (no parity is
     checked here). Timed with HIP events around whole passes."""
     dev, bf, f32 = "cuda", torch.bfloat16, torch.float32
@@ -389,7 +392,9 @@ def bench_stack(sh, layers, steps, warmup):
           "vx": torch.empty(act, dtype=bf, device=dev), "km": torch.empty(act, dtype=bf, device=dev),
           "vm": torch.empty(act, dtype=bf, device=dev), "o": torch.empty(act, dtype=bf, device=dev),
           "lse": torch.empty((B, H, T), dtype=f32, device=dev),
-          "dgate": torch.empty((H,), dtype=f32, device=dev)} for _ in range(layers)]
+          "dgate": torch.empty((H,), dtype=f32, device=dev),
+          "gates": rnd(4, HD, std=0.7, dt=f32),
+          "dgates": torch.empty((4, HD), dtype=f32, device=dev)} for _ in range(layers)]
     m = rnd(B, T, d)
     km, vm = (torch.empty(act, dtype=bf, device=dev) for _ in range(2))
     dkm, dvm = (torch.empty(act, dtype=f32, device=dev) for _ in range(2))
@@ -399,6 +404,8 @@ def bench_stack(sh, layers, steps, warmup):
     dWk, dWv = (torch.empty((HD, d), dtype=f32, device=dev) for _ in range(2))
     loss = torch.empty((1,), dtype=f32, device=dev)
     ws_sh = torch.empty((rms.maglev_swa_inject_bwd_shared_workspace(B, T, H, Dh, W),),
+                        dtype=torch.uint8, device=dev)
+    ws_sg = torch.empty((rms.maglev_swa_inject_bwd_shared_gated_workspace(B, T, H, Dh, W),),
                         dtype=torch.uint8, device=dev)
     ws_pb = torch.empty((rms.maglev_mem_project_bwd_workspace(B, T, H, Dh, d),), dtype=torch.uint8,
                         device=dev)
@@ -424,6 +431,22 @@ def bench_stack(sh, layers, steps, warmup):
         rms.maglev_consistency_loss(m, mp, sh.lam, loss=loss, dm=dm, dm_prime=dmp, accumulate=2,
                                     workspace=ws_ls)
 
+    def gated_shared_pass():
+        rms.maglev_mem_project(mp, WK, WV, H, Dh, shift=1, kmem=km, vmem=vm)
+        for x in L:
+            rms.maglev_mix_entries_gated(x["k"], x["v"], km, vm, x["gates"], kmix=x["kx"],
+                                         vmix=x["vx"])
+            rms.maglev_swa_inject_fwd(x["q"], x["kx"], x["vx"], W, o=x["o"], lse=x["lse"])
+        for i, x in enumerate(reversed(L)):
+            rms.maglev_swa_inject_bwd_shared_gated(x["q"], x["kx"], x["vx"], x["k"], x["v"], km, vm,
+                                                   x["gates"], x["o"], x["lse"], x["dO"], dkm, dvm,
+                                                   W, accumulate=1 if i else 0, dq=dq, dk=dk,
+                                                   dv=dv, dgates=x["dgates"], workspace=ws_sg)
+        rms.maglev_mem_project_bwd(dkm, dvm, mp, WK, WV, dm_prime=dmp, dW_Km=dWk, dW_Vm=dWv,
+                                   workspace=ws_pb)
+        rms.maglev_consistency_loss(m, mp, sh.lam, loss=loss, dm=dm, dm_prime=dmp, accumulate=2,
+                                    workspace=ws_ls)
+
     def per_layer_pass():
         for x in L:
             rms.maglev_mem_project(x["mp"], x["WK"], x["WV"], H, Dh, shift=1, kmem=x["km"],
@@ -444,7 +467,9 @@ def bench_stack(sh, layers, steps, warmup):
     proj = 2.0 * B * T * d * 2 * HD
     out = {}
     for name, fn, flops in (("shared_projection", shared_pass, layers * 6 * attn + 3 * proj),
-                            ("projection_per_layer", per_layer_pass, layers * (6 * attn + 3 * proj))):
+                            ("projection_per_layer", per_layer_pass, layers * (6 * attn + 3 * proj)),
+                            ("gated_shared_projection", gated_shared_pass,
+                             layers * 6 * attn + 3 * proj)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()

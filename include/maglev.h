@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define MAGLEV_ABI_VERSION 5
+#define MAGLEV_ABI_VERSION 6
 
 typedef enum {
     MAGLEV_OK = 0,
@@ -338,6 +338,46 @@ maglev_status_t maglev_swa_inject_bwd_shared(const maglev_geom_t *g, const void 
                                              float *dgate, unsigned accumulate, void *workspace,
                                              size_t workspace_bytes, hipStream_t stream);
 
+/* The gated form over one shared projection ([R-step]: one projection of the
+ * shifted memory for every layer, a per-layer gate, RMSNorm on the recurrent
+ * key). Per pass:
+ *   maglev_mem_project(shift = 1, no mixing arguments) once -> kproj, vmem
+ *     (the projections before the norm);
+ *   per layer l: maglev_mix_entries_gated(k_l, v_l, kproj, vmem, gates_l) and
+ *     maglev_swa_inject_fwd; backward maglev_swa_inject_bwd_shared_gated,
+ *     which sums every layer's gradients of kproj and vmem into float32
+ *     dkproj, dvmem;
+ *   maglev_mem_project_bwd(dkproj, dvmem) once: dm' and dW from the sums.
+ * The norm is per layer's use of kproj (each layer normalises the same rows),
+ * so its backward runs per layer and the sums are of pre-norm gradients. */
+
+/* The gated mix of one layer from the shared pre-norm projections (the mixing
+ * half of maglev_mem_project_gated): k, v, kproj, vmem, kmix, vmix
+ * [B,T,H,Dh] dtype; gates [4][H*Dh] float32 logits; eps >= 0. H*Dh <= 4096. */
+maglev_status_t maglev_mix_entries_gated(const maglev_geom_t *g, const void *k, const void *v,
+                                         const void *kproj, const void *vmem, const float *gates,
+                                         float eps, void *kmix, void *vmix, hipStream_t stream);
+
+/* Bytes of device workspace maglev_swa_inject_bwd_shared_gated needs (0 on
+ * invalid geometry or H*Dh > 4096). */
+size_t maglev_swa_inject_bwd_shared_gated_workspace(const maglev_geom_t *g);
+
+/* Backward of one gated layer whose recurrent terms come from a shared
+ * projection (attention, gates, rotation and norm; no projection):
+ *   dq, dk, dv [B,T,H,Dh] dtype (overwritten): gradients w.r.t. q, k, v;
+ *   dkproj, dvmem [B,T,H,Dh] float32: the layer's share of the gradients of
+ *     the shared kproj (before the norm) and vmem (accumulate bit 0: added);
+ *   dgates [4][H*Dh] float32, the layer's gate-logit gradients (bit 2: added).
+ * Inputs as maglev_swa_inject_bwd_gated without m_prime and the weights (kmix,
+ * vmix from maglev_mix_entries_gated). accumulate: only bits 0 and 2.
+ * Deterministic (fixed-order sums, no atomics). */
+maglev_status_t maglev_swa_inject_bwd_shared_gated(
+    const maglev_geom_t *g, const void *q, const void *kmix, const void *vmix, const void *k,
+    const void *v, const void *kproj, const void *vmem, const float *gates, float eps,
+    const void *o, const float *lse, const void *dO, void *dq, void *dk, void *dv, float *dkproj,
+    float *dvmem, float *dgates, unsigned accumulate, void *workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
 /* Bytes of device workspace maglev_mem_project_bwd needs (0 on invalid geometry). */
 size_t maglev_mem_project_bwd_workspace(const maglev_geom_t *g);
 
@@ -450,6 +490,19 @@ int maglev_abi_version(void);
  * The events add a small gap between kernels; timing is off by default. */
 maglev_status_t maglev_profile_enable(int on, const char *only);
 int maglev_profile_count(void);
+
+/* Debug mode (diagnostic; off by default, on at load when the environment
+ * variable MAGLEV_DEBUG is set to anything but "0"): after each kernel launch
+ * (or the few launches of one step) the library takes the launch error and
+ * synchronises the launch stream, so that a failure is reported by the call
+ * that launched the faulting kernel, as MAGLEV_ERR_HIP with
+ * maglev_last_error() = "<kernel name>: <HIP error>". Launches on a stream
+ * under graph capture are not checked. Slow: every launch waits for the GPU.
+ * maglev_debug_enable(on) switches it for the whole process;
+ * maglev_debug_enabled() returns 1 while it is on. */
+maglev_status_t maglev_debug_enable(int on);
+int maglev_debug_enabled(void);
+
 maglev_status_t maglev_profile_entry(int index, const char **name, int64_t *launches,
                                      double *total_ms);
 

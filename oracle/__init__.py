@@ -305,6 +305,27 @@ def swa_inject_bwd_gated(q, k, v, m_prime, W_Km, W_Vm, gates, dO, W: int, pos0: 
     return out
 
 
+def swa_inject_bwd_shared_gated(layers, m_prime, W_Km, W_Vm, W: int, pos0: int = 0,
+                                rope_base: float = 10000.0, scale: float = 0.0,
+                                eps: float = RMS_EPS):
+    """Gradients of a stack of gated layers that share one projection of the
+    shifted memory (the same m', W_Km, W_Vm for every layer) and each have
+    their own q, k, v, four gate-logit vectors ("gates") and upstream
+    gradient dO. The stack's objective is the sum over layers, so each layer
+    contributes its single-layer gradient (swa_inject_bwd_gated) and the
+    shared parameters and m' collect the sum.
+    Returns (per_layer, shared): per_layer[l] holds dq, dk, dv and the four
+    d<gate name> vectors; shared holds dm_prime, dW_Km, dW_Vm."""
+    per_layer, shared = [], None
+    for x in layers:
+        g = swa_inject_bwd_gated(x["q"], x["k"], x["v"], m_prime, W_Km, W_Vm, x["gates"], x["dO"],
+                                 W, pos0=pos0, rope_base=rope_base, scale=scale, eps=eps)
+        per_layer.append({n: g[n] for n in ("dq", "dk", "dv") + tuple("d" + a for a in GATE_NAMES)})
+        part = {n: g[n] for n in ("dm_prime", "dW_Km", "dW_Vm")}
+        shared = part if shared is None else {n: shared[n] + part[n] for n in part}
+    return per_layer, shared
+
+
 def decode_step_gated(q, k, v, kproj, vmem, gates, kcache: np.ndarray, vcache: np.ndarray,
                       pos, rope_base: float = 10000.0, scale: float = 0.0,
                       eps: float = RMS_EPS, ring_bf16: bool = True):

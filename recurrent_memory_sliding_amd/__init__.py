@@ -26,6 +26,7 @@ __all__ = [
     "maglev_consistency_loss_noalloc",
     "maglev_consistency_loss_workspace", "maglev_decode_step", "maglev_decode_workspace",
     "maglev_decode_advance", "maglev_prepare", "maglev_abi_version", "maglev_profile_enable",
+    "maglev_debug_enable", "maglev_debug_enabled",
     "maglev_profile_read", "maglev_lm_head", "maglev_lm_head_workspace", "LM_CAP",
 ]
 
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
             "maglev_mix_entries": ([G] + [vp] * 7 + [vp], i32),
             "maglev_swa_inject_bwd_shared_workspace": ([G], sz),
             "maglev_swa_inject_bwd_shared": ([G] + [vp] * 15 + [u32, vp, sz, vp], i32),
+            "maglev_mix_entries_gated": ([G] + [vp] * 5 + [f32, vp, vp, vp], i32),
+            "maglev_swa_inject_bwd_shared_gated_workspace": ([G], sz),
+            "maglev_swa_inject_bwd_shared_gated": ([G] + [vp] * 8 + [f32] + [vp] * 9
+                                                   + [u32, vp, sz, vp], i32),
             "maglev_mem_project_bwd_workspace": ([G], sz),
             "maglev_mem_project_bwd": ([G] + [vp] * 8 + [u32, vp, sz, vp], i32),
             "maglev_rope_keys": ([G, vp, vp, vp], i32),
@@ -99,6 +104,8 @@ def lib() -> ctypes.CDLL:
             "maglev_last_error": ([], ctypes.c_char_p),
             "maglev_abi_version": ([], ctypes.c_int),
             "maglev_profile_enable": ([ctypes.c_int, ctypes.c_char_p], i32),
+            "maglev_debug_enable": ([ctypes.c_int], i32),
+            "maglev_debug_enabled": ([], ctypes.c_int),
             "maglev_profile_count": ([], ctypes.c_int),
             "maglev_profile_entry": ([ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
                                       ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double)], i32),
@@ -169,6 +176,17 @@ def make_geom(B, T, H, Dh, d, W, pos0=0, rope_base=10000.0, scale=0.0, dtype=MAG
 
 def maglev_abi_version() -> int:
     return lib().maglev_abi_version()
+
+
+def maglev_debug_enable(on: bool = True) -> None:
+    """Debug mode: every launch is followed by a stream synchronisation and an
+    error check; a failure is reported by the launching call with the
+    kernel's name. Also switched on at load by MAGLEV_DEBUG=1."""
+    _check(lib().maglev_debug_enable(1 if on else 0), "maglev_debug_enable")
+
+
+def maglev_debug_enabled() -> bool:
+    return bool(lib().maglev_debug_enabled())
 
 
 def maglev_profile_enable(on: bool = True, only: Optional[str] = None):
@@ -604,6 +622,68 @@ def maglev_swa_inject_bwd_shared(q, kmix, vmix, kmem, vmem, gate_logit, o, lse, 
         _ptr(dgate), accumulate, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)), "maglev_swa_inject_bwd_shared")
     return dq, dk, dv, dgate
+
+
+# Gated form over one shared projection: mem_project (no mixing arguments)
+# once per pass gives the pre-norm kproj and vmem; per layer
+# mix_entries_gated / swa_inject_fwd / swa_inject_bwd_shared_gated (summing
+# the projections' gradients in float32); then mem_project_bwd once.
+def maglev_mix_entries_gated(k, v, kproj, vmem, gates, eps: float = RMS_EPS, pos0: int = 0,
+                             rope_base: float = 10000.0, kmix=None, vmix=None, stream=None):
+    """(kmix, vmix) of one gated layer from the shared pre-norm projections."""
+    B, T, H, Dh = k.shape
+    gates = gate_tensor(gates, H * Dh, k.device)
+    _dev(k, v, kproj, vmem, gates, kmix, vmix)
+    _same(k, v, kproj, vmem, kmix, vmix)
+    for t in (v, kproj, vmem):
+        if tuple(t.shape) != tuple(k.shape):
+            raise MaglevError("k, v, kproj, vmem must all be [B,T,H,Dh]")
+    kmix = torch.empty_like(k) if kmix is None else kmix
+    vmix = torch.empty_like(k) if vmix is None else vmix
+    g = make_geom(B, T, H, Dh, H * Dh, 1, pos0, rope_base, 0.0, _dtype_code(k))
+    _check(lib().maglev_mix_entries_gated(ctypes.byref(g), _ptr(k), _ptr(v), _ptr(kproj),
+                                          _ptr(vmem), _ptr(gates), float(eps), _ptr(kmix),
+                                          _ptr(vmix), _stream(stream)), "maglev_mix_entries_gated")
+    return kmix, vmix
+
+
+def maglev_swa_inject_bwd_shared_gated_workspace(B, T, H, Dh, W, dtype=MAGLEV_BF16) -> int:
+    g = make_geom(B, T, H, Dh, H * Dh, W, dtype=dtype)
+    return int(lib().maglev_swa_inject_bwd_shared_gated_workspace(ctypes.byref(g)))
+
+
+def maglev_swa_inject_bwd_shared_gated(q, kmix, vmix, k, v, kproj, vmem, gates, o, lse, dO,
+                                       dkproj, dvmem, W: int, eps: float = RMS_EPS, pos0: int = 0,
+                                       rope_base: float = 10000.0, scale: float = 0.0,
+                                       accumulate: int = 0, dq=None, dk=None, dv=None,
+                                       dgates=None, workspace=None, stream=None):
+    """One gated layer's backward over shared projections: returns
+    (dq, dk, dv, dgates [4, H*Dh] float32); dkproj/dvmem (float32 [B,T,H,Dh])
+    receive the layer's share of the projections' gradients (added with bit 0)."""
+    B, T, H, Dh = q.shape
+    gates = gate_tensor(gates, H * Dh, q.device)
+    _dev(q, kmix, vmix, k, v, kproj, vmem, gates, o, lse, dO, dkproj, dvmem, dq, dk, dv, dgates,
+         workspace)
+    _same(q, kmix, vmix, k, v, kproj, vmem, o, dO, dq, dk, dv)
+    for t in (dkproj, dvmem):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(q.shape):
+            raise MaglevError("dkproj / dvmem must be float32 [B,T,H,Dh]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if dgates is None:
+        dgates = torch.empty((4, H * Dh), dtype=torch.float32, device=q.device)
+    g = make_geom(B, T, H, Dh, H * Dh, W, pos0, rope_base, scale, _dtype_code(q))
+    if workspace is None:
+        need = int(lib().maglev_swa_inject_bwd_shared_gated_workspace(ctypes.byref(g)))
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().maglev_swa_inject_bwd_shared_gated(
+        ctypes.byref(g), _ptr(q), _ptr(kmix), _ptr(vmix), _ptr(k), _ptr(v), _ptr(kproj),
+        _ptr(vmem), _ptr(gates), float(eps), _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dkproj), _ptr(dvmem), _ptr(dgates), accumulate, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)),
+        "maglev_swa_inject_bwd_shared_gated")
+    return dq, dk, dv, dgates
 
 
 def maglev_mem_project_bwd_workspace(B, T, H, Dh, d, dtype=MAGLEV_BF16) -> int:

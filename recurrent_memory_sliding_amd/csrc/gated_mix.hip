@@ -260,10 +260,25 @@ MAGLEV_DEV float2 group_sum2(float x, float y, float2 *red, int nw, int wi)
     return t;
 }
 
-template <typename T, int DH>
+// Eight projection gradients into dkp/dvm: rounded to the storage type, or
+// (float32 targets of a stack sharing one projection) written or added.
+MAGLEV_DEV void put8(bf16 *p, const float *in, bool) { store8(p, in); }
+MAGLEV_DEV void put8(float *p, const float *in, bool add)
+{
+    if (!add) { store8(p, in); return; }
+    f32x4 a = *reinterpret_cast<const f32x4 *>(p), b = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] += in[i]; b[i] += in[4 + i]; }
+    *reinterpret_cast<f32x4 *>(p) = a;
+    *reinterpret_cast<f32x4 *>(p + 4) = b;
+}
+
+// PT: type of the projection gradients dkp, dvm (T, or float32 sums over the
+// layers of a shared projection; padd: add to them).
+template <typename T, int DH, typename PT>
 __global__ __launch_bounds__(256, 2) void gated_mix_bwd(GatedArgs a, const T *k, const T *v,
                                                       const T *kp, const T *vm, T *dk, T *dv,
-                                                      T *dkp, T *dvm, float *gpart)
+                                                      PT *dkp, PT *dvm, bool padd, float *gpart)
 {
     // The workgroup is nh row groups of rt threads (nh = 2 when a row needs at
     // most 128 threads): group h takes rows r0 + h, r0 + h + nh, ..., so that
@@ -340,8 +355,8 @@ __global__ __launch_bounds__(256, 2) void gated_mix_bwd(GatedArgs a, const T *k,
             dnl[e] = (dnl[e] - nl[e] * mu) * rs;
             dnh[e] = (dnh[e] - nh[e] * mu) * rs;
         }
-        store8(dkp + base + cp.lo, dnl);
-        store8(dkp + base + cp.hi, dnh);
+        put8(dkp + base + cp.lo, dnl, padd);
+        put8(dkp + base + cp.hi, dnh, padd);
         float kl[8], kh[8];
         d[2][0].get(kl);
         d[2][1].get(kh);
@@ -395,8 +410,8 @@ __global__ __launch_bounds__(256, 2) void gated_mix_bwd(GatedArgs a, const T *k,
         }
         store8(dv + base + cp.lo, vl);
         store8(dv + base + cp.hi, vh);
-        store8(dvm + base + cp.lo, ml);
-        store8(dvm + base + cp.hi, mh);
+        put8(dvm + base + cp.lo, ml, padd);
+        put8(dvm + base + cp.hi, mh, padd);
     };
     // One row in flight per group: the second group is what overlaps a row's
     // loads with another's reduction (a prefetched row per group costs the
@@ -489,10 +504,10 @@ void fwd_t(const Geom &g, const void *k, const void *v, const void *kp, const vo
                        static_cast<T *>(kx), static_cast<T *>(vx));
 }
 
-template <typename T, int DH>
+template <typename T, int DH, typename PT>
 void bwd_t(const Geom &g, const void *k, const void *v, const void *kp, const void *vm,
-           const float *gates, float eps, const float2 *rope, void *dk, void *dv,
-           const BwdWorkspace &ws, float *dgates, unsigned acc, hipStream_t s)
+           const float *gates, float eps, const float2 *rope, void *dk, void *dv, PT *dkp,
+           PT *dvm, bool padd, const BwdWorkspace &ws, float *dgates, unsigned acc, hipStream_t s)
 {
     const GatedArgs a = gated_args(g, gates, eps, rope, ws.g_rows);
     {
@@ -500,12 +515,10 @@ void bwd_t(const Geom &g, const void *k, const void *v, const void *kp, const vo
         const unsigned rt = row_threads(g.HD()), nh = rt <= 128 ? 2u : 1u;
         const size_t lds = gate_lds_bytes(g.HD()) + (nh > 1 ? (size_t)64 * rt * sizeof(float) : 0);
         prof::Scope ts("gated_mix_bwd", s);
-        hipLaunchKernelGGL((gated_mix_bwd<T, DH>), dim3((unsigned)ws.g_blocks), dim3(nh * rt), lds,
-                           s, a,
-                           static_cast<const T *>(k),
-                           static_cast<const T *>(v), static_cast<const T *>(kp),
-                           static_cast<const T *>(vm), static_cast<T *>(dk), static_cast<T *>(dv),
-                           static_cast<T *>(ws.dkp), static_cast<T *>(ws.dvm), ws.gpart);
+        hipLaunchKernelGGL((gated_mix_bwd<T, DH, PT>), dim3((unsigned)ws.g_blocks), dim3(nh * rt),
+                           lds, s, a, static_cast<const T *>(k), static_cast<const T *>(v),
+                           static_cast<const T *>(kp), static_cast<const T *>(vm),
+                           static_cast<T *>(dk), static_cast<T *>(dv), dkp, dvm, padd, ws.gpart);
     }
     const int n = 4 * g.HD();
     prof::Scope ts("gate_grad_reduce", s);
@@ -544,15 +557,23 @@ hipError_t launch_gated_mix(const Geom &g, const void *k, const void *v, const v
 hipError_t launch_gated_mix_bwd(const Geom &g, const void *k, const void *v, const void *kp,
                                 const void *vm, const float *gates, float eps,
                                 const float2 *rope, void *dk, void *dv, const BwdWorkspace &ws,
-                                float *dgates, unsigned acc, hipStream_t s)
+                                float *dgates, unsigned acc, float *dkp32, float *dvm32,
+                                hipStream_t s)
 {
+    const bool f32 = dkp32 != nullptr, padd = f32 && (acc & 1u);
+#define MAGLEV_GATED_BWD(T, DH)                                                               \
+    (f32 ? bwd_t<T, DH, float>(g, k, v, kp, vm, gates, eps, rope, dk, dv, dkp32, dvm32, padd,  \
+                               ws, dgates, acc, s)                                            \
+         : bwd_t<T, DH, T>(g, k, v, kp, vm, gates, eps, rope, dk, dv, static_cast<T *>(ws.dkp), \
+                           static_cast<T *>(ws.dvm), false, ws, dgates, acc, s))
     if (g.dtype == MAGLEV_BF16) {
-        if (g.Dh == 128) bwd_t<bf16, 128>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
-        else bwd_t<bf16, 64>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+        if (g.Dh == 128) MAGLEV_GATED_BWD(bf16, 128);
+        else MAGLEV_GATED_BWD(bf16, 64);
     } else {
-        if (g.Dh == 128) bwd_t<float, 128>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
-        else bwd_t<float, 64>(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+        if (g.Dh == 128) MAGLEV_GATED_BWD(float, 128);
+        else MAGLEV_GATED_BWD(float, 64);
     }
+#undef MAGLEV_GATED_BWD
     return hipGetLastError();
 }
 

@@ -70,8 +70,9 @@ struct BwdWorkspace {
 // Which backward the workspace serves: the sigma-gated layer path, the gated
 // layer path, or attention alone (no memory term, no projection).
 // Shared: one layer of a stack sharing a projection (attention backward and
-// the memory-gradient accumulation); Proj: that projection's backward alone.
-enum class BwdKind { Sigma, Gated, Attn, Shared, Proj };
+// the memory-gradient accumulation); SharedGated: the same for the gated mix;
+// Proj: that projection's backward alone.
+enum class BwdKind { Sigma, Gated, Attn, Shared, SharedGated, Proj };
 constexpr int kSharedTokens = 128;   // tokens per workgroup of the shared accumulation
 size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *layout, char *base, BwdKind kind);
 
@@ -89,10 +90,13 @@ hipError_t launch_gated_mix(const Geom &g, const void *k, const void *v, const v
                             const void *vmem, const float *gates, float eps, const float2 *rope,
                             void *kmix, void *vmix, hipStream_t s);
 // dk/dv: in = gradients of the mixed entries, out = gradients of k and v.
+// The projection gradients go to ws.dkp/ws.dvm (dtype), or with dkp32 != null
+// to the float32 dkp32/dvm32 (accumulate bit 0: added).
 hipError_t launch_gated_mix_bwd(const Geom &g, const void *k, const void *v, const void *kproj,
                                 const void *vmem, const float *gates, float eps,
                                 const float2 *rope, void *dk, void *dv, const BwdWorkspace &ws,
-                                float *dgates, unsigned accumulate, hipStream_t s);
+                                float *dgates, unsigned accumulate, float *dkp32, float *dvm32,
+                                hipStream_t s);
 hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kmix, const void *vmix,
                             const void *k, const void *v, const void *kproj, const void *vmem,
                             const float *gates, float eps, const void *o, const float *lse,
@@ -119,6 +123,17 @@ hipError_t launch_bwd_shared(const Geom &g, const void *q, const void *kmix, con
                              void *dk, void *dv, float *dkmem, float *dvmem, float *dgate,
                              unsigned accumulate, const BwdWorkspace &ws, const float2 *rope,
                              hipStream_t s);
+// Gated form over a shared projection, per layer: attention backward, the
+// gated mix backward (dk, dv of the local features, dgates), and the layer's
+// share of the gradients of the shared pre-norm projections kp, vm into the
+// float32 dkp, dvm (accumulate bit 0: added; bit 2: dgates added).
+hipError_t launch_bwd_shared_gated(const Geom &g, const void *q, const void *kmix,
+                                   const void *vmix, const void *k, const void *v,
+                                   const void *kproj, const void *vmem, const float *gates,
+                                   float eps, const void *o, const float *lse, const void *dO,
+                                   void *dq, void *dk, void *dv, float *dkp, float *dvm,
+                                   float *dgates, unsigned accumulate, const BwdWorkspace &ws,
+                                   const float2 *rope, hipStream_t s);
 // Once per pass: dm' and dW from the summed float32 memory gradients.
 hipError_t launch_mem_project_bwd(const Geom &g, const float *dkmem, const float *dvmem,
                                   const void *m_prime, const void *W_Km, const void *W_Vm,

@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "internal.hpp"
+#include "profile.hpp"
 
 namespace maglev {
 namespace {
@@ -27,9 +28,24 @@ maglev_status_t fail(maglev_status_t st, const char *msg)
 
 maglev_status_t hip_status(hipError_t e)
 {
+    // debug mode: a failure seen after one of this call's launches names its kernel
+    const char *kern = nullptr;
+    hipError_t de = hipSuccess;
+    if (prof::debug_take(&kern, &de)) {
+        g_last_error = std::string(kern ? kern : "?") + ": " + hipGetErrorString(de);
+        return MAGLEV_ERR_HIP;
+    }
     if (e == hipSuccess) return MAGLEV_OK;
     g_last_error = hipGetErrorString(e);
     return MAGLEV_ERR_HIP;
+}
+
+// The status of a call that launched work on `s`; in debug mode also the
+// check after its last launches (those outside a named kernel scope included).
+maglev_status_t launched(hipStream_t s, hipError_t e)
+{
+    if (e == hipSuccess) prof::debug_after("end of call", s);
+    return hip_status(e);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -223,7 +239,7 @@ maglev_status_t maglev_mem_project(const maglev_geom_t *g, int shift, const void
     hipError_t e = launch_project(G, shift, m, W_Km, W_Vm, kmem, vmem, stream);
     if (e == hipSuccess && nmix)
         e = launch_mix(G, k, v, kmem, vmem, gate_logit, rope, kmix, vmix, stream);
-    return hip_status(e);
+    return launched(stream, e);
 }
 
 maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, const void *kmix,
@@ -239,7 +255,7 @@ maglev_status_t maglev_swa_inject_fwd(const maglev_geom_t *g, const void *q, con
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_attn_fwd(G, q, kmix, vmix, rope, o, lse, stream));
+    return launched(stream, launch_attn_fwd(G, q, kmix, vmix, rope, o, lse, stream));
 }
 
 size_t maglev_swa_inject_bwd_workspace(const maglev_geom_t *g)
@@ -279,7 +295,7 @@ maglev_status_t maglev_swa_inject_bwd(const maglev_geom_t *g, const void *q, con
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_bwd(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km,
+    return launched(stream, launch_bwd(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, m_prime, W_Km,
                                  W_Vm, dq, dk, dv, dm_prime, dW_Km, dW_Vm, dgate, accumulate,
                                  layout, rope, stream));
 }
@@ -324,7 +340,7 @@ maglev_status_t maglev_consistency_loss(int64_t N, int32_t d, float lambda, int3
     if (!workspace || workspace_bytes < need)
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (!aligned16(workspace)) return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    return hip_status(launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
+    return launched(stream, launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
                                   workspace, stream));
 }
 
@@ -342,7 +358,7 @@ maglev_status_t maglev_consistency_loss_noalloc(int64_t N, int32_t d, float lamb
     float *scr = nullptr;
     st = hip_status(loss_scratch_address(&scr));
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
+    return launched(stream, launch_loss(N, d, lambda, dtype, m, m_prime, loss, dm, dm_prime, accumulate,
                                   scr, stream));
 }
 
@@ -386,7 +402,7 @@ maglev_status_t maglev_lm_head(int64_t N, int32_t d, int64_t V, float cap, float
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (!aligned16(workspace)) return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     lm_head_workspace_bytes(N, d, V, dtype, &L, static_cast<char *>(workspace));
-    return hip_status(launch_lm_head(N, d, V, cap, eps, lambda, dtype, h, U, targets, m_prime, m,
+    return launched(stream, launch_lm_head(N, d, V, cap, eps, lambda, dtype, h, U, targets, m_prime, m,
                                      loss, dh, dU, accumulate, L, stream));
 }
 
@@ -425,7 +441,7 @@ maglev_status_t maglev_decode_step(int32_t Bs, int32_t H, int32_t Dh, int32_t W,
     if (workspace && !aligned16(workspace))
         return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)Dh));
-    return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kmem, vmem,
+    return launched(stream, launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kmem, vmem,
                                     mem_stride, gate_logit, nullptr, 0.0f, kcache, vcache, pos, o,
                                     workspace, stream));
 }
@@ -464,7 +480,7 @@ maglev_status_t maglev_mem_project_gated(const maglev_geom_t *g, int shift, cons
     hipError_t e = launch_project(G, shift, m, W_Km, W_Vm, kproj, vmem, stream);
     if (e == hipSuccess)
         e = launch_gated_mix(G, k, v, kproj, vmem, gates, eps, rope, kmix, vmix, stream);
-    return hip_status(e);
+    return launched(stream, e);
 }
 
 size_t maglev_swa_inject_bwd_gated_workspace(const maglev_geom_t *g)
@@ -505,7 +521,7 @@ maglev_status_t maglev_swa_inject_bwd_gated(
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_bwd_gated(G, q, kmix, vmix, k, v, kproj, vmem, gates, eps, o, lse, dO,
+    return launched(stream, launch_bwd_gated(G, q, kmix, vmix, k, v, kproj, vmem, gates, eps, o, lse, dO,
                                        m_prime, W_Km, W_Vm, dq, dk, dv, dm_prime, dW_Km, dW_Vm,
                                        dgates, accumulate, layout, rope, stream));
 }
@@ -542,7 +558,7 @@ maglev_status_t maglev_decode_step_gated(int32_t Bs, int32_t H, int32_t Dh, int3
     if (workspace && !aligned16(workspace))
         return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
     const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)Dh));
-    return hip_status(launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kproj, vmem,
+    return launched(stream, launch_decode(Bs, H, Dh, W, rope_base, sc, dtype, q, k, v, kproj, vmem,
                                     mem_stride, nullptr, gates, eps, kcache, vcache, pos, o,
                                     workspace, stream));
 }
@@ -562,7 +578,7 @@ maglev_status_t maglev_rope_keys(const maglev_geom_t *g, const void *k, void *kr
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_rope_keys(G, k, rope, krot, stream));
+    return launched(stream, launch_rope_keys(G, k, rope, krot, stream));
 }
 
 size_t maglev_attn_bwd_workspace(const maglev_geom_t *g)
@@ -592,7 +608,7 @@ maglev_status_t maglev_attn_bwd(const maglev_geom_t *g, const void *q, const voi
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_attn_bwd(G, q, krot, v, o, lse, dO, dq, dk, dv, layout, rope, stream));
+    return launched(stream, launch_attn_bwd(G, q, krot, v, o, lse, dO, dq, dk, dv, layout, rope, stream));
 }
 
 // ---- layers sharing one memory projection ---------------------------------------
@@ -611,7 +627,7 @@ maglev_status_t maglev_mix_entries(const maglev_geom_t *g, const void *k, const 
     const float2 *rope = nullptr;
     st = table_for(G, stream, &rope);
     if (st != MAGLEV_OK) return st;
-    return hip_status(launch_mix(G, k, v, kmem, vmem, gate_logit, rope, kmix, vmix, stream));
+    return launched(stream, launch_mix(G, k, v, kmem, vmem, gate_logit, rope, kmix, vmix, stream));
 }
 
 size_t maglev_swa_inject_bwd_shared_workspace(const maglev_geom_t *g)
@@ -651,9 +667,70 @@ maglev_status_t maglev_swa_inject_bwd_shared(const maglev_geom_t *g, const void 
         st = table_for(G, stream, &rope);
         if (st != MAGLEV_OK) return st;
     }
-    return hip_status(launch_bwd_shared(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, dq,
+    return launched(stream, launch_bwd_shared(G, q, kmix, vmix, kmem, vmem, gate_logit, o, lse, dO, dq,
                                         dk, dv, dkmem, dvmem, dgate, accumulate, layout, rope,
                                         stream));
+}
+
+maglev_status_t maglev_mix_entries_gated(const maglev_geom_t *g, const void *k, const void *v,
+                                         const void *kproj, const void *vmem, const float *gates,
+                                         float eps, void *kmix, void *vmix, hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    st = check_gated(G, gates, eps);
+    if (st != MAGLEV_OK) return st;
+    if (G.N() == 0) return MAGLEV_OK;
+    st = check_ptrs({k, v, kproj, vmem, kmix, vmix});
+    if (st != MAGLEV_OK) return st;
+    const float2 *rope = nullptr;
+    st = table_for(G, stream, &rope);
+    if (st != MAGLEV_OK) return st;
+    return launched(stream, launch_gated_mix(G, k, v, kproj, vmem, gates, eps, rope, kmix, vmix, stream));
+}
+
+size_t maglev_swa_inject_bwd_shared_gated_workspace(const maglev_geom_t *g)
+{
+    Geom G;
+    if (check_geom(g, &G) != MAGLEV_OK || G.HD() > 4096) return 0;
+    BwdWorkspace layout;
+    return bwd_workspace_bytes(G, &layout, nullptr, BwdKind::SharedGated);
+}
+
+maglev_status_t maglev_swa_inject_bwd_shared_gated(
+    const maglev_geom_t *g, const void *q, const void *kmix, const void *vmix, const void *k,
+    const void *v, const void *kproj, const void *vmem, const float *gates, float eps,
+    const void *o, const float *lse, const void *dO, void *dq, void *dk, void *dv, float *dkproj,
+    float *dvmem, float *dgates, unsigned accumulate, void *workspace, size_t workspace_bytes,
+    hipStream_t stream)
+{
+    Geom G;
+    maglev_status_t st = check_geom(g, &G);
+    if (st != MAGLEV_OK) return st;
+    st = check_gated(G, gates, eps);
+    if (st != MAGLEV_OK) return st;
+    if (!dgates) return fail(MAGLEV_ERR_INVALID_VALUE, "dgates is NULL");
+    if (accumulate & ~5u) return fail(MAGLEV_ERR_INVALID_VALUE, "unknown accumulate bits");
+    if (G.N() > 0) {
+        st = check_ptrs({q, kmix, vmix, k, v, kproj, vmem, o, lse, dO, dq, dk, dv, dkproj, dvmem});
+        if (st != MAGLEV_OK) return st;
+    }
+    BwdWorkspace layout;
+    const size_t need =
+        bwd_workspace_bytes(G, &layout, static_cast<char *>(workspace), BwdKind::SharedGated);
+    if (G.N() > 0 && (!workspace || workspace_bytes < need))
+        return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
+    if (workspace && !aligned16(workspace))
+        return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+    const float2 *rope = nullptr;
+    if (G.N() > 0) {
+        st = table_for(G, stream, &rope);
+        if (st != MAGLEV_OK) return st;
+    }
+    return launched(stream, launch_bwd_shared_gated(G, q, kmix, vmix, k, v, kproj, vmem, gates, eps, o,
+                                              lse, dO, dq, dk, dv, dkproj, dvmem, dgates,
+                                              accumulate, layout, rope, stream));
 }
 
 size_t maglev_mem_project_bwd_workspace(const maglev_geom_t *g)
@@ -685,7 +762,7 @@ maglev_status_t maglev_mem_project_bwd(const maglev_geom_t *g, const float *dkme
         return fail(MAGLEV_ERR_WORKSPACE, "workspace missing or too small");
     if (workspace && !aligned16(workspace))
         return fail(MAGLEV_ERR_MISALIGNED, "workspace is not 16-byte aligned");
-    return hip_status(launch_mem_project_bwd(G, dkmem, dvmem, m_prime, W_Km, W_Vm, dm_prime, dW_Km,
+    return launched(stream, launch_mem_project_bwd(G, dkmem, dvmem, m_prime, W_Km, W_Vm, dm_prime, dW_Km,
                                              dW_Vm, accumulate, layout, stream));
 }
 
@@ -694,7 +771,7 @@ maglev_status_t maglev_decode_advance(int32_t Bs, int64_t *pos, hipStream_t stre
     if (Bs < 0) return fail(MAGLEV_ERR_INVALID_VALUE, "Bs must be >= 0");
     if (!pos) return fail(MAGLEV_ERR_INVALID_VALUE, "pos is NULL");
     if (Bs == 0) return MAGLEV_OK;
-    return hip_status(launch_advance(Bs, pos, stream));
+    return launched(stream, launch_advance(Bs, pos, stream));
 }
 
 }  // extern "C"

@@ -350,6 +350,8 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     const bool proj = kind == BwdKind::Sigma || kind == BwdKind::Gated || kind == BwdKind::Proj;
     const bool attn = kind != BwdKind::Proj;          // an attention backward runs
     const bool gated = kind == BwdKind::Gated;
+    // the gated mix backward runs (its gate partials are needed)
+    const bool gmix = gated || kind == BwdKind::SharedGated;
     const bool shared = kind == BwdKind::Shared;
     const size_t esz = bf ? 2 : 4;
     const size_t BHT = (size_t)g.B * g.H * g.T;
@@ -361,7 +363,7 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     L->ksplit = bf && proj ? mfma::dw_ksplit(g) : 0;
     L->Tp = (g.T + 31) / 32 * 32;
     L->g_rows = L->g_blocks = 0;
-    if (gated) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
+    if (gmix) gated_partition(g.N(), &L->g_rows, &L->g_blocks);
     // float32 path: row sums D and, for the sigma form, the per-key gate terms;
     // a layer of a shared projection: per-block gate terms (both paths)
     const size_t nsp = (size_t)g.B * g.H * ((g.T + kSharedTokens - 1) / kSharedTokens);
@@ -402,7 +404,7 @@ size_t bwd_workspace_bytes(const Geom &g, BwdWorkspace *L, char *base, BwdKind k
     L->rowdot = reinterpret_cast<float *>(at(oR, bf && kind == BwdKind::Sigma));
     L->dkp = at(oKp, nact > 0);
     L->dvm = at(oVm, nact > 0);
-    L->gpart = reinterpret_cast<float *>(at(oG, gated));
+    L->gpart = reinterpret_cast<float *>(at(oG, gmix));
     return off;
 }
 
@@ -482,7 +484,8 @@ hipError_t launch_bwd_gated(const Geom &g, const void *q, const void *kx, const 
                                                dq, dk, dv, ws, rope, s);
     }
     // 2. gates, rotation and norm backward: dk, dv final; gradients of the projection
-    hipError_t e = launch_gated_mix_bwd(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, s);
+    hipError_t e = launch_gated_mix_bwd(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc,
+                                        nullptr, nullptr, s);
     if (e != hipSuccess) return e;
     // 3. shift and projection backward (no further gate factor)
     if (!(acc & 1u) && g.dtype != MAGLEV_BF16) {
@@ -574,6 +577,37 @@ hipError_t launch_bwd_shared(const Geom &g, const void *q, const void *kx, const
     hipLaunchKernelGGL(dgate_reduce, dim3(g.H), dim3(256), 0, s, ws.ds_part, g.B, g.H,
                        (int64_t)((g.T + kSharedTokens - 1) / kSharedTokens), gate, dgate, acc);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd_shared_gated(const Geom &g, const void *q, const void *kx, const void *vx,
+                                   const void *k, const void *v, const void *kp, const void *vm,
+                                   const float *gates, float eps, const void *o, const float *lse,
+                                   const void *dO, void *dq, void *dk, void *dv, float *dkp,
+                                   float *dvm, float *dgates, unsigned acc, const BwdWorkspace &ws,
+                                   const float2 *rope, hipStream_t s)
+{
+    if (g.N() == 0) {
+        if (!(acc & 4u))
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((4 * g.HD() + 255) / 256)), dim3(256), 0,
+                               s, dgates, (int64_t)4 * g.HD());
+        return hipGetLastError();
+    }
+    // 1. attention backward: dq, and the gradients of the mixed entries into dk/dv
+    if (g.dtype == MAGLEV_BF16) {
+        mfma::launch_attn_bwd_bf16(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, true, s);
+    } else if (g.Dh == 128) {
+        attn_bwd_simt<float, 128, false, false>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO,
+                                                dq, dk, dv, ws, rope, s);
+    } else {
+        attn_bwd_simt<float, 64, false, false>(g, q, kx, vx, nullptr, nullptr, nullptr, o, lse, dO,
+                                               dq, dk, dv, ws, rope, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // 2. gates, rotation and norm backward: dk, dv final; this layer's share of
+    // the shared projections' gradients written or added in float32
+    return launch_gated_mix_bwd(g, k, v, kp, vm, gates, eps, rope, dk, dv, ws, dgates, acc, dkp,
+                                dvm, s);
 }
 
 hipError_t launch_mem_project_bwd(const Geom &g, const float *dkm, const float *dvm,

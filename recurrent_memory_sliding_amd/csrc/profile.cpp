@@ -1,6 +1,9 @@
 // profile.cpp -- event pool and per-name totals behind maglev_profile_*.
 #include "profile.hpp"
 
+#include <stdlib.h>
+#include <string.h>
+
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -29,6 +32,38 @@ std::string g_only;   // record only this kernel name when non-empty
 std::map<int, std::vector<hipEvent_t>> g_pool;   // free events per device
 std::vector<Pending> g_pending;
 std::map<std::string, Total> g_totals;
+
+bool env_debug()
+{
+    const char *v = getenv("MAGLEV_DEBUG");
+    return v && *v && strcmp(v, "0") != 0;
+}
+std::atomic<bool> g_debug{env_debug()};
+thread_local const char *t_dbg_kernel = nullptr;
+thread_local hipError_t t_dbg_err = hipSuccess;
+
+}  // namespace
+
+// Debug mode, after the launches of one Scope: their launch error, else what
+// synchronising the stream reports (a fault in them or in earlier work).
+void debug_check(const char *name, hipStream_t s)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess && t_dbg_err == hipSuccess) {
+        t_dbg_err = e;
+        t_dbg_kernel = name;
+    }
+}
+
+void debug_after(const char *name, hipStream_t s)
+{
+    if (g_debug.load(std::memory_order_relaxed)) debug_check(name, s);
+}
+
+namespace {
 
 hipEvent_t take(int dev)
 {
@@ -92,14 +127,26 @@ Scope::Scope(const char *name, hipStream_t s) : name_(name), s_(s)
 
 Scope::~Scope()
 {
-    if (!start_) return;
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (hipEventRecord(stop_, s_) == hipSuccess) {
-        g_pending.push_back({name_, dev_, start_, stop_});
-    } else {
-        give(dev_, start_);
-        give(dev_, stop_);
+    if (start_) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (hipEventRecord(stop_, s_) == hipSuccess) {
+            g_pending.push_back({name_, dev_, start_, stop_});
+        } else {
+            give(dev_, start_);
+            give(dev_, stop_);
+        }
     }
+    if (g_debug.load(std::memory_order_relaxed)) debug_check(name_, s_);
+}
+
+bool debug_take(const char **kernel, hipError_t *err)
+{
+    if (t_dbg_err == hipSuccess) return false;
+    *kernel = t_dbg_kernel;
+    *err = t_dbg_err;
+    t_dbg_err = hipSuccess;
+    t_dbg_kernel = nullptr;
+    return true;
 }
 
 }  // namespace prof
@@ -108,6 +155,14 @@ Scope::~Scope()
 using namespace maglev::prof;
 
 extern "C" {
+
+maglev_status_t maglev_debug_enable(int on)
+{
+    g_debug.store(on != 0);
+    return MAGLEV_OK;
+}
+
+int maglev_debug_enabled(void) { return g_debug.load() ? 1 : 0; }
 
 maglev_status_t maglev_profile_enable(int on, const char *only)
 {

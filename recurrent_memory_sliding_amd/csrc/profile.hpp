@@ -4,6 +4,12 @@
 // launch records one event before and one after it on the launch stream. The
 // pairs are resolved and summed per kernel name by maglev_profile_count().
 // Launches on a stream under graph capture are not recorded.
+//
+// Debug mode (the environment variable MAGLEV_DEBUG set to a value other than
+// "0" when the library loads, or maglev_debug_enable): when a Scope ends, it
+// also takes the launch error and synchronises its stream (not under graph
+// capture); the first failure on this thread is kept, with the Scope's kernel
+// name, for the C-ABI layer to report.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +30,11 @@ private:
     hipEvent_t start_ = nullptr, stop_ = nullptr;
     int dev_ = -1;
 };
+
+// Debug mode only: the check a Scope makes when it ends, for launches outside one.
+void debug_after(const char *name, hipStream_t s);
+// Takes (and clears) the failure debug mode recorded on this thread; false if none.
+bool debug_take(const char **kernel, hipError_t *err);
 
 }  // namespace prof
 }  // namespace maglev

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.maglev_abi_version() == 5
+    assert L.maglev_abi_version() == 6
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
     assert L.maglev_status_string(WORKSPACE) == b"MAGLEV_ERR_WORKSPACE"
     assert L.maglev_status_string(99) == b"MAGLEV_ERR_UNKNOWN"
@@ -381,3 +381,23 @@ def test_no_alloc_loss_validation(L):
     assert call(mp=FAKE_ODD) == MISALIGNED
     assert call(dm=FAKE_ODD) == MISALIGNED
     assert call(acc=8) == INVALID
+
+
+def test_debug_mode_switch(L):
+    """maglev_debug_enable switches the debug mode without touching a GPU;
+    MAGLEV_DEBUG in the environment sets it at load (checked in a child)."""
+    import subprocess
+    import sys
+    before = L.maglev_debug_enabled()
+    try:
+        assert L.maglev_debug_enable(1) == 0 and L.maglev_debug_enabled() == 1
+        assert L.maglev_debug_enable(0) == 0 and L.maglev_debug_enabled() == 0
+    finally:
+        L.maglev_debug_enable(before)
+    code = ("import ctypes, sys; L = ctypes.CDLL(sys.argv[1]); "
+            "print(L.maglev_debug_enabled())")
+    for env, want in (("1", "1"), ("0", "0"), ("", "0")):
+        out = subprocess.run([sys.executable, "-c", code, rms.library_path()],
+                             env=dict(os.environ, MAGLEV_DEBUG=env), capture_output=True,
+                             text=True, check=True).stdout.strip()
+        assert out == want, (env, out)

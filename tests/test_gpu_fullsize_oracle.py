@@ -119,6 +119,21 @@ def test_d20_shared_projection_stack_every_element():
         check_dw(n, t, sg[n], sh.dtype)
 
 
+def test_d20_gated_shared_projection_stack_every_element():
+    """Two gated d20 layers (B=4) over one projection of the shifted m': every
+    layer's o, dq, dk, dv and four gate-logit gradients, and the shared dm',
+    dW_Km, dW_Vm, with the bars of the small gated stacks."""
+    from test_gpu_shared_gated import compare, run_gpu
+    sh = wl.D20_STACK
+    L = 2
+    flush("gated shared-projection stack, %d layers at %s" % (L, sh))
+    raws = [wl.layer_inputs(sh, 3200 + l, grads=True) for l in range(L)]
+    gates = [wl.gate_vectors(sh.H, sh.Dh, 3200 + l, std=0.7) for l in range(L)]
+    got, shared_got = run_gpu(sh, raws, gates)
+    flush("  oracle")
+    compare(sh, raws, gates, got, shared_got)
+
+
 def test_d20_full_attention_layer_backward_every_element():
     """The prefiller's full-attention layer (no injection) at B=8, T=W=2048:
     the GPU runs the whole batch; sequences are independent, so the oracle

@@ -141,6 +141,30 @@ def test_backward_is_deterministic():
         assert torch.equal(a[n], b[n]), n
 
 
+def test_debug_mode_gives_the_same_results():
+    """Debug mode (a synchronisation and an error check after every launch)
+    returns OK and changes no result: forward, backward and loss bit-equal."""
+    sh = shape(B=2, T=333, W=100)
+    inp = wl.layer_inputs(sh, 12, grads=True)
+
+    def run():
+        g, km, vm, o, lse = gpu_forward(inp, sh)
+        gr = gpu_backward(g, km, vm, o, lse, sh)
+        loss, dm, dmp = rms.maglev_consistency_loss(g["m"], g["m_prime"], sh.lam)
+        torch.cuda.synchronize()
+        return dict(gr, o=o, lse=lse, loss=loss, dm=dm, dmp=dmp)
+
+    plain = run()
+    rms.maglev_debug_enable(True)
+    try:
+        assert rms.maglev_debug_enabled()
+        dbg = run()
+    finally:
+        rms.maglev_debug_enable(False)
+    for n in plain:
+        assert torch.equal(plain[n], dbg[n]), n
+
+
 def test_loss_bf16_and_accumulate():
     sh = shape(B=3, T=500, d=1280)
     inp = wl.layer_inputs(sh, 12)

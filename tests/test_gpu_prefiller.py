@@ -114,3 +114,43 @@ def test_full_attention_beyond_stored_score_tiles_dh128():
     """T = W = 2600 (82 query tiles a key tile, above the 80 whose dS the
     dK/dV pass stores): the dQ pass recomputes the scores instead."""
     run_case(shape(B=1, T=2600, W=2600, H=1, Dh=128, d=128), 88)
+
+
+# Reach of a non-finite entry in the bf16 path beyond the band's edges: waves of
+# 32 queries take whole key tiles of at most 64 keys, and the scores are masked
+# (not the value operands), so 0 * NaN reaches at most 31 + 63 rows further.
+NONFINITE_REACH_BF16 = 94
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_nonfinite_value_reach(dtype):
+    """A NaN in one value row j of one head: every row whose band holds j is
+    non-finite (as in the oracle); in bf16 no row further than
+    NONFINITE_REACH_BF16 beyond the band's edges is, in float32 (one key at a
+    time) exactly the band; every finite row matches the oracle run with that
+    value row zeroed, and the other head is untouched."""
+    sh = shape(B=1, T=700, W=100, H=2, Dh=128, dtype=dtype)
+    flush("non-finite value row, %s" % (sh,))
+    inp = wl.layer_inputs(sh, 83)
+    j, hb = 350, 1
+    v = inp["v"].clone()
+    v[0, j, hb, 5] = float("nan")
+    g = {n: inp[n].cuda() for n in ("q", "k")}
+    o, _, _ = rms.maglev_attn_fwd(g["q"], g["k"], v.cuda(), sh.W)
+    torch.cuda.synchronize()
+    o = o.cpu().double().numpy()
+    hit = np.nonzero(~np.isfinite(o[0, :, hb, :]).all(axis=-1))[0]
+    band = np.arange(j, j + sh.W)
+    assert np.isin(band, hit).all()
+    reach = NONFINITE_REACH_BF16 if dtype == wl.BF16 else 0
+    assert hit.min() >= j - reach and hit.max() <= j + sh.W - 1 + reach, (hit.min(), hit.max())
+    flush("  non-finite rows %d..%d, band %d..%d" % (hit.min(), hit.max(), band[0], band[-1]))
+    assert np.isfinite(o[0, :, 1 - hb, :]).all()
+    clean = dict(inp)
+    vc = inp["v"].clone()
+    vc[0, j, hb, :] = 0
+    clean["v"] = vc
+    ro, _, _, _ = plain_oracle(clean, sh, False)
+    ok = np.ones(sh.T, bool)
+    ok[hit] = False
+    check_act("o (finite rows)", o[0][ok][None], ro[0][ok][None], dtype)

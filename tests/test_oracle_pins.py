@@ -561,3 +561,28 @@ def test_shared_projection_stack_matches_finite_differences():
             gname = "dgate" if name == "gate_logit" else "d" + name
             np.testing.assert_allclose(per[l][gname], fd(layers[l], name), rtol=1e-6, atol=1e-7,
                                        err_msg="layer %d %s" % (l, gname))
+
+
+def test_nonfinite_value_reaches_exactly_the_band():
+    """The oracle's reading of the band: query i attends to keys
+    i-W+1..i only, so a NaN in value row j reaches exactly the outputs of
+    rows j..j+W-1 (and of no other head); the other rows are what they are
+    with that value row zeroed."""
+    sh = wl.LayerShape(B=1, T=40, W=6, d=8, H=2, Dh=4, dtype=wl.F32)
+    raw = wl.layer_inputs(sh, 81)
+    q, k, v = (oracle.f64(raw[n]) for n in ("q", "k", "v"))
+    zero = np.zeros_like(q)
+    off = np.full(sh.H, -np.inf)
+    j = 17
+    bad = v.copy()
+    bad[0, j, 1, 2] = np.nan
+    o, _ = oracle.swa_inject_fwd(q, k, bad, zero, zero, off, sh.W)
+    clean = v.copy()
+    clean[0, j, 1, :] = 0.0
+    oc, _ = oracle.swa_inject_fwd(q, k, clean, zero, zero, off, sh.W)
+    hit = ~np.isfinite(o[0, :, 1, :]).all(axis=-1)
+    assert np.array_equal(np.nonzero(hit)[0], np.arange(j, j + sh.W))
+    assert np.isfinite(o[0, :, 0, :]).all()
+    rest = np.ones(sh.T, bool)
+    rest[j:j + sh.W] = False
+    np.testing.assert_array_equal(o[0, rest], oc[0, rest])

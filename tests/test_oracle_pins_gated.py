@@ -165,6 +165,63 @@ def test_gated_backward_matches_finite_differences(W, pos0, base, eps):
     assert not g["dm_prime"][0, -1].any()
 
 
+def _gated_stack_objective(layers, shared, W, eps):
+    H, Dh = layers[0]["q"].shape[2], layers[0]["q"].shape[3]
+    kp, vm = oracle.mem_project(shared["m_prime"], shared["W_Km"], shared["W_Vm"], H, Dh, shift=1)
+    tot = 0.0
+    for x in layers:
+        kx, vx = oracle.gated_entries(x["k"], x["v"], kp, vm, x["gates"], eps=eps)
+        o, _ = oracle.swa_attend_fwd(x["q"], kx, vx, W)
+        tot += float(np.sum(o * x["dO"]))
+    return tot
+
+
+def test_gated_shared_projection_stack_matches_finite_differences():
+    """Two gated layers over one projection of the same m' by the same
+    weights, each with its own q, k, v, gates and dO: every gradient of the
+    summed objective, the forward composed from the projection, the gated mix
+    and the attention oracle (not from the backward's own composition)."""
+    sh = wl.LayerShape(B=1, T=10, W=3, d=8, H=2, Dh=4, dtype=wl.F32)
+    eps = 1e-6
+    raws = [wl.layer_inputs(sh, seed=70 + l, grads=True) for l in range(2)]
+    layers = []
+    for l, r in enumerate(raws):
+        x = {n: oracle.f64(r[n]) for n in ("q", "k", "v", "dO")}
+        x["gates"] = {n: oracle.f64(a) for n, a in wl.gate_vectors(sh.H, sh.Dh, 70 + l, std=1.0).items()}
+        layers.append(x)
+    shared = {n: oracle.f64(raws[0][n]) for n in ("m_prime", "W_Km", "W_Vm")}
+    per, sg = oracle.swa_inject_bwd_shared_gated(layers, shared["m_prime"], shared["W_Km"],
+                                                 shared["W_Vm"], sh.W, eps=eps)
+    h = 1e-6
+
+    def fd(store, name):
+        flat = store[name].reshape(-1)
+        out = np.empty(flat.size)
+        for i in range(flat.size):
+            keep = flat[i]
+            flat[i] = keep + h
+            fp = _gated_stack_objective(layers, shared, sh.W, eps)
+            flat[i] = keep - h
+            fm = _gated_stack_objective(layers, shared, sh.W, eps)
+            flat[i] = keep
+            out[i] = (fp - fm) / (2 * h)
+        return out.reshape(store[name].shape)
+
+    for name, gname in (("m_prime", "dm_prime"), ("W_Km", "dW_Km"), ("W_Vm", "dW_Vm")):
+        np.testing.assert_allclose(sg[gname], fd(shared, name), rtol=1e-6, atol=1e-7, err_msg=gname)
+    for l in range(2):
+        for name in ("q", "k", "v"):
+            np.testing.assert_allclose(per[l]["d" + name], fd(layers[l], name), rtol=1e-6,
+                                       atol=1e-7, err_msg="layer %d d%s" % (l, name))
+        for n in NAMES:
+            np.testing.assert_allclose(per[l]["d" + n], fd(layers[l]["gates"], n), rtol=1e-6,
+                                       atol=1e-7, err_msg="layer %d d%s" % (l, n))
+    # both layers really reach the shared parameters
+    _, first = oracle.swa_inject_bwd_shared_gated(layers[:1], shared["m_prime"], shared["W_Km"],
+                                                  shared["W_Vm"], sh.W, eps=eps)
+    assert np.max(np.abs(sg["dW_Km"] - first["dW_Km"])) > 1e-3
+
+
 def test_gated_backward_matches_torch_autograd_dense():
     """Torch fp64 autograd through a dense masked-softmax layer with the gated
     mix written from library ops (torch.rsqrt, complex rotation, sigmoid)."""
