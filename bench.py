@@ -531,6 +531,7 @@ def bench_loss_head(N, d, V, steps, warmup):
         "lm_logits": (gemm, nd + 2.0 * V * d + 4.0 * N * V),
         "head_ce": (0.0, 4.0 * N * V + 2.0 * N * V + 8.0 * N),
         "lm_dm": (gemm, 2.0 * N * V + 2.0 * V * d + 4.0 * N * d),
+        "lm_dm_transpose": (0.0, 4.0 * V * d),
         "lm_du": (gemm, 2.0 * N * V + nd + 4.0 * V * d),
         "head_norm": (0.0, 2.0 * nd + 4.0 * N),
         "head_norm_bwd": (0.0, nd + 8.0 * N * d + 4.0 * N),

@@ -159,6 +159,7 @@ struct HeadWorkspace {
     float *rowsum = nullptr;   // [N, column tiles] partial sums of exp(logit)
     void *dz = nullptr;        // [N, V] dtype, gradient w.r.t. the raw logits
     float *dm = nullptr;       // [N, d] gradient w.r.t. m
+    void *ut = nullptr;        // [d, V] bf16: U transposed for the dm product (bf16 path)
     void *loss_ws = nullptr;   // consistency-loss partial sums
 };
 // Bytes of workspace; with base != nullptr, also carves it into *L.

@@ -206,6 +206,7 @@ size_t lm_head_workspace_bytes(int64_t N, int d, int64_t V, int dtype, HeadWorks
     const size_t oZ = take((size_t)N * V * esz);
     const size_t oM = take((size_t)N * d * sizeof(float));
     const size_t oS = take(loss_workspace_bytes(N, d));
+    const size_t oU = take(dtype == MAGLEV_BF16 ? (size_t)d * V * 2 : 0);
     L->rstd = base ? reinterpret_cast<float *>(base + oR) : nullptr;
     L->ce = base ? reinterpret_cast<float *>(base + oC) : nullptr;
     L->logits = base ? reinterpret_cast<float *>(base + oL) : nullptr;
@@ -213,6 +214,7 @@ size_t lm_head_workspace_bytes(int64_t N, int d, int64_t V, int dtype, HeadWorks
     L->dz = base ? static_cast<void *>(base + oZ) : nullptr;
     L->dm = base ? reinterpret_cast<float *>(base + oM) : nullptr;
     L->loss_ws = base ? static_cast<void *>(base + oS) : nullptr;
+    L->ut = base && dtype == MAGLEV_BF16 ? static_cast<void *>(base + oU) : nullptr;
     return off;
 }
 
@@ -250,7 +252,7 @@ static hipError_t lm_head_t(int64_t N, int d, int64_t V, float cap, float eps, f
     }
     if (grads) {
         if constexpr (sizeof(T) == 2) {
-            mfma::launch_lm_dm_bf16(N, V, d, ws.dz, Uv, ws.dm, s);
+            mfma::launch_lm_dm_bf16(N, V, d, ws.dz, Uv, ws.ut, ws.dm, s);
             if (dU) mfma::launch_lm_du_bf16(N, V, d, ws.dz, m, dU, (acc & 2u) != 0, s);
         } else {
             const float *dz = static_cast<const float *>(ws.dz);

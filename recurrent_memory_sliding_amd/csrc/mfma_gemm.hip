@@ -678,6 +678,24 @@ struct LmDm {
         *reinterpret_cast<f32x4 *>(dm + row * N + n) = x;
     }
 };
+// dm = dz U with U read from its transposed copy ut [d][V], so that both
+// operands are K-major (256 x 320 tiles take K-major operands only).
+struct LmDmT {
+    static constexpr bool A_KMAJOR = true, B_KMAJOR = true;
+    const bf16 *dz, *ut;
+    float *dm;
+    int64_t M, N, K, T;
+    static constexpr int64_t a_kseg = 0, b_kseg = 0, a_ld = 0, b_ld = 0;
+    MAGLEV_DEV const bf16 *a_ptr(int64_t row, int64_t k) const { return dz + row * K + k; }
+    MAGLEV_DEV const bf16 *b_ptr(int64_t n, int64_t k) const { return ut + n * K + k; }
+    MAGLEV_DEV const bf16 *a_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV const bf16 *b_lin(int64_t, int64_t) const { return nullptr; }
+    MAGLEV_DEV void store(int64_t row, int64_t, int64_t n, float x, int) const { dm[row * N + n] = x; }
+    MAGLEV_DEV void store4(int64_t row, int64_t, int64_t n, f32x4 x, int) const
+    {
+        *reinterpret_cast<f32x4 *>(dm + row * N + n) = x;
+    }
+};
 struct LmDu {
     static constexpr bool A_KMAJOR = false, B_KMAJOR = false;
     const bf16 *dz, *m;
@@ -740,6 +758,37 @@ static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const 
                        p, kper, group_m);
 }
 
+// out[c][r] = in[r][c] for a bf16 [R][C] matrix (C and R multiples of 8),
+// one workgroup per 64 x 64 block staged through LDS, so that both the reads
+// and the writes are 16-byte runs.
+__global__ __launch_bounds__(256) void transpose_bf16(const bf16 *in, bf16 *out, int64_t R, int C)
+{
+    __shared__ float tile[64][65];
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int c0 = blockIdx.x * 64;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q;   // 512 chunks of 8: row c / 8, chunk c % 8
+        const int rr = c >> 3, cc = c0 + 8 * (c & 7);
+        float x[8] = {};
+        if (r0 + rr < R && cc < C) load8(in + (r0 + rr) * C + cc, x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tile[8 * (c & 7) + u][rr] = x[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int c = threadIdx.x + 256 * q;   // output row c0 + c / 8, chunk c % 8 of r
+        const int cc = c >> 3;
+        const int64_t r = r0 + 8 * (c & 7);
+        if (c0 + cc >= C || r >= R) continue;
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = tile[cc][8 * (c & 7) + u];
+        store8(out + (int64_t)(c0 + cc) * R + r, x);
+    }
+}
+
 // Loss-head products, timed at N = 16384, d = 1280, V = 65536 with random
 // operands: the logits (a short reduction, d = 1280, like the projection) on
 // 256 x 320 tiles with the single-barrier loop (2.95 ms against 3.28 ms for
@@ -765,9 +814,27 @@ void launch_lm_logits_bf16(int64_t N, int64_t V, int d, float cap, const void *m
     run_gemm<LmLogitsCfg>(p, 1, p.K, s, "lm_logits", 8);
 }
 
-void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, float *dm,
-                       hipStream_t s)
+void launch_lm_dm_bf16(int64_t N, int64_t V, int d, const void *dz, const void *u, void *ut,
+                       float *dm, hipStream_t s)
 {
+    if (proj_big_tiles(N, d)) {
+        // 256 x 320 tiles over K-major operands: U transposed once into ut
+        // [d][V]; then each row block of dz is read by d / 320 column tiles
+        // (four at d = 1280) instead of d / 128, in one round of the CUs
+        {
+            prof::Scope ts("lm_dm_transpose", s);
+            hipLaunchKernelGGL(transpose_bf16, dim3((unsigned)((d + 63) / 64), (unsigned)((V + 63) / 64)),
+                               dim3(256), 0, s, static_cast<const bf16 *>(u),
+                               static_cast<bf16 *>(ut), V, d);
+        }
+        LmDmT p;
+        p.dz = static_cast<const bf16 *>(dz);
+        p.ut = static_cast<const bf16 *>(ut);
+        p.dm = dm;
+        p.M = N; p.N = d; p.K = V; p.T = 0;
+        run_gemm<ProjBigCfg>(p, 1, p.K, s, "lm_dm", 8);
+        return;
+    }
     LmDm p;
     p.dz = static_cast<const bf16 *>(dz);
     p.u = static_cast<const bf16 *>(u);

@@ -161,3 +161,24 @@ def test_head_full_size_sampled():
     mask = torch.ones(N, dtype=torch.bool)
     mask[torch.as_tensor(rows)] = False
     assert not torch.any(dh.cpu()[mask])
+
+
+def test_head_transposed_dm_path_ragged():
+    """N = 16400 (a ragged last row tile of 256), d = 1280, V = 1000 (not a
+    multiple of the transpose's 64-row blocks): sizes that take the dm
+    product on 256 x 320 tiles over U transposed. Every target valid, so
+    dh of each sampled row is (S/N) times the oracle's over the sampled rows
+    alone (property (1) of the full-size test), the last row included."""
+    N, d, V = 16400, 1280, 1000
+    x = wl.head_inputs(N, d, V, 13, wl.BF16)
+    rng = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, 255, 16383, 16384, N - 1], rng.integers(0, N, 8)]))
+    S = rows.size
+    tol = TOL[wl.BF16]
+    flush("loss head transposed dm path N=%d d=%d V=%d" % (N, d, V))
+    loss, m, dh, dU = gpu_head(x, 0.5, True)
+    ref = oracle.lm_head(oracle.f64(x["h"])[rows], oracle.f64(x["U"]), x["targets"].numpy()[rows],
+                         m_prime=oracle.f64(x["m_prime"])[rows], lam=0.5)
+    f = S / N
+    for i, n in enumerate(rows):
+        check("dh row %d" % n, dh[int(n)], f * ref["dh"][i], tol, rel_scale(f * ref["dh"][i]))
