@@ -55,7 +55,9 @@ def build(jobs: int = 0) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+    # only the maglev_* C functions are exported (maglev.map)
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950",
+           "-Wl,--version-script=" + os.path.join(CSRC, "maglev.map"), "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

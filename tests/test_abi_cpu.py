@@ -42,6 +42,17 @@ def test_library_exports_every_declared_symbol(L):
     assert not missing, missing
 
 
+def test_library_exports_nothing_else():
+    """The dynamic symbol table holds the declared C functions and nothing of
+    the library's internals (kernels, launchers, helpers)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rms.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    names = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    ours = {n for n in names if "maglev" in n}
+    assert ours == set(declared_functions()), sorted(ours ^ set(declared_functions()))
+
+
 def test_abi_version_and_status_strings(L):
     assert L.maglev_abi_version() == 6
     assert L.maglev_status_string(OK) == b"MAGLEV_OK"
