@@ -559,8 +559,9 @@ hipError_t launch_bwd_shared(const Geom &g, const void *q, const void *kx, const
                              float *dkm, float *dvm, float *dgate, unsigned acc,
                              const BwdWorkspace &ws, const float2 *rope, hipStream_t s)
 {
-    if (g.N() == 0) {
-        if (!(acc & 4u)) hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, s, dgate, (int64_t)g.H);
+    if (g.N() == 0) {   // no tokens: only dgate is written (zero), unless it accumulates
+        if (acc & 4u) return hipSuccess;
+        hipLaunchKernelGGL(fill_zero, dim3(1), dim3(256), 0, s, dgate, (int64_t)g.H);
         return hipGetLastError();
     }
     hipError_t e = launch_attn_bwd(g, q, kx, vx, o, lse, dO, dq, dk, dv, ws, rope, s);
@@ -586,10 +587,10 @@ hipError_t launch_bwd_shared_gated(const Geom &g, const void *q, const void *kx,
                                    float *dvm, float *dgates, unsigned acc, const BwdWorkspace &ws,
                                    const float2 *rope, hipStream_t s)
 {
-    if (g.N() == 0) {
-        if (!(acc & 4u))
-            hipLaunchKernelGGL(fill_zero, dim3((unsigned)((4 * g.HD() + 255) / 256)), dim3(256), 0,
-                               s, dgates, (int64_t)4 * g.HD());
+    if (g.N() == 0) {   // no tokens: only dgates is written (zero), unless it accumulates
+        if (acc & 4u) return hipSuccess;
+        hipLaunchKernelGGL(fill_zero, dim3((unsigned)((4 * g.HD() + 255) / 256)), dim3(256), 0, s,
+                           dgates, (int64_t)4 * g.HD());
         return hipGetLastError();
     }
     // 1. attention backward: dq, and the gradients of the mixed entries into dk/dv

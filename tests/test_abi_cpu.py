@@ -284,6 +284,42 @@ def test_shared_projection_validation(L):
     assert L.maglev_mem_project_bwd(ctypes.byref(g), *bad, 0, FAKE, pneed, None) == INVALID
 
 
+def test_gated_shared_projection_validation(L):
+    g = geom(B=4, T=2048, H=10, Dh=128, d=1280, W=512)
+    ff, vp = ctypes.c_float, ctypes.c_void_p
+    mix = lambda g, a=(FAKE,) * 5, eps=1e-6, out=(FAKE, FAKE): L.maglev_mix_entries_gated(
+        ctypes.byref(g), *a, ff(eps), *out, None)     # k v kproj vmem gates | kmix vmix
+    assert mix(geom(Dh=96)) == UNSUPPORTED
+    assert mix(geom(H=40)) == UNSUPPORTED              # H*Dh above 4096
+    assert mix(g, eps=-1.0) == INVALID
+    assert mix(g, a=(FAKE,) * 4 + (None,)) == INVALID  # gates
+    assert mix(g, out=(FAKE, FAKE_ODD)) == MISALIGNED
+    assert mix(geom(B=0)) == OK
+    need = L.maglev_swa_inject_bwd_shared_gated_workspace(ctypes.byref(g))
+    # the attention scratch and the gate partials, no projection scratch
+    assert L.maglev_attn_bwd_workspace(ctypes.byref(g)) < need
+    assert need < L.maglev_swa_inject_bwd_gated_workspace(ctypes.byref(g))
+    assert L.maglev_swa_inject_bwd_shared_gated_workspace(ctypes.byref(geom(H=40))) == 0
+    head = [FAKE] * 8                 # q kmix vmix k v kproj vmem gates
+    tail = [FAKE] * 9                 # o lse dO dq dk dv dkproj dvmem dgates
+    call = lambda h=head, eps=1e-6, t=tail, acc=0, ws=FAKE, n=need: \
+        L.maglev_swa_inject_bwd_shared_gated(ctypes.byref(g), *h, ff(eps), *t, acc, ws, n, None)
+    assert call(acc=2) == INVALID     # only bits 0 and 2
+    assert call(eps=float("nan")) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(n=need - 1) == WORKSPACE
+    assert call(ws=FAKE_ODD) == MISALIGNED
+    bad = list(head); bad[7] = None   # gates
+    assert call(h=bad) == INVALID
+    bad = list(tail); bad[8] = None   # dgates
+    assert call(t=bad) == INVALID
+    bad = list(tail); bad[6] = None   # dkproj
+    assert call(t=bad) == INVALID
+    assert L.maglev_swa_inject_bwd_shared_gated(ctypes.byref(geom(B=0)), *([None] * 7), FAKE,
+                                                ff(1e-6), *([None] * 8), FAKE, 4, None, 0,
+                                                None) == OK   # dgates kept (bit 2), nothing read
+
+
 def test_loss_head_workspace_and_validation(L):
     need = L.maglev_lm_head_workspace(16384, 1280, 65536, 1)
     # float32 logits and bf16 dz dominate: 6 N V bytes
