@@ -800,9 +800,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // all eight operand reads are issued before the first product waits
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, NF, 0);
-        // this tile's statistics: loaded before the last DMA issued
-        if (it + ST - 2 < nt) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
+        // this tile's statistics: issued before the last step's tile loads
+        // (PER, when there were any) and its four dS stores
+        if (it + ST - 2 < nt) wait_vmcnt<PER + 4>();
+        else wait_vmcnt<4>();
         if (hf == 0) {
             // every (query, key) pair of this block in the band: no mask
             const bool interior = (i0 >= kw0 + 31) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
@@ -828,8 +829,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         for (int q4 = 0; q4 < 4; ++q4)
             X[par][pr][hf][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
         // the next tile's stage (issued one iteration ago) lands before the
-        // barrier publishes it
-        wait_vmcnt<0>();
+        // barrier publishes it; only the last step's four dS stores, issued
+        // after those loads, may still be in flight
+        wait_vmcnt<4>();
         __syncthreads();
 
         // the transposed operands of this tile's eight products, read before
@@ -859,34 +861,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
             pf[t] = acc_to_operand(P, t);
             dsf[t] = acc_to_operand(dS, t);
         }
-        // dS of this 32 x 32 tile as the dK product takes it (the bf16 operand
-        // registers themselves), for the dQ pass: [key][query] tiles of
-        // 64-byte rows. Lane l32 holds key kw0 + l32; operand t holds queries
-        // i0 + 16t + 4g + (0..3) and i0 + 16t + 8 + 4g + (0..3), bytes
+        // The next tile's statistics, the tile loads two steps ahead, then
+        // this tile's dS stores, last, so that no wait in the loop waits for a
+        // store: the vector memory counter counts loads and stores in issue
+        // order. dS of this 32 x 32 tile as the dK product takes it (the bf16
+        // operand registers themselves) goes to the dQ pass as [key][query]
+        // tiles of 64-byte rows. Lane l32 holds key kw0 + l32; operand t holds
+        // queries i0 + 16t + 4g + (0..3) and i0 + 16t + 8 + 4g + (0..3), bytes
         // 32t + 8g and 32t + 16 + 8g of the row: four 8-byte buffer stores
-        // from the pair's first wave, through a per-tile descriptor (uniform
-        // registers) and one 32-bit lane offset, so that they take no
-        // registers the loop needs. Tiles outside the stored range (a query
-        // tile before the keys, or beyond the window) are not stored. The
-        // stores go out before this step's statistics and tile loads: the
-        // vector memory counter counts stores too, and the next step's waits
-        // for those loads would otherwise wait for the younger stores.
-        if (dso && hf == 0) {
-            const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
-            if (jj >= 0 && jj < nK) {
-                bf16 *tile = dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024;
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
-                const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
-                const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
-            }
-        }
+        // through a per-tile descriptor (uniform registers) and one 32-bit
+        // lane offset, so that they take no registers the loop needs. Every
+        // wave issues the four stores on every tile, so that the counts the
+        // waits above leave in flight are exact; where nothing is stored (the
+        // pair's second wave, a query tile before the keys or beyond the
+        // window, no dS storage) the descriptor holds no bytes and the bounds
+        // check drops them.
         if (it + 1 < nt) load_stats(it + 1, next);
         if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
+        {
+            const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
+            const bool st = dso && hf == 0 && jj >= 0 && jj < nK;
+            bf16 *tile = st ? dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024 : dk;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, st ? 2048 : 0, kBufferWord3);
+            const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
+            const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
