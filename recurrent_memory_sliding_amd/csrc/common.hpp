@@ -137,6 +137,14 @@ MAGLEV_DEV void dma16(const bf16 *src, bf16 *lds_wave_base)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
                  : "memory", "m0");
 }
+// 4 bytes a lane from global memory straight into LDS: lane L's word lands at
+// lds_wave_base + 4 L (global_load_lds_dword); otherwise as dma16.
+MAGLEV_DEV void dma4(const float *src, void *lds_wave_base)
+{
+    const unsigned m = (unsigned)(uintptr_t)(lds_bf16 *)static_cast<bf16 *>(lds_wave_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).

@@ -26,6 +26,8 @@
 // reads (4 rows x 64 bytes a half-wave pass) hit every LDS bank once. Key
 // tiles wholly outside a wave's band are skipped, and only tiles that
 // straddle a band edge are masked.
+#include <type_traits>
+
 #include "common.hpp"
 #include "mfma_kernels.hpp"
 #include "profile.hpp"
@@ -745,35 +747,44 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
             dma16(in ? obase + off : g_attn_zero, ot + ins * 512);
         }
     };
-    // The statistic of this lane's 16 queries of tile it that the wave's role
-    // needs: lse2 (first wave, for P) or D (second wave, which sends dP - D).
-    // Rows are padded to Tp, so a tile never leaves its row. Two register
-    // sets, one per tile parity, so that no copy is needed. (The compiler
-    // cannot count the tile loads, which are inline assembly, so its wait
-    // for these loads also covers the tile loads issued after them; staging
-    // the statistics in LDS instead would need more LDS than two workgroups
-    // a CU leave.)
+    // The statistics of tile it that the wave's role needs, lse2 (first wave,
+    // for P) or D (second wave, which sends dP - D) of its 32 queries, travel
+    // like the tiles: the wave loads them straight into its own exchange slot
+    // of the tile's parity (free from the previous step's barrier on, and
+    // overwritten by the wave itself once it has read them), then reads its
+    // 16 values from there. So the loop holds no load the compiler tracks,
+    // and none of its waits covers the tile loads behind them. Rows are
+    // padded to Tp, so a tile never leaves its row; lanes 32..63 load copies
+    // of lanes 0..31.
+    const float *srow = hf ? drow : lrow;
+    auto dma_stats = [&](int it) {
+        dma4(srow + j0 + it * QT + l32, &X[it & 1][pr][hf][0][0]);
+    };
     struct Stats {
         f32x4 v[4];
     };
-    const float *srow = hf ? drow : lrow;
-    auto load_stats = [&](int it, Stats &st) {
-        const int i0 = j0 + it * QT;
+    auto read_stats = [&](int it, Stats &st) {
+        const float *sl = reinterpret_cast<const float *>(&X[it & 1][pr][hf][0][0]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            st.v[q4] = *reinterpret_cast<const f32x4 *>(srow + i0 + 8 * q4 + 4 * g);
+            st.v[q4] = *reinterpret_cast<const f32x4 *>(sl + 8 * q4 + 4 * g);
     };
-    Stats sa, sb;
     // Tiles 0 .. ST-2 and the statistics of tile 0 in flight; all landed and
     // tile 0 visible to every wave.
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nt) issue(s0);
-    load_stats(0, sa);
+    if (nt > 0) dma_stats(0);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 
-    f32x16 dva[2], dka[2];   // blocks hf and hf + 2 of 32 channels
+    // The rest runs once per role, the role a compile-time constant (R = 0:
+    // S, P and the lse2 statistics; R = 1: dP - D and the D statistics),
+    // picked by a wave-uniform branch, so that no per-lane selects between
+    // the roles' operands remain.
+    auto run = [&](auto role) {
+    constexpr int R = decltype(role)::value;
+    f32x16 dva[2], dka[2];   // blocks R and R + 2 of 32 channels
 #pragma unroll
     for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
@@ -781,14 +792,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
 
     // this lane's byte offset in a stored dS tile: key row l32, queries 4 g..
     const int ds_voff = l32 * 64 + 8 * g;
-    auto tile_step = [&](int it, const Stats &cur, Stats &next) {
+    auto tile_step = [&](int it) {
         const int i0 = j0 + it * QT;
         const int buf = it % ST;
         const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+        // this tile's statistics: their load was issued before the last
+        // step's tile loads (PER, when there were any) and its four dS stores
+        if (it + ST - 2 < nt) wait_vmcnt<PER + 4>();
+        else wait_vmcnt<4>();
+        Stats cur;
+        read_stats(it, cur);
 
         // S (first wave) or dP (second wave); element e: query
         // i0 + 8(e/4) + 4g + e%4, key kj
-        const bf16 *rt = hf ? ot : qt;
+        const bf16 *rt = R ? ot : qt;
         f32x16 mine;
 #pragma unroll
         for (int e = 0; e < 16; ++e) mine[e] = 0.0f;
@@ -800,11 +817,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // all eight operand reads are issued before the first product waits
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, NF, 0);
-        // this tile's statistics: issued before the last step's tile loads
-        // (PER, when there were any) and its four dS stores
-        if (it + ST - 2 < nt) wait_vmcnt<PER + 4>();
-        else wait_vmcnt<4>();
-        if (hf == 0) {
+        if constexpr (R == 0) {
             // every (query, key) pair of this block in the band: no mask
             const bool interior = (i0 >= kw0 + 31) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
             if (interior) {
@@ -827,7 +840,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         const int par = it & 1;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            X[par][pr][hf][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
+            X[par][pr][R][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
         // the next tile's stage (issued one iteration ago) lands before the
         // barrier publishes it; only the last step's four dS stores, issued
         // after those loads, may still be in flight
@@ -841,18 +854,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int lb = 0; lb < 2; ++lb) {
-                trv[t][lb] = tile_tr<DH>(ot, t, hf + 2 * lb, lane);
-                trq[t][lb] = tile_tr<DH>(qt, t, hf + 2 * lb, lane);
+                trv[t][lb] = tile_tr<DH>(ot, t, R + 2 * lb, lane);
+                trq[t][lb] = tile_tr<DH>(qt, t, R + 2 * lb, lane);
             }
         f32x16 P, dS;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 o = X[par][pr][hf ^ 1][q4][lane];
+            const f32x4 o = X[par][pr][R ^ 1][q4][lane];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int e = 4 * q4 + u;
-                P[e] = hf ? o[u] : mine[e];
-                dS[e] = P[e] * (hf ? mine[e] : o[u]);   // P (dP - D)
+                P[e] = R ? o[u] : mine[e];
+                dS[e] = P[e] * (R ? mine[e] : o[u]);   // P (dP - D)
             }
         }
         bf16x8 pf[2], dsf[2];
@@ -876,11 +889,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // pair's second wave, a query tile before the keys or beyond the
         // window, no dS storage) the descriptor holds no bytes and the bounds
         // check drops them.
-        if (it + 1 < nt) load_stats(it + 1, next);
+        if (it + 1 < nt) dma_stats(it + 1);
         if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
         {
             const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
-            const bool st = dso && hf == 0 && jj >= 0 && jj < nK;
+            const bool st = dso && R == 0 && jj >= 0 && jj < nK;
             bf16 *tile = st ? dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024 : dk;
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, st ? 2048 : 0, kBufferWord3);
@@ -903,22 +916,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
     };
     for (int it = 0; it < nt; it += 2) {
-        tile_step(it, sa, sb);
-        if (it + 1 < nt) tile_step(it + 1, sb, sa);
+        tile_step(it);
+        if (it + 1 < nt) tile_step(it + 1);
     }
 
-    // Epilogue: element e of local block lb is channel 32 (hf + 2 lb) +
+    // Epilogue: element e of local block lb is channel 32 (R + 2 lb) +
     // 8(e/4) + 4g + e%4 of key kj.
     if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
         const float2 *cs =
-            (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) + 32 * hf : nullptr;
+            (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) + 32 * R : nullptr;
         scale_rotate_pair(dka[0], dka[1], cs, g, a.scale);
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                const int c = 32 * (hf + 2 * lb) + 8 * i4 + 4 * g;
+                const int c = 32 * (R + 2 * lb) + 8 * i4 + 4 * g;
                 bf16x4 k4, v4;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -929,6 +942,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
                 *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
             }
     }
+    };
+    if (hf) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
 }
 
 // Query-stationary pass: each wave owns 32 queries; key tiles of KT in the
