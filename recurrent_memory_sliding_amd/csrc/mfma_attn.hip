@@ -792,14 +792,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
 
     // this lane's byte offset in a stored dS tile: key row l32, queries 4 g..
     const int ds_voff = l32 * 64 + 8 * g;
+    bool stored = false;   // the last step issued its four dS stores
     auto tile_step = [&](int it) {
         const int i0 = j0 + it * QT;
         const int buf = it % ST;
         const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
         // this tile's statistics: their load was issued before the last
         // step's tile loads (PER, when there were any) and its four dS stores
-        if (it + ST - 2 < nt) wait_vmcnt<PER + 4>();
-        else wait_vmcnt<4>();
+        if (it + ST - 2 < nt) {
+            if (stored) wait_vmcnt<PER + 4>();
+            else wait_vmcnt<PER>();
+        } else {
+            if (stored) wait_vmcnt<4>();
+            else wait_vmcnt<0>();
+        }
         Stats cur;
         read_stats(it, cur);
 
@@ -844,7 +850,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // the next tile's stage (issued one iteration ago) lands before the
         // barrier publishes it; only the last step's four dS stores, issued
         // after those loads, may still be in flight
-        wait_vmcnt<4>();
+        if (stored) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
         __syncthreads();
 
         // the transposed operands of this tile's eight products, read before
@@ -883,26 +890,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // queries i0 + 16t + 4g + (0..3) and i0 + 16t + 8 + 4g + (0..3), bytes
         // 32t + 8g and 32t + 16 + 8g of the row: four 8-byte buffer stores
         // through a per-tile descriptor (uniform registers) and one 32-bit
-        // lane offset, so that they take no registers the loop needs. Every
-        // wave issues the four stores on every tile, so that the counts the
-        // waits above leave in flight are exact; where nothing is stored (the
-        // pair's second wave, a query tile before the keys or beyond the
-        // window, no dS storage) the descriptor holds no bytes and the bounds
-        // check drops them.
+        // lane offset, so that they take no registers the loop needs. Only the
+        // pair's first wave stores, and only tiles inside the stored range (not
+        // a query tile before the keys or beyond the window); `stored` (uniform)
+        // tells the waits of the next step how many stores are behind the loads
+        // they wait for.
         if (it + 1 < nt) dma_stats(it + 1);
         if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
         {
             const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
-            const bool st = dso && R == 0 && jj >= 0 && jj < nK;
-            bf16 *tile = st ? dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024 : dk;
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, st ? 2048 : 0, kBufferWord3);
-            const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
-            const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
+            stored = R == 0 && dso && jj >= 0 && jj < nK;
+            if (stored) {
+                bf16 *tile = dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024;
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
+                const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
+                const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
+            }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t)
