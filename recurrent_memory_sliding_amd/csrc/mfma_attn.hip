@@ -662,6 +662,18 @@ MAGLEV_DEV void scale_rotate_pair(f32x16 &lo, f32x16 &hi, const float2 *cs, int 
     }
 }
 
+// Calls f(it + U, U) for U = U0 .. N-1 while it + U < nt, each U a
+// compile-time constant.
+template <int U, int N, class F>
+MAGLEV_DEV void unrolled_steps(int it, int nt, F &f)
+{
+    if constexpr (U < N) {
+        if (it + U >= nt) return;
+        f(it + U, std::integral_constant<int, U>{});
+        unrolled_steps<U + 1, N>(it, nt, f);
+    }
+}
+
 // Key-stationary pass with each 32-key block split over a pair of waves
 // (Dh = 128): four waves, two pairs, 64 keys a workgroup; 32-query tiles of
 // Q^ and dO stream through LDS in ST stages. Per tile, the pair's first wave
@@ -731,8 +743,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     }
     wait_vmcnt<0>();
 
-    auto issue = [&](int it) {
-        const int buf = it % ST;
+    // tile `it` into stage `buf` (it mod ST)
+    auto issue = [&](int it, int buf) {
         const int i0 = j0 + it * QT;
         bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
 #pragma unroll
@@ -757,14 +769,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     // padded to Tp, so a tile never leaves its row; lanes 32..63 load copies
     // of lanes 0..31.
     const float *srow = hf ? drow : lrow;
-    auto dma_stats = [&](int it) {
-        dma4(srow + j0 + it * QT + l32, &X[it & 1][pr][hf][0][0]);
+    auto dma_stats = [&](int it, int par) {   // par = it mod 2
+        dma4(srow + j0 + it * QT + l32, &X[par][pr][hf][0][0]);
     };
     struct Stats {
         f32x4 v[4];
     };
-    auto read_stats = [&](int it, Stats &st) {
-        const float *sl = reinterpret_cast<const float *>(&X[it & 1][pr][hf][0][0]);
+    auto read_stats = [&](int par, Stats &st) {
+        const float *sl = reinterpret_cast<const float *>(&X[par][pr][hf][0][0]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             st.v[q4] = *reinterpret_cast<const f32x4 *>(sl + 8 * q4 + 4 * g);
@@ -773,8 +785,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     // tile 0 visible to every wave.
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
-        if (s0 < nt) issue(s0);
-    if (nt > 0) dma_stats(0);
+        if (s0 < nt) issue(s0, s0);
+    if (nt > 0) dma_stats(0, 0);
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
 
@@ -793,9 +805,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     // this lane's byte offset in a stored dS tile: key row l32, queries 4 g..
     const int ds_voff = l32 * 64 + 8 * g;
     bool stored = false;   // the last step issued its four dS stores
-    auto tile_step = [&](int it) {
+    // Step `it`; U = it mod 2 ST, a compile-time constant, so that the stage
+    // (it mod ST) and the exchange parity (it mod 2) are constants and every
+    // LDS address of the step is a lane base plus an immediate offset.
+    auto tile_step = [&](int it, auto u) {
+        constexpr int U = decltype(u)::value;
         const int i0 = j0 + it * QT;
-        const int buf = it % ST;
+        constexpr int buf = U % ST;
         const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
         // this tile's statistics: their load was issued before the last
         // step's tile loads (PER, when there were any) and its four dS stores
@@ -806,9 +822,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
             if (stored) wait_vmcnt<4>();
             else wait_vmcnt<0>();
         }
-        Stats cur;
-        read_stats(it, cur);
-
         // S (first wave) or dP (second wave); element e: query
         // i0 + 8(e/4) + 4g + e%4, key kj
         const bf16 *rt = R ? ot : qt;
@@ -820,8 +833,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         for (int s = 0; s < NF; ++s) rows[s] = tile_rows<DH>(rt, 0, s, lane);
 #pragma unroll
         for (int s = 0; s < NF; ++s) mine = mfma32(rows[s], kvf[s], mine);
-        // all eight operand reads are issued before the first product waits
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF, 0);
+        Stats cur;
+        read_stats(U & 1, cur);
+        // all eight operand reads, then the four statistics reads, are issued
+        // before the first product waits
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF + 4, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, NF, 0);
         if constexpr (R == 0) {
             // every (query, key) pair of this block in the band: no mask
@@ -843,7 +859,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
 #pragma unroll
             for (int e = 0; e < 16; ++e) mine[e] -= cur.v[e >> 2][e & 3];
         }
-        const int par = it & 1;
+        constexpr int par = U & 1;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             X[par][pr][R][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
@@ -895,8 +911,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         // a query tile before the keys or beyond the window); `stored` (uniform)
         // tells the waits of the next step how many stores are behind the loads
         // they wait for.
-        if (it + 1 < nt) dma_stats(it + 1);
-        if (it + ST - 1 < nt) issue(it + ST - 1);   // into the stage tile it - 1 used
+        if (it + 1 < nt) dma_stats(it + 1, (U + 1) & 1);
+        if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);   // the stage tile it - 1 used
         {
             const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
             stored = R == 0 && dso && jj >= 0 && jj < nK;
@@ -923,10 +939,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
         __builtin_amdgcn_sched_group_barrier(kSchedValu, 64, 1);
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
     };
-    for (int it = 0; it < nt; it += 2) {
-        tile_step(it);
-        if (it + 1 < nt) tile_step(it + 1);
-    }
+    for (int it = 0; it < nt; it += 2 * ST) unrolled_steps<0, 2 * ST>(it, nt, tile_step);
 
     // Epilogue: element e of local block lb is channel 32 (R + 2 lb) +
     // 8(e/4) + 4g + e%4 of key kj.
