@@ -222,6 +222,18 @@ MAGLEV_DEV void pipeline_wait(int it, int nt)
     __builtin_amdgcn_s_barrier();
 }
 
+// Calls f(it + U, U) for U = U0 .. N-1 while it + U < nt, each U a
+// compile-time constant.
+template <int U, int N, class F>
+MAGLEV_DEV void unrolled_steps(int it, int nt, F &f)
+{
+    if constexpr (U < N) {
+        if (it + U >= nt) return;
+        f(it + U, std::integral_constant<int, U>{});
+        unrolled_steps<U + 1, N>(it, nt, f);
+    }
+}
+
 // ============================================================================
 // Forward
 // ============================================================================
@@ -262,13 +274,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     wait_vmcnt<0>();
     const float c2 = a.scale * kLog2e;   // scores -> log2 units
 
-    auto issue = [&](int it) {
-        bf16 *kt = lds + (it % ST) * 2 * TE;
+    // tile `it` into stage `buf` (it mod ST)
+    auto issue = [&](int it, int buf) {
+        bf16 *kt = lds + buf * 2 * TE;
         issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
-        if (s0 < nt) issue(s0);
+        if (s0 < nt) issue(s0, s0);
 
     f32x16 acc[NB];
 #pragma unroll
@@ -281,12 +294,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const int wlo = qw0 - W + 1;
     const int whi = qw0 + 31 < T - 1 ? qw0 + 31 : T - 1;
 
-    for (int it = 0; it < nt; ++it) {
+    // Step `it`; U = it mod ST is a compile-time constant, so that every LDS
+    // address of the step is a lane base plus an immediate offset.
+    auto step = [&](int it, auto u) {
+        constexpr int U = decltype(u)::value;
         pipeline_wait<ST, PER>(it, nt);
-        if (it + ST - 1 < nt) issue(it + ST - 1);
+        if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);
         const int j0 = jstart + it * KT;
-        if (!active || j0 > whi || j0 + KT - 1 < wlo) continue;
-        const bf16 *kt = lds + (it % ST) * 2 * TE, *vt = kt + TE;
+        if (!active || j0 > whi || j0 + KT - 1 < wlo) return;
+        const bf16 *kt = lds + U * 2 * TE, *vt = kt + TE;
 
         f32x16 sc[KB];
 #pragma unroll
@@ -347,7 +363,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         for (int db = 0; db < NB; ++db)
 #pragma unroll
             for (int t = 0; t < 2 * KB; ++t) acc[db] = mfma32(vfr[db][t], pf[t], acc[db]);
-    }
+    };
+    for (int it = 0; it < nt; it += ST) unrolled_steps<0, ST>(it, nt, step);
 
     if (qi < T) {
         const float inv = 1.0f / l_run;
@@ -659,18 +676,6 @@ MAGLEV_DEV void scale_rotate_pair(f32x16 &lo, f32x16 &hi, const float2 *cs, int 
             lo[e] *= scale;
             hi[e] *= scale;
         }
-    }
-}
-
-// Calls f(it + U, U) for U = U0 .. N-1 while it + U < nt, each U a
-// compile-time constant.
-template <int U, int N, class F>
-MAGLEV_DEV void unrolled_steps(int it, int nt, F &f)
-{
-    if constexpr (U < N) {
-        if (it + U >= nt) return;
-        f(it + U, std::integral_constant<int, U>{});
-        unrolled_steps<U + 1, N>(it, nt, f);
     }
 }
 
@@ -1157,8 +1162,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
     // K~ tile of the workgroup (two instructions a wave) and this wave's dS
     // tile of the same keys (two more: 16 rows of 64 bytes each), read from
     // the zero page where the wave has no such tile.
-    auto issue = [&](int it) {
-        bf16 *st = lds + (it % ST) * SE;
+    auto issue = [&](int it, int buf) {   // buf = it mod ST
+        bf16 *st = lds + buf * SE;
         const int j0 = jstart + it * KT;
 #pragma unroll
         for (int i = 0; i < Dma::PER_WAVE; ++i) {
@@ -1177,7 +1182,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
-        if (s0 < nt) issue(s0);
+        if (s0 < nt) issue(s0, s0);
 
     f32x16 acc[NB];
 #pragma unroll
@@ -1185,12 +1190,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
 
-    for (int it = 0; it < nt; ++it) {
+    // Step `it`; U = it mod ST is a compile-time constant, so that every LDS
+    // address of the step is a lane base plus an immediate offset.
+    auto step = [&](int it, auto u) {
+        constexpr int U = decltype(u)::value;
         pipeline_wait<ST, PER>(it, nt);
-        if (it + ST - 1 < nt) issue(it + ST - 1);
+        if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);
         const int kt = (jstart >> 5) + it;
-        if (!active || kt < wkt_lo || kt > wqt) continue;
-        const bf16 *kt_lds = lds + (it % ST) * SE;
+        if (!active || kt < wkt_lo || kt > wqt) return;
+        const bf16 *kt_lds = lds + U * SE;
         const bf16 *ds_lds = kt_lds + TE + w * DSE;
         bf16x8 ktr[NB][2], dsf[2];
 #pragma unroll
@@ -1207,7 +1215,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int db = 0; db < NB; ++db) acc[db] = mfma32(ktr[db][t], dsf[t], acc[db]);
-    }
+    };
+    for (int it = 0; it < nt; it += ST) unrolled_steps<0, ST>(it, nt, step);
 
     if (qi < T) {
         const int64_t base = act_row(a, b, qi, h) * DH;
