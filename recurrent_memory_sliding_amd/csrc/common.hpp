@@ -137,6 +137,16 @@ MAGLEV_DEV void dma16(const bf16 *src, bf16 *lds_wave_base)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m)
                  : "memory", "m0");
 }
+// As dma16, from a raw buffer: lane L's 16 bytes at byte offset voff of the
+// buffer described by rs (buffer_load_dwordx4 ... lds). The callers keep
+// every offset inside the buffer.
+MAGLEV_DEV void dma16_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, bf16 *lds_wave_base)
+{
+    const unsigned m = (unsigned)(uintptr_t)(lds_bf16 *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+                 "s"(m)
+                 : "memory", "m0");
+}
 // 4 bytes a lane from global memory straight into LDS: lane L's word lands at
 // lds_wave_base + 4 L (global_load_lds_dword); otherwise as dma16.
 MAGLEV_DEV void dma4(const float *src, void *lds_wave_base)

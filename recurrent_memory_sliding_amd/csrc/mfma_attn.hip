@@ -748,10 +748,37 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     }
     wait_vmcnt<0>();
 
-    // tile `it` into stage `buf` (it mod ST)
+    // Byte offset of this lane's chunk of each of its DMA instructions inside
+    // a tile of QT token rows (the same for Q^ and dO).
+    unsigned voff[Dma::PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < Dma::PER_WAVE; ++i) {
+        const int ins = w * Dma::PER_WAVE + i;
+        const int r = Dma::row(ins, lane);
+        voff[i] = (unsigned)(r * tok_stride + Dma::chunk(r, lane) * 8) * 2u;
+    }
+    // tile `it` into stage `buf` (it mod ST). A tile inside the sequence is
+    // read through a buffer descriptor of its QT rows (uniform registers,
+    // built per tile) at the fixed lane offsets; the last tile of a sequence
+    // reads rows beyond T from the zero page.
     auto issue = [&](int it, int buf) {
         const int i0 = j0 + it * QT;
         bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+        if (i0 + QT <= T) {
+            const int64_t toff = (int64_t)i0 * tok_stride;
+            const unsigned bytes = (unsigned)(QT * tok_stride) * 2u;
+            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16 *>(qbase + toff), (short)0, bytes, kBufferWord3);
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16 *>(obase + toff), (short)0, bytes, kBufferWord3);
+#pragma unroll
+            for (int i = 0; i < Dma::PER_WAVE; ++i) {
+                const int ins = w * Dma::PER_WAVE + i;
+                dma16_buf(rq, voff[i], qt + ins * 512);
+                dma16_buf(ro, voff[i], ot + ins * 512);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < Dma::PER_WAVE; ++i) {
             const int ins = w * Dma::PER_WAVE + i;
