@@ -191,11 +191,46 @@ MAGLEV_DEV bf16x8 acc_to_operand(const f32x16 &x, int half)
 
 // Keys j0 .. j0+KT-1 of (b, h) from kx and vx into one K tile and one V tile
 // (this wave's share); rows at or beyond T read zeros.
+// Byte offsets of this lane's chunks of a wave's DMA instructions inside a
+// tile of KT token rows, rows tok_stride elements apart.
 template <int DH, int KT>
-MAGLEV_DEV void issue_kv_tile(const bf16 *kbase, const bf16 *vbase, int tok_stride, int T, int j0,
-                              bf16 *kt, bf16 *vt, int w, int lane)
+MAGLEV_DEV void kv_tile_offsets(int tok_stride, int w, int lane,
+                                unsigned (&voff)[TileDma<DH, KT, 4>::PER_WAVE])
 {
     using Dma = TileDma<DH, KT, 4>;
+#pragma unroll
+    for (int i = 0; i < Dma::PER_WAVE; ++i) {
+        const int ins = w * Dma::PER_WAVE + i;
+        const int r = Dma::row(ins, lane);
+        voff[i] = (unsigned)(r * tok_stride + Dma::chunk(r, lane) * 8) * 2u;
+    }
+}
+
+// DMA of the K~ and V~ tiles of keys j0 .. j0+KT-1 (four waves). A tile inside
+// the sequence is read through buffer descriptors of its KT rows (uniform
+// registers) at the lane offsets voff, with no vector instructions; a tile
+// reaching past T reads those rows from the zero page.
+template <int DH, int KT>
+MAGLEV_DEV void issue_kv_tile(const bf16 *kbase, const bf16 *vbase, int tok_stride, int T, int j0,
+                              bf16 *kt, bf16 *vt, int w, int lane,
+                              const unsigned (&voff)[TileDma<DH, KT, 4>::PER_WAVE])
+{
+    using Dma = TileDma<DH, KT, 4>;
+    if (j0 + KT <= T) {
+        const int64_t toff = (int64_t)j0 * tok_stride;
+        const unsigned bytes = (unsigned)(KT * tok_stride) * 2u;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16 *>(kbase + toff), (short)0, bytes, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16 *>(vbase + toff), (short)0, bytes, kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < Dma::PER_WAVE; ++i) {
+            const int ins = w * Dma::PER_WAVE + i;
+            dma16_buf(rk, voff[i], kt + ins * 512);
+            dma16_buf(rv, voff[i], vt + ins * 512);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < Dma::PER_WAVE; ++i) {
         const int ins = w * Dma::PER_WAVE + i;
@@ -274,10 +309,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     wait_vmcnt<0>();
     const float c2 = a.scale * kLog2e;   // scores -> log2 units
 
+    unsigned voff[TileDma<DH, KT, 4>::PER_WAVE];
+    kv_tile_offsets<DH, KT>(tok_stride, w, lane, voff);
     // tile `it` into stage `buf` (it mod ST)
     auto issue = [&](int it, int buf) {
         bf16 *kt = lds + buf * 2 * TE;
-        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane, voff);
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
@@ -1048,9 +1085,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(AttnArgs a, const b
     }
     wait_vmcnt<0>();
 
+    unsigned voff[TileDma<DH, KT, 4>::PER_WAVE];
+    kv_tile_offsets<DH, KT>(tok_stride, w, lane, voff);
     auto issue = [&](int it) {
         bf16 *kt = lds + (it % ST) * 2 * TE;
-        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane);
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane, voff);
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
@@ -1189,23 +1228,46 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
     // K~ tile of the workgroup (two instructions a wave) and this wave's dS
     // tile of the same keys (two more: 16 rows of 64 bytes each), read from
     // the zero page where the wave has no such tile.
+    // A K~ tile inside the sequence and a dS tile the wave has are read
+    // through buffer descriptors (uniform registers, built per tile) at fixed
+    // lane offsets; otherwise rows beyond T, or the whole dS tile, come from
+    // the zero page.
+    unsigned voff[Dma::PER_WAVE];
+    kv_tile_offsets<DH, KT>(tok_stride, w, lane, voff);
+    const unsigned ds_off = (unsigned)lane * 16u;
     auto issue = [&](int it, int buf) {   // buf = it mod ST
         bf16 *st = lds + buf * SE;
         const int j0 = jstart + it * KT;
+        if (j0 + KT <= T) {
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16 *>(kbase + (int64_t)j0 * tok_stride), (short)0,
+                (unsigned)(KT * tok_stride) * 2u, kBufferWord3);
 #pragma unroll
-        for (int i = 0; i < Dma::PER_WAVE; ++i) {
-            const int ins = w * Dma::PER_WAVE + i;
-            const int r = Dma::row(ins, lane);
-            const int c = Dma::chunk(r, lane);
-            const int j = j0 + r;
-            dma16(j < T ? kbase + (int64_t)j * tok_stride + c * 8 : g_attn_zero, st + ins * 512);
+            for (int i = 0; i < Dma::PER_WAVE; ++i)
+                dma16_buf(rk, voff[i], st + (w * Dma::PER_WAVE + i) * 512);
+        } else {
+#pragma unroll
+            for (int i = 0; i < Dma::PER_WAVE; ++i) {
+                const int ins = w * Dma::PER_WAVE + i;
+                const int r = Dma::row(ins, lane);
+                const int c = Dma::chunk(r, lane);
+                const int j = j0 + r;
+                dma16(j < T ? kbase + (int64_t)j * tok_stride + c * 8 : g_attn_zero, st + ins * 512);
+            }
         }
         const int kt = j0 >> 5;
         const bool have = active && kt >= wkt_lo && kt <= wqt;
-        const bf16 *src = dsbase + ((int64_t)kt * nK + (wqt - kt)) * DSE;
         bf16 *dst = st + TE + w * DSE;
+        if (have) {
+            const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<bf16 *>(dsbase + ((int64_t)kt * nK + (wqt - kt)) * DSE), (short)0,
+                DSE * 2, kBufferWord3);
+            dma16_buf(rd, ds_off, dst);
+            dma16_buf(rd, ds_off + 1024u, dst + 512);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(have ? src + i * 512 + lane * 8 : g_attn_zero, dst + i * 512);
+            for (int i = 0; i < 2; ++i) dma16(g_attn_zero, dst + i * 512);
+        }
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
