@@ -330,6 +330,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const bool active = qw0 < T;
     const int wlo = qw0 - W + 1;
     const int whi = qw0 + 31 < T - 1 ? qw0 + 31 : T - 1;
+    // keys qi - band + 1 .. qi are seen by query qi (none past T: its row is
+    // not stored)
+    const unsigned band = qi < T ? (unsigned)W : 0u;
 
     // Step `it`; U = it mod ST is a compile-time constant, so that every LDS
     // address of the step is a lane base plus an immediate offset.
@@ -354,13 +357,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         }
         const bool inside = (j0 + KT - 1 <= qw0) && (j0 >= qw0 + 31 - W + 1) && (j0 + KT - 1 < T);
         if (!inside) {
+            // key j is in query qi's band iff 0 <= qi - j < band
+            const int d0 = qi - j0 - 4 * g;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = j0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                    if ((key > qi) | (key < qi - W + 1) | (key >= T)) sc[kb][e] = -INFINITY;
-                }
+                for (int e = 0; e < 16; ++e)
+                    if ((unsigned)(d0 - 32 * kb - 8 * (e >> 2) - (e & 3)) >= band) sc[kb][e] = -INFINITY;
         }
         // running maximum of the raw scores (c2 > 0 keeps the order)
         float mx = -INFINITY;
@@ -771,6 +774,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     const float *drow = Dp + (int64_t)bh * Tp;
 
     const int qend = j0 + KB - 1 + W < T ? j0 + KB - 1 + W : T;   // exclusive
+    // queries kj .. kj + band - 1 see key kj: band = min(W, T - kj), 0 past T
+    const unsigned band = kj < T ? (unsigned)(W < T - kj ? W : T - kj) : 0u;
     const int nt = (qend - j0 + QT - 1) / QT;
 
     // This lane's key row of K~ (first wave) or V~ (second wave) as B
@@ -916,10 +921,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
                 for (int e = 0; e < 16; ++e)
                     mine[e] = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
             } else {
+                // query i is in key kj's band iff 0 <= i - kj < band
+                const int d0 = i0 + 4 * g - kj;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int i = i0 + 8 * (e >> 2) + 4 * g + (e & 3);
-                    const bool ok = (i >= kj) & (i - kj < W) & (i < T);
+                    const bool ok = (unsigned)(d0 + 8 * (e >> 2) + (e & 3)) < band;
                     const float p = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
                     mine[e] = ok ? p : 0.0f;
                 }
