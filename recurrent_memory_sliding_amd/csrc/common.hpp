@@ -147,6 +147,15 @@ MAGLEV_DEV void dma16_buf(__amdgpu_buffer_rsrc_t rs, unsigned voff, bf16 *lds_wa
                  "s"(m)
                  : "memory", "m0");
 }
+// As dma16_buf for data read once (nontemporal: not kept in the caches that
+// hold re-read tiles).
+MAGLEV_DEV void dma16_buf_once(__amdgpu_buffer_rsrc_t rs, unsigned voff, bf16 *lds_wave_base)
+{
+    const unsigned m = (unsigned)(uintptr_t)(lds_bf16 *)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff),
+                 "s"(rs), "s"(m)
+                 : "memory", "m0");
+}
 // 4 bytes a lane from global memory straight into LDS: lane L's word lands at
 // lds_wave_base + 4 L (global_load_lds_dword); otherwise as dma16.
 MAGLEV_DEV void dma4(const float *src, void *lds_wave_base)

@@ -1268,8 +1268,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
             const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<bf16 *>(dsbase + ((int64_t)kt * nK + (wqt - kt)) * DSE), (short)0,
                 DSE * 2, kBufferWord3);
-            dma16_buf(rd, ds_off, dst);
-            dma16_buf(rd, ds_off + 1024u, dst + 512);
+            dma16_buf_once(rd, ds_off, dst);
+            dma16_buf_once(rd, ds_off + 1024u, dst + 512);
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i) dma16(g_attn_zero, dst + i * 512);
