@@ -79,10 +79,14 @@ def test_fp32_backward_dh128():
     run_fwd_case(shape(B=1, T=97, W=30, H=2, Dh=128, d=64, dtype=wl.F32), 4, grads=True)
 
 
-@pytest.mark.parametrize("T,W", [(130, 500), (257, 1), (1, 512), (64, 64), (129, 2), (640, 512)])
+@pytest.mark.parametrize("T,W", [(130, 500), (257, 1), (1, 512), (64, 64), (129, 2), (640, 512),
+                                 (575, 512), (96, 96)])
 def test_bf16_window_edges(T, W):
     """Window covering the sequence (full causal), a single key, one token,
-    a window equal to one tile, two keys, and the d20 window over a ragged T."""
+    a window equal to one tile, two keys, the d20 window over T a multiple of
+    the 32-row tiles and one short of one (the last tile of a sequence is
+    loaded with rows past T read as zeros, the others whole), and a window
+    covering three whole tiles."""
     run_fwd_case(shape(B=1, T=T, W=W, H=2, Dh=128, d=128), 10 + T + W, grads=True)
 
 
