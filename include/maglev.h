@@ -88,7 +88,8 @@ typedef enum { MAGLEV_F32 = 0, MAGLEV_BF16 = 1 } maglev_dtype_t;
 
 /* Geometry of one attention layer call.
  *   B, T      batch and sequence length (T >= 1)
- *   H, Dh     heads and head width; Dh in {64, 128}
+ *   H, Dh     heads and head width; Dh in {64, 128}, H*Dh <= 65536
+ *             (else MAGLEV_ERR_UNSUPPORTED)
  *   d         width of the memory m (d_model); multiple of 16
  *   W         window: query i sees keys max(0, i-W+1) .. i (W >= 1)
  *   pos0      absolute position of t = 0 (RoPE angle uses pos0 + t), >= 0

@@ -63,6 +63,9 @@ maglev_status_t check_geom(const maglev_geom_t *g, Geom *out)
     if (g->B < 0 || g->T < 0) return fail(MAGLEV_ERR_INVALID_VALUE, "B and T must be >= 0");
     if (g->H < 1) return fail(MAGLEV_ERR_INVALID_VALUE, "H must be >= 1");
     if (g->Dh != 64 && g->Dh != 128) return fail(MAGLEV_ERR_UNSUPPORTED, "Dh must be 64 or 128");
+    // the attention passes address a tile of 32 token rows (H*Dh elements
+    // apart) with 32-bit byte offsets
+    if ((int64_t)g->H * g->Dh > 65536) return fail(MAGLEV_ERR_UNSUPPORTED, "H*Dh must be at most 65536");
     if (g->d < 16 || (g->d % 16) != 0)
         return fail(MAGLEV_ERR_INVALID_VALUE, "d must be a positive multiple of 16");
     if (g->W < 1) return fail(MAGLEV_ERR_INVALID_VALUE, "W must be >= 1");

@@ -82,7 +82,7 @@ def project(L, g, shift=1, ptrs=None):
     (dict(Dh=96), UNSUPPORTED), (dict(Dh=32), UNSUPPORTED), (dict(H=0), INVALID),
     (dict(d=100), INVALID), (dict(d=0), INVALID), (dict(W=0), INVALID), (dict(B=-1), INVALID),
     (dict(T=-5), INVALID), (dict(pos0=-1), INVALID), (dict(dtype=7), INVALID),
-    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(H=513, Dh=128), UNSUPPORTED),
 ])
 def test_projection_rejects_bad_geometry(L, kw, status):
     assert project(L, geom(**kw)) == status
