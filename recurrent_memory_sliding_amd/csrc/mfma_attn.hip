@@ -1356,13 +1356,13 @@ void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const vo
 {
     const AttnArgs a = make_args(g, q, nullptr, kx, vx, rope);
     const unsigned nwg = (unsigned)(g.B * g.H * ((g.T + 127) / 128));
-    prof::Scope ts("attn_fwd", s);
+    prof::Scope ts("attn_fwd", s, prof::Scope::Attach{});
     if (g.Dh == 128)
-        hipLaunchKernelGGL((attn_fwd_kernel<128, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s, a,
-                           static_cast<bf16 *>(o), lse);
+        hipExtLaunchKernelGGL((attn_fwd_kernel<128, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s,
+                              ts.start(), ts.stop(), 0, a, static_cast<bf16 *>(o), lse);
     else
-        hipLaunchKernelGGL((attn_fwd_kernel<64, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s, a,
-                           static_cast<bf16 *>(o), lse);
+        hipExtLaunchKernelGGL((attn_fwd_kernel<64, kFwdKT, kFwdST>), dim3(nwg), dim3(256), 0, s,
+                              ts.start(), ts.stop(), 0, a, static_cast<bf16 *>(o), lse);
 }
 
 template <int DH>
@@ -1372,45 +1372,47 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
 {
     {
         const unsigned pre_blocks = (unsigned)((rows * (DH / 16) + 255) / 256);
-        prof::Scope ts("attn_bwd_prep", s);
-        hipLaunchKernelGGL(bwd_prep_kernel<DH>, dim3(pre_blocks), dim3(256), 0, s, o, dO, a.q, lse,
-                           a.rope, static_cast<bf16 *>(ws.q_rot), ws.Dp, ws.lse2, rows, a.H, a.T,
-                           ws.Tp, a.pos0);
+        prof::Scope ts("attn_bwd_prep", s, prof::Scope::Attach{});
+        hipExtLaunchKernelGGL(bwd_prep_kernel<DH>, dim3(pre_blocks), dim3(256), 0, s, ts.start(),
+                              ts.stop(), 0, o, dO, a.q, lse, a.rope,
+                              static_cast<bf16 *>(ws.q_rot), ws.Dp, ws.lse2, rows, a.H, a.T,
+                              ws.Tp, a.pos0);
     }
     {
-        prof::Scope ts("attn_bwd_dkdv", s);
+        prof::Scope ts("attn_bwd_dkdv", s, prof::Scope::Attach{});
         if constexpr (DH == 128) {
             // one workgroup per 64 keys of a (sequence, head)
             const unsigned npw = (unsigned)(a.B * a.H * ((a.T + 63) / 64));
             bf16 *dso = static_cast<bf16 *>(ws.ds);
             if (entries)
-                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, false>), dim3(npw),
-                                   dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
-                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), dso,
-                                   ws.ds_tiles, ws.nt32);
+                hipExtLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, false>), dim3(npw),
+                                      dim3(256), 0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2,
+                                      ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
+                                      static_cast<bf16 *>(dv), dso, ws.ds_tiles, ws.nt32);
             else
-                hipLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, true>), dim3(npw),
-                                   dim3(256), 0, s, a, dO, ws.lse2, ws.Dp, ws.Tp,
-                                   static_cast<bf16 *>(dk), static_cast<bf16 *>(dv), dso,
-                                   ws.ds_tiles, ws.nt32);
+                hipExtLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, true>), dim3(npw),
+                                      dim3(256), 0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2,
+                                      ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
+                                      static_cast<bf16 *>(dv), dso, ws.ds_tiles, ws.nt32);
         } else if (entries) {
-            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256), 0,
-                               s, a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
-                               static_cast<bf16 *>(dv));
+            hipExtLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, false>), dim3(nwg), dim3(256),
+                                  0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2, ws.Dp, ws.Tp,
+                                  static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
         } else {
-            hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256), 0, s,
-                               a, dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
-                               static_cast<bf16 *>(dv));
+            hipExtLaunchKernelGGL((attn_bwd_dkdv_kernel<DH, kBwdST, true>), dim3(nwg), dim3(256),
+                                  0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2, ws.Dp, ws.Tp,
+                                  static_cast<bf16 *>(dk), static_cast<bf16 *>(dv));
         }
     }
-    prof::Scope ts("attn_bwd_dq", s);
+    prof::Scope ts("attn_bwd_dq", s, prof::Scope::Attach{});
     if (DH == 128 && ws.ds)
-        hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<kDqDsST>), dim3(nwg), dim3(256), 0, s, a,
-                           static_cast<const bf16 *>(ws.ds), ws.ds_tiles, ws.nt32,
-                           static_cast<bf16 *>(dq));
+        hipExtLaunchKernelGGL((attn_bwd_dq_ds_kernel<kDqDsST>), dim3(nwg), dim3(256), 0, s,
+                              ts.start(), ts.stop(), 0, a, static_cast<const bf16 *>(ws.ds),
+                              ws.ds_tiles, ws.nt32, static_cast<bf16 *>(dq));
     else
-        hipLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s, a,
-                           dO, ws.lse2, ws.Dp, ws.Tp, static_cast<bf16 *>(dq));
+        hipExtLaunchKernelGGL((attn_bwd_dq_kernel<DH, kDqKT, kDqST>), dim3(nwg), dim3(256), 0, s,
+                              ts.start(), ts.stop(), 0, a, dO, ws.lse2, ws.Dp, ws.Tp,
+                              static_cast<bf16 *>(dq));
 }
 
 void launch_attn_bwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,

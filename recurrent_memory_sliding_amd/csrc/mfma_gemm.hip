@@ -753,9 +753,9 @@ static void run_gemm(const P &p, int ksplit, int64_t kper, hipStream_t s, const 
     const int64_t ntm = (p.M + Cfg::BM - 1) / Cfg::BM;
     const int64_t ntn = (p.N + Cfg::BN - 1) / Cfg::BN;
     if (group_m > ntm) group_m = (int)ntm;
-    prof::Scope ts(name, s);
-    hipLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn * ksplit)), dim3(Cfg::NT), 0, s,
-                       p, kper, group_m);
+    prof::Scope ts(name, s, prof::Scope::Attach{});
+    hipExtLaunchKernelGGL((gemm_bf16<Cfg, P>), dim3((unsigned)(ntm * ntn * ksplit)), dim3(Cfg::NT), 0,
+                          s, ts.start(), ts.stop(), 0, p, kper, group_m);
 }
 
 // out[c][r] = in[r][c] for a bf16 [R][C] matrix (C and R multiples of 8),

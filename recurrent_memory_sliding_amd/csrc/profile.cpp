@@ -105,12 +105,19 @@ void drain()
 
 }  // namespace
 
-Scope::Scope(const char *name, hipStream_t s) : name_(name), s_(s)
+Scope::Scope(const char *name, hipStream_t s) : name_(name), s_(s) { open(s); }
+
+Scope::Scope(const char *name, hipStream_t s, Attach) : name_(name), s_(s), attach_(true)
+{
+    open(s);
+}
+
+void Scope::open(hipStream_t s)
 {
     if (!g_on.load(std::memory_order_relaxed)) return;
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        if (!g_only.empty() && g_only != name) return;
+        if (!g_only.empty() && g_only != name_) return;
     }
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
@@ -118,7 +125,7 @@ Scope::Scope(const char *name, hipStream_t s) : name_(name), s_(s)
     std::lock_guard<std::mutex> lk(g_mu);
     start_ = take(dev_);
     stop_ = take(dev_);
-    if (!start_ || !stop_ || hipEventRecord(start_, s) != hipSuccess) {
+    if (!start_ || !stop_ || (!attach_ && hipEventRecord(start_, s) != hipSuccess)) {
         give(dev_, start_);
         give(dev_, stop_);
         start_ = stop_ = nullptr;
@@ -129,7 +136,11 @@ Scope::~Scope()
 {
     if (start_) {
         std::lock_guard<std::mutex> lk(g_mu);
-        if (hipEventRecord(stop_, s_) == hipSuccess) {
+        // Attach mode: the launch recorded both events, unless it failed (then
+        // they still hold an earlier launch's times and are not read).
+        const bool ok = attach_ ? hipPeekAtLastError() == hipSuccess
+                                : hipEventRecord(stop_, s_) == hipSuccess;
+        if (ok) {
             g_pending.push_back({name_, dev_, start_, stop_});
         } else {
             give(dev_, start_);
