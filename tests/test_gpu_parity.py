@@ -169,6 +169,43 @@ def test_debug_mode_gives_the_same_results():
         assert torch.equal(plain[n], dbg[n]), n
 
 
+def test_profiling_gives_the_same_results_and_times_every_kernel():
+    """Per-kernel timing (events bound to the attention and GEMM dispatches,
+    event records around the other kernels) changes no result, times each
+    kernel of the pass once per launch, and with a name times only that one."""
+    sh = shape(B=2, T=333, W=100)
+    inp = wl.layer_inputs(sh, 13, grads=True)
+
+    def run():
+        g, km, vm, o, lse = gpu_forward(inp, sh)
+        gr = gpu_backward(g, km, vm, o, lse, sh)
+        loss, dm, dmp = rms.maglev_consistency_loss(g["m"], g["m_prime"], sh.lam)
+        torch.cuda.synchronize()
+        return dict(gr, o=o, lse=lse, loss=loss, dm=dm, dmp=dmp)
+
+    plain = run()
+    try:
+        rms.maglev_profile_enable(True)
+        timed = run()
+        rms.maglev_profile_enable(False)
+        every = rms.maglev_profile_read()
+        rms.maglev_profile_enable(True, only="attn_bwd_dkdv")
+        run()
+        rms.maglev_profile_enable(False)
+        one = rms.maglev_profile_read()
+    finally:
+        rms.maglev_profile_enable(False)
+    for n in plain:
+        assert torch.equal(plain[n], timed[n]), n
+    flush("  timed %s" % {k: "%d x %.3f ms" % v for k, v in every.items()})
+    for k in ("attn_fwd", "attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq", "mix", "loss_partial",
+              "loss_final"):
+        assert k in every, k
+    for k, (n, ms) in every.items():
+        assert n >= 1 and 0.0 < ms < 1000.0 * n, (k, n, ms)
+    assert list(one) == ["attn_bwd_dkdv"] and one["attn_bwd_dkdv"][0] == 1, one
+
+
 def test_loss_bf16_and_accumulate():
     sh = shape(B=3, T=500, d=1280)
     inp = wl.layer_inputs(sh, 12)
