@@ -254,7 +254,8 @@ def train_step(sh, g, buf):
 def bench_train(sh, steps, warmup, mix="sigma"):
     """Wall time per step over the timed steps. Every kernel is timed with HIP
     events during the warmup steps after the first (the per-kernel table); the
-    timed steps then record events around the kernel with the most time only."""
+    timed steps then time the kernel with the most time only (with events the
+    library binds to that kernel's dispatch, on its launch stream)."""
     g, buf = train_setup(sh, mix=mix)
     step = train_step_gated if mix == "gated" else train_step
     step(sh, g, buf)

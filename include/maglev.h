@@ -478,8 +478,11 @@ const char *maglev_last_error(void);
 int maglev_abi_version(void);
 
 /* Kernel timing (diagnostic, for measurement tools). While switched on, every
- * kernel the library launches is bracketed by two HIP events recorded on its
- * launch stream; launches on a stream under graph capture are not recorded.
+ * kernel the library launches is timed with two HIP events on its launch
+ * stream: the attention kernels and the GEMMs carry both events with their
+ * dispatch (its own start and end times), the other kernels get one event
+ * recorded on each side; launches on a stream under graph capture are not
+ * recorded.
  *   maglev_profile_enable(1, only) clears earlier totals and starts recording
  *   every kernel (only == NULL) or just the kernel named `only` (host string,
  *   copied; fewer events leave fewer gaps in the stream);
@@ -488,7 +491,7 @@ int maglev_abi_version(void);
  *   per-kernel totals and returns the number of kernel names;
  *   maglev_profile_entry(i, ...) gives name i (static until the next enable),
  *   its launch count and its summed duration in milliseconds.
- * The events add a small gap between kernels; timing is off by default. */
+ * Recorded events add a small gap between kernels; timing is off by default. */
 maglev_status_t maglev_profile_enable(int on, const char *only);
 int maglev_profile_count(void);
 
