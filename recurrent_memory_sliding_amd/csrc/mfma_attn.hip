@@ -269,6 +269,28 @@ MAGLEV_DEV void unrolled_steps(int it, int nt, F &f)
     }
 }
 
+// Tile order of a pass that sweeps nt tiles of ts tokens, the first at token
+// `first`, in rotated order: step it takes the tile whose absolute index is
+// congruent to it modulo nt. The forward's query blocks of one (sequence,
+// head) that share a key tile (five at W = 512) then read it at about the
+// same step, while it is still in L2, instead of one after another as each
+// sweeps its own band from its start: the six (sequence, head) pairs resident
+// on one XCD hold 6 MB of K~/V~, more than its 4 MB L2. (The dK/dV and dQ
+// passes keep the plain order: their resident tiles fit in L2 and the
+// rotation did not change their time.)
+struct TileSweep {
+    int nt, phase;
+    MAGLEV_DEV TileSweep(int first, int nt_, int ts) : nt(nt_)
+    {
+        phase = nt > 0 ? (nt - (first / ts) % nt) % nt : 0;
+    }
+    MAGLEV_DEV int rel(int it) const
+    {
+        const int r = it + phase;
+        return r < nt ? r : r - nt;
+    }
+};
+
 // ============================================================================
 // Forward
 // ============================================================================
@@ -298,6 +320,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     const int khi = i0 + 128 < T ? i0 + 128 : T;
     const int jstart = (klo / KT) * KT;
     const int nt = (khi - jstart + KT - 1) / KT;
+    const TileSweep sweep(jstart, nt, KT);
     // The query operands are complete before any tile load is issued (see the
     // dQ pass for why). They are bf16(R q) unscaled, the operand the backward
     // recomputes the scores from, so that its probabilities are the ones whose
@@ -314,7 +337,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
     // tile `it` into stage `buf` (it mod ST)
     auto issue = [&](int it, int buf) {
         bf16 *kt = lds + buf * 2 * TE;
-        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + it * KT, kt, kt + TE, w, lane, voff);
+        issue_kv_tile<DH, KT>(kbase, vbase, tok_stride, T, jstart + sweep.rel(it) * KT, kt, kt + TE,
+                              w, lane, voff);
     };
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
@@ -340,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a, bf16 *o, f
         constexpr int U = decltype(u)::value;
         pipeline_wait<ST, PER>(it, nt);
         if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);
-        const int j0 = jstart + it * KT;
+        const int j0 = jstart + sweep.rel(it) * KT;
         if (!active || j0 > whi || j0 + KT - 1 < wlo) return;
         const bf16 *kt = lds + U * 2 * TE, *vt = kt + TE;
 
