@@ -11,7 +11,9 @@
 // v~_j = v_j + s_h vmem_j arrive precomputed (the projection call writes them).
 //
 // Design (gfx950): 256-thread workgroups of four 64-wide waves, each wave
-// owning 32 rows; v_mfma_f32_32x32x16_bf16 with fp32 accumulation. Scores are
+// owning 32 rows; v_mfma_f32_32x32x16_bf16 with fp32 accumulation (the dK/dV
+// pass for Dh = 128: 16 keys a wave, v_mfma_f32_16x16x32_bf16, so that three
+// workgroups share a CU and no values cross between waves). Scores are
 // computed transposed (S^T = K~ Q^T) where that makes each lane own one query
 // (or key) column: the softmax state is per lane, the probabilities stay in
 // registers and feed the next product directly (their key order is permuted
@@ -713,83 +715,58 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
     }
 }
 
-// Scale and inverse rotation of one channel-pair block: lo holds channels
-// c = c0 + 8(e/4) + 4g + e%4 of one key, hi the channels c + DH/2; cs is the
-// key's rotation table at entry c0 (nullptr: scale only).
-MAGLEV_DEV void scale_rotate_pair(f32x16 &lo, f32x16 &hi, const float2 *cs, int g, float scale)
+// Key-stationary pass with one wave per 16 keys (Dh = 128): four waves, 64
+// keys a workgroup, each wave computing all of its keys' work alone with
+// v_mfma_f32_16x16x32_bf16, so that no values cross between waves and the
+// only shared state is the ring of 32-query Q^ / dO tiles (and their lse2 / D
+// rows) in LDS. Per tile a wave forms S = Q^ K~^T and dP = dO V~^T (lane l:
+// key l % 16, queries 16 qb + 4 (l / 16) + i), P = exp(scale S - lse) on the
+// band, dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^^T dS with the
+// probabilities' query order matched by the transposed reads (lane l of the
+// result: key l % 16, channels 16 cb + 4 (l / 16) + i). dS, rounded to bf16 as
+// the dK product takes it, is stored for the dQ pass as [key][query] tiles of
+// 32 keys x 32 queries (64-byte rows; a wave writes its 16 key rows).
+namespace k16 {
+// Swizzle of the Q^ / dO tiles: chunk c of row r sits in slot c ^ swz(r),
+// with bits 2-3 of swz from r mod 4 and bits 0-1 a bijection of (r / 4) mod 4
+// that puts rows 4 apart into opposite halves of bit 1. The transposed reads
+// (rows 4g .. 4g+3 of two chunks for g = 0, 1 or 2, 3 in a half-wave pass)
+// then meet every slot once. The row reads take chunk s + 4 (lane / 16) in
+// step s; with chunk 4 s + lane / 16 instead, the same swizzle measured 3.9
+// bank-conflict cycles a ds_read_b128 (SQ_LDS_BANK_CONFLICT), and the 32-row
+// passes' swizzle conflicts on these transposed reads.
+MAGLEV_DEV int swz(int r)
 {
-    if (cs) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float *t = reinterpret_cast<const float *>(cs + 8 * q + 4 * g);
-            const f32x4 t0 = *reinterpret_cast<const f32x4 *>(t);
-            const f32x4 t1 = *reinterpret_cast<const f32x4 *>(t + 4);
-            const float cx[4] = {t0[0], t0[2], t1[0], t1[2]};
-            const float sy[4] = {t0[1], t0[3], t1[1], t1[3]};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = 4 * q + u;
-                const float x = lo[e] * scale, y = hi[e] * scale;
-                lo[e] = x * cx[u] + y * sy[u];
-                hi[e] = -x * sy[u] + y * cx[u];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            lo[e] *= scale;
-            hi[e] *= scale;
-        }
-    }
+    const int g = (r >> 2) & 3;
+    return ((r & 3) << 2) | ((g & 1) << 1) | (g >> 1);
 }
+MAGLEV_DEV int off(int r, int c) { return r * 128 + ((c ^ swz(r)) << 3); }
+constexpr int TE = 32 * 128;            // elements of one 32-row tile
+constexpr int STATS = 4 * 64;           // floats: one 64-float slot a wave
+constexpr int SE = 2 * TE + 2 * STATS;  // bf16 elements of one stage
+constexpr int PER = 5;                  // vector memory operations a wave issues per stage
+}  // namespace k16
 
-// Key-stationary pass with each 32-key block split over a pair of waves
-// (Dh = 128): four waves, two pairs, 64 keys a workgroup; 32-query tiles of
-// Q^ and dO stream through LDS in ST stages. Per tile, the pair's first wave
-// forms S = Q^ K~^T and P = exp(scale S - lse), its second wave
-// dP - D = dO V~^T - D; they swap P and dP - D through LDS (one barrier a
-// tile, which also publishes the next tile's stage), both form
-// dS = P (dP - D), and each
-// accumulates dV~^T += dO^T P and dK~^T += Q^^T dS for its half of the
-// channels: blocks hf and hf + 2 of 32 channels (hf = the wave's place in
-// the pair), so that the rotation pairs (c, c + 64) stay in one wave. A wave
-// holds one of K~, V~ and a quarter of the accumulators, and a workgroup
-// needs 80 KB of LDS, so two workgroups share a CU: they run out of step, and
-// one's MFMA work covers the other's softmax, exchange and barrier. Each
-// phase issues all of its LDS operand reads before its first product (one
-// read in flight per product left every product waiting for LDS latency).
-// The lse (first wave) or D (second wave) values of the next tile are loaded
-// into registers while the current one is used (issued before the DMA that
-// follows them, so the in-order count of vector memory operations tells when
-// they have arrived).
 template <int ST, bool ROTATE>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, const bf16 *dO,
-                                                                     const float *lse2,
-                                                                     const float *Dp, int64_t Tp,
-                                                                     bf16 *dk, bf16 *dv, bf16 *dso,
-                                                                     int nK, int nt32)
+__global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, const bf16 *dO,
+                                                                    const float *lse2,
+                                                                    const float *Dp, int64_t Tp,
+                                                                    bf16 *dk, bf16 *dv, bf16 *dso,
+                                                                    int nK, int nt32)
 {
-    static_assert(ST >= 3, "the next tile is published one tile ahead");
-    constexpr int DH = 128, NF = DH / 16, NPAIR = 2, KB = 32 * NPAIR;
-    constexpr int QT = 32;
-    constexpr int TE = QT * DH;
-    using Dma = TileDma<DH, QT, 2 * NPAIR>;
-    constexpr int PER = 2 * Dma::PER_WAVE;
-    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * 2 * TE];   // [stage][Q^, dO]
-    // [tile parity][pair][role][quad][lane]: P (role 0) and dP - D (role 1) in
-    // the accumulator layout, four 16-byte groups a lane
-    __shared__ __attribute__((aligned(16))) f32x4 X[2][NPAIR][2][4][64];
+    static_assert(ST >= 2, "at least one tile in flight");
+    constexpr int DH = 128, QT = 32, PER = k16::PER;
+    __shared__ __attribute__((aligned(1024))) bf16 lds[ST * k16::SE];   // [stage][Q^, dO, stats]
 
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pr = w >> 1, hf = w & 1;
     const int T = (int)a.T, W = a.W;
-    const int nkt = (T + KB - 1) / KB;
+    const int nkt = (T + 63) / 64;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int kt = bid % nkt, bh = bid / nkt;
     const int h = bh % a.H;
     const int64_t b = bh / a.H;
-    const int j0 = kt * KB, kw0 = j0 + 32 * pr, kj = kw0 + l32;
+    const int j0 = kt * 64, kw0 = j0 + 16 * w, kj = kw0 + l16;
     const float qscale = a.scale * kLog2e;
     const int tok_stride = a.H * DH;
     const bf16 *qbase = a.qr + act_row(a, b, 0, h) * DH;
@@ -797,39 +774,45 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
     const float *lrow = lse2 + (int64_t)bh * Tp;
     const float *drow = Dp + (int64_t)bh * Tp;
 
-    const int qend = j0 + KB - 1 + W < T ? j0 + KB - 1 + W : T;   // exclusive
+    const int qend = j0 + 63 + W < T ? j0 + 63 + W : T;   // exclusive
     // queries kj .. kj + band - 1 see key kj: band = min(W, T - kj), 0 past T
     const unsigned band = kj < T ? (unsigned)(W < T - kj ? W : T - kj) : 0u;
     const int nt = (qend - j0 + QT - 1) / QT;
 
-    // This lane's key row of K~ (first wave) or V~ (second wave) as B
-    // operands, complete before any tile load is issued.
-    bf16x8 kvf[NF];
+    // This lane's key row of K~ and of V~ as B operands: fragment s holds
+    // chunk s + 4 (lane / 16), channels 8 s + 32 (lane / 16) .. +7 (the order
+    // of the channels inside a product is free; this one keeps the row reads
+    // below free of bank conflicts). Complete before any tile load.
+    bf16x8 kf[4], vf[4];
     if (kj < T) {
-        const bf16 *src = (hf ? a.vx : a.kx) + act_row(a, b, kj, h) * DH;
+        const bf16 *ks = a.kx + act_row(a, b, kj, h) * DH;
+        const bf16 *vs = a.vx + act_row(a, b, kj, h) * DH;
 #pragma unroll
-        for (int s = 0; s < NF; ++s) kvf[s] = *reinterpret_cast<const bf16x8 *>(src + 16 * s + 8 * g);
+        for (int s = 0; s < 4; ++s) {
+            kf[s] = *reinterpret_cast<const bf16x8 *>(ks + 8 * s + 32 * g4);
+            vf[s] = *reinterpret_cast<const bf16x8 *>(vs + 8 * s + 32 * g4);
+        }
     } else {
-        zero_frags(kvf, NF);
+        zero_frags(kf, 4);
+        zero_frags(vf, 4);
     }
     wait_vmcnt<0>();
 
-    // Byte offset of this lane's chunk of each of its DMA instructions inside
-    // a tile of QT token rows (the same for Q^ and dO).
-    unsigned voff[Dma::PER_WAVE];
+    // DMA: instruction ins (0..7) of a tile fills rows 4 ins .. +3; the lane's
+    // LDS slot is fixed, its source chunk is slot ^ swz(row). This wave issues
+    // instructions 2w and 2w + 1 of the Q^ tile and of the dO tile, then its
+    // own 64-float statistics slot (lse2 of the tile's 32 queries, then D).
+    unsigned voff[2];
 #pragma unroll
-    for (int i = 0; i < Dma::PER_WAVE; ++i) {
-        const int ins = w * Dma::PER_WAVE + i;
-        const int r = Dma::row(ins, lane);
-        voff[i] = (unsigned)(r * tok_stride + Dma::chunk(r, lane) * 8) * 2u;
+    for (int i = 0; i < 2; ++i) {
+        const int r = 4 * (2 * w + i) + (lane >> 4);
+        voff[i] = (unsigned)(r * tok_stride + ((l16 ^ k16::swz(r)) << 3)) * 2u;
     }
-    // tile `it` into stage `buf` (it mod ST). A tile inside the sequence is
-    // read through a buffer descriptor of its QT rows (uniform registers,
-    // built per tile) at the fixed lane offsets; the last tile of a sequence
-    // reads rows beyond T from the zero page.
+    const float *ssrc = lane < 32 ? lrow + lane : drow + (lane - 32);
     auto issue = [&](int it, int buf) {
         const int i0 = j0 + it * QT;
-        bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
+        bf16 *qt = lds + buf * k16::SE, *ot = qt + k16::TE;
+        float *st = reinterpret_cast<float *>(ot + k16::TE) + 64 * w;
         if (i0 + QT <= T) {
             const int64_t toff = (int64_t)i0 * tok_stride;
             const unsigned bytes = (unsigned)(QT * tok_stride) * 2u;
@@ -838,233 +821,170 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_pair_kernel(AttnArgs a, 
             const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<bf16 *>(obase + toff), (short)0, bytes, kBufferWord3);
 #pragma unroll
-            for (int i = 0; i < Dma::PER_WAVE; ++i) {
-                const int ins = w * Dma::PER_WAVE + i;
+            for (int i = 0; i < 2; ++i) {
+                const int ins = 2 * w + i;
                 dma16_buf(rq, voff[i], qt + ins * 512);
                 dma16_buf(ro, voff[i], ot + ins * 512);
             }
-            return;
-        }
+        } else {
 #pragma unroll
-        for (int i = 0; i < Dma::PER_WAVE; ++i) {
-            const int ins = w * Dma::PER_WAVE + i;
-            const int r = Dma::row(ins, lane);
-            const int c = Dma::chunk(r, lane);
-            const int qi = i0 + r;
-            const bool in = qi < T;
-            const int64_t off = (int64_t)qi * tok_stride + c * 8;
-            dma16(in ? qbase + off : g_attn_zero, qt + ins * 512);
-            dma16(in ? obase + off : g_attn_zero, ot + ins * 512);
+            for (int i = 0; i < 2; ++i) {
+                const int ins = 2 * w + i;
+                const int r = 4 * ins + (lane >> 4);
+                const int qi = i0 + r;
+                const int64_t o = (int64_t)qi * tok_stride + ((l16 ^ k16::swz(r)) << 3);
+                dma16(qi < T ? qbase + o : g_attn_zero, qt + ins * 512);
+                dma16(qi < T ? obase + o : g_attn_zero, ot + ins * 512);
+            }
         }
+        // rows are padded to Tp (a multiple of 32), so the tile's 32 values exist
+        dma4(ssrc + i0, st);
     };
-    // The statistics of tile it that the wave's role needs, lse2 (first wave,
-    // for P) or D (second wave, which sends dP - D) of its 32 queries, travel
-    // like the tiles: the wave loads them straight into its own exchange slot
-    // of the tile's parity (free from the previous step's barrier on, and
-    // overwritten by the wave itself once it has read them), then reads its
-    // 16 values from there. So the loop holds no load the compiler tracks,
-    // and none of its waits covers the tile loads behind them. Rows are
-    // padded to Tp, so a tile never leaves its row; lanes 32..63 load copies
-    // of lanes 0..31.
-    const float *srow = hf ? drow : lrow;
-    auto dma_stats = [&](int it, int par) {   // par = it mod 2
-        dma4(srow + j0 + it * QT + l32, &X[par][pr][hf][0][0]);
-    };
-    struct Stats {
-        f32x4 v[4];
-    };
-    auto read_stats = [&](int par, Stats &st) {
-        const float *sl = reinterpret_cast<const float *>(&X[par][pr][hf][0][0]);
+
+    f32x4 dva[8], dka[8];   // dV^T, dK^T: channels 16 cb + 4 (lane / 16) + i of key kj
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            st.v[q4] = *reinterpret_cast<const f32x4 *>(sl + 8 * q4 + 4 * g);
-    };
-    // Tiles 0 .. ST-2 and the statistics of tile 0 in flight; all landed and
-    // tile 0 visible to every wave.
+    for (int cb = 0; cb < 8; ++cb) dva[cb] = dka[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nt) issue(s0, s0);
-    if (nt > 0) dma_stats(0, 0);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
 
-    // The rest runs once per role, the role a compile-time constant (R = 0:
-    // S, P and the lse2 statistics; R = 1: dP - D and the D statistics),
-    // picked by a wave-uniform branch, so that no per-lane selects between
-    // the roles' operands remain.
-    auto run = [&](auto role) {
-    constexpr int R = decltype(role)::value;
-    f32x16 dva[2], dka[2];   // blocks R and R + 2 of 32 channels
-#pragma unroll
-    for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dva[lb][e] = dka[lb][e] = 0.0f;
-
-    // this lane's byte offset in a stored dS tile: key row l32, queries 4 g..
-    const int ds_voff = l32 * 64 + 8 * g;
-    bool stored = false;   // the last step issued its four dS stores
-    // Step `it`; U = it mod 2 ST, a compile-time constant, so that the stage
-    // (it mod ST) and the exchange parity (it mod 2) are constants and every
-    // LDS address of the step is a lane base plus an immediate offset.
-    auto tile_step = [&](int it, auto u) {
+    // dS tile of this wave: key row 16 (w % 2) + l16 of 32-key tile kw0 / 32,
+    // bytes 8 g4 (queries 4 g4 .. +3) and 32 + 8 g4 (queries 16 + 4 g4 .. +3)
+    const int kt32 = kw0 >> 5;
+    const int ds_voff = (16 * (w & 1) + l16) * 64 + 8 * g4;
+    int s1 = 0, s2 = 0;   // dS stores issued in the last and the one before
+    auto step = [&](int it, auto u) {
         constexpr int U = decltype(u)::value;
+        // tile it has landed once at most the operations issued after it are
+        // outstanding: step it-2's stores, tile it+1, step it-1's stores
+        // (loads and stores complete in issue order)
+        switch (s1 + s2 + (it + 1 < nt ? PER : 0)) {
+        case 0: wait_vmcnt<0>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case PER: wait_vmcnt<PER>(); break;
+        case PER + 2: wait_vmcnt<PER + 2>(); break;
+        default: wait_vmcnt<PER + 4>(); break;
+        }
+        __builtin_amdgcn_s_barrier();
+        if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);   // the stage tile it-1 used
         const int i0 = j0 + it * QT;
-        constexpr int buf = U % ST;
-        const bf16 *qt = lds + buf * 2 * TE, *ot = qt + TE;
-        // this tile's statistics: their load was issued before the last
-        // step's tile loads (PER, when there were any) and its four dS stores
-        if (it + ST - 2 < nt) {
-            if (stored) wait_vmcnt<PER + 4>();
-            else wait_vmcnt<PER>();
-        } else {
-            if (stored) wait_vmcnt<4>();
-            else wait_vmcnt<0>();
+        const bf16 *qt = lds + U * k16::SE, *ot = qt + k16::TE;
+        const float *st = reinterpret_cast<const float *>(ot + k16::TE) + 64 * w;
+        // dS for the dQ pass, for the query tiles it reads (the first at the
+        // key tile's own queries, nK in all)
+        const int jj = (i0 >> 5) - kt32;
+        const bool stored = dso && jj >= 0 && jj < nK;
+        s2 = s1;
+        s1 = stored ? 2 : 0;
+        // S and dP: blocks qb of 16 queries, 4 K steps of 32 channels (lane
+        // group g4 holds chunk s + 4 g4 of its row, as the B operands)
+        f32x4 sa[2], pa[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            sa[qb] = pa[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int r = 16 * qb + l16;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(qt + k16::off(r, s + 4 * g4));
+                sa[qb] = mfma16(aq, kf[s], sa[qb]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 ao = *reinterpret_cast<const bf16x8 *>(ot + k16::off(r, s + 4 * g4));
+                pa[qb] = mfma16(ao, vf[s], pa[qb]);
+            }
         }
-        // S (first wave) or dP (second wave); element e: query
-        // i0 + 8(e/4) + 4g + e%4, key kj
-        const bf16 *rt = R ? ot : qt;
-        f32x16 mine;
+        f32x4 l2[2], dd[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mine[e] = 0.0f;
-        bf16x8 rows[NF];
+        for (int qb = 0; qb < 2; ++qb) {
+            l2[qb] = *reinterpret_cast<const f32x4 *>(st + 16 * qb + 4 * g4);
+            dd[qb] = *reinterpret_cast<const f32x4 *>(st + 32 + 16 * qb + 4 * g4);
+        }
+        // every (query, key) pair of the wave's block in the band: no mask
+        const bool interior = (i0 >= kw0 + 15) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
+        bf16x8 pf, dsf;
 #pragma unroll
-        for (int s = 0; s < NF; ++s) rows[s] = tile_rows<DH>(rt, 0, s, lane);
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int s = 0; s < NF; ++s) mine = mfma32(rows[s], kvf[s], mine);
-        Stats cur;
-        read_stats(U & 1, cur);
-        // all eight operand reads, then the four statistics reads, are issued
-        // before the first product waits
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NF + 4, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, NF, 0);
-        if constexpr (R == 0) {
-            // every (query, key) pair of this block in the band: no mask
-            const bool interior = (i0 >= kw0 + 31) & (i0 + QT - 1 - kw0 < W) & (i0 + QT - 1 < T);
-            if (interior) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    mine[e] = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
-            } else {
-                // query i is in key kj's band iff 0 <= i - kj < band
-                const int d0 = i0 + 4 * g - kj;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const bool ok = (unsigned)(d0 + 8 * (e >> 2) + (e & 3)) < band;
-                    const float p = fast_exp2(mine[e] * qscale - cur.v[e >> 2][e & 3]);
-                    mine[e] = ok ? p : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                float p = fast_exp2(sa[qb][i] * qscale - l2[qb][i]);
+                if (!interior) {
+                    // query q is in key kj's band iff 0 <= q - kj < band
+                    const bool ok = (unsigned)(i0 + 16 * qb + 4 * g4 + i - kj) < band;
+                    p = ok ? p : 0.0f;
                 }
+                pf[4 * qb + i] = f2bf(p);
+                dsf[4 * qb + i] = f2bf(p * (pa[qb][i] - dd[qb][i]));
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mine[e] -= cur.v[e >> 2][e & 3];
+        if (stored) {
+            bf16 *tile = dso + (((int64_t)bh * nt32 + kt32) * nK + jj) * 1024;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
+            const u32x4 x = __builtin_bit_cast(u32x4, dsf);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x[0], (int)x[1]}, rs, ds_voff, 0, kNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x[2], (int)x[3]}, rs, ds_voff, 32, kNontemporal);
         }
-        constexpr int par = U & 1;
+        // dV^T += dO^T P, dK^T += Q^^T dS: A operand of block cb is column
+        // 16 cb + l16 at queries 4 g4 + 0..3 and 16 + 4 g4 + 0..3 (the order of
+        // the probabilities' entries), from two transposed reads whose lane j
+        // addresses row 4 g4 + j / 4 (+16) at column 16 cb + 4 (j % 4)
+        const int ra = 4 * g4 + (l16 >> 2);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            X[par][pr][R][q4][lane] = f32x4{mine[4 * q4], mine[4 * q4 + 1], mine[4 * q4 + 2], mine[4 * q4 + 3]};
-        // the next tile's stage (issued one iteration ago) lands before the
-        // barrier publishes it; only the last step's four dS stores, issued
-        // after those loads, may still be in flight
-        if (stored) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-
-        // the transposed operands of this tile's eight products, read before
-        // the exchange so that their latency overlaps the dS arithmetic
-        bf16x8 trv[2][2], trq[2][2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int lb = 0; lb < 2; ++lb) {
-                trv[t][lb] = tile_tr<DH>(ot, t, R + 2 * lb, lane);
-                trq[t][lb] = tile_tr<DH>(qt, t, R + 2 * lb, lane);
-            }
-        f32x16 P, dS;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 o = X[par][pr][R ^ 1][q4][lane];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int e = 4 * q4 + u;
-                P[e] = R ? o[u] : mine[e];
-                dS[e] = P[e] * (R ? mine[e] : o[u]);   // P (dP - D)
-            }
+        for (int cb = 0; cb < 8; ++cb) {
+            const int n = 16 * cb + 4 * (l16 & 3);
+            const int c = n >> 3, e = n & 7;
+            const bf16x8 ao = join_tr(lds_read_tr16(ot + k16::off(ra, c) + e),
+                                      lds_read_tr16(ot + k16::off(ra + 16, c) + e));
+            const bf16x8 aq = join_tr(lds_read_tr16(qt + k16::off(ra, c) + e),
+                                      lds_read_tr16(qt + k16::off(ra + 16, c) + e));
+            dva[cb] = mfma16(ao, pf, dva[cb]);
+            dka[cb] = mfma16(aq, dsf, dka[cb]);
         }
-        bf16x8 pf[2], dsf[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            pf[t] = acc_to_operand(P, t);
-            dsf[t] = acc_to_operand(dS, t);
-        }
-        // The next tile's statistics, the tile loads two steps ahead, then
-        // this tile's dS stores, last, so that no wait in the loop waits for a
-        // store: the vector memory counter counts loads and stores in issue
-        // order. dS of this 32 x 32 tile as the dK product takes it (the bf16
-        // operand registers themselves) goes to the dQ pass as [key][query]
-        // tiles of 64-byte rows. Lane l32 holds key kw0 + l32; operand t holds
-        // queries i0 + 16t + 4g + (0..3) and i0 + 16t + 8 + 4g + (0..3), bytes
-        // 32t + 8g and 32t + 16 + 8g of the row: four 8-byte buffer stores
-        // through a per-tile descriptor (uniform registers) and one 32-bit
-        // lane offset, so that they take no registers the loop needs. Only the
-        // pair's first wave stores, and only tiles inside the stored range (not
-        // a query tile before the keys or beyond the window); `stored` (uniform)
-        // tells the waits of the next step how many stores are behind the loads
-        // they wait for.
-        if (it + 1 < nt) dma_stats(it + 1, (U + 1) & 1);
-        if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);   // the stage tile it - 1 used
-        {
-            const int kt = kw0 >> 5, jj = (i0 >> 5) - kt;
-            stored = R == 0 && dso && jj >= 0 && jj < nK;
-            if (stored) {
-                bf16 *tile = dso + (((int64_t)bh * nt32 + kt) * nK + jj) * 1024;
-                const __amdgpu_buffer_rsrc_t rs =
-                    __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
-                const u32x4 a = __builtin_bit_cast(u32x4, dsf[0]);
-                const u32x4 c = __builtin_bit_cast(u32x4, dsf[1]);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[0], (int)a[1]}, rs, ds_voff, 0, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)a[2], (int)a[3]}, rs, ds_voff, 16, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[0], (int)c[1]}, rs, ds_voff, 32, kNontemporal);
-                __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)c[2], (int)c[3]}, rs, ds_voff, 48, kNontemporal);
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int lb = 0; lb < 2; ++lb) {
-                dva[lb] = mfma32(trv[t][lb], pf[t], dva[lb]);
-                dka[lb] = mfma32(trq[t][lb], dsf[t], dka[lb]);
-            }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 20, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, 64, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 1);
     };
-    for (int it = 0; it < nt; it += 2 * ST) unrolled_steps<0, 2 * ST>(it, nt, tile_step);
+    for (int it = 0; it < nt; it += ST) unrolled_steps<0, ST>(it, nt, step);
 
-    // Epilogue: element e of local block lb is channel 32 (R + 2 lb) +
-    // 8(e/4) + 4g + e%4 of key kj.
+    // Epilogue: lane holds key kj, channels 16 cb + 4 g4 + i; dk = scale R^T dK~
+    // (pairs c, c + 64 are blocks cb, cb + 4 of the same lane)
     if (kj < T) {
         const int64_t base = act_row(a, b, kj, h) * DH;
-        const float2 *cs =
-            (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) + 32 * R : nullptr;
-        scale_rotate_pair(dka[0], dka[1], cs, g, a.scale);
+        const float2 *cs = (a.rope && ROTATE) ? a.rope + (a.pos0 + kj) * (DH / 2) : nullptr;
 #pragma unroll
-        for (int lb = 0; lb < 2; ++lb)
+        for (int cb = 0; cb < 4; ++cb) {
+            f32x4 &lo = dka[cb], &hi = dka[cb + 4];
+            if (cs) {
+                const float *t = reinterpret_cast<const float *>(cs + 16 * cb + 4 * g4);
+                const f32x4 t0 = *reinterpret_cast<const f32x4 *>(t);
+                const f32x4 t1 = *reinterpret_cast<const f32x4 *>(t + 4);
+                const float cx[4] = {t0[0], t0[2], t1[0], t1[2]};
+                const float sy[4] = {t0[1], t0[3], t1[1], t1[3]};
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int c = 32 * (R + 2 * lb) + 8 * i4 + 4 * g;
-                bf16x4 k4, v4;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    k4[u] = f2bf(dka[lb][4 * i4 + u]);
-                    v4[u] = f2bf(dva[lb][4 * i4 + u]);
+                for (int i = 0; i < 4; ++i) {
+                    const float x = lo[i] * a.scale, y = hi[i] * a.scale;
+                    lo[i] = x * cx[i] + y * sy[i];
+                    hi[i] = -x * sy[i] + y * cx[i];
                 }
-                *reinterpret_cast<bf16x4 *>(dk + base + c) = k4;
-                *reinterpret_cast<bf16x4 *>(dv + base + c) = v4;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] *= a.scale;
+                    hi[i] *= a.scale;
+                }
             }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+            bf16x4 k4, v4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                k4[i] = f2bf(dka[cb][i]);
+                v4[i] = f2bf(dva[cb][i]);
+            }
+            *reinterpret_cast<bf16x4 *>(dk + base + 16 * cb + 4 * g4) = k4;
+            *reinterpret_cast<bf16x4 *>(dv + base + 16 * cb + 4 * g4) = v4;
+        }
     }
-    };
-    if (hf) run(std::integral_constant<int, 1>{});
-    else run(std::integral_constant<int, 0>{});
 }
 
 // Query-stationary pass: each wave owns 32 queries; key tiles of KT in the
@@ -1371,9 +1291,9 @@ static AttnArgs make_args(const Geom &g, const void *q, const void *qr, const vo
 
 // Tile shapes and pipeline depths: forward and dQ stream K~/V~ tiles of
 // kFwdKT keys through kFwdST stages; dK/dV streams 32-query tiles through
-// kBwdST stages (kPairST in the wave-pair pass used for Dh = 128).
-constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4, kPairST = 3,
-              kDqDsST = 3;
+// kBwdST stages (kK16ST in the 16-keys-a-wave pass used for Dh = 128).
+constexpr int kFwdKT = 32, kFwdST = 2, kDqKT = 32, kDqST = 2, kBwdST = 4, kDqDsST = 3,
+              kK16ST = 3;
 
 void launch_attn_fwd_bf16(const Geom &g, const void *q, const void *kx, const void *vx,
                           const float2 *rope, void *o, float *lse, hipStream_t s)
@@ -1409,12 +1329,12 @@ static void launch_attn_bwd_t(const AttnArgs &a, const bf16 *o, const bf16 *dO, 
             const unsigned npw = (unsigned)(a.B * a.H * ((a.T + 63) / 64));
             bf16 *dso = static_cast<bf16 *>(ws.ds);
             if (entries)
-                hipExtLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, false>), dim3(npw),
+                hipExtLaunchKernelGGL((attn_bwd_dkdv_k16_kernel<kK16ST, false>), dim3(npw),
                                       dim3(256), 0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2,
                                       ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
                                       static_cast<bf16 *>(dv), dso, ws.ds_tiles, ws.nt32);
             else
-                hipExtLaunchKernelGGL((attn_bwd_dkdv_pair_kernel<kPairST, true>), dim3(npw),
+                hipExtLaunchKernelGGL((attn_bwd_dkdv_k16_kernel<kK16ST, true>), dim3(npw),
                                       dim3(256), 0, s, ts.start(), ts.stop(), 0, a, dO, ws.lse2,
                                       ws.Dp, ws.Tp, static_cast<bf16 *>(dk),
                                       static_cast<bf16 *>(dv), dso, ws.ds_tiles, ws.nt32);
