@@ -849,10 +849,14 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
     for (int s0 = 0; s0 < ST - 1; ++s0)
         if (s0 < nt) issue(s0, s0);
 
-    // dS tile of this wave: key row 16 (w % 2) + l16 of 32-key tile kw0 / 32,
-    // bytes 8 g4 (queries 4 g4 .. +3) and 32 + 8 g4 (queries 16 + 4 g4 .. +3)
+    // dS of this wave: half w % 2 (keys 16 (w % 2) .. +15) of the 32-key
+    // tile kw0 / 32, stored in the lanes' own order so that one 16-byte store
+    // a lane writes the half's whole kilobyte: lane 16 g4 + l16 (key l16 of
+    // the half; queries 4 g4 .. +3, then 16 + 4 g4 .. +3) takes 16-byte slot
+    // 16 g4 + (l16 ^ 4 g4) (the XOR keeps the dQ pass's transposed reads of
+    // the tile free of bank conflicts)
     const int kt32 = kw0 >> 5;
-    const int ds_voff = (16 * (w & 1) + l16) * 64 + 8 * g4;
+    const int ds_voff = 1024 * (w & 1) + 16 * (16 * g4 + (l16 ^ (4 * g4)));
     int s1 = 0, s2 = 0;   // dS stores issued in the last and the one before
     auto step = [&](int it, auto u) {
         constexpr int U = decltype(u)::value;
@@ -861,11 +865,11 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
         // (loads and stores complete in issue order)
         switch (s1 + s2 + (it + 1 < nt ? PER : 0)) {
         case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
         case 2: wait_vmcnt<2>(); break;
-        case 4: wait_vmcnt<4>(); break;
         case PER: wait_vmcnt<PER>(); break;
-        case PER + 2: wait_vmcnt<PER + 2>(); break;
-        default: wait_vmcnt<PER + 4>(); break;
+        case PER + 1: wait_vmcnt<PER + 1>(); break;
+        default: wait_vmcnt<PER + 2>(); break;
         }
         __builtin_amdgcn_s_barrier();
         if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);   // the stage tile it-1 used
@@ -877,7 +881,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
         const int jj = (i0 >> 5) - kt32;
         const bool stored = dso && jj >= 0 && jj < nK;
         s2 = s1;
-        s1 = stored ? 2 : 0;
+        s1 = stored ? 1 : 0;
         // S and dP: blocks qb of 16 queries, 4 K steps of 32 channels (lane
         // group g4 holds chunk s + 4 g4 of its row, as the B operands)
         f32x4 sa[2], pa[2];
@@ -922,9 +926,8 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
             bf16 *tile = dso + (((int64_t)bh * nt32 + kt32) * nK + jj) * 1024;
             const __amdgpu_buffer_rsrc_t rs =
                 __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, 2048, kBufferWord3);
-            const u32x4 x = __builtin_bit_cast(u32x4, dsf);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x[0], (int)x[1]}, rs, ds_voff, 0, kNontemporal);
-            __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)x[2], (int)x[3]}, rs, ds_voff, 32, kNontemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsf), rs, ds_voff, 0,
+                                                   kNontemporal);
         }
         // dV^T += dO^T P, dK^T += Q^^T dS: A operand of block cb is column
         // 16 cb + l16 at queries 4 g4 + 0..3 and 16 + 4 g4 + 0..3 (the order of
@@ -1138,10 +1141,11 @@ MAGLEV_DEV bf16x8 tile_tr_nat(const bf16 *t, int tt, int db, int lane)
 // workgroup's band and each wave's own dS tile of the same 32 keys stream
 // through LDS in ST stages. Per tile: dQ^^T += K~^T dS^T (8 products), no
 // scores, no softmax. Epilogue as the recomputing pass: dq = scale R^T dQ^.
-// A dS tile sits in LDS as stored, 32 key rows of 64 bytes; its operand
-// (query column, 8 consecutive keys) comes from transposed reads, whose
-// half-wave passes cover four whole rows, 256 contiguous bytes: every bank
-// once.
+// A dS tile sits in LDS as stored: two halves of 16 keys, each as the dK/dV
+// pass's lanes held it (16-byte slot 16a + (key ^ 4a) holds one key's
+// queries 4a .. 4a+3 and 16 + 4a .. +3). Its operand (query column, 8
+// consecutive keys) comes from transposed reads of those 8-byte query runs;
+// the XOR puts the 16 runs a lane group reads in 16 different bank groups.
 template <int ST>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, const bf16 *ds, int nK,
                                                                  int nt32, bf16 *dq)
@@ -1242,11 +1246,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(AttnArgs a, cons
         bf16x8 ktr[NB][2], dsf[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            // keys 16t + 8g + (0..3) and (4..7) of query column l32
-            const int j = lane & 15;
-            const bf16 *p = ds_lds + (16 * t + 8 * g + (j >> 2)) * 32 + 16 * ((lane >> 4) & 1) +
-                            4 * (j & 3);
-            dsf[t] = join_tr(lds_read_tr16(p), lds_read_tr16(p + 4 * 32));
+            // keys 16t + 8g + (0..3) and (4..7) of query column l32. Half t of
+            // the tile holds key kk of the half and queries 4a .. 4a+3 (and
+            // 16 + 4a .. +3) in 16-byte slot 16a + (kk ^ 4a); lane j of a
+            // group of 16 addresses key 8g + j/4 (+4) of queries 4(j%4) .. +3,
+            // the half of the slot that holds query block (lane / 16) % 2.
+            const int j = lane & 15, qa = j & 3, kk = 8 * g + (j >> 2);
+            const bf16 *p = ds_lds + 512 * t + 4 * ((lane >> 4) & 1);
+            dsf[t] = join_tr(lds_read_tr16(p + 8 * (16 * qa + (kk ^ (4 * qa)))),
+                             lds_read_tr16(p + 8 * (16 * qa + ((kk + 4) ^ (4 * qa)))));
 #pragma unroll
             for (int db = 0; db < NB; ++db) ktr[db][t] = tile_tr_nat(kt_lds, t, db, lane);
         }
