@@ -724,8 +724,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(AttnArgs a, const bf
 // band, dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^^T dS with the
 // probabilities' query order matched by the transposed reads (lane l of the
 // result: key l % 16, channels 16 cb + 4 (l / 16) + i). dS, rounded to bf16 as
-// the dK product takes it, is stored for the dQ pass as [key][query] tiles of
-// 32 keys x 32 queries (64-byte rows; a wave writes its 16 key rows).
+// the dK product takes it, is stored for the dQ pass in tiles of 32 keys x
+// 32 queries (2 KB; a wave writes the kilobyte of its 16 keys in its own lane
+// order, one 16-byte store a lane).
 namespace k16 {
 // Swizzle of the Q^ / dO tiles: chunk c of row r sits in slot c ^ swz(r),
 // with bits 2-3 of swz from r mod 4 and bits 0-1 a bijection of (r / 4) mod 4
