@@ -277,9 +277,11 @@ MAGLEV_DEV void unrolled_steps(int it, int nt, F &f)
 // head) that share a key tile (five at W = 512) then read it at about the
 // same step, while it is still in L2, instead of one after another as each
 // sweeps its own band from its start: the six (sequence, head) pairs resident
-// on one XCD hold 6 MB of K~/V~, more than its 4 MB L2. (The dK/dV and dQ
-// passes keep the plain order: their resident tiles fit in L2 and the
-// rotation did not change their time.)
+// on one XCD hold 6 MB of K~/V~, more than its 4 MB L2. The dK/dV pass for
+// Dh = 128 sweeps its query tiles the same way (three workgroups a CU keep
+// three pairs' Q^ / dO resident per XCD; the rotation took its fetched bytes
+// from 283 to 215 MB a launch at d20, its time unchanged). The dQ pass keeps
+// the plain order: its resident K~ tiles fit in L2.
 struct TileSweep {
     int nt, phase;
     MAGLEV_DEV TileSweep(int first, int nt_, int ts) : nt(nt_)
@@ -779,6 +781,10 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
     // queries kj .. kj + band - 1 see key kj: band = min(W, T - kj), 0 past T
     const unsigned band = kj < T ? (unsigned)(W < T - kj ? W : T - kj) : 0u;
     const int nt = (qend - j0 + QT - 1) / QT;
+    // step it takes the query tile whose absolute index is congruent to it
+    // modulo nt, so that the workgroups sharing a tile read it at about the
+    // same step (the sums over tiles are order-free)
+    const TileSweep sweep(j0, nt, QT);
 
     // This lane's key row of K~ and of V~ as B operands: fragment s holds
     // chunk s + 4 (lane / 16), channels 8 s + 32 (lane / 16) .. +7 (the order
@@ -811,7 +817,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
     }
     const float *ssrc = lane < 32 ? lrow + lane : drow + (lane - 32);
     auto issue = [&](int it, int buf) {
-        const int i0 = j0 + it * QT;
+        const int i0 = j0 + sweep.rel(it) * QT;
         bf16 *qt = lds + buf * k16::SE, *ot = qt + k16::TE;
         float *st = reinterpret_cast<float *>(ot + k16::TE) + 64 * w;
         if (i0 + QT <= T) {
@@ -874,7 +880,7 @@ __global__ __launch_bounds__(256, 3) void attn_bwd_dkdv_k16_kernel(AttnArgs a, c
         }
         __builtin_amdgcn_s_barrier();
         if (it + ST - 1 < nt) issue(it + ST - 1, (U + ST - 1) % ST);   // the stage tile it-1 used
-        const int i0 = j0 + it * QT;
+        const int i0 = j0 + sweep.rel(it) * QT;
         const bf16 *qt = lds + U * k16::SE, *ot = qt + k16::TE;
         const float *st = reinterpret_cast<const float *>(ot + k16::TE) + 64 * w;
         // dS for the dQ pass, for the query tiles it reads (the first at the
